@@ -1,0 +1,78 @@
+"""The oracle's pins are not vacuous: each plausible mistake, planted in a
+copy of the oracle's C source and compiled on the CPU, fails at least one pin.
+
+Every mutation is an in-bounds change (no planted mistake can read or write
+outside its arrays), so a mutant can fail but cannot crash the test process.
+"""
+
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = open(oracle.SRC).read()
+
+# (name, text in mnb_oracle.c, replacement)
+MUTANTS = [
+    ("pack_nibble_order_swapped",
+     "if (k % 2 == 0)\n                packed[byte] |= v;",
+     "if (k % 2 == 1)\n                packed[byte] |= v;"),
+    ("unpack_nibble_order_swapped",
+     "q[n * K + k] = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
+     "q[n * K + k] = (k % 2 == 1) ? (byte & 0x0F) : (byte >> 4);"),
+    ("zero_point_nibble_order_swapped",
+     "zp[n * nb + b] = (b % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
+     "zp[n * nb + b] = (b % 2 == 1) ? (byte & 0x0F) : (byte >> 4);"),
+    ("zero_point_pack_swapped",
+     "if (b % 2 == 0)\n                packed[n * row + b / 2] |= v;",
+     "if (b % 2 == 1)\n                packed[n * row + b / 2] |= v;"),
+    ("default_zero_point_7", "zp ? zp[n * nb + b] : 8;", "zp ? zp[n * nb + b] : 7;"),
+    ("zero_point_dropped", "(double)((int)q[n * K + k] - zero)",
+     "(double)((int)q[n * K + k])"),
+    ("block_index_halved", "int64_t b = k / bs;", "int64_t b = k / bs / 2;"),
+    ("sign_flipped_sum", "acc += p;", "acc -= p;"),
+    ("bias_dropped", "acc += (double)bias[n];", "acc += 0.0;"),
+    ("scale_index_transposed", "load_value(act_dtype, scales, n * nb + b)",
+     "load_value(act_dtype, scales, b * N + n)"),
+    ("tolerance_sum_without_abs", "mag += fabs(p);", "mag += p;"),
+    ("bf16_ties_away", "double r = nearbyint(ldexp(ax, -quantum));",
+     "double r = round(ldexp(ax, -quantum));"),
+    ("bf16_truncates", "double r = nearbyint(ldexp(ax, -quantum));",
+     "double r = floor(ldexp(ax, -quantum));"),
+    ("bf16_one_bit_short", "int quantum = e - 8;", "int quantum = e - 7;"),
+    ("pad_nibbles_not_cleared", "memset(packed, 0, (size_t)(N * col_bytes));",
+     "memset(packed, 0x80, (size_t)(N * col_bytes));"),
+    ("dequant_int_zero_point_dropped",
+     "(int8_t)((int)q[n * K + k] - (zp ? zp[n * nb + k / bs] : 8))",
+     "(int8_t)((int)q[n * K + k] - (zp ? 8 : 8))"),
+    ("f32_rounding_toward_zero", "out[i] = (float)x[i]; /* one RTNE rounding */",
+     "out[i] = nextafterf((float)x[i], 0.0f); /* one RTNE rounding */"),
+    ("dequant_scale_from_wrong_block", "double s = load_value(scale_dtype, scales, n * nb + b);",
+     "double s = load_value(scale_dtype, scales, n * nb + (b == 0 ? 0 : b - 1));"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    assert SRC.count(old) >= 1, f"mutation site for {name} not found in source"
+    src = tmp_path / f"{name}.c"
+    src.write_text(SRC.replace(old, new))
+    lib = oracle.build(str(src), str(tmp_path / f"lib{name}.so"))
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} survived every pin"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    src = tmp_path / "copy.c"
+    src.write_text(SRC)
+    orc = oracle.Oracle(oracle.build(str(src), str(tmp_path / "libcopy.so")))
+    for pin in ALL_PINS:
+        pin(orc)
