@@ -1,0 +1,248 @@
+"""Benchmark of the weight-only block-INT4 MatMul on one MI355X.
+
+Headline workload: the Qwen3-0.6B-shaped INT4 decode step (M = 1, fp32
+activations, block 32, per-block zero points): 28 layers x {fused QKV
+1024->4096, o 2048->1024, gate||up 1024->6144, down 3072->1024} + LM head
+1024->151936 = 113 launches over 381,802,496 bytes of packed weights, scales
+and zero points.  One step = that whole sequence, replayed as one captured HIP
+graph on one stream; inputs are seeded synthetic tensors already resident in
+HBM.  value = packed-weight bytes per step / step time (GB/s).
+
+Also printed in the same JSON line (``extra``): the Qwen3-4B decode step and
+the two prefill steps (TFLOP/s), and the eager (non-graph) decode step time.
+
+roofline: the dominant kernel of the headline step is the decode GEMV; its
+algorithmic bytes (packed weights + scales + zero points of every launch) are
+divided by its launch durations measured with HIP events around each launch
+on the launch stream.  cpu_baseline: the CPU oracle timed on the host cores
+on a bounded sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak, TFLOP/s
+METRIC = "INT4 GEMV weight GB/s (% HBM peak) at M=1; prefill TFLOP/s (% MFMA peak)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_steps(step, steps, warmup, graph):
+    import torch
+    run = step.replay if graph else step.run
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def per_launch_durations(step, reps):
+    """Average duration (ms) of every launch of the step, each bracketed by
+    its own pair of events on the launch stream."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in step.items]
+    tot = [0.0] * len(step.items)
+    for _ in range(reps):
+        for (pw, a, y), (s, e) in zip(step.items, ev):
+            s.record()
+            pw.matmul(a, out=y)
+            e.record()
+        torch.cuda.synchronize()
+        for i, (s, e) in enumerate(ev):
+            tot[i] += s.elapsed_time(e)
+    return [t / reps for t in tot]
+
+
+def cpu_baseline(cfg, budget_s):
+    """The oracle (as it is) on the host cores: launches of the step in order
+    until the time budget is used; returns a dict in the metric's unit."""
+    import oracle
+    from workloads import workload
+    from workloads.generate import projection_inputs
+    import numpy as np
+    import torch
+
+    w = workload(cfg)
+    orc = oracle.get()
+    cores = len(os.sched_getaffinity(0))
+    done_bytes = done_flops = 0
+    spent = 0.0
+    names = []
+    rows = w.M if w.M == 1 else 2
+    for i, L in enumerate(w.launches):
+        inp = projection_inputs(w, i, 0, "cpu")
+        a = inp.a[:rows]
+        act = (a.numpy() if w.act_dtype == "f32"
+               else a.view(torch.int16).numpy().view(np.uint16))
+        sc = (inp.scales.numpy() if w.act_dtype == "f32"
+              else inp.scales.view(torch.int16).numpy().view(np.uint16))
+        t0 = time.perf_counter()
+        orc.matmul(act, inp.q.numpy(), None if inp.zp is None else inp.zp.numpy(), sc,
+                   w.block_size, bias=None if inp.bias is None else inp.bias.numpy(),
+                   nthreads=cores)
+        spent += time.perf_counter() - t0
+        done_bytes += w.weight_bytes(L)
+        done_flops += 2 * rows * L.K * L.N
+        names.append(L.name)
+        if spent >= budget_s:
+            break
+    if w.M == 1:
+        val, unit = done_bytes / spent / 1e9, "GB/s"
+        sample = (f"{len(names)} of {len(w.launches)} launches of the step "
+                  f"({names[0]}..{names[-1]}), full columns, M=1")
+    else:
+        val, unit = done_flops / spent / 1e12, "TFLOP/s"
+        sample = (f"{len(names)} launches ({names[0]}..{names[-1]}), "
+                  f"{rows} of {w.M} rows")
+    return {"value": val, "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds": round(spent, 2)}
+
+
+def measure_config(cfg, steps, warmup, graph=True, launch_reps=5):
+    import torch
+    from weight_only_int4_matmulnbits_amd.step import Step
+    from workloads import workload
+
+    w = workload(cfg)
+    log(f"[bench] config {cfg}: {w.title}: building ({len(w.launches)} launches)")
+    step = Step(w, "cuda", seed=0)
+    step.run()
+    torch.cuda.synchronize()
+    if graph:
+        step.capture()
+    ms, wall = time_steps(step, steps, warmup, graph)
+    log(f"[bench] config {cfg}: {ms:.4f} ms/step (graph={graph})")
+    durs = per_launch_durations(step, launch_reps)
+    out = {"ms_per_step": ms, "wall_ms_per_step": wall, "launches": step.launches,
+           "weight_bytes": step.weight_bytes, "flops": w.step_flops(),
+           "pack_ms": step.pack_seconds * 1e3, "sum_launch_ms": sum(durs),
+           "launch_ms": durs}
+    if w.M == 1:
+        ms_eager, _ = time_steps(step, steps, warmup, False)
+        out["eager_ms_per_step"] = ms_eager
+    step.close()
+    del step
+    torch.cuda.empty_cache()
+    return w, out
+
+
+def roofline_for(w, r):
+    if w.M == 1:
+        achieved = r["weight_bytes"] / (r["sum_launch_ms"] * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "gemv_kernel (all launches of the step)",
+                "bytes_per_launch": r["weight_bytes"] / r["launches"],
+                "avg_launch_us": r["sum_launch_ms"] * 1e3 / r["launches"]}
+    achieved = r["flops"] / (r["sum_launch_ms"] * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+            "kernel": "gemm_kernel (all launches of the step)",
+            "flops_per_launch": r["flops"] / r["launches"],
+            "avg_launch_us": r["sum_launch_ms"] * 1e3 / r["launches"]}
+
+
+def summary(w, r):
+    s = {"workload": w.title, "ms_per_step": round(r["ms_per_step"], 5),
+         "launches": r["launches"]}
+    if w.M == 1:
+        s["weight_GBps"] = r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+        s["hbm_frac"] = s["weight_GBps"] / HBM_PEAK_GBS
+        s["eager_ms_per_step"] = round(r["eager_ms_per_step"], 5)
+    else:
+        s["TFLOPs"] = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
+        s["mfma_frac"] = s["TFLOPs"] / BF16_PEAK_TFLOPS
+    rf = roofline_for(w, r)
+    s["kernel_" + rf["unit"].replace("/", "p")] = rf["achieved"]
+    s["kernel_frac"] = rf["frac"]
+    return s
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-extra", action="store_true", help="headline config only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (the path has no multi-GPU sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    w, r = measure_config(args.config, args.steps, args.warmup)
+    dec = w.M == 1
+    value = (r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 if dec
+             else r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12)
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GB/s" if dec else "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.act_dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.title, "config_index": args.config, "M": w.M,
+                   "block_size": w.block_size, "launches": r["launches"],
+                   "projections": w.n_projections, "weight_bytes": r["weight_bytes"],
+                   "flops": r["flops"], "graph_replay": True},
+        "roofline": roofline_for(w, r),
+    }
+    line["roofline"].pop("launch_ms", None)
+    line["pack_ms"] = r["pack_ms"]
+    if dec:
+        line["eager_ms_per_step"] = r["eager_ms_per_step"]
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_budget)
+    if not args.no_extra:
+        extra = {}
+        for c in (4, 3, 5):
+            if c == args.config:
+                continue
+            st = max(3, args.steps // (10 if c == 5 else 2))
+            wc, rc = measure_config(c, st, max(2, args.warmup // 2))
+            extra[f"config{c}"] = summary(wc, rc)
+        line["extra"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * mnb.h -- C ABI of libmnb, a weight-only block-INT4 MatMul for AMD MI355X
+ * (gfx950), following the com.microsoft::MatMulNBits contract.
+ *
+ *   Y[M][N] = A[M][K] x dequant(B)[K][N] (+ bias[N])
+ *   dequant(B)[k][n] = (q[n][k] - zp[n][k / block_size]) * scale[n][k / block_size]
+ *
+ * Sources (page "Qwen3 CPU Inference Critical Path"):
+ *   "Exact kernel inventory", com.microsoft::MatMulNBits v1 row -- FP32
+ *     activations, packed UINT8 storage of 4-bit weights, FP32 scales,
+ *     block_size 32; weights stay compressed; GEMV decode and GEMM prefill.
+ *   "INT4 MatMul is first", "Prepared weight-only plan" -- the plan captures
+ *     K, N, nibble order, signedness, block size, tails, per-block scales and
+ *     optional zero points, and packed storage aligned for the kernel; decode
+ *     kernels unpack in registers, apply zero point and scale, accumulate in
+ *     float32, and never expand the whole matrix.
+ *   "INT4 MatMul is first", int4_gemv / int4_gemm -- decode (M == 1) and
+ *     prefill are separate algorithms.
+ *   "Export contract", qwen3-int4-qdq -- UINT4 stored low nibble first, one
+ *     scale and zero point per block along K; BF16 activations and scales.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every tensor argument is a DEVICE pointer (memory of the current
+ *           HIP device), row-major and contiguous, allocated and owned by the
+ *           caller.  The library never allocates device memory, never frees,
+ *           and keeps no pointer after a call returns (graph handles, below,
+ *           are the one documented exception: they record the pointers given
+ *           at creation).
+ * Ordering. Work is enqueued on `stream` (a hipStream_t passed as void*;
+ *           NULL is the null stream) and the call returns once it is
+ *           enqueued.  Results are valid after the stream is synchronized.
+ * Errors.   Every call returns an mnb_status.  Arguments are validated on the
+ *           host BEFORE any HIP call, so validation errors are reported even
+ *           on a machine without a GPU and leave every buffer untouched.  A
+ *           kernel-launch failure returns MNB_E_HIP; faults inside a kernel
+ *           surface at the caller's next synchronization.  After any error the
+ *           output buffers are undefined.  No call aborts the process or
+ *           throws across the ABI.  mnb_last_error() gives a human-readable
+ *           detail of the most recent error on the calling thread.
+ * Threads.  Calls are reentrant; concurrent calls on different streams are
+ *           safe.
+ *
+ * Data layouts (N-major: every column of B is one contiguous run of bytes)
+ * ------------------------------------------------------------------------
+ *   nb           = ceil(K / block_size)
+ *   q (logical)  uint8 [N][K], values 0..15 (bits above the low nibble are
+ *                ignored)
+ *   B (packed)   uint8 [N][nb][block_size/2].  Value k of column n is in byte
+ *                n*nb*(block_size/2) + k/2, low nibble for even k, high
+ *                nibble for odd k; nibbles past K in the last, partial block
+ *                are written as 0 by mnb_pack and never affect results.
+ *   zp (logical) uint8 [N][nb], values 0..15
+ *   zp (packed)  uint8 [N][ceil(nb/2)].  Block b of column n is in byte
+ *                n*ceil(nb/2) + b/2, low nibble for even b; when absent every
+ *                zero point is 8.
+ *   scales       [N][nb] in the activation dtype (float32 or bfloat16).
+ *   A            [M][K] float32 or bfloat16;  Y [M][N] in the same dtype.
+ *   bias         float32 [N], optional, added after the K reduction and
+ *                before the output is rounded.
+ * bfloat16 values are raw 16-bit patterns; float32 -> bfloat16 output rounding
+ * is round-to-nearest-even.
+ */
+#ifndef MNB_H
+#define MNB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mnb_status {
+    MNB_OK = 0,
+    MNB_E_ARG = -1,          /* null pointer, bad shape, M out of range      */
+    MNB_E_UNSUPPORTED = -2,  /* bits != 4, block size, dtype, reserved != 0  */
+    MNB_E_ALIGN = -3,        /* a pointer violates its alignment rule        */
+    MNB_E_OVERFLOW = -4,     /* a size does not fit the index arithmetic     */
+    MNB_E_HIP = -5           /* the HIP runtime reported an error            */
+} mnb_status;
+
+typedef enum mnb_dtype { MNB_F32 = 0, MNB_BF16 = 1 } mnb_dtype;
+
+/* The prepared-plan description ("Prepared weight-only plan": logical K and
+ * N, block size, signedness and nibble order are fixed by this ABI: unsigned
+ * 4-bit, low nibble first). */
+typedef struct mnb_desc {
+    int64_t K;               /* reduction length, >= 1                        */
+    int64_t N;               /* output columns, >= 1                          */
+    int32_t bits;            /* must be 4                                     */
+    int32_t block_size;      /* 16, 32, 64, 128 or 256                        */
+    int32_t act_dtype;       /* mnb_dtype of A, scales and Y                  */
+    int32_t has_zero_points; /* 0: every zero point is 8                      */
+    int32_t accuracy_level;  /* MatMulNBits attribute; recorded, never lowers
+                                the precision of any computation              */
+    int32_t reserved;        /* must be 0                                     */
+} mnb_desc;
+
+/* Checks `d` (and M >= 1) on the host; no HIP call.  MNB_OK or an error. */
+int mnb_validate(const mnb_desc* d, int64_t M);
+
+/* Buffer sizes in bytes for a valid descriptor; 0 when `d` is invalid or a
+ * size overflows.  Packed weights: N*nb*block_size/2.  Scales: N*nb*(4 or 2).
+ * Packed zero points: N*ceil(nb/2) when has_zero_points, else 0. */
+size_t mnb_packed_weight_bytes(const mnb_desc* d);
+size_t mnb_scale_bytes(const mnb_desc* d);
+size_t mnb_zero_point_bytes(const mnb_desc* d);
+
+/* Largest K that mnb_gemv serves with its register-resident decode kernel
+ * for this descriptor's block size; larger K is served, with the same
+ * results contract, by the tiled prefill kernel at M = 1. */
+int64_t mnb_gemv_max_k(const mnb_desc* d);
+
+/* mnb_pack -- the preparation step ("Prepared weight-only plan": packed
+ * constant storage aligned for the kernel; first-use packing time).
+ *   q_nk        uint8 [N][K] logical weights (device).
+ *   zp_nb       uint8 [N][nb] logical zero points (device); must be NULL iff
+ *               d->has_zero_points == 0.
+ *   b_packed    out, mnb_packed_weight_bytes(d) bytes, 16-byte aligned.
+ *   zp_packed   out, mnb_zero_point_bytes(d) bytes; NULL iff no zero points.
+ * Pad nibbles are written as 0.  The call writes every byte of both outputs. */
+int mnb_pack(const mnb_desc* d, const uint8_t* q_nk, const uint8_t* zp_nb,
+             uint8_t* b_packed, uint8_t* zp_packed, void* stream);
+
+/* mnb_gemv -- decode, M == 1 ("int4_gemv": output columns partitioned so
+ * each weight byte is streamed once; unpack in registers; float32
+ * accumulation).
+ *   a           [1][K] act_dtype, 16-byte aligned.
+ *   b_packed    packed weights, 16-byte aligned.
+ *   scales      [N][nb] act_dtype, aligned to its element size.
+ *   zp_packed   packed zero points or NULL (iff !has_zero_points).
+ *   bias        float32 [N] or NULL.
+ *   y           [1][N] act_dtype, aligned to its element size.
+ * M must be 1 (MNB_E_ARG otherwise).  For a given (K, block_size) the
+ * float32 summation order of a column does not depend on N or on the
+ * column's position, so a launch over concatenated weights (fused QKV,
+ * gate||up) is bit-identical to separate launches. */
+int mnb_gemv(const mnb_desc* d, int64_t M, const void* a,
+             const uint8_t* b_packed, const void* scales,
+             const uint8_t* zp_packed, const float* bias, void* y,
+             void* stream);
+
+/* mnb_gemm -- prefill, any M >= 1 ("int4_gemm": activation panels and
+ * weight blocks reused on chip).  Same arguments as mnb_gemv with A [M][K]
+ * and Y [M][N]; `a` and `b_packed` 16-byte aligned.  Weight tiles are
+ * unpacked on chip to exact bfloat16 integers (q - zp); products run on the
+ * bf16 matrix cores with float32 accumulation; the per-block scale is applied
+ * to the float32 partial sums.  float32 activations are split into two
+ * bfloat16 terms (hi + lo) so results stay within float32 tolerance. */
+int mnb_gemm(const mnb_desc* d, int64_t M, const void* a,
+             const uint8_t* b_packed, const void* scales,
+             const uint8_t* zp_packed, const float* bias, void* y,
+             void* stream);
+
+/* mnb_dequant -- test hook: writes the dequantized weights w[N][K] (the
+ * transposed logical B) so they can be compared bit-for-bit.
+ *   out_kind 0: float32, one round-to-nearest-even rounding of (q-zp)*scale;
+ *   out_kind 1: bfloat16, one round-to-nearest-even rounding of the exact
+ *               (q-zp)*scale;
+ *   out_kind 2: int8, the exact integer q - zp (what the prefill kernel
+ *               places in its bf16 weight tiles).
+ *   w_nk        [N][K] of the chosen type. */
+int mnb_dequant(const mnb_desc* d, const uint8_t* b_packed, const void* scales,
+                const uint8_t* zp_packed, int32_t out_kind, void* w_nk,
+                void* stream);
+
+/* ---- decode-step driver ------------------------------------------------------
+ * One projection of a step: mnb_gemv when M == 1 and K <= mnb_gemv_max_k,
+ * mnb_gemm otherwise.  A fused QKV or gate||up projection is one entry whose
+ * weights are concatenated along N. */
+typedef struct mnb_matmul_args {
+    mnb_desc desc;
+    int64_t M;
+    const void* a;
+    const uint8_t* b_packed;
+    const void* scales;
+    const uint8_t* zp_packed;
+    const float* bias;
+    void* y;
+} mnb_matmul_args;
+
+/* Validates every entry first (nothing is launched if one is invalid; the
+ * error detail names the entry), then enqueues them in order on `stream`. */
+int mnb_matmul_sequence(const mnb_matmul_args* ops, int64_t n_ops,
+                        void* stream);
+
+/* A captured HIP graph of a sequence, replayed with one launch.  The handle
+ * records the pointers in `ops`; the caller keeps those buffers alive until
+ * mnb_graph_destroy.  Creation captures on a private stream of default
+ * priority and launches nothing on the device. */
+typedef struct mnb_graph mnb_graph;
+int mnb_graph_create(const mnb_matmul_args* ops, int64_t n_ops,
+                     mnb_graph** out);
+int mnb_graph_launch(mnb_graph* g, void* stream);
+int mnb_graph_destroy(mnb_graph* g);
+
+/* Text for a status code (static storage). */
+const char* mnb_status_string(int status);
+/* Detail of the most recent error on the calling thread ("" if none). */
+const char* mnb_last_error(void);
+/* Library version string. */
+const char* mnb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MNB_H */

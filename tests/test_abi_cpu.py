@@ -1,0 +1,160 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+symbol include/mnb.h declares, and rejects every invalid call on the host
+before any HIP call (so no call here reaches a kernel)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_only_int4_matmulnbits_amd as mnb
+from weight_only_int4_matmulnbits_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "mnb.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mnb_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = mnb.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert mnb.version().startswith("mnb")
+
+
+def test_sizes():
+    d = mnb.make_desc(1024, 3072, 32)
+    assert mnb.packed_weight_bytes(d) == 3072 * 1024 // 2
+    assert mnb.scale_bytes(d) == 3072 * 32 * 4
+    assert mnb.zero_point_bytes(d) == 0
+    d = mnb.make_desc(2560, 151936, 128, has_zero_points=True)
+    assert mnb.packed_weight_bytes(d) == 151936 * 20 * 64
+    assert mnb.zero_point_bytes(d) == 151936 * 10
+    d = mnb.make_desc(20, 3, 16, has_zero_points=True)   # partial block, odd nb
+    assert mnb.packed_weight_bytes(d) == 3 * 2 * 8
+    assert mnb.zero_point_bytes(d) == 3 * 1
+    d = mnb.make_desc(100, 5, 64, act_dtype=__import__("torch").bfloat16)
+    assert mnb.scale_bytes(d) == 5 * 2 * 2
+    # the memory gate on the page "Qwen3 CPU Inference Critical Path"
+    # ("Benchmark gates", INT4 memory: packed <= 1.25x serialized): the packed
+    # layout IS the serialized MatMulNBits layout, i.e. exactly 1.00x
+    for K, N, bs in [(1024, 3072, 32), (9728, 2560, 128), (1000, 7, 16)]:
+        d = mnb.make_desc(K, N, bs, has_zero_points=True)
+        nb = -(-K // bs)
+        serialized = N * nb * bs // 2 + N * nb * 4 + N * (-(-nb // 2))
+        got = mnb.packed_weight_bytes(d) + mnb.scale_bytes(d) + mnb.zero_point_bytes(d)
+        assert got == serialized
+
+
+def _status(desc, M=1):
+    return mnb.lib().mnb_validate(ctypes.byref(desc), M)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("bits", 8, -2), ("bits", 2, -2), ("block_size", 24, -2), ("block_size", 8, -2),
+    ("block_size", 512, -2), ("act_dtype", 2, -2), ("reserved", 1, -2),
+    ("K", 0, -1), ("N", 0, -1), ("K", -5, -1), ("has_zero_points", 2, -1),
+    ("accuracy_level", 5, -1), ("K", 1 << 31, -4), ("N", 1 << 40, -4),
+])
+def test_validate_rejects(field, value, status):
+    d = mnb.make_desc(64, 8, 32)
+    setattr(d, field, value)
+    assert _status(d) == status
+    assert mnb.lib().mnb_last_error().decode()
+
+
+def test_validate_accepts_contract():
+    for bs in (16, 32, 64, 128, 256):
+        for al in range(5):
+            assert _status(mnb.make_desc(1, 1, bs, accuracy_level=al)) == 0
+    assert _status(mnb.make_desc(64, 8, 32), M=0) == -1
+
+
+def test_sizes_of_invalid_desc_are_zero():
+    d = mnb.make_desc(64, 8, 24)
+    assert mnb.packed_weight_bytes(d) == 0 and mnb.scale_bytes(d) == 0
+
+
+P16 = 0x10000          # fake, never dereferenced: each call below fails validation
+P_MIS = 0x10008        # 8-byte aligned only
+
+
+def _gemv(d, M=1, a=P16, b=P16, s=P16, zp=None, bias=None, y=P16, fn="mnb_gemv"):
+    f = getattr(mnb.lib(), fn)
+    return f(ctypes.byref(d), M, a, b, s, zp, bias, y, None)
+
+
+@pytest.mark.parametrize("fn", ["mnb_gemv", "mnb_gemm"])
+def test_matmul_argument_errors(fn):
+    d = mnb.make_desc(64, 8, 32)
+    dz = mnb.make_desc(64, 8, 32, has_zero_points=True)
+    assert _gemv(d, a=None, fn=fn) == -1
+    assert _gemv(d, y=None, fn=fn) == -1
+    assert _gemv(d, s=None, fn=fn) == -1
+    assert _gemv(d, zp=P16, fn=fn) == -1          # zp given without has_zero_points
+    assert _gemv(dz, zp=None, fn=fn) == -1        # has_zero_points without zp
+    assert _gemv(d, a=P_MIS, fn=fn) == -3
+    assert _gemv(d, b=P_MIS, fn=fn) == -3
+    assert _gemv(d, y=0x10002, fn=fn) == -3       # f32 output needs 4-byte alignment
+    assert _gemv(d, bias=0x10002, fn=fn) == -3
+    assert _gemv(d, M=0, fn=fn) == -1
+    bad = mnb.make_desc(64, 8, 32)
+    bad.bits = 3
+    assert _gemv(bad, fn=fn) == -2
+    assert "bits" in mnb.lib().mnb_last_error().decode()
+
+
+def test_gemv_requires_single_row():
+    d = mnb.make_desc(64, 8, 32)
+    assert _gemv(d, M=2) == -1
+    assert "M == 1" in mnb.lib().mnb_last_error().decode()
+    assert _gemv(d, M=(65535 * 128) + 1, fn="mnb_gemm") == -4
+
+
+def test_pack_and_dequant_argument_errors():
+    L = mnb.lib()
+    d = mnb.make_desc(64, 8, 32)
+    dz = mnb.make_desc(64, 8, 32, has_zero_points=True)
+    assert L.mnb_pack(ctypes.byref(d), None, None, P16, None, None) == -1
+    assert L.mnb_pack(ctypes.byref(d), P16, None, P_MIS, None, None) == -3
+    assert L.mnb_pack(ctypes.byref(dz), P16, None, P16, None, None) == -1
+    assert L.mnb_pack(ctypes.byref(d), P16, P16, P16, P16, None) == -1
+    assert L.mnb_dequant(ctypes.byref(d), P16, P16, None, 3, P16, None) == -1
+    assert L.mnb_dequant(ctypes.byref(d), P16, None, None, 0, P16, None) == -1
+    assert L.mnb_dequant(ctypes.byref(d), P16, P16, None, 0, 0x10002, None) == -3
+
+
+def test_sequence_validates_every_entry_before_launching():
+    L = mnb.lib()
+    good = _lib.MatmulArgs(desc=mnb.make_desc(64, 8, 32), M=1, a=P16, b_packed=P16,
+                           scales=P16, zp_packed=None, bias=None, y=P16)
+    bad = _lib.MatmulArgs(desc=mnb.make_desc(64, 8, 24), M=1, a=P16, b_packed=P16,
+                          scales=P16, zp_packed=None, bias=None, y=P16)
+    arr = (_lib.MatmulArgs * 2)(good, bad)
+    # the invalid second entry stops the call before the first is launched
+    assert L.mnb_matmul_sequence(arr, 2, None) == -2
+    assert "entry 1" in L.mnb_last_error().decode()
+    g = ctypes.c_void_p()
+    assert L.mnb_graph_create(arr, 2, ctypes.byref(g)) == -2
+    assert not g.value
+    assert L.mnb_graph_create(arr, 2, None) == -1
+    assert L.mnb_graph_launch(None, None) == -1
+    assert L.mnb_graph_destroy(None) == 0
+    assert L.mnb_matmul_sequence(arr, -1, None) == -1
+
+
+def test_status_strings():
+    L = mnb.lib()
+    for s in (0, -1, -2, -3, -4, -5):
+        assert L.mnb_status_string(s).decode().startswith("MNB_")
+    assert b"unknown" in L.mnb_status_string(42)

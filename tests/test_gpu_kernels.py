@@ -1,0 +1,297 @@
+"""GPU parity of every kernel against the CPU oracle, through the C ABI.
+
+Bit-exact: packed bytes, dequantized weights (f32, bf16, the integer tile),
+exact-arithmetic cases, identity / one-hot, fusion and permutation, pad
+contents, default zero point, run-to-run determinism.  Within tolerance: GEMV
+and GEMM sweeps over ragged K, N and M, every block size, with and without
+zero points and bias, float32 and bfloat16.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import weight_only_int4_matmulnbits_amd as mnb
+from parity import act_np, assert_close, log, oracle_ref, out_f64
+from workloads.generate import random_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(K, N, M, bs, dt, zp, bias, seed):
+    inp = random_inputs(K, N, M, bs, dt, zp, bias, seed=seed)
+    return inp, inp.to(DEV)
+
+
+def _packed(g, bs):
+    return mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, g.bias, block_size=bs)
+
+
+# ---------------------------------------------------------------------------
+# pack and dequant: bit-exact
+# ---------------------------------------------------------------------------
+
+PACK_K = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 127, 128, 129, 255, 256, 257, 1000]
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
+def test_pack_bytes_match_oracle(orc, bs):
+    for K, N, zp in itertools.product(PACK_K, [1, 2, 3, 65], [False, True]):
+        log(f"pack bs={bs} K={K} N={N} zp={zp}")
+        inp, g = _inputs(K, N, 1, bs, "f32", zp, False, seed=K * 7 + N)
+        b, zpp = mnb.pack(g.q, g.zp, bs)
+        ref = orc.pack_weights(inp.q.numpy(), bs)
+        assert np.array_equal(b.cpu().numpy(), ref), (bs, K, N)
+        if zp:
+            assert np.array_equal(zpp.cpu().numpy(), orc.pack_zero_points(inp.zp.numpy()))
+
+
+def test_pack_ignores_high_bits(orc):
+    inp, g = _inputs(100, 7, 1, 32, "f32", True, False, seed=3)
+    b0, z0 = mnb.pack(g.q, g.zp, 32)
+    b1, z1 = mnb.pack(g.q | 0xF0, g.zp | 0x30, 32)
+    assert torch.equal(b0, b1) and torch.equal(z0, z1)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("bs", [16, 32, 128])
+def test_dequant_bit_exact(orc, dt, bs):
+    for K, N, zp in [(1, 1, False), (33, 5, True), (257, 9, True), (1000, 17, False),
+                     (bs * 3, 4, True)]:
+        log(f"dequant {dt} bs={bs} K={K} N={N} zp={zp}")
+        inp, g = _inputs(K, N, 1, bs, dt, zp, False, seed=K + N)
+        pw = _packed(g, bs)
+        adt = torch.float32 if dt == "f32" else torch.bfloat16
+        kw = dict(K=K, N=N, block_size=bs, act_dtype=adt)
+        w_exact = orc.dequant(inp.q.numpy(), None if inp.zp is None else inp.zp.numpy(),
+                              act_np(inp.scales), bs)
+        w32 = mnb.dequant(pw.b_packed, pw.scales, pw.zp_packed, out_kind=mnb.DEQUANT_F32, **kw)
+        assert np.array_equal(w32.cpu().numpy().view(np.uint32),
+                              orc.round_to_f32(w_exact).view(np.uint32))
+        w16 = mnb.dequant(pw.b_packed, pw.scales, pw.zp_packed, out_kind=mnb.DEQUANT_BF16, **kw)
+        assert np.array_equal(act_np(w16), orc.round_to_bf16(w_exact))
+        wi = mnb.dequant(pw.b_packed, pw.scales, pw.zp_packed, out_kind=mnb.DEQUANT_INT8, **kw)
+        assert np.array_equal(wi.cpu().numpy(),
+                              orc.dequant_int(inp.q.numpy(),
+                                              None if inp.zp is None else inp.zp.numpy(), bs))
+
+
+def test_dequant_rounding_ties(orc):
+    """Scales chosen so that (q - zp) * s falls exactly between two bfloat16
+    values (ties to even) or two float32 values."""
+    N, K, bs = 4, 16, 16
+    q = torch.full((N, K), 8, dtype=torch.uint8)
+    q[:, :4] = torch.tensor([9, 11, 7, 9], dtype=torch.uint8)
+    s = torch.tensor([[1.00390625], [1.00390625], [1.01171875],
+                      [np.frombuffer(np.uint32(0x3F800001).tobytes(), np.float32)[0]]],
+                     dtype=torch.float32)
+    g_q, g_s = q.to(DEV), s.to(DEV)
+    pw = mnb.PackedWeight.from_logical(g_q, g_s, block_size=bs)
+    w_exact = orc.dequant(q.numpy(), None, s.numpy(), bs)
+    w16 = mnb.dequant(pw.b_packed, pw.scales, None, K=K, N=N, block_size=bs,
+                      out_kind=mnb.DEQUANT_BF16)
+    assert np.array_equal(act_np(w16), orc.round_to_bf16(w_exact))
+    w32 = mnb.dequant(pw.b_packed, pw.scales, None, K=K, N=N, block_size=bs)
+    assert np.array_equal(w32.cpu().numpy(), orc.round_to_f32(w_exact))
+
+
+# ---------------------------------------------------------------------------
+# GEMV / GEMM: within tolerance
+# ---------------------------------------------------------------------------
+
+GEMV_K = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 127, 128, 129, 255, 256, 257,
+          1000, 1024, 2048, 2560, 3072, 4096, 9728, 10240]
+GEMV_N = [1, 2, 3, 63, 64, 65, 127, 129]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
+def test_gemv_parity_sweep(orc, dt, bs):
+    rng = np.random.default_rng(bs)
+    worst = 0.0
+    for K in GEMV_K:
+        Ns = GEMV_N if K <= 1024 else [1, 65, 129]
+        for N in Ns:
+            zp, bias = bool(rng.integers(2)), bool(rng.integers(2))
+            log(f"gemv {dt} bs={bs} K={K} N={N} zp={zp} bias={bias}")
+            inp, g = _inputs(K, N, 1, bs, dt, zp, bias, seed=K * 131 + N)
+            y = _packed(g, bs).matmul(g.a)
+            y_ref, S = oracle_ref(orc, inp)
+            worst = max(worst, assert_close(out_f64(y), y_ref, S, dt, f"K={K} N={N}"))
+    log(f"gemv {dt} bs={bs}: worst err/tol {worst:.3g}")
+
+
+GEMM_CASES = [  # (M, K, N)
+    (1, 64, 64), (2, 33, 5), (3, 257, 129), (17, 1000, 63), (64, 128, 128),
+    (65, 129, 130), (128, 256, 256), (130, 512, 200), (257, 320, 300),
+    (512, 1024, 257), (33, 2560, 96), (40, 9728, 64), (7, 16, 1), (300, 1, 9),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
+def test_gemm_parity_sweep(orc, dt, bs):
+    rng = np.random.default_rng(100 + bs)
+    worst = 0.0
+    for M, K, N in GEMM_CASES:
+        zp, bias = bool(rng.integers(2)), bool(rng.integers(2))
+        log(f"gemm {dt} bs={bs} M={M} K={K} N={N} zp={zp} bias={bias}")
+        inp, g = _inputs(K, N, M, bs, dt, zp, bias, seed=M * 7 + K * 131 + N)
+        pw = _packed(g, bs)
+        y = mnb.gemm(g.a, pw.b_packed, pw.scales, pw.zp_packed, pw.bias, K=K, N=N,
+                     block_size=bs)
+        y_ref, S = oracle_ref(orc, inp)
+        worst = max(worst, assert_close(out_f64(y), y_ref, S, dt, f"M={M} K={K} N={N}"))
+    log(f"gemm {dt} bs={bs}: worst err/tol {worst:.3g}")
+
+
+def test_gemv_beyond_register_limit_uses_gemm(orc):
+    """K above mnb_gemv_max_k is served at M = 1 by the tiled kernel."""
+    K, N, bs = 12288 + 32, 40, 32
+    d = mnb.make_desc(K, N, bs)
+    assert mnb.gemv_max_k(d) < K
+    inp, g = _inputs(K, N, 1, bs, "f32", True, True, seed=5)
+    y = _packed(g, bs).matmul(g.a)
+    y_ref, S = oracle_ref(orc, inp)
+    assert_close(out_f64(y), y_ref, S, "f32", "K beyond gemv limit")
+
+
+# ---------------------------------------------------------------------------
+# bit-exact special cases and invariants
+# ---------------------------------------------------------------------------
+
+def _exact_case(K, N, M, bs, dt, seed):
+    """Power-of-two scales and small-integer activations: every partial sum is
+    exact in float32, so any summation order gives the exact result."""
+    rng = np.random.default_rng(seed)
+    nb = -(-K // bs)
+    q = torch.from_numpy(rng.integers(0, 16, (N, K), dtype=np.uint8))
+    zp = torch.from_numpy(rng.integers(0, 16, (N, nb), dtype=np.uint8))
+    sc = torch.from_numpy((2.0 ** -rng.integers(5, 9, (N, nb))).astype(np.float32))
+    a = torch.from_numpy(rng.integers(-8, 9, (M, K)).astype(np.float32))
+    bias = torch.from_numpy((rng.integers(-64, 65, N) / 8.0).astype(np.float32))
+    if dt == "bf16":
+        sc, a = sc.to(torch.bfloat16), a.to(torch.bfloat16)
+    return q, zp, sc, a, bias
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("M", [1, 5, 130])
+def test_exact_arithmetic_bit_exact(orc, dt, M):
+    for K, N, bs in [(1024, 70, 32), (2560, 33, 128), (333, 17, 16)]:
+        log(f"exact {dt} M={M} K={K} N={N} bs={bs}")
+        q, zp, sc, a, bias = _exact_case(K, N, M, bs, dt, seed=K + M)
+        pw = mnb.PackedWeight.from_logical(q.to(DEV), sc.to(DEV), zp.to(DEV), bias.to(DEV),
+                                           block_size=bs)
+        y = pw.matmul(a.to(DEV))
+        y_ref, _ = orc.matmul(act_np(a), q.numpy(), zp.numpy(), act_np(sc), bs,
+                              bias=bias.numpy())
+        if dt == "f32":
+            assert np.array_equal(y.cpu().numpy(), orc.round_to_f32(y_ref)), (K, N, M)
+        else:
+            assert np.array_equal(act_np(y), orc.round_to_bf16(y_ref)), (K, N, M)
+
+
+def test_identity_and_one_hot_return_dequantized_weights(orc):
+    K, N, bs = 96, 40, 32
+    inp, g = _inputs(K, N, 1, bs, "f32", True, False, seed=11)
+    pw = _packed(g, bs)
+    w = orc.round_to_f32(orc.dequant(inp.q.numpy(), inp.zp.numpy(), inp.scales.numpy(), bs))
+    y = mnb.gemm(torch.eye(K, device=DEV), pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N,
+                 block_size=bs)
+    assert np.array_equal(y.cpu().numpy(), w.T)
+    for k in (0, 1, 31, 32, 95):
+        a = torch.zeros(1, K, device=DEV)
+        a[0, k] = 1.0
+        yv = pw.matmul(a)
+        assert np.array_equal(yv.cpu().numpy()[0], w[:, k]), k
+
+
+@pytest.mark.parametrize("M", [1, 64])
+def test_fused_launch_bit_identical_to_separate(M):
+    """gate||up in one launch == the two launches; any column permutation of
+    the packed matrix permutes y exactly."""
+    for K, bs, dt in [(1024, 32, "f32"), (2560, 128, "f32"), (2560, 128, "bf16")]:
+        log(f"fusion M={M} K={K} bs={bs} {dt}")
+        _, g1 = _inputs(K, 300, M, bs, dt, True, False, seed=1)
+        _, g2 = _inputs(K, 200, M, bs, dt, True, False, seed=2)
+        p1, p2 = _packed(g1, bs), _packed(g2, bs)
+        a = g1.a
+        y1, y2 = p1.matmul(a), p2.matmul(a)
+        q = torch.cat([g1.q, g2.q])
+        fused = mnb.PackedWeight.from_logical(q, torch.cat([g1.scales, g2.scales]),
+                                              torch.cat([g1.zp, g2.zp]), block_size=bs)
+        yf = fused.matmul(a)
+        assert torch.equal(yf, torch.cat([y1, y2], 1))
+        perm = torch.randperm(500, generator=torch.Generator().manual_seed(0)).to(DEV)
+        pp = mnb.PackedWeight.from_logical(q[perm], torch.cat([g1.scales, g2.scales])[perm],
+                                           torch.cat([g1.zp, g2.zp])[perm], block_size=bs)
+        assert torch.equal(pp.matmul(a), yf[:, perm])
+
+
+@pytest.mark.parametrize("M", [1, 20])
+def test_pad_nibbles_do_not_matter(M):
+    K, N, bs = 100, 33, 64          # partial last block (36 of 64 values)
+    _, g = _inputs(K, N, M, bs, "f32", True, True, seed=4)
+    pw = _packed(g, bs)
+    y0 = pw.matmul(g.a)
+    nb = 2
+    b = pw.b_packed.view(N, nb * bs // 2).clone()
+    b[:, K // 2:] = 0xFF                        # every pad nibble set to 15
+    zp = pw.zp_packed.clone()                   # nb = 2: no zero-point pad nibble
+    y1 = mnb.PackedWeight(K, N, bs, torch.float32, b.view(-1).contiguous(), pw.scales, zp,
+                          pw.bias).matmul(g.a)
+    assert torch.equal(y0, y1)
+    # odd number of blocks: the pad nibble of the zero-point row
+    K3 = 150
+    _, g3 = _inputs(K3, N, M, bs, "f32", True, False, seed=5)
+    p3 = _packed(g3, bs)
+    z3 = p3.zp_packed.view(N, 2).clone()
+    z3[:, 1] |= 0xF0
+    y3a = p3.matmul(g3.a)
+    y3b = mnb.PackedWeight(K3, N, bs, torch.float32, p3.b_packed, p3.scales,
+                           z3.view(-1).contiguous()).matmul(g3.a)
+    assert torch.equal(y3a, y3b)
+
+
+@pytest.mark.parametrize("M", [1, 48])
+def test_default_zero_point_equals_explicit_eight(M):
+    K, N, bs = 700, 90, 32
+    _, g = _inputs(K, N, M, bs, "f32", False, True, seed=6)
+    y0 = _packed(g, bs).matmul(g.a)
+    z8 = torch.full((N, -(-K // bs)), 8, dtype=torch.uint8, device=DEV)
+    y8 = mnb.PackedWeight.from_logical(g.q, g.scales, z8, g.bias, block_size=bs).matmul(g.a)
+    assert torch.equal(y0, y8)
+
+
+@pytest.mark.parametrize("M", [1, 96])
+def test_deterministic(M):
+    K, N, bs = 2048, 1024, 32
+    _, g = _inputs(K, N, M, bs, "f32", True, True, seed=8)
+    pw = _packed(g, bs)
+    y0 = pw.matmul(g.a).clone()
+    for _ in range(3):
+        assert torch.equal(pw.matmul(g.a), y0)
+
+
+def test_scaling_by_powers_of_two_is_exact():
+    K, N, bs = 512, 64, 32
+    _, g = _inputs(K, N, 1, bs, "f32", True, False, seed=9)
+    y = _packed(g, bs).matmul(g.a)
+    y2 = _packed(g, bs).matmul(g.a * 4.0)
+    assert torch.equal(y2, y * 4.0)
+    ys = mnb.PackedWeight.from_logical(g.q, g.scales * 0.5, g.zp, block_size=bs).matmul(g.a)
+    assert torch.equal(ys, y * 0.5)
+
+
+def test_unaligned_view_is_rejected():
+    K, N, bs = 64, 8, 32
+    _, g = _inputs(K, N, 1, bs, "f32", False, False, seed=1)
+    pw = _packed(g, bs)
+    big = torch.zeros(K + 1, device=DEV)
+    with pytest.raises(mnb.MnbError) as e:
+        mnb.gemv(big[1:].view(1, K), pw.b_packed, pw.scales, K=K, N=N, block_size=bs)
+    assert e.value.status == -3

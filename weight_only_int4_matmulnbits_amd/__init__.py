@@ -1,0 +1,272 @@
+"""Weight-only block-INT4 MatMul (MatMulNBits contract) for AMD MI355X.
+
+Thin Python binding over libmnb's C ABI (include/mnb.h).  This module only
+checks torch tensors (device, dtype, shape, contiguity), allocates outputs with
+torch, and passes raw pointers and the current HIP stream; every step of the
+computation runs in the library's gfx950 kernels.  There is no fallback path:
+a missing library raises.
+
+    Y[M][N] = A[M][K] x dequant(B)[K][N] (+ bias)
+    dequant(B)[k][n] = (q[n][k] - zp[n][k // block_size]) * scale[n][k // block_size]
+
+Storage follows MatMulNBits: packed weights [N][nb][block_size/2] uint8 with
+the low nibble holding the even k, scales [N][nb] in the activation dtype,
+packed zero points [N][ceil(nb/2)] uint8 (default 8 when absent).
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import List, Optional, Sequence as TSeq, Tuple
+
+import torch
+
+from ._lib import BF16, F32, Desc, MatmulArgs, MnbError, check, lib  # noqa: F401
+
+__all__ = [
+    "Desc", "MnbError", "make_desc", "validate", "packed_weight_bytes",
+    "scale_bytes", "zero_point_bytes", "gemv_max_k", "pack", "gemv", "gemm",
+    "dequant", "PackedWeight", "Sequence", "version",
+]
+
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def _code(dtype: torch.dtype) -> int:
+    if dtype not in _DTYPES:
+        raise TypeError(f"activation dtype must be float32 or bfloat16, got {dtype}")
+    return _DTYPES[dtype]
+
+
+def make_desc(K: int, N: int, block_size: int = 32,
+              act_dtype: torch.dtype = torch.float32,
+              has_zero_points: bool = False, accuracy_level: int = 4,
+              bits: int = 4) -> Desc:
+    return Desc(K=int(K), N=int(N), bits=int(bits), block_size=int(block_size),
+                act_dtype=_code(act_dtype), has_zero_points=int(bool(has_zero_points)),
+                accuracy_level=int(accuracy_level), reserved=0)
+
+
+def validate(desc: Desc, M: int = 1) -> None:
+    check(lib().mnb_validate(ctypes.byref(desc), int(M)), "mnb_validate")
+
+
+def packed_weight_bytes(desc: Desc) -> int:
+    return int(lib().mnb_packed_weight_bytes(ctypes.byref(desc)))
+
+
+def scale_bytes(desc: Desc) -> int:
+    return int(lib().mnb_scale_bytes(ctypes.byref(desc)))
+
+
+def zero_point_bytes(desc: Desc) -> int:
+    return int(lib().mnb_zero_point_bytes(ctypes.byref(desc)))
+
+
+def gemv_max_k(desc: Desc) -> int:
+    return int(lib().mnb_gemv_max_k(ctypes.byref(desc)))
+
+
+def version() -> str:
+    return lib().mnb_version().decode()
+
+
+# ---- tensor plumbing ---------------------------------------------------------
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtype: torch.dtype,
+          numel: Optional[int] = None, shape: Optional[Tuple[int, ...]] = None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def _nb(K: int, bs: int) -> int:
+    return -(-K // bs)
+
+
+# ---- entry points --------------------------------------------------------------
+
+def pack(q: torch.Tensor, zp: Optional[torch.Tensor] = None, block_size: int = 32,
+         act_dtype: torch.dtype = torch.float32, stream=None
+         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Pack logical weights q[N][K] (uint8, 0..15) and optional zero points
+    zp[N][nb] (uint8) into MatMulNBits storage on the GPU."""
+    N, K = q.shape
+    d = make_desc(K, N, block_size, act_dtype, zp is not None)
+    _need(q, "q", torch.uint8, shape=(N, K))
+    if zp is not None:
+        _need(zp, "zp", torch.uint8, shape=(N, _nb(K, block_size)))
+    b = torch.empty(packed_weight_bytes(d) or 1, dtype=torch.uint8, device=q.device)
+    zpp = None
+    if zp is not None:
+        zpp = torch.empty(zero_point_bytes(d) or 1, dtype=torch.uint8, device=q.device)
+    check(lib().mnb_pack(ctypes.byref(d), _ptr(q), _ptr(zp), _ptr(b), _ptr(zpp),
+                         _stream(stream)), "mnb_pack")
+    return b, zpp
+
+
+def _matmul(fn: str, a: torch.Tensor, b_packed: torch.Tensor, scales: torch.Tensor,
+            zp_packed: Optional[torch.Tensor], bias: Optional[torch.Tensor],
+            K: int, N: int, block_size: int, out: Optional[torch.Tensor],
+            stream) -> torch.Tensor:
+    if a.dim() == 1:
+        a = a.view(1, -1)
+    M = a.shape[0]
+    d = make_desc(K, N, block_size, a.dtype, zp_packed is not None)
+    _need(a, "a", a.dtype, shape=(M, K))
+    _need(b_packed, "b_packed", torch.uint8, numel=packed_weight_bytes(d))
+    _need(scales, "scales", a.dtype, numel=N * _nb(K, block_size))
+    if zp_packed is not None:
+        _need(zp_packed, "zp_packed", torch.uint8, numel=zero_point_bytes(d))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, numel=N)
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    _need(out, "out", a.dtype, shape=(M, N))
+    f = getattr(lib(), fn)
+    check(f(ctypes.byref(d), M, _ptr(a), _ptr(b_packed), _ptr(scales), _ptr(zp_packed),
+            _ptr(bias), _ptr(out), _stream(stream)), fn)
+    return out
+
+
+def gemv(a, b_packed, scales, zp_packed=None, bias=None, *, K, N, block_size,
+         out=None, stream=None) -> torch.Tensor:
+    """Decode GEMV: a is [1][K] (or [K]); returns y [1][N] in a's dtype."""
+    return _matmul("mnb_gemv", a, b_packed, scales, zp_packed, bias, K, N, block_size,
+                   out, stream)
+
+
+def gemm(a, b_packed, scales, zp_packed=None, bias=None, *, K, N, block_size,
+         out=None, stream=None) -> torch.Tensor:
+    """Prefill GEMM: a is [M][K]; returns y [M][N] in a's dtype."""
+    return _matmul("mnb_gemm", a, b_packed, scales, zp_packed, bias, K, N, block_size,
+                   out, stream)
+
+
+DEQUANT_F32, DEQUANT_BF16, DEQUANT_INT8 = 0, 1, 2
+
+
+def dequant(b_packed, scales, zp_packed=None, *, K, N, block_size,
+            act_dtype=torch.float32, out_kind=DEQUANT_F32, stream=None) -> torch.Tensor:
+    """Test hook: dequantized weights w[N][K] (float32, bfloat16, or the int8
+    integers q - zp)."""
+    d = make_desc(K, N, block_size, act_dtype, zp_packed is not None)
+    _need(b_packed, "b_packed", torch.uint8, numel=packed_weight_bytes(d))
+    if out_kind != DEQUANT_INT8:
+        _need(scales, "scales", act_dtype, numel=N * _nb(K, block_size))
+    odt = {DEQUANT_F32: torch.float32, DEQUANT_BF16: torch.bfloat16,
+           DEQUANT_INT8: torch.int8}[out_kind]
+    w = torch.empty((N, K), dtype=odt, device=b_packed.device)
+    check(lib().mnb_dequant(ctypes.byref(d), _ptr(b_packed), _ptr(scales),
+                            _ptr(zp_packed), int(out_kind), _ptr(w), _stream(stream)),
+          "mnb_dequant")
+    return w
+
+
+# ---- prepared plans and step driver ---------------------------------------------
+
+class PackedWeight:
+    """A prepared weight-only plan: packed weights, scales, optional packed
+    zero points and optional fp32 bias of one (possibly fused) projection."""
+
+    def __init__(self, K: int, N: int, block_size: int, act_dtype: torch.dtype,
+                 b_packed: torch.Tensor, scales: torch.Tensor,
+                 zp_packed: Optional[torch.Tensor] = None,
+                 bias: Optional[torch.Tensor] = None):
+        self.K, self.N, self.block_size, self.act_dtype = K, N, block_size, act_dtype
+        self.b_packed, self.scales, self.zp_packed, self.bias = b_packed, scales, zp_packed, bias
+        self.desc = make_desc(K, N, block_size, act_dtype, zp_packed is not None)
+        _need(b_packed, "b_packed", torch.uint8, numel=packed_weight_bytes(self.desc))
+        _need(scales, "scales", act_dtype, numel=N * _nb(K, block_size))
+        if zp_packed is not None:
+            _need(zp_packed, "zp_packed", torch.uint8, numel=zero_point_bytes(self.desc))
+        if bias is not None:
+            _need(bias, "bias", torch.float32, numel=N)
+
+    @classmethod
+    def from_logical(cls, q: torch.Tensor, scales: torch.Tensor,
+                     zp: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                     block_size: int = 32, stream=None) -> "PackedWeight":
+        N, K = q.shape
+        b, zpp = pack(q, zp, block_size, scales.dtype, stream)
+        return cls(K, N, block_size, scales.dtype, b, scales.contiguous(), zpp, bias)
+
+    @property
+    def weight_bytes(self) -> int:
+        return (self.b_packed.numel() + self.scales.numel() * self.scales.element_size()
+                + (0 if self.zp_packed is None else self.zp_packed.numel()))
+
+    def matmul(self, a: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+        fn = gemv if (a.dim() == 1 or a.shape[0] == 1) else gemm
+        return fn(a, self.b_packed, self.scales, self.zp_packed, self.bias, K=self.K,
+                  N=self.N, block_size=self.block_size, out=out, stream=stream)
+
+    def args(self, a: torch.Tensor, y: torch.Tensor) -> MatmulArgs:
+        M = 1 if a.dim() == 1 else a.shape[0]
+        _need(a, "a", self.act_dtype, numel=M * self.K)
+        _need(y, "y", self.act_dtype, numel=M * self.N)
+        return MatmulArgs(desc=self.desc, M=M, a=a.data_ptr(),
+                          b_packed=self.b_packed.data_ptr(),
+                          scales=self.scales.data_ptr(),
+                          zp_packed=None if self.zp_packed is None else self.zp_packed.data_ptr(),
+                          bias=None if self.bias is None else self.bias.data_ptr(),
+                          y=y.data_ptr())
+
+
+class Sequence:
+    """An ordered list of projections run back to back on one stream (a decode
+    or prefill step), either eagerly or as one captured HIP graph.  The caller
+    keeps every tensor alive while the sequence exists."""
+
+    def __init__(self, items: TSeq[Tuple[PackedWeight, torch.Tensor, torch.Tensor]]):
+        self._keep: List = list(items)
+        n = len(self._keep)
+        self._args = (MatmulArgs * max(n, 1))()
+        for i, (w, a, y) in enumerate(self._keep):
+            self._args[i] = w.args(a, y)
+        self.n = n
+        self._graph = None
+
+    def run(self, stream=None) -> None:
+        check(lib().mnb_matmul_sequence(self._args, self.n, _stream(stream)),
+              "mnb_matmul_sequence")
+
+    def capture(self) -> None:
+        g = ctypes.c_void_p()
+        check(lib().mnb_graph_create(self._args, self.n, ctypes.byref(g)), "mnb_graph_create")
+        self._graph = g
+
+    def replay(self, stream=None) -> None:
+        if self._graph is None:
+            raise RuntimeError("capture() first")
+        check(lib().mnb_graph_launch(self._graph, _stream(stream)), "mnb_graph_launch")
+
+    def close(self) -> None:
+        if self._graph is not None:
+            check(lib().mnb_graph_destroy(self._graph), "mnb_graph_destroy")
+            self._graph = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+

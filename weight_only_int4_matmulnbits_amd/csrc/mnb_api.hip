@@ -1,0 +1,302 @@
+// The C ABI of libmnb (declared and documented in include/mnb.h): host-side
+// validation, derived sizes, dispatch to the kernels, the step driver and
+// captured graphs.  Validation runs before any HIP call.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "mnb_internal.h"
+
+#define MNB_VERSION_STRING "mnb 0.1 (gfx950)"
+
+namespace mnb {
+
+static thread_local char g_last_error[512];
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;   // K, N: int32 block math
+constexpr int64_t kMaxM = int64_t(65535) * 128;       // grid.y of the GEMM
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_desc(const mnb_desc* d, const char* who) {
+    if (!d) return fail(MNB_E_ARG, "%s: descriptor is NULL", who);
+    if (d->bits != 4) return fail(MNB_E_UNSUPPORTED, "%s: bits=%d, only 4 is supported", who, d->bits);
+    const int bs = d->block_size;
+    if (bs != 16 && bs != 32 && bs != 64 && bs != 128 && bs != 256)
+        return fail(MNB_E_UNSUPPORTED, "%s: block_size=%d, must be 16, 32, 64, 128 or 256", who, bs);
+    if (d->act_dtype != MNB_F32 && d->act_dtype != MNB_BF16)
+        return fail(MNB_E_UNSUPPORTED, "%s: act_dtype=%d unknown", who, d->act_dtype);
+    if (d->has_zero_points != 0 && d->has_zero_points != 1)
+        return fail(MNB_E_ARG, "%s: has_zero_points=%d, must be 0 or 1", who, d->has_zero_points);
+    if (d->accuracy_level < 0 || d->accuracy_level > 4)
+        return fail(MNB_E_ARG, "%s: accuracy_level=%d, must be 0..4", who, d->accuracy_level);
+    if (d->reserved != 0) return fail(MNB_E_UNSUPPORTED, "%s: reserved field must be 0", who);
+    if (d->K < 1 || d->N < 1)
+        return fail(MNB_E_ARG, "%s: K=%lld N=%lld, both must be >= 1", who, (long long)d->K, (long long)d->N);
+    if (d->K > kMaxDim || d->N > kMaxDim)
+        return fail(MNB_E_OVERFLOW, "%s: K=%lld N=%lld exceed 2^31-1", who, (long long)d->K, (long long)d->N);
+    return MNB_OK;
+}
+
+void fill_problem(const mnb_desc* d, int64_t M, Problem* p) {
+    p->M = M;
+    p->K = d->K;
+    p->N = d->N;
+    p->bs = d->block_size;
+    p->nb = (int)((d->K + d->block_size - 1) / d->block_size);
+    p->col_bytes = (int64_t)p->nb * (d->block_size / 2);
+    p->zp_row = (p->nb + 1) / 2;
+    p->bf16 = d->act_dtype == MNB_BF16;
+    p->has_zp = d->has_zero_points != 0;
+}
+
+// Shared validation of gemv / gemm arguments.
+int check_matmul(const char* who, const mnb_desc* d, int64_t M, const void* a,
+                 const uint8_t* b, const void* scales, const uint8_t* zp,
+                 const float* bias, void* y, bool gemv, Problem* p) {
+    int st = check_desc(d, who);
+    if (st != MNB_OK) return st;
+    if (gemv && M != 1) return fail(MNB_E_ARG, "%s: M=%lld, the decode GEMV takes M == 1", who, (long long)M);
+    if (M < 1) return fail(MNB_E_ARG, "%s: M=%lld, must be >= 1", who, (long long)M);
+    if (M > kMaxM) return fail(MNB_E_OVERFLOW, "%s: M=%lld exceeds %lld", who, (long long)M, (long long)kMaxM);
+    if (!a || !b || !scales || !y) return fail(MNB_E_ARG, "%s: a, b_packed, scales and y must be non-NULL", who);
+    if ((zp != nullptr) != (d->has_zero_points != 0))
+        return fail(MNB_E_ARG, "%s: zp_packed must be given iff has_zero_points", who);
+    const uintptr_t esz = d->act_dtype == MNB_BF16 ? 2 : 4;
+    if (!aligned(a, 16)) return fail(MNB_E_ALIGN, "%s: a must be 16-byte aligned", who);
+    if (!aligned(b, 16)) return fail(MNB_E_ALIGN, "%s: b_packed must be 16-byte aligned", who);
+    if (!aligned(scales, esz)) return fail(MNB_E_ALIGN, "%s: scales must be %d-byte aligned", who, (int)esz);
+    if (!aligned(y, esz)) return fail(MNB_E_ALIGN, "%s: y must be %d-byte aligned", who, (int)esz);
+    if (bias && !aligned(bias, 4)) return fail(MNB_E_ALIGN, "%s: bias must be 4-byte aligned", who);
+    fill_problem(d, M, p);
+    p->a = a; p->b = b; p->scales = scales; p->zp = zp; p->bias = bias; p->y = y;
+    return MNB_OK;
+}
+
+int run(const Problem& p, hipStream_t s) {
+    if (p.M == 1 && p.K <= gemv_max_k(p.bs)) return launch_gemv(p, s);
+    return launch_gemm(p, s);
+}
+
+}  // namespace
+}  // namespace mnb
+
+using namespace mnb;
+
+struct mnb_graph {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+extern "C" {
+
+int mnb_validate(const mnb_desc* d, int64_t M) {
+    int st = check_desc(d, "mnb_validate");
+    if (st != MNB_OK) return st;
+    if (M < 1) return fail(MNB_E_ARG, "mnb_validate: M=%lld, must be >= 1", (long long)M);
+    if (M > kMaxM) return fail(MNB_E_OVERFLOW, "mnb_validate: M=%lld too large", (long long)M);
+    return MNB_OK;
+}
+
+size_t mnb_packed_weight_bytes(const mnb_desc* d) {
+    if (check_desc(d, "mnb_packed_weight_bytes") != MNB_OK) return 0;
+    Problem p;
+    fill_problem(d, 1, &p);
+    return (size_t)(p.N * p.col_bytes);
+}
+
+size_t mnb_scale_bytes(const mnb_desc* d) {
+    if (check_desc(d, "mnb_scale_bytes") != MNB_OK) return 0;
+    Problem p;
+    fill_problem(d, 1, &p);
+    return (size_t)(p.N * p.nb * (p.bf16 ? 2 : 4));
+}
+
+size_t mnb_zero_point_bytes(const mnb_desc* d) {
+    if (check_desc(d, "mnb_zero_point_bytes") != MNB_OK) return 0;
+    if (!d->has_zero_points) return 0;
+    Problem p;
+    fill_problem(d, 1, &p);
+    return (size_t)(p.N * p.zp_row);
+}
+
+int64_t mnb_gemv_max_k(const mnb_desc* d) {
+    if (check_desc(d, "mnb_gemv_max_k") != MNB_OK) return 0;
+    return gemv_max_k(d->block_size);
+}
+
+int mnb_pack(const mnb_desc* d, const uint8_t* q_nk, const uint8_t* zp_nb,
+             uint8_t* b_packed, uint8_t* zp_packed, void* stream) {
+    int st = check_desc(d, "mnb_pack");
+    if (st != MNB_OK) return st;
+    if (!q_nk || !b_packed) return fail(MNB_E_ARG, "mnb_pack: q_nk and b_packed must be non-NULL");
+    const bool zp = d->has_zero_points != 0;
+    if ((zp_nb != nullptr) != zp || (zp_packed != nullptr) != zp)
+        return fail(MNB_E_ARG, "mnb_pack: zp_nb and zp_packed must be given iff has_zero_points");
+    if (!aligned(b_packed, 16)) return fail(MNB_E_ALIGN, "mnb_pack: b_packed must be 16-byte aligned");
+    return launch_pack(d->K, d->N, d->block_size, q_nk, zp_nb, b_packed, zp_packed,
+                       static_cast<hipStream_t>(stream));
+}
+
+int mnb_gemv(const mnb_desc* d, int64_t M, const void* a, const uint8_t* b_packed,
+             const void* scales, const uint8_t* zp_packed, const float* bias, void* y,
+             void* stream) {
+    Problem p;
+    int st = check_matmul("mnb_gemv", d, M, a, b_packed, scales, zp_packed, bias, y, true, &p);
+    if (st != MNB_OK) return st;
+    return run(p, static_cast<hipStream_t>(stream));
+}
+
+int mnb_gemm(const mnb_desc* d, int64_t M, const void* a, const uint8_t* b_packed,
+             const void* scales, const uint8_t* zp_packed, const float* bias, void* y,
+             void* stream) {
+    Problem p;
+    int st = check_matmul("mnb_gemm", d, M, a, b_packed, scales, zp_packed, bias, y, false, &p);
+    if (st != MNB_OK) return st;
+    return launch_gemm(p, static_cast<hipStream_t>(stream));
+}
+
+int mnb_dequant(const mnb_desc* d, const uint8_t* b_packed, const void* scales,
+                const uint8_t* zp_packed, int32_t out_kind, void* w_nk, void* stream) {
+    int st = check_desc(d, "mnb_dequant");
+    if (st != MNB_OK) return st;
+    if (out_kind < 0 || out_kind > 2) return fail(MNB_E_ARG, "mnb_dequant: out_kind=%d, must be 0, 1 or 2", out_kind);
+    if (!b_packed || !w_nk || (out_kind != 2 && !scales))
+        return fail(MNB_E_ARG, "mnb_dequant: b_packed, w_nk (and scales unless out_kind 2) must be non-NULL");
+    if ((zp_packed != nullptr) != (d->has_zero_points != 0))
+        return fail(MNB_E_ARG, "mnb_dequant: zp_packed must be given iff has_zero_points");
+    const uintptr_t esz = d->act_dtype == MNB_BF16 ? 2 : 4;
+    if (scales && !aligned(scales, esz)) return fail(MNB_E_ALIGN, "mnb_dequant: scales misaligned");
+    const uintptr_t osz = out_kind == 0 ? 4 : out_kind == 1 ? 2 : 1;
+    if (!aligned(w_nk, osz)) return fail(MNB_E_ALIGN, "mnb_dequant: w_nk misaligned");
+    Problem p;
+    fill_problem(d, 1, &p);
+    p.a = nullptr; p.b = b_packed; p.scales = scales; p.zp = zp_packed; p.bias = nullptr; p.y = nullptr;
+    return launch_dequant(p, out_kind, w_nk, static_cast<hipStream_t>(stream));
+}
+
+static int check_sequence(const mnb_matmul_args* ops, int64_t n_ops, std::vector<Problem>* out) {
+    if (n_ops < 0 || (n_ops > 0 && !ops)) return fail(MNB_E_ARG, "sequence: ops NULL or n_ops < 0");
+    out->resize((size_t)n_ops);
+    for (int64_t i = 0; i < n_ops; i++) {
+        const mnb_matmul_args& o = ops[i];
+        int st = check_matmul("sequence entry", &o.desc, o.M, o.a, o.b_packed, o.scales, o.zp_packed,
+                              o.bias, o.y, false, &(*out)[(size_t)i]);
+        if (st != MNB_OK) {
+            char msg[512];
+            snprintf(msg, sizeof msg, "%s", g_last_error);
+            return fail(st, "entry %lld: %s", (long long)i, msg);
+        }
+    }
+    return MNB_OK;
+}
+
+int mnb_matmul_sequence(const mnb_matmul_args* ops, int64_t n_ops, void* stream) {
+    std::vector<Problem> probs;
+    int st;
+    try {
+        st = check_sequence(ops, n_ops, &probs);
+    } catch (const std::bad_alloc&) {
+        return fail(MNB_E_ARG, "sequence: out of host memory");
+    }
+    if (st != MNB_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (size_t i = 0; i < probs.size(); i++) {
+        st = run(probs[i], s);
+        if (st != MNB_OK) return st;
+    }
+    return MNB_OK;
+}
+
+int mnb_graph_create(const mnb_matmul_args* ops, int64_t n_ops, mnb_graph** out) {
+    if (!out) return fail(MNB_E_ARG, "mnb_graph_create: out is NULL");
+    *out = nullptr;
+    std::vector<Problem> probs;
+    int st;
+    try {
+        st = check_sequence(ops, n_ops, &probs);
+    } catch (const std::bad_alloc&) {
+        return fail(MNB_E_ARG, "mnb_graph_create: out of host memory");
+    }
+    if (st != MNB_OK) return st;
+    hipStream_t cs;
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e != hipSuccess) return fail(MNB_E_HIP, "mnb_graph_create: stream: %s", hipGetErrorString(e));
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+        (void)hipStreamDestroy(cs);
+        return fail(MNB_E_HIP, "mnb_graph_create: begin capture: %s", hipGetErrorString(e));
+    }
+    for (size_t i = 0; i < probs.size() && st == MNB_OK; i++) st = run(probs[i], cs);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    (void)hipStreamDestroy(cs);
+    if (st != MNB_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return st;
+    }
+    if (e != hipSuccess) return fail(MNB_E_HIP, "mnb_graph_create: end capture: %s", hipGetErrorString(e));
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(graph);
+        return fail(MNB_E_HIP, "mnb_graph_create: instantiate: %s", hipGetErrorString(e));
+    }
+    mnb_graph* g = new (std::nothrow) mnb_graph{graph, exec};
+    if (!g) {
+        (void)hipGraphExecDestroy(exec);
+        (void)hipGraphDestroy(graph);
+        return fail(MNB_E_ARG, "mnb_graph_create: out of host memory");
+    }
+    *out = g;
+    return MNB_OK;
+}
+
+int mnb_graph_launch(mnb_graph* g, void* stream) {
+    if (!g) return fail(MNB_E_ARG, "mnb_graph_launch: graph is NULL");
+    hipError_t e = hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MNB_E_HIP, "mnb_graph_launch: %s", hipGetErrorString(e));
+    return MNB_OK;
+}
+
+int mnb_graph_destroy(mnb_graph* g) {
+    if (!g) return MNB_OK;
+    hipError_t e1 = hipGraphExecDestroy(g->exec);
+    hipError_t e2 = hipGraphDestroy(g->graph);
+    delete g;
+    if (e1 != hipSuccess || e2 != hipSuccess)
+        return fail(MNB_E_HIP, "mnb_graph_destroy: %s",
+                    hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+    return MNB_OK;
+}
+
+const char* mnb_status_string(int status) {
+    switch (status) {
+        case MNB_OK: return "MNB_OK";
+        case MNB_E_ARG: return "MNB_E_ARG: invalid argument";
+        case MNB_E_UNSUPPORTED: return "MNB_E_UNSUPPORTED: unsupported configuration";
+        case MNB_E_ALIGN: return "MNB_E_ALIGN: misaligned pointer";
+        case MNB_E_OVERFLOW: return "MNB_E_OVERFLOW: size out of range";
+        case MNB_E_HIP: return "MNB_E_HIP: HIP runtime error";
+        default: return "unknown mnb status";
+    }
+}
+
+const char* mnb_last_error(void) { return g_last_error; }
+
+const char* mnb_version(void) { return MNB_VERSION_STRING; }
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal declarations shared by the libmnb translation units (not part of
+// the public ABI, which is include/mnb.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mnb.h"
+
+namespace mnb {
+
+// Fully validated, derived parameters of one matmul launch.
+struct Problem {
+    int64_t M, K, N;
+    int bs;               // block_size
+    int nb;               // ceil(K / bs)
+    int64_t col_bytes;    // nb * bs / 2: bytes of one packed column
+    int zp_row;           // ceil(nb / 2): bytes of one packed zero-point row
+    bool bf16;            // activations, scales and Y are bfloat16
+    bool has_zp;
+    const void* a;
+    const uint8_t* b;
+    const void* scales;
+    const uint8_t* zp;
+    const float* bias;
+    void* y;
+};
+
+// Records `detail` as the calling thread's last error and returns `status`.
+int fail(int status, const char* fmt, ...);
+
+// Kernel launchers (one per translation unit).  They return MNB_OK or
+// MNB_E_HIP and never validate: the ABI layer has already done so.
+int launch_pack(int64_t K, int64_t N, int bs, const uint8_t* q,
+                const uint8_t* zp, uint8_t* b_packed, uint8_t* zp_packed,
+                hipStream_t s);
+int launch_dequant(const Problem& p, int out_kind, void* w, hipStream_t s);
+int launch_gemv(const Problem& p, hipStream_t s);
+int launch_gemm(const Problem& p, hipStream_t s);
+int64_t gemv_max_k(int bs);
+
+// ---- device helpers ---------------------------------------------------------
+
+// float32 -> bfloat16 bit pattern, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rtne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+// A 32-bit AND whose result the compiler cannot see through, so that byte
+// extraction of the result maps onto v_cvt_f32_ubyte{0,1,2,3} instead of a
+// bit-field extract followed by a conversion.
+__device__ __forceinline__ uint32_t opaque_and(uint32_t x, uint32_t m) {
+    uint32_t r;
+    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(m));
+    return r;
+}
+
+template <int B>
+__device__ __forceinline__ float ubyte_to_f32(uint32_t x) {
+    return (float)((x >> (8 * B)) & 0xFFu);
+}
+
+}  // namespace mnb
