@@ -103,7 +103,7 @@ def test_dequant_rounding_ties(orc):
 # ---------------------------------------------------------------------------
 
 GEMV_K = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 127, 128, 129, 255, 256, 257,
-          1000, 1024, 2048, 2560, 3072, 4096, 9728, 10240]
+          1000, 1024, 1536, 2048, 2560, 3072, 4096, 5120, 6144, 8192 + 96, 9728, 12288]
 GEMV_N = [1, 2, 3, 63, 64, 65, 127, 129]
 
 
@@ -148,15 +148,18 @@ def test_gemm_parity_sweep(orc, dt, bs):
     log(f"gemm {dt} bs={bs}: worst err/tol {worst:.3g}")
 
 
-def test_gemv_beyond_register_limit_uses_gemm(orc):
-    """K above mnb_gemv_max_k is served at M = 1 by the tiled kernel."""
-    K, N, bs = 12288 + 32, 40, 32
+@pytest.mark.parametrize("K,bs", [(4096, 16), (4096 + 16, 16), (14560, 32),
+                                  (14560 + 32, 32), (12288, 128), (16384 + 100, 256)])
+def test_gemv_long_k_and_beyond_register_limit(orc, K, bs):
+    """Split-K across wavefronts up to mnb_gemv_max_k; K above it is served
+    at M = 1 by the tiled kernel."""
+    N = 40
     d = mnb.make_desc(K, N, bs)
-    assert mnb.gemv_max_k(d) < K
+    log(f"long K={K} bs={bs} max_k={mnb.gemv_max_k(d)}")
     inp, g = _inputs(K, N, 1, bs, "f32", True, True, seed=5)
     y = _packed(g, bs).matmul(g.a)
     y_ref, S = oracle_ref(orc, inp)
-    assert_close(out_f64(y), y_ref, S, "f32", "K beyond gemv limit")
+    assert_close(out_f64(y), y_ref, S, "f32", f"K={K} bs={bs}")
 
 
 # ---------------------------------------------------------------------------

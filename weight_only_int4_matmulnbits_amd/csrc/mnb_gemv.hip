@@ -9,25 +9,38 @@
 // Mapping on CDNA4.  The packed weights are N-major: column n is one run of
 // col_bytes contiguous bytes.  A "chunk" is CB = min(16, bs/2) bytes of one
 // column (CK = 2*CB values of K, inside one quantization block); a column has
-// S = ceil(K / CK) chunks.  Each column is handled by L lanes of one
-// wavefront (L a power of two <= 64, G = 64 / L columns per wavefront at a
-// time); lane p owns chunks p, p + L, ..., p + (J-1)L of EVERY column it
+// S = ceil(K / CK) chunks.  A column is handled by a team of W wavefronts
+// (split-K across wavefronts, W in {1, 2, 4}) with L lanes each (L a power
+// of two <= 64; G = 64 / L columns per wavefront step when W == 1).  Team
+// lane p owns chunks p, p + L*W, ..., p + (J-1)*L*W of EVERY column it
 // visits, so its J*CK activations are loaded once into registers and reused
-// for all of the wavefront's columns.  For a fixed column the L lanes read L
-// consecutive chunks: one fully coalesced 16-byte-per-lane load.  Per chunk a
-// lane forms dot = sum a_k q_k (nibbles -> float via v_cvt_f32_ubyte), then
-// acc += s * (dot - zp * sum a_k); the L partial sums of a column meet in a
-// fixed butterfly across lanes.  L and J depend only on (K, block_size), so
-// the float32 summation order of a column is the same whatever N is and
-// wherever the column sits: concatenated launches (fused QKV, gate||up) are
+// for all of the team's columns.  For a fixed column the lanes read
+// consecutive chunks: fully coalesced 16-byte-per-lane loads, marked
+// non-temporal (each weight byte is read once).
+//
+// Inner product in float32 on the vector ALU, about 2.25 instructions per
+// weight: per 32-bit word (8 nibbles) one AND keeps the even nibbles and one
+// AND keeps the odd nibbles in place (16*q), v_cvt_f32_ubyte{0..3} turn each
+// byte into a float, and one FMA per weight accumulates; odd-k activations
+// are held pre-multiplied by 1/16 so that (16q)(a/16) = q*a exactly.  Per
+// chunk a lane forms dot = sum a_k q_k and t = dot - zp * sum a_k, then
+// acc += s * t.  The L partial sums of a wavefront meet in
+// a fixed DPP tree (quad_perm, row_half_mirror, row_mirror, ds_swizzle,
+// readlane); the W wavefront sums meet in LDS in wavefront order.  Grid
+// size, unroll and prefetch only change which wavefront handles a column,
+// never the arithmetic: (L, J, W) depend only on (K, block_size), so the
+// float32 summation order of a column is the same whatever N is and wherever
+// the column sits -- concatenated launches (fused QKV, gate||up) are
 // bit-identical to separate ones.  No atomics, no workspace.
 #include "mnb_internal.h"
 
 namespace mnb {
 namespace {
 
-constexpr int kJMax = 5;          // chunks per lane held in registers
+constexpr int kJMax = 4;          // chunks per lane held in registers
+constexpr int kWMax = 4;          // wavefronts per column (split-K)
 constexpr int kWavesPerBlock = 4;
+constexpr size_t kMaxLds = 64 * 1024;    // staged activations per workgroup
 
 struct GemvArgs {
     const void* a;
@@ -40,23 +53,26 @@ struct GemvArgs {
     int nb, zp_row, S, log2_bs, log2_L;
 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 template <int CB>
 struct ChunkT;
 template <>
-struct ChunkT<16> { using type = uint4; };
+struct ChunkT<16> { using type = u32x4; };
 template <>
-struct ChunkT<8> { using type = uint2; };
+struct ChunkT<8> { using type = u32x2; };
 
+// One 32-bit word of a chunk holds values 8d..8d+7, two per byte, the even
+// one in the low nibble.  av[] holds the chunk's activations with the odd
+// ones pre-multiplied by 1/16.
 template <int NW>
 __device__ __forceinline__ float dot_words(const uint32_t (&w)[NW], const float* av) {
-    // av[i] is the activation of value i of the chunk; word d holds values
-    // 8d..8d+7, two per byte, the even one in the low nibble.
-    const uint32_t m = 0x0F0F0F0Fu;
     float de = 0.f, dd = 0.f;
 #pragma unroll
     for (int d = 0; d < NW; d++) {
-        uint32_t lo = opaque_and(w[d], m);        // values 8d, 8d+2, 8d+4, 8d+6
-        uint32_t hi = opaque_and(w[d] >> 4, m);   // values 8d+1, 8d+3, ...
+        const uint32_t lo = opaque_and(w[d], 0x0F0F0F0Fu);   // q(8d), q(8d+2), ...
+        const uint32_t hi = opaque_and(w[d], 0xF0F0F0F0u);   // 16*q(8d+1), ...
         de = fmaf(av[8 * d + 0], ubyte_to_f32<0>(lo), de);
         dd = fmaf(av[8 * d + 1], ubyte_to_f32<0>(hi), dd);
         de = fmaf(av[8 * d + 2], ubyte_to_f32<1>(lo), de);
@@ -69,101 +85,164 @@ __device__ __forceinline__ float dot_words(const uint32_t (&w)[NW], const float*
     return de + dd;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true);
+    return v + __builtin_bit_cast(float, t);
+}
+
+// Sum over aligned groups of 2^log2_L lanes; every lane of a group ends with
+// the same bits.  The tree is fixed: pairs, quads, eights, sixteens,
+// thirty-twos, then the two halves of the wavefront.
+__device__ __forceinline__ float reduce_lanes(float v, int log2_L) {
+    if (log2_L >= 1) v = add_dpp<0xB1>(v);     // quad_perm [1,0,3,2]
+    if (log2_L >= 2) v = add_dpp<0x4E>(v);     // quad_perm [2,3,0,1]
+    if (log2_L >= 3) v = add_dpp<0x141>(v);    // row_half_mirror
+    if (log2_L >= 4) v = add_dpp<0x140>(v);    // row_mirror
+    if (log2_L >= 5)                           // lanes i, i^16 of each half
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+    if (log2_L >= 6)
+        v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    return v;
+}
+
+// One iteration's loads, kept raw: decoding a scale or a zero-point nibble
+// here would make the wavefront wait for the load it just issued.
 template <bool BF16, bool HAS_ZP, int CB, int J, int U>
+struct Group {
+    using Chunk = typename ChunkT<CB>::type;
+    Chunk w[U][J];
+    uint32_t sc[U][J];   // float32 bits, or bfloat16 bits in the low half
+    uint32_t zb[U][J];   // packed zero-point byte (HAS_ZP)
+};
+
+template <bool BF16, bool HAS_ZP, int CB, int J, int U>
+__device__ __forceinline__ void load_group(const GemvArgs& g, int64_t base, int p, int LT, int G,
+                                           int gsub, Group<BF16, HAS_ZP, CB, J, U>& r) {
+    using Chunk = typename ChunkT<CB>::type;
+    constexpr int CK = 2 * CB;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int64_t gi = base + u;
+        const int64_t col = gi * G + gsub;
+        const bool ok = gi < g.n_groups && col < g.N;
+        const uint8_t* bc = g.b + col * g.col_bytes;
+#pragma unroll
+        for (int j = 0; j < J; j++) {
+            const int c = p + j * LT;
+            if (ok && c < g.S) {
+                r.w[u][j] = __builtin_nontemporal_load(
+                    reinterpret_cast<const Chunk*>(bc + (int64_t)c * CB));
+                const int blk = (c * CK) >> g.log2_bs;
+                const int64_t si = col * g.nb + blk;
+                r.sc[u][j] = BF16 ? (uint32_t)static_cast<const uint16_t*>(g.scales)[si]
+                                  : static_cast<const uint32_t*>(g.scales)[si];
+                if constexpr (HAS_ZP) r.zb[u][j] = g.zp[col * g.zp_row + (blk >> 1)];
+            } else {
+                r.w[u][j] = Chunk{};
+                r.sc[u][j] = 0;
+                if constexpr (HAS_ZP) r.zb[u][j] = 0x88;
+            }
+        }
+    }
+}
+
+// W wavefronts per column team, U column groups per team per iteration,
+// PF: load the next iteration's weights before computing the current one.
+template <bool BF16, bool HAS_ZP, int CB, int J, int U, int W, bool PF>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     constexpr int CK = 2 * CB;        // values of K per chunk
     constexpr int NW = CB / 4;        // 32-bit words per chunk
-    using Chunk = typename ChunkT<CB>::type;
+    constexpr int TEAMS = kWavesPerBlock / W;
+    static_assert(W == 1 || U == 1, "split-K teams take one column at a time");
+    __shared__ float red[kWavesPerBlock];
 
     const int lane = threadIdx.x & 63;
-    const int L = 1 << g.log2_L;
-    const int p = lane & (L - 1);     // position of this lane within its column
-    const int G = 64 >> g.log2_L;     // columns per wavefront step
+    const int wave = threadIdx.x >> 6;
+    const int team = wave / W;
+    const int wt = wave - team * W;   // wavefront index within the team
+    const int L = 1 << g.log2_L;      // lanes per column in one wavefront
+    const int LT = L * W;             // lanes per column in the team
+    const int p = wt * L + (lane & (L - 1));
+    const int G = 64 >> g.log2_L;
     const int gsub = lane >> g.log2_L;
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    const int64_t n_waves = (int64_t)gridDim.x * kWavesPerBlock;
 
-    // ---- activations of this lane's chunks, kept in registers ----
+    // iteration space: WG-uniform, so barriers (W > 1) are reached by all
+    const int64_t stride = (int64_t)gridDim.x * TEAMS * U;
+    int64_t base = ((int64_t)blockIdx.x * TEAMS + team) * U;
+    const int64_t team0 = (int64_t)blockIdx.x * TEAMS * U;
+
+    Group<BF16, HAS_ZP, CB, J, U> cur;
+    load_group(g, base, p, LT, G, gsub, cur);     // weights first: they do not wait on A
+
+    // ---- activations: staged once per workgroup in LDS (coalesced loads,
+    // converted to float32, chunk rows padded to CK+4 floats so that the
+    // per-lane 16-byte reads below hit distinct banks), then each lane copies
+    // its chunks into registers ----
+    extern __shared__ __attribute__((aligned(16))) float a_lds[];
+    constexpr int ROW = CK + 4;
+    {
+        const int64_t nvec = (int64_t)g.S * (CK / 4);       // float4 slots
+        const bool vec = (g.K & 3) == 0;
+        for (int64_t i = threadIdx.x; i < nvec; i += 64 * kWavesPerBlock) {
+            const int64_t k = 4 * i;
+            float4 v;
+            if (vec && k + 4 <= g.K) {
+                if constexpr (BF16) {
+                    const uint2 x = *reinterpret_cast<const uint2*>(
+                        static_cast<const uint16_t*>(g.a) + k);
+                    v = make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u),
+                                    __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xFFFF0000u));
+                } else {
+                    v = *reinterpret_cast<const float4*>(static_cast<const float*>(g.a) + k);
+                }
+            } else {
+                float e[4];
+#pragma unroll
+                for (int h = 0; h < 4; h++) {
+                    e[h] = 0.f;
+                    if (k + h < g.K)
+                        e[h] = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(g.a)[k + h])
+                                    : static_cast<const float*>(g.a)[k + h];
+                }
+                v = make_float4(e[0], e[1], e[2], e[3]);
+            }
+            const int64_t c = k / CK;
+            *reinterpret_cast<float4*>(&a_lds[c * ROW + (k - c * CK)]) = v;
+        }
+    }
+    __syncthreads();
+    // this lane's chunks of A in registers (odd k pre-scaled by 1/16) and
+    // the chunk sums of the unscaled values
     float av[J][CK];
     float asum[J];
 #pragma unroll
     for (int j = 0; j < J; j++) {
-        const int64_t k0 = (int64_t)(p + j * L) * CK;
-        if (k0 + CK <= g.K) {
-            if constexpr (BF16) {
-                const uint4* src = reinterpret_cast<const uint4*>(
-                    static_cast<const uint16_t*>(g.a) + k0);
+        const int c = p + j * LT;
+        if (c < g.S) {
 #pragma unroll
-                for (int v = 0; v < CK / 8; v++) {
-                    uint4 x = src[v];
-                    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-                    for (int h = 0; h < 4; h++) {
-                        av[j][8 * v + 2 * h] = __uint_as_float(xs[h] << 16);
-                        av[j][8 * v + 2 * h + 1] = __uint_as_float(xs[h] & 0xFFFF0000u);
-                    }
-                }
-            } else {
-                const float4* src = reinterpret_cast<const float4*>(
-                    static_cast<const float*>(g.a) + k0);
-#pragma unroll
-                for (int v = 0; v < CK / 4; v++) {
-                    float4 x = src[v];
-                    av[j][4 * v] = x.x; av[j][4 * v + 1] = x.y;
-                    av[j][4 * v + 2] = x.z; av[j][4 * v + 3] = x.w;
-                }
+            for (int v = 0; v < CK / 4; v++) {
+                const float4 x = *reinterpret_cast<const float4*>(&a_lds[c * ROW + 4 * v]);
+                av[j][4 * v] = x.x; av[j][4 * v + 1] = x.y;
+                av[j][4 * v + 2] = x.z; av[j][4 * v + 3] = x.w;
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < CK; i++) {
-                const int64_t k = k0 + i;
-                float v = 0.f;
-                if (k < g.K)
-                    v = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(g.a)[k])
-                             : static_cast<const float*>(g.a)[k];
-                av[j][i] = v;
-            }
+            for (int i = 0; i < CK; i++) av[j][i] = 0.f;
         }
         float s = 0.f;
 #pragma unroll
         for (int i = 0; i < CK; i++) s += av[j][i];
         asum[j] = s;
+#pragma unroll
+        for (int i = 1; i < CK; i += 2) av[j][i] *= 0.0625f;
     }
 
-    // ---- columns: U groups of G columns per iteration ----
-    for (int64_t base = wave * U; base < g.n_groups; base += n_waves * U) {
-        Chunk w[U][J];
-        float sc[U][J];
-        float zf[U][J];
-        int64_t col[U];
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int64_t gi = base + u;
-            col[u] = gi * G + gsub;
-            const bool ok = gi < g.n_groups && col[u] < g.N;
-            const uint8_t* bc = g.b + col[u] * g.col_bytes;
-#pragma unroll
-            for (int j = 0; j < J; j++) {
-                const int c = p + j * L;
-                if (ok && c < g.S) {
-                    w[u][j] = *reinterpret_cast<const Chunk*>(bc + (int64_t)c * CB);
-                    const int blk = (c * CK) >> g.log2_bs;
-                    const int64_t si = col[u] * g.nb + blk;
-                    sc[u][j] = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(g.scales)[si])
-                                    : static_cast<const float*>(g.scales)[si];
-                    if constexpr (HAS_ZP) {
-                        const uint8_t zb = g.zp[col[u] * g.zp_row + (blk >> 1)];
-                        zf[u][j] = (float)((blk & 1) ? (zb >> 4) : (zb & 0xF));
-                    } else {
-                        zf[u][j] = 8.f;
-                    }
-                } else {
-                    w[u][j] = Chunk{};
-                    sc[u][j] = 0.f;
-                    zf[u][j] = 0.f;
-                }
-            }
-        }
+    for (int64_t it0 = team0; it0 < g.n_groups; it0 += stride, base += stride) {
+        // groups past the end load as zeros, so every register is defined
+        Group<BF16, HAS_ZP, CB, J, U> nxt;
+        if constexpr (PF) load_group(g, base + stride, p, LT, G, gsub, nxt);
         float acc[U];
 #pragma unroll
         for (int u = 0; u < U; u++) {
@@ -171,35 +250,52 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
 #pragma unroll
             for (int j = 0; j < J; j++) {
                 uint32_t words[NW];
-                const uint32_t* wp = reinterpret_cast<const uint32_t*>(&w[u][j]);
 #pragma unroll
-                for (int d = 0; d < NW; d++) words[d] = wp[d];
+                for (int d = 0; d < NW; d++) words[d] = cur.w[u][j][d];
                 const float dot = dot_words<NW>(words, av[j]);
-                const float t = fmaf(-zf[u][j], asum[j], dot);
-                s = fmaf(sc[u][j], t, s);
+                float zf = 8.f;
+                if constexpr (HAS_ZP) {
+                    const int blk = ((p + j * LT) * CK) >> g.log2_bs;
+                    const uint32_t zb = cur.zb[u][j];
+                    zf = (float)((blk & 1) ? (zb >> 4) : (zb & 0xF));
+                }
+                const float sc = BF16 ? __uint_as_float(cur.sc[u][j] << 16)
+                                      : __uint_as_float(cur.sc[u][j]);
+                const float t = fmaf(-zf, asum[j], dot);
+                s = fmaf(sc, t, s);
             }
-            acc[u] = s;
+            acc[u] = reduce_lanes(s, g.log2_L);
         }
-        // butterfly over the L lanes of each column: fixed order, every lane
-        // of the column ends with the same bits
-        for (int off = L >> 1; off > 0; off >>= 1) {
+        if constexpr (W > 1) {
+            if (lane == 0) red[wave] = acc[0];
+            __syncthreads();
+            if (wt == 0) {
+                float v = red[team * W];
 #pragma unroll
-            for (int u = 0; u < U; u++) acc[u] += __shfl_xor(acc[u], off, 64);
+                for (int w2 = 1; w2 < W; w2++) v += red[team * W + w2];
+                acc[0] = v;
+            }
+            __syncthreads();
         }
-        if (p == 0) {
+        if (wt == 0 && (lane & (L - 1)) == 0) {
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int64_t gi = base + u;
-                if (gi < g.n_groups && col[u] < g.N) {
+                const int64_t col = gi * G + gsub;
+                if (gi < g.n_groups && col < g.N) {
                     float v = acc[u];
-                    if (g.bias) v += g.bias[col[u]];
+                    if (g.bias) v += g.bias[col];
                     if constexpr (BF16)
-                        static_cast<uint16_t*>(g.y)[col[u]] = f32_to_bf16_rtne(v);
+                        static_cast<uint16_t*>(g.y)[col] = f32_to_bf16_rtne(v);
                     else
-                        static_cast<float*>(g.y)[col[u]] = v;
+                        static_cast<float*>(g.y)[col] = v;
                 }
             }
         }
+        if constexpr (PF)
+            cur = nxt;
+        else
+            load_group(g, base + stride, p, LT, G, gsub, cur);
     }
 }
 
@@ -209,41 +305,105 @@ int ilog2(int64_t v) {
     return r;
 }
 
-// Lanes per column and chunks per lane: a function of S = ceil(K / CK) only.
-void geometry(int64_t S, int* log2_L, int* J) {
-    int lL = S >= 64 ? 6 : ilog2(S);
-    *log2_L = lL;
-    *J = (int)((S + (1 << lL) - 1) >> lL);
+struct Geometry {
+    int log2_L, J, W;
+};
+
+// Lanes per wavefront, chunks per lane and wavefronts per column: a function
+// of S = ceil(K / CK) only.  Highest lane efficiency S / (L*W*J) first, then
+// fewer wavefronts, then fewer chunks per lane.  J == 0: no register kernel.
+Geometry geometry(int64_t S, bool allow_split) {
+    Geometry best{0, 0, 0};
+    double best_eff = -1.0;
+    for (int W = 1; W <= (allow_split ? kWMax : 1); W *= 2) {
+        for (int lL = 0; lL <= 6; lL++) {
+            if (W > 1 && lL != 6) continue;    // split-K teams use whole wavefronts
+            const int64_t LT = (int64_t(1) << lL) * W;
+            if (LT > 2 * S && lL > 0) continue; // more than twice the lanes needed
+            const int64_t J = (S + LT - 1) / LT;
+            if (J > kJMax) continue;
+            const double eff = (double)S / (double)(LT * J);
+            const bool better = eff > best_eff + 1e-9 ||
+                                (eff > best_eff - 1e-9 && (W < best.W || (W == best.W && J < best.J)));
+            if (better) {
+                best = Geometry{lL, (int)J, W};
+                best_eff = eff;
+            }
+        }
+    }
+    return best;
 }
 
-// Columns unrolled per iteration: enough independent loads in flight with
-// few chunks per lane, fewer registers with many.
+// Columns unrolled per iteration when there are plenty of columns.
 constexpr int unroll_for(int J) { return J == 1 ? 4 : J == 2 ? 2 : 1; }
+// Resident wavefronts per SIMD that the register use of (J, U) allows
+// (from the compiler's resource report for gfx950).
+constexpr int occupancy_for(int J, int U) {
+    return U == 1 ? (J == 1 ? 7 : J == 2 ? 4 : 2) : (J == 1 ? 3 : 2);
+}
 
-template <bool BF16, bool HAS_ZP, int CB>
-hipError_t dispatch_j(int J, dim3 grid, hipStream_t s, const GemvArgs& a) {
-    switch (J) {
-        case 1: hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, 1, unroll_for(1)>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, 2, unroll_for(2)>), grid, dim3(256), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, 3, unroll_for(3)>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, 4, unroll_for(4)>), grid, dim3(256), 0, s, a); break;
-        case 5: hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, 5, unroll_for(5)>), grid, dim3(256), 0, s, a); break;
-        default: return hipErrorInvalidValue;
+template <bool BF16, bool HAS_ZP, int CB, int J>
+hipError_t launch_j(int U, int W, unsigned blocks, size_t lds, hipStream_t s, const GemvArgs& a) {
+    constexpr int UJ = unroll_for(J);
+    constexpr bool PF = J <= 3;
+    if (W == 1 && U == 1)
+        hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, J, 1, 1, PF>), dim3(blocks), dim3(256), lds, s, a);
+    else if (W == 1)
+        hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, J, UJ, 1, PF>), dim3(blocks), dim3(256), lds, s, a);
+    else if constexpr (CB == 16) {
+        if (W == 2)
+            hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, J, 1, 2, PF>), dim3(blocks), dim3(256), lds, s, a);
+        else
+            hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, J, 1, 4, PF>), dim3(blocks), dim3(256), lds, s, a);
+    } else {
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+template <bool BF16, bool HAS_ZP, int CB>
+hipError_t launch_cb(int J, int U, int W, unsigned blocks, size_t lds, hipStream_t s, const GemvArgs& a) {
+    switch (J) {
+        case 1: return launch_j<BF16, HAS_ZP, CB, 1>(U, W, blocks, lds, s, a);
+        case 2: return launch_j<BF16, HAS_ZP, CB, 2>(U, W, blocks, lds, s, a);
+        case 3: return launch_j<BF16, HAS_ZP, CB, 3>(U, W, blocks, lds, s, a);
+        case 4: return launch_j<BF16, HAS_ZP, CB, 4>(U, W, blocks, lds, s, a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <bool BF16, bool HAS_ZP>
-hipError_t dispatch_cb(int CB, int J, dim3 grid, hipStream_t s, const GemvArgs& a) {
-    return CB == 16 ? dispatch_j<BF16, HAS_ZP, 16>(J, grid, s, a)
-                    : dispatch_j<BF16, HAS_ZP, 8>(J, grid, s, a);
+hipError_t launch_dt(int CB, int J, int U, int W, unsigned blocks, size_t lds, hipStream_t s,
+                     const GemvArgs& a) {
+    return CB == 16 ? launch_cb<BF16, HAS_ZP, 16>(J, U, W, blocks, lds, s, a)
+                    : launch_cb<BF16, HAS_ZP, 8>(J, U, W, blocks, lds, s, a);
+}
+
+int compute_units() {
+    static thread_local int cached_dev = -1, cached_cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached_dev = dev;
+        cached_cus = cus;
+    }
+    return cached_cus;
 }
 
 }  // namespace
 
 int64_t gemv_max_k(int bs) {
+    // limited by the register geometry (S <= 64 * W * kJMax chunks) and by
+    // the staged activations (S rows of CK + 4 floats in kMaxLds bytes)
     const int CK = bs >= 32 ? 32 : 16;
-    return (int64_t)64 * kJMax * CK;
+    const int W = bs >= 32 ? kWMax : 1;
+    int64_t s_max = (int64_t)64 * W * kJMax;
+    const int64_t s_lds = (int64_t)(kMaxLds / ((CK + 4) * sizeof(float)));
+    if (s_lds < s_max) s_max = s_lds;
+    return s_max * CK;
 }
 
 int launch_gemv(const Problem& p, hipStream_t s) {
@@ -256,23 +416,38 @@ int launch_gemv(const Problem& p, hipStream_t s) {
     a.nb = p.nb; a.zp_row = p.zp_row;
     a.S = (int)((p.K + CK - 1) / CK);
     a.log2_bs = ilog2(p.bs);
-    int J;
-    geometry(a.S, &a.log2_L, &J);
-    if (J > kJMax) return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld beyond the register kernel", (long long)p.K);
-    const int G = 64 >> a.log2_L;
+    const Geometry geo = geometry(a.S, CB == 16);
+    if (geo.J == 0)
+        return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld beyond the register kernel", (long long)p.K);
+    a.log2_L = geo.log2_L;
+    const int G = geo.W == 1 ? (64 >> geo.log2_L) : 1;
     a.n_groups = (p.N + G - 1) / G;
-    // at most about 2048 wavefronts (8 per CU); each takes U groups per pass
-    const int U = unroll_for(J);
-    int64_t waves = (a.n_groups + U - 1) / U;
-    if (waves > 2048) waves = 2048;
-    const unsigned blocks = (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+    // Fill the chip: resident wavefronts = CUs x 4 SIMDs x occupancy; each
+    // team of W wavefronts takes U groups per iteration.  Unroll only when
+    // there are enough groups to give every resident team U of them.
+    const int64_t simds = (int64_t)compute_units() * 4;
+    const int UJ = unroll_for(geo.J);
+    int U = 1;
+    int64_t slots = simds * occupancy_for(geo.J, 1) / geo.W;
+    if (geo.W == 1 && UJ > 1 && a.n_groups >= simds * occupancy_for(geo.J, UJ) * UJ) {
+        U = UJ;
+        slots = simds * occupancy_for(geo.J, UJ);
+    }
+    int64_t teams = (a.n_groups + U - 1) / U;
+    if (teams > slots) teams = slots;
+    const int teams_per_block = kWavesPerBlock / geo.W;
+    const unsigned blocks = (unsigned)((teams + teams_per_block - 1) / teams_per_block);
+    // staged activations: S chunk rows of CK + 4 floats
+    const size_t lds = (size_t)a.S * (CK + 4) * sizeof(float);
+    if (lds > kMaxLds)
+        return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld needs %zu bytes of LDS", (long long)p.K, lds);
     hipError_t e;
     if (p.bf16)
-        e = p.has_zp ? dispatch_cb<true, true>(CB, J, dim3(blocks), s, a)
-                     : dispatch_cb<true, false>(CB, J, dim3(blocks), s, a);
+        e = p.has_zp ? launch_dt<true, true>(CB, geo.J, U, geo.W, blocks, lds, s, a)
+                     : launch_dt<true, false>(CB, geo.J, U, geo.W, blocks, lds, s, a);
     else
-        e = p.has_zp ? dispatch_cb<false, true>(CB, J, dim3(blocks), s, a)
-                     : dispatch_cb<false, false>(CB, J, dim3(blocks), s, a);
+        e = p.has_zp ? launch_dt<false, true>(CB, geo.J, U, geo.W, blocks, lds, s, a)
+                     : launch_dt<false, false>(CB, geo.J, U, geo.W, blocks, lds, s, a);
     if (e != hipSuccess) return fail(MNB_E_HIP, "gemv launch: %s", hipGetErrorString(e));
     return MNB_OK;
 }

@@ -67,4 +67,13 @@ __device__ __forceinline__ float ubyte_to_f32(uint32_t x) {
     return (float)((x >> (8 * B)) & 0xFFu);
 }
 
+// (x & m) | e in one v_and_or_b32.  gfx9 VOP3 encodings take no literal
+// constants, so the compiler otherwise splits this into an AND and an OR; the
+// masks are loop invariants that live in VGPRs.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t e) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(e));
+    return r;
+}
+
 }  // namespace mnb
