@@ -298,3 +298,40 @@ def test_unaligned_view_is_rejected():
     with pytest.raises(mnb.MnbError) as e:
         mnb.gemv(big[1:].view(1, K), pw.b_packed, pw.scales, K=K, N=N, block_size=bs)
     assert e.value.status == -3
+
+
+@pytest.mark.parametrize("K,N,bs,zp", [(256, 300, 128, True), (160, 70, 32, False),
+                                       (48, 33, 16, True), (80, 17, 16, False)])
+def test_bf16_gemm_identity_returns_bf16_dequant(orc, K, N, bs, zp):
+    """With bfloat16 activations the prefill kernel multiplies the bf16
+    rounding of the exact weight: A = I_K must return exactly the bf16
+    dequantization (itself checked bit-exactly against the oracle)."""
+    inp, g = _inputs(K, N, 1, bs, "bf16", zp, False, seed=K + N)
+    pw = _packed(g, bs)
+    w16 = mnb.dequant(pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N, block_size=bs,
+                      act_dtype=torch.bfloat16, out_kind=mnb.DEQUANT_BF16)
+    w_exact = orc.dequant(inp.q.numpy(), None if inp.zp is None else inp.zp.numpy(),
+                          act_np(inp.scales), bs)
+    assert np.array_equal(act_np(w16), orc.round_to_bf16(w_exact))
+    eye = torch.eye(K, device=DEV, dtype=torch.bfloat16)
+    y = mnb.gemm(eye, pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N, block_size=bs)
+    assert np.array_equal(act_np(y), act_np(w16).T)
+
+
+@pytest.mark.parametrize("M,K,N,bs,zp,bias", [(1000, 192, 24676, 64, True, True),
+                                              (2048, 128, 12288, 128, False, False),
+                                              (1030, 320, 24600, 32, True, False)])
+def test_bf16_gemm_large_grid_sampled(orc, M, K, N, bs, zp, bias):
+    """Grids of >= 384 tiles of 256x256 take the LDS-ring prefill kernel
+    (K a multiple of 64 and of the block size); ragged M and N, an odd
+    number of K steps; sampled rows x columns against the oracle."""
+    log(f"large bf16 gemm M={M} K={K} N={N} bs={bs} zp={zp} bias={bias}")
+    inp, g = _inputs(K, N, M, bs, "bf16", zp, bias, seed=M + K + N)
+    pw = _packed(g, bs)
+    y = mnb.gemm(g.a, pw.b_packed, pw.scales, pw.zp_packed, pw.bias, K=K, N=N, block_size=bs)
+    rng = np.random.default_rng(M)
+    rows = sorted({0, M - 1, 255, 256, *rng.choice(M, 12, replace=False).tolist()})
+    cols = sorted({0, N - 1, 255, 256, N - 257, *rng.choice(N, 40, replace=False).tolist()})
+    y_ref, S = oracle_ref(orc, inp, rows, cols)
+    ys = y[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)]
+    assert_close(out_f64(ys), y_ref, S, "bf16", f"M={M} K={K} N={N}")

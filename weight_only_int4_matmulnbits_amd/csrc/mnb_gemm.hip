@@ -27,6 +27,7 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int PAD = 8;              // bf16 elements of padding per LDS row
@@ -246,6 +247,478 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// bfloat16 activations: scaled bf16 weight tiles, one MFMA per product.
+//
+// For bf16 activations the scales are bf16 too, so (q - zp) * s is exact in
+// float32 (at most 5 + 8 significant bits) and its bf16 rounding is a single
+// rounding of the exact weight -- the same value mnb_dequant's bf16 output
+// gives.  The weight panel is therefore dequantized once per workgroup into
+// LDS as bf16 and multiplied directly: no per-block partial sums, one MFMA per
+// product.
+//
+// Tile BM x BN x 64 per workgroup of 8 wavefronts (2 along M x 4 along N;
+// each wavefront (BM/2) x (BN/4) = TM x TN MFMA 32x32x16 tiles).  LDS is
+// double-buffered (A and B panels as bf16, rows padded by 16 bytes so that the
+// lanes' 16-byte operand reads fall in distinct banks); the next K step is
+// fetched into registers while the current one is multiplied, so one barrier
+// per K step suffices.  Global reads go through buffer resources: 32-bit
+// offsets advanced by a constant per K step, and reads past a tensor's end
+// return zeros (rows past M, columns past N; values past K are zeroed
+// explicitly and pad nibbles only ever meet zero activations).  Workgroups
+// are remapped so that consecutive output tiles (the row tiles sharing one
+// weight panel first) run on the same XCD and share its L2.
+// ---------------------------------------------------------------------------
+constexpr int B2_K = 64;
+constexpr int B2_LDR = B2_K + 8;                  // bf16 per LDS row
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int2 xcd_tile(int bid, int nblk, int mt) {
+    // bijective remap: the blocks that land on XCD x (bid % 8 == x) take a
+    // contiguous range of tiles; tile t -> (m = t % mt, n = t / mt)
+    const int q = nblk / 8, r = nblk % 8;
+    const int x = bid % 8, j = bid / 8;
+    const int t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+    return make_int2(t % mt, t / mt);
+}
+
+struct Bf16Args {
+    const void* a;
+    const uint8_t* b;
+    const void* scales;
+    const uint8_t* zp;
+    const float* bias;
+    void* y;
+    int M, K, N, col_bytes, k_pad, nb, zp_row, log2_bs;
+    uint32_t a_bytes, b_bytes, s_bytes, z_bytes;
+};
+
+template <int BM, int BN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(Bf16Args g) {
+    constexpr int T = 64 * WAVES;
+    constexpr int WN = WAVES / 2;                       // wavefronts along N (2 along M)
+    constexpr int TM = BM / 64, TN = BN / WN / 32;      // MFMA tiles per wavefront
+    constexpr int AR = BM * 8 / T;                      // 16-byte A chunks per thread
+    constexpr int BR = (BN * 2 + T - 1) / T;            // 16-byte packed-B chunks per thread
+    static_assert(AR >= 1 && TN >= 1, "tile too small for the wavefront count");
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * B2_LDR];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * B2_LDR];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int mt = (g.M + BM - 1) / BM;
+    const int nt = (g.N + BN - 1) / BN;
+    const int2 tile = xcd_tile(blockIdx.x, mt * nt, mt);
+    const int m0 = tile.x * BM;
+    const int n0 = tile.y * BN;
+
+    const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(g.a), (short)0, (int)g.a_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(g.b), (short)0, (int)g.b_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(g.scales), (short)0, (int)g.s_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(g.zp ? g.zp : g.b), (short)0, (int)(g.zp ? g.z_bytes : 0), 0x00020000);
+
+    // staging roles: A chunk q = t + T*i is row q/8, 16-byte chunk q%8 of the
+    // 64-wide K step; packed-B chunk q = t + T*i is column q/2, 16 bytes (32
+    // values) half q%2
+    const int a_r = t >> 3, a_c = t & 7;
+    const uint32_t a_base = (uint32_t)(m0 + a_r) * (uint32_t)g.K * 2u + 16u * a_c;
+    const uint32_t a_step = (uint32_t)(T / 8) * (uint32_t)g.K * 2u;   // rows between a thread's chunks
+
+    struct StageA {
+        u32x4 a[AR];
+    };
+    struct StageB {
+        u32x4 b[BR];
+        uint32_t s[BR][2], z[BR][2];   // scale bits and zero point of values 0-15, 16-31
+    };
+
+    auto fetch_a = [&](int k0, StageA& st) {
+        const bool k_in = k0 + 8 * a_c < g.K;            // K % 8 == 0: whole chunk in or out
+#pragma unroll
+        for (int i = 0; i < AR; i++) {
+            st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_base + a_step * i + 2u * k0, 0, 0);
+            if (!k_in) st.a[i] = u32x4{0, 0, 0, 0};
+        }
+    };
+    auto fetch_b = [&](int k0, StageB& st) {
+#pragma unroll
+        for (int i = 0; i < BR; i++) {
+            const int q = t + T * i;
+            if (q < 2 * BN) {
+                const int col = n0 + (q >> 1), half = q & 1;
+                const int kb = k0 + 32 * half;
+                st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rb_rs, (uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)kb / 2u, 0, 0);
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const uint32_t blk = (uint32_t)(kb + 16 * h) >> g.log2_bs;
+                    st.s[i][h] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rs_rs, 2u * ((uint32_t)col * (uint32_t)g.nb + blk), 0, 0);
+                    st.z[i][h] = g.zp ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
+                                            rz_rs, (uint32_t)col * (uint32_t)g.zp_row + (blk >> 1), 0, 0)
+                                            | ((blk & 1u) << 8)
+                                      : 0x8u;
+                }
+            }
+        }
+    };
+
+    auto stash_a = [&](const StageA& st, int buf) {
+#pragma unroll
+        for (int i = 0; i < AR; i++)
+            *reinterpret_cast<u32x4*>(&As[buf][(a_r + (T / 8) * i) * B2_LDR + 8 * a_c]) = st.a[i];
+    };
+    auto stash_b = [&](const StageB& st, int buf) {
+#pragma unroll
+        for (int i = 0; i < BR; i++) {
+            const int q = t + T * i;
+            if (q < 2 * BN) {
+                const int c = q >> 1, half = q & 1;
+#pragma unroll
+                for (int d = 0; d < 4; d++) {
+                    // (q - zp) * s exact in float32, then one RTNE rounding to bf16
+                    const uint32_t zraw = st.z[i][d >> 1];
+                    const uint32_t zq = g.zp ? ((zraw & 0x100u) ? ((zraw >> 4) & 0xFu) : (zraw & 0xFu)) : 8u;
+                    const float s = __uint_as_float(st.s[i][d >> 1] << 16);
+                    const float zs = (float)zq * s;
+                    const uint32_t lo = opaque_and(st.b[i][d], 0x0F0F0F0Fu);
+                    const uint32_t hi = opaque_and(st.b[i][d] >> 4, 0x0F0F0F0Fu);
+                    float v[8];
+                    v[0] = fmaf(ubyte_to_f32<0>(lo), s, -zs); v[1] = fmaf(ubyte_to_f32<0>(hi), s, -zs);
+                    v[2] = fmaf(ubyte_to_f32<1>(lo), s, -zs); v[3] = fmaf(ubyte_to_f32<1>(hi), s, -zs);
+                    v[4] = fmaf(ubyte_to_f32<2>(lo), s, -zs); v[5] = fmaf(ubyte_to_f32<2>(hi), s, -zs);
+                    v[6] = fmaf(ubyte_to_f32<3>(lo), s, -zs); v[7] = fmaf(ubyte_to_f32<3>(hi), s, -zs);
+                    uint32_t o[4];
+#pragma unroll
+                    for (int h = 0; h < 4; h++) {
+                        bf16x2 pr;
+                        pr[0] = (__bf16)v[2 * h];
+                        pr[1] = (__bf16)v[2 * h + 1];
+                        o[h] = __builtin_bit_cast(uint32_t, pr);
+                    }
+                    *reinterpret_cast<u32x4*>(&Bs[buf][c * B2_LDR + 32 * half + 8 * d]) =
+                        u32x4{o[0], o[1], o[2], o[3]};
+                }
+            }
+        }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    auto multiply = [&](int buf) {
+#pragma unroll 1
+        for (int ks = 0; ks < B2_K / 16; ks++) {
+            const int koff = ks * 16 + 8 * (lane >> 5);
+            bf16x8 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+                af[i] = *reinterpret_cast<const bf16x8*>(
+                    &As[buf][(wm * (BM / 2) + i * 32 + (lane & 31)) * B2_LDR + koff]);
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+                bfr[j] = *reinterpret_cast<const bf16x8*>(
+                    &Bs[buf][(wn * (BN / WN) + j * 32 + (lane & 31)) * B2_LDR + koff]);
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // Pipeline over K steps (one barrier per step).  While step s is
+    // multiplied from LDS buffer s % 2, step s + 1 is moved from registers to
+    // the other buffer, the weights of step s + 2 and the activations of step
+    // s + 1 are requested.  Each half of the unrolled loop is one basic block
+    // (reads past the end return zeros or are never used, and the last,
+    // redundant stash goes to a buffer that is not read again) so the
+    // scheduler can interleave the unpacking and LDS traffic with the MFMAs.
+    const int steps = (g.k_pad + B2_K - 1) / B2_K;
+    StageA sa;
+    StageB sb0, sb1;
+    fetch_a(0, sa);
+    fetch_b(0, sb0);
+    stash_a(sa, 0);
+    stash_b(sb0, 0);
+    fetch_a(B2_K, sa);
+    fetch_b(B2_K, sb1);
+    __syncthreads();
+    for (int st = 0; st < steps; st += 2) {
+        fetch_b((st + 2) * B2_K, sb0);
+        multiply(0);
+        stash_a(sa, 1);
+        stash_b(sb1, 1);
+        fetch_a((st + 2) * B2_K, sa);
+        __syncthreads();
+        if (st + 1 >= steps) break;
+        fetch_b((st + 3) * B2_K, sb1);
+        multiply(1);
+        stash_a(sa, 0);
+        stash_b(sb0, 0);
+        fetch_a((st + 3) * B2_K, sa);
+        __syncthreads();
+    }
+
+    // epilogue: + bias, RTNE to bf16, store
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+        const int n = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
+        if (n >= g.N) continue;
+        const float bv = g.bias ? g.bias[n] : 0.f;
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (m < g.M)
+                    static_cast<uint16_t*>(g.y)[(int64_t)m * g.N + n] = f32_to_bf16_rtne(acc[i][j][r] + bv);
+            }
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// bf16 activations, large grids: 256 x 256 x 64 tiles on 4 wavefronts of
+// 128 x 128 (16 MFMA 32x32x16 tiles each, accumulators in AGPRs).
+//
+//  * The activation panel goes from HBM straight into LDS (buffer loads with
+//    the LDS destination, no registers), into a ring of three K-step slots, two
+//    steps ahead of its use.  Each 128-byte row holds its eight 16-byte chunks
+//    XOR-swizzled by (row & 7), so the MFMA operand reads of 8 consecutive
+//    rows hit distinct banks without padding.
+//  * The packed weights (with their scales and zero points) are read into
+//    registers two steps ahead and unpacked to scaled bf16 into one of two
+//    LDS buffers (same swizzle) one step ahead.
+//  * One vmcnt wait and one barrier per K step: the LDS-direct loads are
+//    invisible to the compiler's wait insertion, so the wait counts the
+//    memory instructions issued in the current step (a compile-time number).
+// Requires K % 64 == 0 and K % block_size == 0 (no partial K step or block).
+// ---------------------------------------------------------------------------
+constexpr int B4_M = 256, B4_N = 256, B4_K = 64, B4_RING = 3;
+
+template <bool HAS_ZP>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_lds_kernel(Bf16Args g) {
+    constexpr int TM = 4, TN = 4;
+    constexpr int A_BYTES = B4_M * B4_K * 2;            // one activation K step: 32 KiB
+    constexpr int B_BYTES = B4_N * B4_K * 2;            // one bf16 weight K step: 32 KiB
+    constexpr int BR = 2;                               // packed-weight chunks per thread
+    // memory instructions a thread issues per K step: 8 activation loads,
+    // and per weight chunk 1 + 2 scale (+ 2 zero-point) loads
+    constexpr int VMEM_PER_STEP = 8 + BR * (HAS_ZP ? 5 : 3);
+    __shared__ __attribute__((aligned(16))) uint8_t lds[B4_RING * A_BYTES + 2 * B_BYTES];
+    uint8_t* const As = lds;
+    uint8_t* const Bs = lds + B4_RING * A_BYTES;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int mt = (g.M + B4_M - 1) / B4_M;
+    const int nt = (g.N + B4_N - 1) / B4_N;
+    const int2 tile = xcd_tile(blockIdx.x, mt * nt, mt);
+    const int m0 = tile.x * B4_M;
+    const int n0 = tile.y * B4_N;
+
+    const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(g.a), (short)0, (int)g.a_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(g.b), (short)0, (int)g.b_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(g.scales), (short)0, (int)g.s_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(HAS_ZP ? g.zp : g.b), (short)0, (int)(HAS_ZP ? g.z_bytes : 0), 0x00020000);
+
+    // activation loads: wavefront w fills rows 64w .. 64w+63 of a slot, eight
+    // rows per instruction; lane l lands in LDS at row l/8, slot l%8 and so
+    // fetches chunk (l%8) ^ (l/8) of its row
+    const int a_row = 64 * wave + (lane >> 3);
+    const int a_chunk = (lane & 7) ^ (lane >> 3);
+    const uint32_t a_off = (uint32_t)(m0 + a_row) * (uint32_t)g.K * 2u + 16u * a_chunk;
+    const uint32_t a_row8 = 8u * (uint32_t)g.K * 2u;        // byte distance of 8 rows
+
+    auto issue_a = [&](int k0, int slot) {
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra_rs, (void __attribute__((address_space(3)))*)(As + slot * A_BYTES + (64 * wave + 8 * i) * 128),
+                16, a_off + a_row8 * i + 2u * k0, 0, 0, 0);
+    };
+
+    struct StageB {
+        u32x4 b[BR];
+        uint32_t s[BR][2], z[BR][2];
+    };
+    auto fetch_b = [&](int k0, StageB& st) {
+#pragma unroll
+        for (int i = 0; i < BR; i++) {
+            const int q = t + 256 * i;
+            const int col = n0 + (q >> 1), half = q & 1;
+            const int kb = k0 + 32 * half;
+            st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                rb_rs, (uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)kb / 2u, 0, 0);
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const uint32_t blk = (uint32_t)(kb + 16 * h) >> g.log2_bs;
+                st.s[i][h] = __builtin_amdgcn_raw_buffer_load_b16(
+                    rs_rs, 2u * ((uint32_t)col * (uint32_t)g.nb + blk), 0, 0);
+                if constexpr (HAS_ZP)
+                    st.z[i][h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
+                                     rz_rs, (uint32_t)col * (uint32_t)g.zp_row + (blk >> 1), 0, 0)
+                                 | ((blk & 1u) << 8);
+                else
+                    st.z[i][h] = 8u;
+            }
+        }
+    };
+    // unpack one 8-value word (chunk i, word d) of a staged weight step into
+    // LDS buffer buf: (q - zp) * s exact in float32, one RTNE rounding to bf16
+    auto stash_piece = [&](const StageB& st, int buf, int i, int d) {
+        const int q = t + 256 * i;
+        const int c = q >> 1, half = q & 1;
+        const uint32_t zraw = st.z[i][d >> 1];
+        const uint32_t zq = HAS_ZP ? ((zraw & 0x100u) ? ((zraw >> 4) & 0xFu) : (zraw & 0xFu)) : 8u;
+        const float sc = __uint_as_float(st.s[i][d >> 1] << 16);
+        const float zs = (float)zq * sc;
+        const uint32_t lo = opaque_and(st.b[i][d], 0x0F0F0F0Fu);
+        const uint32_t hi = opaque_and(st.b[i][d] >> 4, 0x0F0F0F0Fu);
+        float v[8];
+        v[0] = fmaf(ubyte_to_f32<0>(lo), sc, -zs); v[1] = fmaf(ubyte_to_f32<0>(hi), sc, -zs);
+        v[2] = fmaf(ubyte_to_f32<1>(lo), sc, -zs); v[3] = fmaf(ubyte_to_f32<1>(hi), sc, -zs);
+        v[4] = fmaf(ubyte_to_f32<2>(lo), sc, -zs); v[5] = fmaf(ubyte_to_f32<2>(hi), sc, -zs);
+        v[6] = fmaf(ubyte_to_f32<3>(lo), sc, -zs); v[7] = fmaf(ubyte_to_f32<3>(hi), sc, -zs);
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 4; h++) {
+            bf16x2 pr;
+            pr[0] = (__bf16)v[2 * h];
+            pr[1] = (__bf16)v[2 * h + 1];
+            o[h] = __builtin_bit_cast(uint32_t, pr);
+        }
+        const int chunk = 4 * half + d;
+        *reinterpret_cast<u32x4*>(Bs + buf * B_BYTES + c * 128 + ((chunk ^ (c & 7)) << 4)) =
+            u32x4{o[0], o[1], o[2], o[3]};
+    };
+    auto stash_b = [&](const StageB& st, int buf) {
+#pragma unroll
+        for (int i = 0; i < BR; i++)
+#pragma unroll
+            for (int d = 0; d < 4; d++) stash_piece(st, buf, i, d);
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    // One K step: 4 substeps of 16 MFMAs on (slot, buf), with the next
+    // substep's operands read ahead and the unpacking of the next weight step
+    // (two 8-value words per substep) interleaved between the MFMAs, so that
+    // the matrix pipe never waits for the vector ALU or for LDS.
+    auto step_body = [&](int slot, int buf, const StageB& next_w) {
+        const uint8_t* a = As + slot * A_BYTES;
+        const uint8_t* b = Bs + buf * B_BYTES;
+        bf16x8 af[2][TM], bfr[2][TN];
+        auto load_frags = [&](int ks, int p) {
+            const int chunk = 2 * ks + (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                const int r = wm * 128 + i * 32 + (lane & 31);
+                af[p][i] = *reinterpret_cast<const bf16x8*>(a + r * 128 + ((chunk ^ (r & 7)) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const int c = wn * 128 + j * 32 + (lane & 31);
+                bfr[p][j] = *reinterpret_cast<const bf16x8*>(b + c * 128 + ((chunk ^ (c & 7)) << 4));
+            }
+        };
+        load_frags(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < B4_K / 16; ks++) {
+            const int p = ks & 1;
+            if (ks + 1 < B4_K / 16) load_frags(ks + 1, p ^ 1);
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][i], bfr[p][j], acc[i][j], 0, 0, 0);
+            // two of the eight unpack pieces per substep
+            stash_piece(next_w, buf ^ 1, (2 * ks) >> 2, (2 * ks) & 3);
+            stash_piece(next_w, buf ^ 1, (2 * ks + 1) >> 2, (2 * ks + 1) & 3);
+#pragma unroll
+            for (int g2 = 0; g2 < 16; g2++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
+            }
+        }
+    };
+
+    // wait until at most N memory instructions of this thread are outstanding
+    // (gfx9 s_waitcnt encoding: vmcnt split over bits 3:0 and 15:14, expcnt
+    // and lgkmcnt left at their maxima)
+    constexpr int WAIT_PREV = VMEM_PER_STEP;
+    constexpr int WAIT_IMM = (WAIT_PREV & 15) | (7 << 4) | (15 << 8) | ((WAIT_PREV >> 4) << 14);
+
+    const int steps = g.K / B4_K;
+    StageB cur, nxt;                      // weights of the next step, of the one after
+    // prologue: steps 0 and 1 requested, step 0 complete and visible
+    issue_a(0, 0);
+    fetch_b(0, nxt);
+    issue_a(B4_K, 1);
+    fetch_b(B4_K, cur);
+    stash_b(nxt, 0);                      // waits (compiler) for step 0's weight loads
+    __builtin_amdgcn_s_waitcnt(WAIT_IMM); // step 0's activation loads have landed
+    __syncthreads();
+    // one straight-line body per K step, so the accumulators stay in AGPRs:
+    // multiply step st (ring slot st % 3, weight buffer st % 2), unpack step
+    // st+1 into the other weight buffer, request step st+2
+    int slot = 0, buf = 0;
+    for (int st = 0; st < steps; st++) {
+        const int nslot = slot == 2 ? 0 : slot + 1;
+        const int fslot = nslot == 2 ? 0 : nslot + 1;
+        fetch_b((st + 2) * B4_K, nxt);
+        issue_a((st + 2) * B4_K, fslot);
+        step_body(slot, buf, cur);
+        __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+        __syncthreads();
+        cur = nxt;
+        slot = nslot;
+        buf ^= 1;
+    }
+
+    // epilogue: + bias, RTNE to bf16, store
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+        const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+        if (n >= g.N) continue;
+        const float bv = g.bias ? g.bias[n] : 0.f;
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (m < g.M)
+                    static_cast<uint16_t*>(g.y)[(int64_t)m * g.N + n] = f32_to_bf16_rtne(acc[i][j][r] + bv);
+            }
+    }
+}
+
 }  // namespace
 
 int launch_gemm(const Problem& p, hipStream_t s) {
@@ -257,11 +730,40 @@ int launch_gemm(const Problem& p, hipStream_t s) {
     a.nb = p.nb; a.zp_row = p.zp_row; a.bs = p.bs;
     const int esz = p.bf16 ? 2 : 4;
     a.vec_a = ((p.K * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(p.a) & 15) == 0);
-    const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
-    if (p.bf16)
+    const int64_t a_bytes = p.M * p.K * esz, b_bytes = p.N * p.col_bytes;
+    const int64_t lim = int64_t(1) << 31;
+    if (p.bf16 && a.vec_a && (p.K % 8) == 0 && a_bytes + 256 * p.K * esz < lim && b_bytes < lim &&
+        p.M * p.N < lim) {
+        Bf16Args b;
+        b.a = p.a; b.b = p.b; b.scales = p.scales; b.zp = p.has_zp ? p.zp : nullptr;
+        b.bias = p.bias; b.y = p.y;
+        b.M = (int)p.M; b.K = (int)p.K; b.N = (int)p.N; b.col_bytes = (int)p.col_bytes;
+        b.k_pad = (int)a.k_pad; b.nb = p.nb; b.zp_row = p.zp_row;
+        int l2 = 0;
+        while ((1 << l2) < p.bs) l2++;
+        b.log2_bs = l2;
+        b.a_bytes = (uint32_t)a_bytes; b.b_bytes = (uint32_t)b_bytes;
+        b.s_bytes = (uint32_t)(p.N * p.nb * 2); b.z_bytes = (uint32_t)(p.N * p.zp_row);
+        // large tiles when they fill the chip, smaller ones otherwise
+        const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+        if (big >= 384 && p.K % B4_K == 0 && p.K % p.bs == 0) {
+            if (p.has_zp)
+                hipLaunchKernelGGL(gemm_bf16_lds_kernel<true>, dim3((unsigned)big), dim3(256), 0, s, b);
+            else
+                hipLaunchKernelGGL(gemm_bf16_lds_kernel<false>, dim3((unsigned)big), dim3(256), 0, s, b);
+        } else if (big >= 384) {
+            hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4>), dim3((unsigned)big), dim3(256), 0, s, b);
+        } else {
+            const int64_t small = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+            hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 8>), dim3((unsigned)small), dim3(512), 0, s, b);
+        }
+    } else if (p.bf16) {
+        const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
         hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(256), 0, s, a);
-    else
+    } else {
+        const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
         hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(256), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MNB_E_HIP, "gemm launch: %s", hipGetErrorString(e));
     return MNB_OK;
