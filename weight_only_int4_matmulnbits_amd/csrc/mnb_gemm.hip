@@ -493,35 +493,38 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(Bf16Args g) {
 
 // ---------------------------------------------------------------------------
 // bf16 activations, large grids: 256 x 256 x 64 tiles on 4 wavefronts of
-// 128 x 128 (16 MFMA 32x32x16 tiles each, accumulators in AGPRs).
+// 128 x 128 (16 MFMA 32x32x16 tiles each, accumulators in AGPRs; one
+// wavefront per SIMD).
 //
-//  * The activation panel goes from HBM straight into LDS (buffer loads with
-//    the LDS destination, no registers), into a ring of three K-step slots, two
-//    steps ahead of its use.  Each 128-byte row holds its eight 16-byte chunks
-//    XOR-swizzled by (row & 7), so the MFMA operand reads of 8 consecutive
-//    rows hit distinct banks without padding.
-//  * The packed weights (with their scales and zero points) are read into
-//    registers two steps ahead and unpacked to scaled bf16 into one of two
-//    LDS buffers (same swizzle) one step ahead.
-//  * One vmcnt wait and one barrier per K step: the LDS-direct loads are
-//    invisible to the compiler's wait insertion, so the wait counts the
-//    memory instructions issued in the current step (a compile-time number).
+//  * Both operand panels of a K step live in LDS as bf16, double-buffered
+//    (4 x 32 KiB): the activations as loaded, the weights unpacked to
+//    bf16((q - zp) * s).  Rows are 128 bytes (64 K values); the eight
+//    16-byte chunks of row r sit at chunk ^ ((r >> 1) & 7), so the operand
+//    reads of 16 consecutive rows (one 256-byte bank sweep) are conflict-free.
+//  * Global reads run two K steps ahead into registers (plain buffer loads,
+//    so the compiler tracks every one of them and waits precisely); while
+//    step s is multiplied, step s + 1 is moved from registers into the other
+//    LDS buffers, interleaved with the MFMAs.
+//  * One barrier per K step; the loop body is two steps with the register
+//    stages swapped (a stage copy would wait for loads just issued) and no
+//    exit in the middle (so the accumulators stay in AGPRs).
 // Requires K % 64 == 0 and K % block_size == 0 (no partial K step or block).
 // ---------------------------------------------------------------------------
-constexpr int B4_M = 256, B4_N = 256, B4_K = 64, B4_RING = 3;
+constexpr int B4_M = 256, B4_N = 256, B4_K = 64;
 
-template <bool HAS_ZP>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_lds_kernel(Bf16Args g) {
+// byte offset of 16-byte chunk c of 128-byte row r
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+template <bool HAS_ZP, bool BS16>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     constexpr int TM = 4, TN = 4;
-    constexpr int A_BYTES = B4_M * B4_K * 2;            // one activation K step: 32 KiB
-    constexpr int B_BYTES = B4_N * B4_K * 2;            // one bf16 weight K step: 32 KiB
-    constexpr int BR = 2;                               // packed-weight chunks per thread
-    // memory instructions a thread issues per K step: 8 activation loads,
-    // and per weight chunk 1 + 2 scale (+ 2 zero-point) loads
-    constexpr int VMEM_PER_STEP = 8 + BR * (HAS_ZP ? 5 : 3);
-    __shared__ __attribute__((aligned(16))) uint8_t lds[B4_RING * A_BYTES + 2 * B_BYTES];
-    uint8_t* const As = lds;
-    uint8_t* const Bs = lds + B4_RING * A_BYTES;
+    constexpr int PANEL = 256 * B4_K * 2;               // one K step of one operand: 32 KiB
+    constexpr int AR = 8;                               // activation chunks per thread per step
+    constexpr int BR = 2;                               // packed-weight chunks per thread per step
+    constexpr int NB = BS16 ? 2 : 1;                    // quantization blocks per 32-value chunk
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * PANEL];
+    uint8_t* const As = lds;                            // [2][PANEL]
+    uint8_t* const Bs = lds + 2 * PANEL;                // [2][PANEL]
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -542,25 +545,32 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_lds_kernel(Bf16Args g) {
     const __amdgpu_buffer_rsrc_t rz_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(HAS_ZP ? g.zp : g.b), (short)0, (int)(HAS_ZP ? g.z_bytes : 0), 0x00020000);
 
-    // activation loads: wavefront w fills rows 64w .. 64w+63 of a slot, eight
-    // rows per instruction; lane l lands in LDS at row l/8, slot l%8 and so
-    // fetches chunk (l%8) ^ (l/8) of its row
-    const int a_row = 64 * wave + (lane >> 3);
-    const int a_chunk = (lane & 7) ^ (lane >> 3);
-    const uint32_t a_off = (uint32_t)(m0 + a_row) * (uint32_t)g.K * 2u + 16u * a_chunk;
-    const uint32_t a_row8 = 8u * (uint32_t)g.K * 2u;        // byte distance of 8 rows
-
-    auto issue_a = [&](int k0, int slot) {
+    // activations: thread t moves chunk t % 8 of rows t / 8 + 32 i (rows past
+    // M read as zeros)
+    const int a_r = t >> 3, a_c = t & 7;
+    const uint32_t a_off = (uint32_t)(m0 + a_r) * (uint32_t)g.K * 2u + 16u * a_c;
+    const uint32_t a_rows32 = 32u * (uint32_t)g.K * 2u;
+    struct StageA {
+        u32x4 v[AR];
+    };
+    auto fetch_a = [&](int k0, StageA& st) {
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra_rs, (void __attribute__((address_space(3)))*)(As + slot * A_BYTES + (64 * wave + 8 * i) * 128),
-                16, a_off + a_row8 * i + 2u * k0, 0, 0, 0);
+        for (int i = 0; i < AR; i++)
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_off + a_rows32 * i + 2u * k0, 0, 0);
+    };
+    auto stash_a = [&](const StageA& st, int buf, int i) {
+        *reinterpret_cast<u32x4*>(As + buf * PANEL + swz(a_r + 32 * i, a_c)) = st.v[i];
     };
 
+    // weights: chunk q = t + 256 i is 16 bytes (32 values) of column q / 2,
+    // K half q % 2 of the step, with its scale(s) and zero point(s); the
+    // loaded values are only read when the step is unpacked, one step later.
+    // zsh: bit offset of the zero-point nibble in its byte.
     struct StageB {
         u32x4 b[BR];
-        uint32_t s[BR][2], z[BR][2];
+        uint16_t s[BR][NB];
+        uint8_t z[BR][NB];
+        uint32_t zsh[BR][NB];
     };
     auto fetch_b = [&](int k0, StageB& st) {
 #pragma unroll
@@ -571,27 +581,26 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_lds_kernel(Bf16Args g) {
             st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(
                 rb_rs, (uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)kb / 2u, 0, 0);
 #pragma unroll
-            for (int h = 0; h < 2; h++) {
+            for (int h = 0; h < NB; h++) {
                 const uint32_t blk = (uint32_t)(kb + 16 * h) >> g.log2_bs;
                 st.s[i][h] = __builtin_amdgcn_raw_buffer_load_b16(
                     rs_rs, 2u * ((uint32_t)col * (uint32_t)g.nb + blk), 0, 0);
-                if constexpr (HAS_ZP)
-                    st.z[i][h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
-                                     rz_rs, (uint32_t)col * (uint32_t)g.zp_row + (blk >> 1), 0, 0)
-                                 | ((blk & 1u) << 8);
-                else
-                    st.z[i][h] = 8u;
+                if constexpr (HAS_ZP) {
+                    st.z[i][h] = __builtin_amdgcn_raw_buffer_load_b8(
+                        rz_rs, (uint32_t)col * (uint32_t)g.zp_row + (blk >> 1), 0, 0);
+                    st.zsh[i][h] = 4u * (blk & 1u);
+                }
             }
         }
     };
-    // unpack one 8-value word (chunk i, word d) of a staged weight step into
-    // LDS buffer buf: (q - zp) * s exact in float32, one RTNE rounding to bf16
-    auto stash_piece = [&](const StageB& st, int buf, int i, int d) {
+    // unpack 8 values (word d of chunk i): (q - zp) * s is exact in float32,
+    // one RTNE rounding to bf16
+    auto stash_b = [&](const StageB& st, int buf, int i, int d) {
         const int q = t + 256 * i;
         const int c = q >> 1, half = q & 1;
-        const uint32_t zraw = st.z[i][d >> 1];
-        const uint32_t zq = HAS_ZP ? ((zraw & 0x100u) ? ((zraw >> 4) & 0xFu) : (zraw & 0xFu)) : 8u;
-        const float sc = __uint_as_float(st.s[i][d >> 1] << 16);
+        const int h = BS16 ? (d >> 1) : 0;
+        const uint32_t zq = HAS_ZP ? __builtin_amdgcn_ubfe((uint32_t)st.z[i][h], st.zsh[i][h], 4) : 8u;
+        const float sc = __uint_as_float((uint32_t)st.s[i][h] << 16);
         const float zs = (float)zq * sc;
         const uint32_t lo = opaque_and(st.b[i][d], 0x0F0F0F0Fu);
         const uint32_t hi = opaque_and(st.b[i][d] >> 4, 0x0F0F0F0Fu);
@@ -602,21 +611,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_lds_kernel(Bf16Args g) {
         v[6] = fmaf(ubyte_to_f32<3>(lo), sc, -zs); v[7] = fmaf(ubyte_to_f32<3>(hi), sc, -zs);
         uint32_t o[4];
 #pragma unroll
-        for (int h = 0; h < 4; h++) {
+        for (int e = 0; e < 4; e++) {
             bf16x2 pr;
-            pr[0] = (__bf16)v[2 * h];
-            pr[1] = (__bf16)v[2 * h + 1];
-            o[h] = __builtin_bit_cast(uint32_t, pr);
+            pr[0] = (__bf16)v[2 * e];
+            pr[1] = (__bf16)v[2 * e + 1];
+            o[e] = __builtin_bit_cast(uint32_t, pr);
         }
-        const int chunk = 4 * half + d;
-        *reinterpret_cast<u32x4*>(Bs + buf * B_BYTES + c * 128 + ((chunk ^ (c & 7)) << 4)) =
-            u32x4{o[0], o[1], o[2], o[3]};
-    };
-    auto stash_b = [&](const StageB& st, int buf) {
-#pragma unroll
-        for (int i = 0; i < BR; i++)
-#pragma unroll
-            for (int d = 0; d < 4; d++) stash_piece(st, buf, i, d);
+        *reinterpret_cast<u32x4*>(Bs + buf * PANEL + swz(c, 4 * half + d)) = u32x4{o[0], o[1], o[2], o[3]};
     };
 
     f32x16 acc[TM][TN];
@@ -627,28 +628,28 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_lds_kernel(Bf16Args g) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    // One K step: 4 substeps of 16 MFMAs on (slot, buf), with the next
-    // substep's operands read ahead and the unpacking of the next weight step
-    // (two 8-value words per substep) interleaved between the MFMAs, so that
-    // the matrix pipe never waits for the vector ALU or for LDS.
-    auto step_body = [&](int slot, int buf, const StageB& next_w) {
-        const uint8_t* a = As + slot * A_BYTES;
-        const uint8_t* b = Bs + buf * B_BYTES;
+    // Multiply the step in LDS buffer buf (4 substeps of 16 MFMAs, operands
+    // of the next substep read ahead) while a quarter of the next step's
+    // activations and weights goes from registers into buffer buf ^ 1 per
+    // substep.
+    auto step_body = [&](int buf, const StageA& na, const StageB& nb) {
+        const uint8_t* a = As + buf * PANEL;
+        const uint8_t* b = Bs + buf * PANEL;
         bf16x8 af[2][TM], bfr[2][TN];
         auto load_frags = [&](int ks, int p) {
             const int chunk = 2 * ks + (lane >> 5);
 #pragma unroll
-            for (int i = 0; i < TM; i++) {
-                const int r = wm * 128 + i * 32 + (lane & 31);
-                af[p][i] = *reinterpret_cast<const bf16x8*>(a + r * 128 + ((chunk ^ (r & 7)) << 4));
-            }
+            for (int i = 0; i < TM; i++)
+                af[p][i] = *reinterpret_cast<const bf16x8*>(a + swz(wm * 128 + i * 32 + (lane & 31), chunk));
 #pragma unroll
-            for (int j = 0; j < TN; j++) {
-                const int c = wn * 128 + j * 32 + (lane & 31);
-                bfr[p][j] = *reinterpret_cast<const bf16x8*>(b + c * 128 + ((chunk ^ (c & 7)) << 4));
-            }
+            for (int j = 0; j < TN; j++)
+                bfr[p][j] = *reinterpret_cast<const bf16x8*>(b + swz(wn * 128 + j * 32 + (lane & 31), chunk));
         };
         load_frags(0, 0);
+        // the first operands cannot be read before the barrier; fill their
+        // latency with unpacking work
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // 8 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // 16 VALU
 #pragma unroll
         for (int ks = 0; ks < B4_K / 16; ks++) {
             const int p = ks & 1;
@@ -658,48 +659,77 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_lds_kernel(Bf16Args g) {
 #pragma unroll
                 for (int j = 0; j < TN; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][i], bfr[p][j], acc[i][j], 0, 0, 0);
-            // two of the eight unpack pieces per substep
-            stash_piece(next_w, buf ^ 1, (2 * ks) >> 2, (2 * ks) & 3);
-            stash_piece(next_w, buf ^ 1, (2 * ks + 1) >> 2, (2 * ks + 1) & 3);
+            stash_a(na, buf ^ 1, 2 * ks);
+            stash_a(na, buf ^ 1, 2 * ks + 1);
+            stash_b(nb, buf ^ 1, (2 * ks) >> 2, (2 * ks) & 3);
+            stash_b(nb, buf ^ 1, (2 * ks + 1) >> 2, (2 * ks + 1) & 3);
+            // per sub-step: each MFMA followed by an LDS read (the next
+            // sub-step's operands) or write (staging) and unpacking work
 #pragma unroll
-            for (int g2 = 0; g2 < 16; g2++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
+            for (int q = 0; q < 8; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+            }
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+                if (q & 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
             }
         }
     };
 
-    // wait until at most N memory instructions of this thread are outstanding
-    // (gfx9 s_waitcnt encoding: vmcnt split over bits 3:0 and 15:14, expcnt
-    // and lgkmcnt left at their maxima)
-    constexpr int WAIT_PREV = VMEM_PER_STEP;
-    constexpr int WAIT_IMM = (WAIT_PREV & 15) | (7 << 4) | (15 << 8) | ((WAIT_PREV >> 4) << 14);
-
+    // One K step st: request step st + 2 (into the `load` stages), multiply
+    // step st from LDS buffer st % 2 while moving step st + 1 (the `use`
+    // stages, requested one step earlier) into the other buffer, barrier.
     const int steps = g.K / B4_K;
-    StageB cur, nxt;                      // weights of the next step, of the one after
-    // prologue: steps 0 and 1 requested, step 0 complete and visible
-    issue_a(0, 0);
-    fetch_b(0, nxt);
-    issue_a(B4_K, 1);
-    fetch_b(B4_K, cur);
-    stash_b(nxt, 0);                      // waits (compiler) for step 0's weight loads
-    __builtin_amdgcn_s_waitcnt(WAIT_IMM); // step 0's activation loads have landed
-    __syncthreads();
-    // one straight-line body per K step, so the accumulators stay in AGPRs:
-    // multiply step st (ring slot st % 3, weight buffer st % 2), unpack step
-    // st+1 into the other weight buffer, request step st+2
-    int slot = 0, buf = 0;
-    for (int st = 0; st < steps; st++) {
-        const int nslot = slot == 2 ? 0 : slot + 1;
-        const int fslot = nslot == 2 ? 0 : nslot + 1;
-        fetch_b((st + 2) * B4_K, nxt);
-        issue_a((st + 2) * B4_K, fslot);
-        step_body(slot, buf, cur);
-        __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+    int buf = 0;
+    auto one_step = [&](int st, const StageA& ua, const StageB& ub, StageA& la, StageB& lb) {
+        fetch_a((st + 2) * B4_K, la);
+        fetch_b((st + 2) * B4_K, lb);
+        __builtin_amdgcn_sched_barrier(0);    // issue the requests first
+        step_body(buf, ua, ub);
+        // the scheduler must not hoist the next step's unpacking (pure
+        // arithmetic) above the barrier, next to the loads that feed it
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        cur = nxt;
-        slot = nslot;
+        __builtin_amdgcn_sched_barrier(0);
         buf ^= 1;
+    };
+    auto stage_all = [&](const StageA& sa, const StageB& sb, int b) {
+#pragma unroll
+        for (int i = 0; i < AR; i++) stash_a(sa, b, i);
+#pragma unroll
+        for (int i = 0; i < BR; i++)
+#pragma unroll
+            for (int d = 0; d < 4; d++) stash_b(sb, b, i, d);
+    };
+    StageA ax, ay;
+    StageB bx, by;
+    int st = 0;
+    if (steps & 1) {
+        // odd step count: peel step 0 so that the loop runs pairs
+        fetch_a(0, ax);
+        fetch_b(0, bx);
+        fetch_a(B4_K, ay);
+        fetch_b(B4_K, by);
+        stage_all(ax, bx, 0);
+        __syncthreads();
+        one_step(0, ay, by, ax, bx);
+        st = 1;
+    } else {
+        fetch_a(0, ay);
+        fetch_b(0, by);
+        fetch_a(B4_K, ax);
+        fetch_b(B4_K, bx);
+        stage_all(ay, by, 0);
+        __syncthreads();
+    }
+    // here ax / bx hold step st + 1
+    for (; st < steps; st += 2) {
+        one_step(st, ax, bx, ay, by);
+        one_step(st + 1, ay, by, ax, bx);
     }
 
     // epilogue: + bias, RTNE to bf16, store
@@ -747,10 +777,10 @@ int launch_gemm(const Problem& p, hipStream_t s) {
         // large tiles when they fill the chip, smaller ones otherwise
         const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
         if (big >= 384 && p.K % B4_K == 0 && p.K % p.bs == 0) {
-            if (p.has_zp)
-                hipLaunchKernelGGL(gemm_bf16_lds_kernel<true>, dim3((unsigned)big), dim3(256), 0, s, b);
-            else
-                hipLaunchKernelGGL(gemm_bf16_lds_kernel<false>, dim3((unsigned)big), dim3(256), 0, s, b);
+            const bool bs16 = p.bs == 16;
+            auto kern = p.has_zp ? (bs16 ? gemm_bf16_wide_kernel<true, true> : gemm_bf16_wide_kernel<true, false>)
+                                 : (bs16 ? gemm_bf16_wide_kernel<false, true> : gemm_bf16_wide_kernel<false, false>);
+            hipLaunchKernelGGL(kern, dim3((unsigned)big), dim3(256), 0, s, b);
         } else if (big >= 384) {
             hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4>), dim3((unsigned)big), dim3(256), 0, s, b);
         } else {
