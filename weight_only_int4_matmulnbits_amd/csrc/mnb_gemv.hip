@@ -51,6 +51,7 @@ struct GemvArgs {
     void* y;
     int64_t K, N, col_bytes, n_groups;
     int nb, zp_row, S, log2_bs, log2_L;
+    int a16;                  // K * element size is a multiple of 16 and A is 16-byte aligned
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -115,42 +116,67 @@ struct Group {
     Chunk w[U][J];
     uint32_t sc[U][J];   // float32 bits, or bfloat16 bits in the low half
     uint32_t zb[U][J];   // packed zero-point byte (HAS_ZP)
+    uint32_t bias[U];    // float32 bits of the column's bias (0 without one)
 };
+
+// One iteration's loads through buffer resources based at the group's
+// first column: every load is issued (a chunk past K or a column past N reads
+// zeros, which contribute nothing), so a wavefront issues the same number of
+// memory instructions on every path.
+constexpr uint32_t kOob = 0x80000000u;    // offset past any resource: reads zero
 
 template <bool BF16, bool HAS_ZP, int CB, int J, int U>
 __device__ __forceinline__ void load_group(const GemvArgs& g, int64_t base, int p, int LT, int G,
                                            int gsub, Group<BF16, HAS_ZP, CB, J, U>& r) {
-    using Chunk = typename ChunkT<CB>::type;
     constexpr int CK = 2 * CB;
+    constexpr int SSZ = BF16 ? 2 : 4;
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const int64_t gi = base + u;
-        const int64_t col = gi * G + gsub;
-        const bool ok = gi < g.n_groups && col < g.N;
-        const uint8_t* bc = g.b + col * g.col_bytes;
+        const int64_t col0 = gi * G;
+        const int64_t ncol = gi < g.n_groups ? (g.N - col0 < G ? g.N - col0 : G) : 0;
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(g.b) + (ncol ? col0 * g.col_bytes : 0), (short)0,
+            (int)(ncol * g.col_bytes), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<uint8_t*>(const_cast<void*>(g.scales)) + (ncol ? col0 * g.nb * SSZ : 0), (short)0,
+            (int)(ncol * g.nb * SSZ), 0x00020000);
+        // the bias goes with the weights: a load issued late and consumed at
+        // once would wait for every load in flight (they complete in order)
+        const __amdgpu_buffer_rsrc_t rbias = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(g.bias ? g.bias : reinterpret_cast<const float*>(g.b)) + (ncol && g.bias ? col0 : 0),
+            (short)0, g.bias ? (int)(ncol * 4) : 0, 0x00020000);
+        r.bias[u] = __builtin_amdgcn_raw_buffer_load_b32(rbias, (uint32_t)(4 * gsub), 0, 0);
+        __amdgpu_buffer_rsrc_t rz;
+        if constexpr (HAS_ZP)
+            rz = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.zp) + (ncol ? col0 * g.zp_row : 0),
+                                                   (short)0, (int)(ncol * g.zp_row), 0x00020000);
 #pragma unroll
         for (int j = 0; j < J; j++) {
             const int c = p + j * LT;
-            if (ok && c < g.S) {
-                r.w[u][j] = __builtin_nontemporal_load(
-                    reinterpret_cast<const Chunk*>(bc + (int64_t)c * CB));
-                const int blk = (c * CK) >> g.log2_bs;
-                const int64_t si = col * g.nb + blk;
-                r.sc[u][j] = BF16 ? (uint32_t)static_cast<const uint16_t*>(g.scales)[si]
-                                  : static_cast<const uint32_t*>(g.scales)[si];
-                if constexpr (HAS_ZP) r.zb[u][j] = g.zp[col * g.zp_row + (blk >> 1)];
+            // offsets of chunks past K forced past the resource (branch-free,
+            // so that every lane issues the same single load)
+            const uint32_t out = c < g.S ? 0u : kOob;
+            const int blk = (c * CK) >> g.log2_bs;
+            const uint32_t ow = (uint32_t)(gsub * g.col_bytes + c * CB) | out;
+            if constexpr (CB == 16) {
+                r.w[u][j] = __builtin_amdgcn_raw_buffer_load_b128(rb, ow, 0, 0);
             } else {
-                r.w[u][j] = Chunk{};
-                r.sc[u][j] = 0;
-                if constexpr (HAS_ZP) r.zb[u][j] = 0x88;
+                const uint64_t x = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rb, ow, 0, 0));
+                r.w[u][j] = u32x2{(uint32_t)x, (uint32_t)(x >> 32)};
             }
+            const uint32_t os = (uint32_t)((gsub * g.nb + blk) * SSZ) | out;
+            r.sc[u][j] = BF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0)
+                              : __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
+            if constexpr (HAS_ZP)
+                r.zb[u][j] = __builtin_amdgcn_raw_buffer_load_b8(
+                    rz, (uint32_t)(gsub * g.zp_row + (blk >> 1)) | out, 0, 0);
         }
     }
 }
 
-// W wavefronts per column team, U column groups per team per iteration,
-// PF: load the next iteration's weights before computing the current one.
-template <bool BF16, bool HAS_ZP, int CB, int J, int U, int W, bool PF>
+// W wavefronts per column team, U column groups per team per iteration.
+template <bool BF16, bool HAS_ZP, int CB, int J, int U, int W>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     constexpr int CK = 2 * CB;        // values of K per chunk
     constexpr int NW = CB / 4;        // 32-bit words per chunk
@@ -159,7 +185,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     __shared__ float red[kWavesPerBlock];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int team = wave / W;
     const int wt = wave - team * W;   // wavefront index within the team
     const int L = 1 << g.log2_L;      // lanes per column in one wavefront
@@ -173,46 +199,76 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     int64_t base = ((int64_t)blockIdx.x * TEAMS + team) * U;
     const int64_t team0 = (int64_t)blockIdx.x * TEAMS * U;
 
-    Group<BF16, HAS_ZP, CB, J, U> cur;
-    load_group(g, base, p, LT, G, gsub, cur);     // weights first: they do not wait on A
-
-    // ---- activations: staged once per workgroup in LDS (coalesced loads,
-    // converted to float32, chunk rows padded to CK+4 floats so that the
-    // per-lane 16-byte reads below hit distinct banks), then each lane copies
-    // its chunks into registers ----
-    extern __shared__ __attribute__((aligned(16))) float a_lds[];
-    constexpr int ROW = CK + 4;
-    {
-        const int64_t nvec = (int64_t)g.S * (CK / 4);       // float4 slots
-        const bool vec = (g.K & 3) == 0;
-        for (int64_t i = threadIdx.x; i < nvec; i += 64 * kWavesPerBlock) {
-            const int64_t k = 4 * i;
-            float4 v;
-            if (vec && k + 4 <= g.K) {
-                if constexpr (BF16) {
-                    const uint2 x = *reinterpret_cast<const uint2*>(
-                        static_cast<const uint16_t*>(g.a) + k);
-                    v = make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u),
-                                    __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xFFFF0000u));
-                } else {
-                    v = *reinterpret_cast<const float4*>(static_cast<const float*>(g.a) + k);
-                }
-            } else {
-                float e[4];
+    // ---- activations: staged once per workgroup in LDS as they are (float32
+    // or bfloat16), one RB-byte row per chunk; the 16-byte pieces of row c sit
+    // at v ^ ((c / (256 / RB)) % NV), so that the per-lane 16-byte reads of 16
+    // consecutive rows below cover all 64 banks once.  The requests go out
+    // before the weights': loads complete in order, so activations queued
+    // behind HBM weight loads would be late ----
+    constexpr int ESZ = BF16 ? 2 : 4;
+    constexpr int RB = CK * ESZ;                 // bytes per chunk row
+    constexpr int NV = RB / 16;                  // 16-byte pieces per row
+    constexpr int RPS = 256 / RB;                // rows per 256-byte bank sweep
+    extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];
+    const int nthr = 64 * kWavesPerBlock;
+    if (g.a16) {
+        // LDS-direct loads: request r puts 64 pieces (1 KiB) at a_lds + 1024 r;
+        // lane l fills row r * 64 / NV + l / NV, position l % NV, with the
+        // piece that the swizzle assigns there; reads past K return zeros
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void*>(g.a), (short)0, (int)(g.K * ESZ), 0x00020000);
+        const int nreq = (g.S * RB + 1023) / 1024;
+        for (int r = wave; r < nreq; r += kWavesPerBlock) {
+            const int row = r * (64 / NV) + lane / NV;
+            const int pos = lane % NV;
+            const int piece = pos ^ ((row / RPS) % NV);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (void __attribute__((address_space(3)))*)(a_lds + 1024 * r), 16,
+                (uint32_t)(row * RB + 16 * piece), 0, 0, 0);
+        }
+    } else {
+        // K * element size not a multiple of 16: element-wise loads
+        for (int i = threadIdx.x; i < g.S * NV; i += nthr) {
+            const int row = i / NV, piece = i % NV;
+            const int64_t k0 = (int64_t)row * CK + piece * (16 / ESZ);
+            uint32_t w[4];
 #pragma unroll
-                for (int h = 0; h < 4; h++) {
-                    e[h] = 0.f;
-                    if (k + h < g.K)
-                        e[h] = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(g.a)[k + h])
-                                    : static_cast<const float*>(g.a)[k + h];
+            for (int e = 0; e < 4; e++) {
+                if constexpr (BF16) {
+                    const int64_t k = k0 + 2 * e;
+                    const uint32_t lo = k < g.K ? static_cast<const uint16_t*>(g.a)[k] : 0u;
+                    const uint32_t hi = k + 1 < g.K ? static_cast<const uint16_t*>(g.a)[k + 1] : 0u;
+                    w[e] = lo | (hi << 16);
+                } else {
+                    const int64_t k = k0 + e;
+                    w[e] = k < g.K ? static_cast<const uint32_t*>(g.a)[k] : 0u;
                 }
-                v = make_float4(e[0], e[1], e[2], e[3]);
             }
-            const int64_t c = k / CK;
-            *reinterpret_cast<float4*>(&a_lds[c * ROW + (k - c * CK)]) = v;
+            *reinterpret_cast<u32x4*>(a_lds + row * RB + 16 * (piece ^ ((row / RPS) % NV))) =
+                u32x4{w[0], w[1], w[2], w[3]};
         }
     }
-    __syncthreads();
+
+    // the first two iterations' weights (the second only if this team has one)
+    Group<BF16, HAS_ZP, CB, J, U> g0, g1;
+    const bool two = base + stride < g.n_groups;     // wave-uniform
+    load_group(g, base, p, LT, G, gsub, g0);
+    if (two) load_group(g, base + stride, p, LT, G, gsub, g1);
+
+    // wait for this wavefront's staging (all memory instructions but the
+    // weight loads just issued, and the LDS writes), then meet the others.
+    // A plain barrier: a fenced one would also wait for the weights.
+    {
+        constexpr int NL = U * (J * (HAS_ZP ? 3 : 2) + 1);     // loads per group
+        static_assert(2 * NL < 64, "vmcnt range");
+        constexpr int W1 = (NL & 15) | (7 << 4) | (0 << 8) | ((NL >> 4) << 14);
+        constexpr int W2 = ((2 * NL) & 15) | (7 << 4) | (0 << 8) | (((2 * NL) >> 4) << 14);
+        if (two)
+            __builtin_amdgcn_s_waitcnt(W2);
+        else
+            __builtin_amdgcn_s_waitcnt(W1);
+        asm volatile("s_barrier" : : : "memory");
+    }
     // this lane's chunks of A in registers (odd k pre-scaled by 1/16) and
     // the chunk sums of the unscaled values
     float av[J][CK];
@@ -222,10 +278,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
         const int c = p + j * LT;
         if (c < g.S) {
 #pragma unroll
-            for (int v = 0; v < CK / 4; v++) {
-                const float4 x = *reinterpret_cast<const float4*>(&a_lds[c * ROW + 4 * v]);
-                av[j][4 * v] = x.x; av[j][4 * v + 1] = x.y;
-                av[j][4 * v + 2] = x.z; av[j][4 * v + 3] = x.w;
+            for (int v = 0; v < NV; v++) {
+                const u32x4 x = *reinterpret_cast<const u32x4*>(a_lds + c * RB + 16 * (v ^ ((c / RPS) % NV)));
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    if constexpr (BF16) {
+                        av[j][8 * v + 2 * e] = __uint_as_float(x[e] << 16);
+                        av[j][8 * v + 2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
+                    } else {
+                        av[j][4 * v + e] = __uint_as_float(x[e]);
+                    }
+                }
             }
         } else {
 #pragma unroll
@@ -239,10 +302,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
         for (int i = 1; i < CK; i += 2) av[j][i] *= 0.0625f;
     }
 
-    for (int64_t it0 = team0; it0 < g.n_groups; it0 += stride, base += stride) {
-        // groups past the end load as zeros, so every register is defined
-        Group<BF16, HAS_ZP, CB, J, U> nxt;
-        if constexpr (PF) load_group(g, base + stride, p, LT, G, gsub, nxt);
+    // Two register stages used alternately (copying a stage would make the
+    // wavefront wait for the loads just issued into it): while one
+    // iteration is reduced, the next one's weights are in flight, and its
+    // own stage is refilled with the iteration after.
+    auto finish = [&](const Group<BF16, HAS_ZP, CB, J, U>& cur, int64_t gbase) {
         float acc[U];
 #pragma unroll
         for (int u = 0; u < U; u++) {
@@ -280,11 +344,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
         if (wt == 0 && (lane & (L - 1)) == 0) {
 #pragma unroll
             for (int u = 0; u < U; u++) {
-                const int64_t gi = base + u;
+                const int64_t gi = gbase + u;
                 const int64_t col = gi * G + gsub;
                 if (gi < g.n_groups && col < g.N) {
                     float v = acc[u];
-                    if (g.bias) v += g.bias[col];
+                    if (g.bias) v += __uint_as_float(cur.bias[u]);
                     if constexpr (BF16)
                         static_cast<uint16_t*>(g.y)[col] = f32_to_bf16_rtne(v);
                     else
@@ -292,10 +356,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
                 }
             }
         }
-        if constexpr (PF)
-            cur = nxt;
-        else
-            load_group(g, base + stride, p, LT, G, gsub, cur);
+    };
+    // it0 is WG-uniform, so the barriers of split-K teams are reached by all.
+    // No exit between the halves (it would cost precise waits): the second
+    // half past the end loads zeros and skips its work.
+    for (int64_t it0 = team0; it0 < g.n_groups; it0 += 2 * stride, base += 2 * stride) {
+        finish(g0, base);
+        if (base + 2 * stride < g.n_groups) load_group(g, base + 2 * stride, p, LT, G, gsub, g0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (it0 + stride < g.n_groups) finish(g1, base + stride);
+        if (base + 3 * stride < g.n_groups) load_group(g, base + 3 * stride, p, LT, G, gsub, g1);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -336,47 +407,37 @@ Geometry geometry(int64_t S, bool allow_split) {
 
 // Columns unrolled per iteration when there are plenty of columns.
 constexpr int unroll_for(int J) { return J == 1 ? 4 : J == 2 ? 2 : 1; }
-// Resident wavefronts per SIMD that the register use of (J, U) allows
-// (from the compiler's resource report for gfx950).
-constexpr int occupancy_for(int J, int U) {
-    return U == 1 ? (J == 1 ? 7 : J == 2 ? 4 : 2) : (J == 1 ? 3 : 2);
-}
+
+using GemvFn = void (*)(GemvArgs);
 
 template <bool BF16, bool HAS_ZP, int CB, int J>
-hipError_t launch_j(int U, int W, unsigned blocks, size_t lds, hipStream_t s, const GemvArgs& a) {
+GemvFn pick_j(int U, int W) {
     constexpr int UJ = unroll_for(J);
-    constexpr bool PF = J <= 3;
-    if (W == 1 && U == 1)
-        hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, J, 1, 1, PF>), dim3(blocks), dim3(256), lds, s, a);
-    else if (W == 1)
-        hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, J, UJ, 1, PF>), dim3(blocks), dim3(256), lds, s, a);
-    else if constexpr (CB == 16) {
-        if (W == 2)
-            hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, J, 1, 2, PF>), dim3(blocks), dim3(256), lds, s, a);
-        else
-            hipLaunchKernelGGL((gemv_kernel<BF16, HAS_ZP, CB, J, 1, 4, PF>), dim3(blocks), dim3(256), lds, s, a);
-    } else {
-        return hipErrorInvalidValue;
+    if (W == 1) return U == 1 ? gemv_kernel<BF16, HAS_ZP, CB, J, 1, 1> : gemv_kernel<BF16, HAS_ZP, CB, J, UJ, 1>;
+    if constexpr (CB == 16) {
+        if (W == 2) return gemv_kernel<BF16, HAS_ZP, CB, J, 1, 2>;
+        if (W == 4) return gemv_kernel<BF16, HAS_ZP, CB, J, 1, 4>;
     }
-    return hipGetLastError();
+    return nullptr;
 }
 
 template <bool BF16, bool HAS_ZP, int CB>
-hipError_t launch_cb(int J, int U, int W, unsigned blocks, size_t lds, hipStream_t s, const GemvArgs& a) {
+GemvFn pick_cb(int J, int U, int W) {
     switch (J) {
-        case 1: return launch_j<BF16, HAS_ZP, CB, 1>(U, W, blocks, lds, s, a);
-        case 2: return launch_j<BF16, HAS_ZP, CB, 2>(U, W, blocks, lds, s, a);
-        case 3: return launch_j<BF16, HAS_ZP, CB, 3>(U, W, blocks, lds, s, a);
-        case 4: return launch_j<BF16, HAS_ZP, CB, 4>(U, W, blocks, lds, s, a);
-        default: return hipErrorInvalidValue;
+        case 1: return pick_j<BF16, HAS_ZP, CB, 1>(U, W);
+        case 2: return pick_j<BF16, HAS_ZP, CB, 2>(U, W);
+        case 3: return pick_j<BF16, HAS_ZP, CB, 3>(U, W);
+        case 4: return pick_j<BF16, HAS_ZP, CB, 4>(U, W);
+        default: return nullptr;
     }
 }
 
-template <bool BF16, bool HAS_ZP>
-hipError_t launch_dt(int CB, int J, int U, int W, unsigned blocks, size_t lds, hipStream_t s,
-                     const GemvArgs& a) {
-    return CB == 16 ? launch_cb<BF16, HAS_ZP, 16>(J, U, W, blocks, lds, s, a)
-                    : launch_cb<BF16, HAS_ZP, 8>(J, U, W, blocks, lds, s, a);
+GemvFn pick(bool bf16, bool has_zp, int CB, int J, int U, int W) {
+    if (bf16)
+        return has_zp ? (CB == 16 ? pick_cb<true, true, 16>(J, U, W) : pick_cb<true, true, 8>(J, U, W))
+                      : (CB == 16 ? pick_cb<true, false, 16>(J, U, W) : pick_cb<true, false, 8>(J, U, W));
+    return has_zp ? (CB == 16 ? pick_cb<false, true, 16>(J, U, W) : pick_cb<false, true, 8>(J, U, W))
+                  : (CB == 16 ? pick_cb<false, false, 16>(J, U, W) : pick_cb<false, false, 8>(J, U, W));
 }
 
 int compute_units() {
@@ -393,15 +454,32 @@ int compute_units() {
     return cached_cus;
 }
 
+// Workgroups of kernel f with lds bytes of staged activations resident per
+// CU (the compiler's register use and the LDS decide), cached per thread.
+int resident_per_cu(GemvFn f, size_t lds) {
+    struct Entry { GemvFn f; size_t lds; int n; };
+    static thread_local Entry cache[64];
+    static thread_local int used = 0;
+    for (int i = 0; i < used; i++)
+        if (cache[i].f == f && cache[i].lds == lds) return cache[i].n;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(f),
+                                                     64 * kWavesPerBlock, lds) != hipSuccess || n < 1)
+        n = 1;
+    cache[used % 64] = Entry{f, lds, n};
+    if (used < 64) used++;
+    return n;
+}
+
 }  // namespace
 
 int64_t gemv_max_k(int bs) {
     // limited by the register geometry (S <= 64 * W * kJMax chunks) and by
-    // the staged activations (S rows of CK + 4 floats in kMaxLds bytes)
+    // the staged activations (S rows of CK float32 in kMaxLds bytes)
     const int CK = bs >= 32 ? 32 : 16;
     const int W = bs >= 32 ? kWMax : 1;
     int64_t s_max = (int64_t)64 * W * kJMax;
-    const int64_t s_lds = (int64_t)(kMaxLds / ((CK + 4) * sizeof(float)));
+    const int64_t s_lds = (int64_t)(kMaxLds / (CK * sizeof(float)));
     if (s_lds < s_max) s_max = s_lds;
     return s_max * CK;
 }
@@ -422,32 +500,36 @@ int launch_gemv(const Problem& p, hipStream_t s) {
     a.log2_L = geo.log2_L;
     const int G = geo.W == 1 ? (64 >> geo.log2_L) : 1;
     a.n_groups = (p.N + G - 1) / G;
-    // Fill the chip: resident wavefronts = CUs x 4 SIMDs x occupancy; each
-    // team of W wavefronts takes U groups per iteration.  Unroll only when
-    // there are enough groups to give every resident team U of them.
-    const int64_t simds = (int64_t)compute_units() * 4;
-    const int UJ = unroll_for(geo.J);
-    int U = 1;
-    int64_t slots = simds * occupancy_for(geo.J, 1) / geo.W;
-    if (geo.W == 1 && UJ > 1 && a.n_groups >= simds * occupancy_for(geo.J, UJ) * UJ) {
-        U = UJ;
-        slots = simds * occupancy_for(geo.J, UJ);
-    }
-    int64_t teams = (a.n_groups + U - 1) / U;
-    if (teams > slots) teams = slots;
-    const int teams_per_block = kWavesPerBlock / geo.W;
-    const unsigned blocks = (unsigned)((teams + teams_per_block - 1) / teams_per_block);
-    // staged activations: S chunk rows of CK + 4 floats
-    const size_t lds = (size_t)a.S * (CK + 4) * sizeof(float);
+    // staged activations: S chunk rows of CK elements
+    const int esz = p.bf16 ? 2 : 4;
+    a.a16 = ((p.K * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(p.a) & 15) == 0) &&
+            p.K * esz < (int64_t(1) << 31);
+    const size_t lds = (size_t)a.S * CK * esz;
     if (lds > kMaxLds)
         return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld needs %zu bytes of LDS", (long long)p.K, lds);
-    hipError_t e;
-    if (p.bf16)
-        e = p.has_zp ? launch_dt<true, true>(CB, geo.J, U, geo.W, blocks, lds, s, a)
-                     : launch_dt<true, false>(CB, geo.J, U, geo.W, blocks, lds, s, a);
-    else
-        e = p.has_zp ? launch_dt<false, true>(CB, geo.J, U, geo.W, blocks, lds, s, a)
-                     : launch_dt<false, false>(CB, geo.J, U, geo.W, blocks, lds, s, a);
+    // Fill the chip with resident teams of W wavefronts (the kernel's real
+    // occupancy); each team takes U groups per iteration.  Unroll only when
+    // every resident team gets at least two iterations of U groups.
+    const int64_t cus = compute_units();
+    const int teams_per_block = kWavesPerBlock / geo.W;
+    int U = 1;
+    GemvFn f = pick(p.bf16, p.has_zp, CB, geo.J, 1, geo.W);
+    const int UJ = unroll_for(geo.J);
+    if (geo.W == 1 && UJ > 1) {
+        GemvFn fu = pick(p.bf16, p.has_zp, CB, geo.J, UJ, 1);
+        const int64_t resident = cus * resident_per_cu(fu, lds) * teams_per_block;
+        if (fu && a.n_groups >= 2 * resident * UJ) {
+            U = UJ;
+            f = fu;
+        }
+    }
+    if (!f) return fail(MNB_E_UNSUPPORTED, "gemv: no kernel for J=%d W=%d", geo.J, geo.W);
+    const int64_t teams = (a.n_groups + U - 1) / U;
+    int64_t blocks = (teams + teams_per_block - 1) / teams_per_block;
+    const int64_t max_blocks = cus * resident_per_cu(f, lds);
+    if (blocks > max_blocks) blocks = max_blocks;
+    hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(64 * kWavesPerBlock), lds, s, a);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MNB_E_HIP, "gemv launch: %s", hipGetErrorString(e));
     return MNB_OK;
 }
