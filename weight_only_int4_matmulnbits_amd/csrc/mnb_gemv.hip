@@ -405,15 +405,12 @@ Geometry geometry(int64_t S, bool allow_split) {
     return best;
 }
 
-// Columns unrolled per iteration when there are plenty of columns.
-constexpr int unroll_for(int J) { return J == 1 ? 4 : J == 2 ? 2 : 1; }
-
 using GemvFn = void (*)(GemvArgs);
 
 template <bool BF16, bool HAS_ZP, int CB, int J>
 GemvFn pick_j(int U, int W) {
-    constexpr int UJ = unroll_for(J);
-    if (W == 1) return U == 1 ? gemv_kernel<BF16, HAS_ZP, CB, J, 1, 1> : gemv_kernel<BF16, HAS_ZP, CB, J, UJ, 1>;
+    if (U != 1) return nullptr;
+    if (W == 1) return gemv_kernel<BF16, HAS_ZP, CB, J, 1, 1>;
     if constexpr (CB == 16) {
         if (W == 2) return gemv_kernel<BF16, HAS_ZP, CB, J, 1, 2>;
         if (W == 4) return gemv_kernel<BF16, HAS_ZP, CB, J, 1, 4>;
@@ -508,21 +505,12 @@ int launch_gemv(const Problem& p, hipStream_t s) {
     if (lds > kMaxLds)
         return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld needs %zu bytes of LDS", (long long)p.K, lds);
     // Fill the chip with resident teams of W wavefronts (the kernel's real
-    // occupancy); each team takes U groups per iteration.  Unroll only when
-    // every resident team gets at least two iterations of U groups.
+    // occupancy), one column group per team per iteration: unrolling several
+    // groups per iteration costs more in occupancy than it saves.
     const int64_t cus = compute_units();
     const int teams_per_block = kWavesPerBlock / geo.W;
-    int U = 1;
+    const int U = 1;
     GemvFn f = pick(p.bf16, p.has_zp, CB, geo.J, 1, geo.W);
-    const int UJ = unroll_for(geo.J);
-    if (geo.W == 1 && UJ > 1) {
-        GemvFn fu = pick(p.bf16, p.has_zp, CB, geo.J, UJ, 1);
-        const int64_t resident = cus * resident_per_cu(fu, lds) * teams_per_block;
-        if (fu && a.n_groups >= 2 * resident * UJ) {
-            U = UJ;
-            f = fu;
-        }
-    }
     if (!f) return fail(MNB_E_UNSUPPORTED, "gemv: no kernel for J=%d W=%d", geo.J, geo.W);
     const int64_t teams = (a.n_groups + U - 1) / U;
     int64_t blocks = (teams + teams_per_block - 1) / teams_per_block;
