@@ -322,9 +322,10 @@ def test_bf16_gemm_identity_returns_bf16_dequant(orc, K, N, bs, zp):
                                               (2048, 128, 12288, 128, False, False),
                                               (1030, 320, 24600, 32, True, False)])
 def test_bf16_gemm_large_grid_sampled(orc, M, K, N, bs, zp, bias):
-    """Grids of >= 384 tiles of 256x256 take the LDS-ring prefill kernel
-    (K a multiple of 64 and of the block size); ragged M and N, an odd
-    number of K steps; sampled rows x columns against the oracle."""
+    """Grids of >= 384 tiles of 256x256 take the 256x256x64 prefill kernel
+    without splitting K (K a multiple of 64 and of the block size); ragged M
+    and N, an odd number of K steps; sampled rows x columns against the
+    oracle."""
     log(f"large bf16 gemm M={M} K={K} N={N} bs={bs} zp={zp} bias={bias}")
     inp, g = _inputs(K, N, M, bs, "bf16", zp, bias, seed=M + K + N)
     pw = _packed(g, bs)
@@ -335,3 +336,53 @@ def test_bf16_gemm_large_grid_sampled(orc, M, K, N, bs, zp, bias):
     y_ref, S = oracle_ref(orc, inp, rows, cols)
     ys = y[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)]
     assert_close(out_f64(ys), y_ref, S, "bf16", f"M={M} K={K} N={N}")
+
+
+SPLIT_CASES = [
+    ("bf16", 512, 4096, 384, 128, True, True),    # 4 tiles of 256x256: 16 K splits
+    ("bf16", 300, 1536, 520, 32, False, False),   # ragged M and N: 6 splits
+    ("f32", 256, 2048, 256, 32, True, True),      # 4 tiles of 128x128: 16 splits
+    ("f32", 200, 1024, 136, 16, True, False),     # block 16, ragged: 8 splits
+]
+
+
+@pytest.mark.parametrize("dt,M,K,N,bs,zp,bias", SPLIT_CASES)
+def test_split_k_gemm_matches_oracle(orc, dt, M, K, N, bs, zp, bias):
+    """Few output tiles: K is split across workgroups and the float32
+    partials are added in split order (+ bias); every output against the
+    oracle, twice (the second call reuses the stream's workspace)."""
+    log(f"split-K gemm {dt} M={M} K={K} N={N} bs={bs} zp={zp} bias={bias}")
+    inp, g = _inputs(K, N, M, bs, dt, zp, bias, seed=M * 3 + K + N)
+    pw = _packed(g, bs)
+    y_ref, S = oracle_ref(orc, inp)
+    y1 = pw.matmul(g.a).clone()
+    y2 = pw.matmul(g.a)
+    assert_close(out_f64(y1), y_ref, S, dt, f"{dt} M={M} K={K} N={N}")
+    assert torch.equal(y1, y2)
+
+
+def test_split_k_graph_matches_direct():
+    """A captured sequence of split products (its own workspace) gives the
+    bits of the same products run directly (the stream's workspace), on
+    every replay."""
+    items = []
+    for i, (dt, M, K, N, bs, zp, bias) in enumerate(SPLIT_CASES):
+        _, g = _inputs(K, N, M, bs, dt, zp, bias, seed=100 + i)
+        pw = _packed(g, bs)
+        items.append((pw, g.a, torch.empty(M, N, device=DEV, dtype=g.a.dtype)))
+    seq = mnb.Sequence(items)
+    seq.run()
+    direct = [y.clone() for _, _, y in items]
+    for _, _, y in items:
+        y.fill_(float("nan"))
+    seq.capture()
+    try:
+        for rep in range(3):
+            seq.replay()
+            torch.cuda.synchronize()
+            for (_, _, y), d in zip(items, direct):
+                assert torch.equal(y, d), rep
+            for _, _, y in items:
+                y.fill_(float("nan"))
+    finally:
+        seq.close()

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -86,9 +87,68 @@ int check_matmul(const char* who, const mnb_desc* d, int64_t M, const void* a,
     return MNB_OK;
 }
 
-int run(const Problem& p, hipStream_t s) {
-    if (p.M == 1 && p.K <= gemv_max_k(p.bs)) return launch_gemv(p, s);
-    return launch_gemm(p, s);
+// Split-K partials of direct calls live in one workspace per (device,
+// stream), grown on demand (never while the stream is being captured: a
+// captured launch then runs without splitting) and kept until the process
+// ends.  Calls on one stream are ordered, so they can share it.
+struct StreamWorkspace {
+    int dev;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
+};
+std::mutex g_ws_mutex;
+std::vector<StreamWorkspace> g_ws;
+
+void* stream_workspace(hipStream_t s, size_t bytes, size_t* have) {
+    *have = 0;
+    if (bytes == 0) return nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    StreamWorkspace* e = nullptr;
+    for (auto& w : g_ws)
+        if (w.dev == dev && w.stream == s) e = &w;
+    if (e && e->bytes >= bytes) {
+        *have = e->bytes;
+        return e->ptr;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    const size_t want = (bytes + (size_t(32) << 20) - 1) / (size_t(32) << 20) * (size_t(32) << 20);
+    if (e) {
+        // earlier launches on this stream may still use the old buffer
+        if (hipStreamSynchronize(s) != hipSuccess) return nullptr;
+        (void)hipFree(e->ptr);
+        e->ptr = nullptr;
+        e->bytes = 0;
+    }
+    void* ptr = nullptr;
+    if (hipMalloc(&ptr, want) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (e) {
+        e->ptr = ptr;
+        e->bytes = want;
+    } else {
+        g_ws.push_back(StreamWorkspace{dev, s, ptr, want});
+    }
+    *have = want;
+    return ptr;
+}
+
+bool takes_gemv(const Problem& p) { return p.M == 1 && p.K <= gemv_max_k(p.bs); }
+
+// ws == nullptr: the stream's own workspace
+int run_gemm(const Problem& p, hipStream_t s, void* ws = nullptr, size_t ws_bytes = 0) {
+    if (!ws) ws = stream_workspace(s, gemm_workspace_bytes(p), &ws_bytes);
+    return launch_gemm(p, s, ws, ws_bytes);
+}
+
+int run(const Problem& p, hipStream_t s, void* ws = nullptr, size_t ws_bytes = 0) {
+    if (takes_gemv(p)) return launch_gemv(p, s);
+    return run_gemm(p, s, ws, ws_bytes);
 }
 
 }  // namespace
@@ -99,6 +159,7 @@ using namespace mnb;
 struct mnb_graph {
     hipGraph_t graph;
     hipGraphExec_t exec;
+    void* ws;          // split-K partials of the captured products (owned)
 };
 
 extern "C" {
@@ -166,7 +227,7 @@ int mnb_gemm(const mnb_desc* d, int64_t M, const void* a, const uint8_t* b_packe
     Problem p;
     int st = check_matmul("mnb_gemm", d, M, a, b_packed, scales, zp_packed, bias, y, false, &p);
     if (st != MNB_OK) return st;
-    return launch_gemm(p, static_cast<hipStream_t>(stream));
+    return run_gemm(p, static_cast<hipStream_t>(stream));
 }
 
 int mnb_dequant(const mnb_desc* d, const uint8_t* b_packed, const void* scales,
@@ -232,33 +293,57 @@ int mnb_graph_create(const mnb_matmul_args* ops, int64_t n_ops, mnb_graph** out)
         return fail(MNB_E_ARG, "mnb_graph_create: out of host memory");
     }
     if (st != MNB_OK) return st;
+    // the graph's own workspace for split-K partials, allocated before the
+    // capture (the products run in order, so they share it)
+    size_t need = 0;
+    for (const Problem& p : probs)
+        if (!takes_gemv(p)) {
+            const size_t b = gemm_workspace_bytes(p);
+            if (b > need) need = b;
+        }
+    void* gws = nullptr;
+    if (need && hipMalloc(&gws, need) != hipSuccess) {
+        (void)hipGetLastError();
+        gws = nullptr;               // no room: the products run without splitting
+    }
     hipStream_t cs;
     hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
-    if (e != hipSuccess) return fail(MNB_E_HIP, "mnb_graph_create: stream: %s", hipGetErrorString(e));
+    if (e != hipSuccess) {
+        if (gws) (void)hipFree(gws);
+        return fail(MNB_E_HIP, "mnb_graph_create: stream: %s", hipGetErrorString(e));
+    }
     e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) {
         (void)hipStreamDestroy(cs);
+        if (gws) (void)hipFree(gws);
         return fail(MNB_E_HIP, "mnb_graph_create: begin capture: %s", hipGetErrorString(e));
     }
-    for (size_t i = 0; i < probs.size() && st == MNB_OK; i++) st = run(probs[i], cs);
+    // without a workspace, pass a non-NULL zero-size one so that no product
+    // reaches for the (capturing) stream's
+    static char none;
+    for (size_t i = 0; i < probs.size() && st == MNB_OK; i++)
+        st = run(probs[i], cs, gws ? gws : &none, gws ? need : 0);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
     (void)hipStreamDestroy(cs);
-    if (st != MNB_OK) {
+    if (st != MNB_OK || e != hipSuccess) {
         if (graph) (void)hipGraphDestroy(graph);
-        return st;
+        if (gws) (void)hipFree(gws);
+        if (st != MNB_OK) return st;
+        return fail(MNB_E_HIP, "mnb_graph_create: end capture: %s", hipGetErrorString(e));
     }
-    if (e != hipSuccess) return fail(MNB_E_HIP, "mnb_graph_create: end capture: %s", hipGetErrorString(e));
     hipGraphExec_t exec = nullptr;
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
     if (e != hipSuccess) {
         (void)hipGraphDestroy(graph);
+        if (gws) (void)hipFree(gws);
         return fail(MNB_E_HIP, "mnb_graph_create: instantiate: %s", hipGetErrorString(e));
     }
-    mnb_graph* g = new (std::nothrow) mnb_graph{graph, exec};
+    mnb_graph* g = new (std::nothrow) mnb_graph{graph, exec, gws};
     if (!g) {
         (void)hipGraphExecDestroy(exec);
         (void)hipGraphDestroy(graph);
+        if (gws) (void)hipFree(gws);
         return fail(MNB_E_ARG, "mnb_graph_create: out of host memory");
     }
     *out = g;
@@ -276,6 +361,11 @@ int mnb_graph_destroy(mnb_graph* g) {
     if (!g) return MNB_OK;
     hipError_t e1 = hipGraphExecDestroy(g->exec);
     hipError_t e2 = hipGraphDestroy(g->graph);
+    // hipFree waits for the device, so a replay still running keeps its memory
+    if (g->ws) {
+        const hipError_t e3 = hipFree(g->ws);
+        if (e1 == hipSuccess && e2 == hipSuccess) e1 = e3;
+    }
     delete g;
     if (e1 != hipSuccess || e2 != hipSuccess)
         return fail(MNB_E_HIP, "mnb_graph_destroy: %s",

@@ -275,6 +275,14 @@ constexpr int B2_LDR = B2_K + 8;                  // bf16 per LDS row
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// bijective remap of block ids: the blocks that land on XCD x (bid % 8 == x)
+// take a contiguous range of virtual indices
+__device__ __forceinline__ int xcd_index(int bid, int nblk) {
+    const int q = nblk / 8, r = nblk % 8;
+    const int x = bid % 8, j = bid / 8;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+}
+
 __device__ __forceinline__ int2 xcd_tile(int bid, int nblk, int mt) {
     // bijective remap: the blocks that land on XCD x (bid % 8 == x) take a
     // contiguous range of tiles; tile t -> (m = t % mt, n = t / mt)
@@ -293,6 +301,11 @@ struct Bf16Args {
     void* y;
     int M, K, N, col_bytes, k_pad, nb, zp_row, log2_bs;
     uint32_t a_bytes, b_bytes, s_bytes, z_bytes;
+    // split-K: workgroup w of tiles * splits takes K steps [split * sps,
+    // split * sps + sps) and, when part is set, stores its float32 partial
+    // tile to part[split][M][N] instead of Y (the reduction adds the bias)
+    int splits, sps;
+    float* part;
 };
 
 template <int BM, int BN, int WAVES>
@@ -532,9 +545,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     const int wm = wave >> 1, wn = wave & 1;
     const int mt = (g.M + B4_M - 1) / B4_M;
     const int nt = (g.N + B4_N - 1) / B4_N;
-    const int2 tile = xcd_tile(blockIdx.x, mt * nt, mt);
-    const int m0 = tile.x * B4_M;
-    const int n0 = tile.y * B4_N;
+    const int tiles = mt * nt;
+    const int v = xcd_index(blockIdx.x, tiles * g.splits);
+    const int split = v / tiles, tt = v - split * tiles;
+    const int m0 = (tt % mt) * B4_M;
+    const int n0 = (tt / mt) * B4_N;
+    const int kbase = split * g.sps * B4_K;                // this split's first K value
 
     const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(g.a), (short)0, (int)g.a_bytes, 0x00020000);
@@ -556,7 +572,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     auto fetch_a = [&](int k0, StageA& st) {
 #pragma unroll
         for (int i = 0; i < AR; i++)
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_off + a_rows32 * i + 2u * k0, 0, 0);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_off + a_rows32 * i + 2u * (kbase + k0), 0, 0);
     };
     auto stash_a = [&](const StageA& st, int buf, int i) {
         *reinterpret_cast<u32x4*>(As + buf * PANEL + swz(a_r + 32 * i, a_c)) = st.v[i];
@@ -577,7 +593,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
         for (int i = 0; i < BR; i++) {
             const int q = t + 256 * i;
             const int col = n0 + (q >> 1), half = q & 1;
-            const int kb = k0 + 32 * half;
+            const int kb = kbase + k0 + 32 * half;
             st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(
                 rb_rs, (uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)kb / 2u, 0, 0);
 #pragma unroll
@@ -683,7 +699,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     // One K step st: request step st + 2 (into the `load` stages), multiply
     // step st from LDS buffer st % 2 while moving step st + 1 (the `use`
     // stages, requested one step earlier) into the other buffer, barrier.
-    const int steps = g.K / B4_K;
+    const int steps = min(g.sps, g.K / B4_K - split * g.sps);
     int buf = 0;
     auto one_step = [&](int st, const StageA& ua, const StageB& ub, StageA& la, StageB& lb) {
         fetch_a((st + 2) * B4_K, la);
@@ -732,26 +748,394 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
         one_step(st + 1, ay, by, ax, bx);
     }
 
-    // epilogue: + bias, RTNE to bf16, store
+    // epilogue: + bias, RTNE to bf16, store (or the float32 partial)
+    float* const part = g.part ? g.part + (int64_t)split * g.M * g.N : nullptr;
 #pragma unroll
     for (int j = 0; j < TN; j++) {
         const int n = n0 + wn * 128 + j * 32 + (lane & 31);
         if (n >= g.N) continue;
-        const float bv = g.bias ? g.bias[n] : 0.f;
+        const float bv = (!part && g.bias) ? g.bias[n] : 0.f;
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m < g.M)
+                if (m >= g.M) continue;
+                if (part)
+                    part[(int64_t)m * g.N + n] = acc[i][j][r];
+                else
                     static_cast<uint16_t*>(g.y)[(int64_t)m * g.N + n] = f32_to_bf16_rtne(acc[i][j][r] + bv);
             }
     }
 }
 
+// ---------------------------------------------------------------------------
+// float32 activations and scales: exact-integer weights on the matrix cores.
+//
+// The weight panel holds the exact integers q - zp (|q - zp| <= 15 is exact
+// in bf16), the activation panel a float32 value split into a bf16 head and
+// tail (a = hi + lo, lo = bf16(a - hi): about 16 significant bits), so one
+// product is two MFMAs and the only weight rounding is the scale's.  The
+// partial sums of one scale period (one quantization block, or the part of
+// it in one K step) are accumulated separately and folded in with that
+// block's scale, acc += s * partial: each lane's 16 MFMA results belong to
+// one output column, so that is one scale per lane.  With A the identity
+// the result is float32((q - zp) * s), the dequantized weight, exactly.
+//
+// Tiles of 128 x 128 x 32 on 4 wavefronts of 64 x 64 (2 x 2 MFMA 32x32x16
+// tiles); the three panels (A hi, A lo, B) and the step's scales sit in LDS,
+// double-buffered (2 x 24.5 KiB), so several workgroups fit on a CU.  Rows
+// are 64 bytes (32 K values) with the four 16-byte pieces of row r at
+// piece ^ ((r >> 2) & 3), so the operand reads of 16 consecutive rows are
+// conflict-free.  Activations (full 128-byte lines per row and K step) and
+// packed weights are read two K steps ahead into registers and staged one
+// step ahead, interleaved with the MFMAs; one barrier per K step; a
+// two-step loop body with alternating register stages.
+// Requires K % 32 == 0 and K % block_size == 0.
+// ---------------------------------------------------------------------------
+constexpr int F_K = 32;
+
+__device__ __forceinline__ int swz64(int r, int piece) { return r * 64 + ((piece ^ ((r >> 2) & 3)) << 4); }
+
+// bf16 head and tail of four floats, packed two per 32-bit word
+__device__ __forceinline__ void split4(const u32x4& x, uint2& hi, uint2& lo) {
+    uint32_t h[2], l[2];
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+        const float a0 = __uint_as_float(x[2 * e]), a1 = __uint_as_float(x[2 * e + 1]);
+        bf16x2 ph;
+        ph[0] = (__bf16)a0;
+        ph[1] = (__bf16)a1;
+        const uint32_t hb = __builtin_bit_cast(uint32_t, ph);
+        bf16x2 pl;
+        pl[0] = (__bf16)(a0 - __uint_as_float(hb << 16));
+        pl[1] = (__bf16)(a1 - __uint_as_float(hb & 0xFFFF0000u));
+        h[e] = hb;
+        l[e] = __builtin_bit_cast(uint32_t, pl);
+    }
+    hi = make_uint2(h[0], h[1]);
+    lo = make_uint2(l[0], l[1]);
+}
+
+template <bool HAS_ZP, bool BS16>
+__global__ __launch_bounds__(256, 2) void gemm_f32_int_kernel(Bf16Args g) {
+    constexpr int TM = 2, TN = 2;
+    constexpr int PANEL = 128 * F_K * 2;                // one K step of one operand: 8 KiB
+    constexpr int SPAN = 128 * 8;                       // the step's scales: 2 per column
+    constexpr int BUF = 3 * PANEL + SPAN;               // A hi, A lo, B, scales
+    constexpr int NS = BS16 ? 2 : 1;                    // scale periods per K step
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int mt = (g.M + 127) / 128;
+    const int nt = (g.N + 127) / 128;
+    const int tiles = mt * nt;
+    const int v = xcd_index(blockIdx.x, tiles * g.splits);
+    const int split = v / tiles, tt = v - split * tiles;
+    const int m0 = (tt % mt) * 128;
+    const int n0 = (tt / mt) * 128;
+    const int kbase = split * g.sps * F_K;                 // this split's first K value
+
+    const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(g.a), (short)0, (int)g.a_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(g.b), (short)0, (int)g.b_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(g.scales), (short)0, (int)g.s_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(HAS_ZP ? g.zp : g.b), (short)0, (int)(HAS_ZP ? g.z_bytes : 0), 0x00020000);
+
+    // activations: thread t moves four floats (chunk t % 8) of rows t / 8 + 32 i
+    const int a_r = t >> 3, a_c = t & 7;
+    const uint32_t a_off = (uint32_t)(m0 + a_r) * (uint32_t)g.K * 4u + 16u * a_c;
+    const uint32_t a_rows32 = 32u * (uint32_t)g.K * 4u;
+    struct StageA {
+        u32x4 v[4];
+    };
+    auto fetch_a = [&](int k0, StageA& st) {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_off + a_rows32 * i + 4u * (kbase + k0), 0, 0);
+    };
+    auto stash_a = [&](const StageA& st, int buf, int i) {
+        uint2 hi, lo;
+        split4(st.v[i], hi, lo);
+        const int off = swz64(a_r + 32 * i, a_c >> 1) + 8 * (a_c & 1);
+        *reinterpret_cast<uint2*>(lds + buf * BUF + off) = hi;
+        *reinterpret_cast<uint2*>(lds + buf * BUF + PANEL + off) = lo;
+    };
+
+    // weights: thread t takes 16 values (8 bytes) of column t / 2, K half
+    // t % 2, which lie in one quantization block
+    const int b_c = t >> 1, b_h = t & 1;
+    struct StageB {
+        uint2 b;
+        uint32_t s;
+        uint8_t z;
+        uint32_t zsh;
+    };
+    auto fetch_b = [&](int k0, StageB& st) {
+        const int col = n0 + b_c;
+        const int kb = kbase + k0 + 16 * b_h;
+        st.b = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             rb_rs, (uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)kb / 2u, 0, 0));
+        const uint32_t blk = (uint32_t)kb >> g.log2_bs;
+        st.s = __builtin_amdgcn_raw_buffer_load_b32(rs_rs, 4u * ((uint32_t)col * (uint32_t)g.nb + blk), 0, 0);
+        if constexpr (HAS_ZP) {
+            st.z = __builtin_amdgcn_raw_buffer_load_b8(rz_rs, (uint32_t)col * (uint32_t)g.zp_row + (blk >> 1), 0, 0);
+            st.zsh = 4u * (blk & 1u);
+        }
+    };
+    // word d (8 values) of a staged weight as the exact bf16 integers q - zp;
+    // the half's scale goes to the step's scale row
+    auto stash_b = [&](const StageB& st, int buf, int d) {
+        const int zq = HAS_ZP ? (int)__builtin_amdgcn_ubfe((uint32_t)st.z, st.zsh, 4) : 8;
+        const uint32_t word = d ? st.b.y : st.b.x;
+        uint32_t v[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const uint32_t byte = (word >> (8 * e)) & 0xFFu;
+            const float w0 = (float)((int)(byte & 0xFu) - zq);
+            const float w1 = (float)((int)(byte >> 4) - zq);
+            v[e] = (__float_as_uint(w0) >> 16) | (__float_as_uint(w1) & 0xFFFF0000u);   // exact
+        }
+        *reinterpret_cast<u32x4*>(lds + buf * BUF + 2 * PANEL + swz64(b_c, 2 * b_h + d)) =
+            u32x4{v[0], v[1], v[2], v[3]};
+        if (d == 0) *reinterpret_cast<uint32_t*>(lds + buf * BUF + 3 * PANEL + 8 * b_c + 4 * b_h) = st.s;
+    };
+
+    f32x16 acc[TM][TN], part[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+    const f32x16 zero = {};
+
+    // one K step from buffer buf: per scale period, the period's MFMAs (the
+    // first of each tile starting from zero) and the fold with the period's
+    // scale; the next step (held in na, nb) is staged into buf ^ 1 in between
+    auto step_body = [&](int buf, const StageA& na, const StageB& nb) {
+        const uint8_t* base = lds + buf * BUF;
+#pragma unroll
+        for (int ks = 0; ks < F_K / 16; ks++) {
+            const int piece = 2 * ks + (lane >> 5);
+            bf16x8 ah[TM], al[TM], bw[TN];
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                const int r = wm * 64 + i * 32 + (lane & 31);
+                ah[i] = *reinterpret_cast<const bf16x8*>(base + swz64(r, piece));
+                al[i] = *reinterpret_cast<const bf16x8*>(base + PANEL + swz64(r, piece));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const int c = wn * 64 + j * 32 + (lane & 31);
+                bw[j] = *reinterpret_cast<const bf16x8*>(base + 2 * PANEL + swz64(c, piece));
+            }
+            stash_a(na, buf ^ 1, 2 * ks);
+            stash_a(na, buf ^ 1, 2 * ks + 1);
+            stash_b(nb, buf ^ 1, ks);
+            const bool first = BS16 || ks == 0;
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++) {
+                    part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], first ? zero : part[i][j], 0, 0, 0);
+                    part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], part[i][j], 0, 0, 0);
+                }
+            if (BS16 || ks == F_K / 16 - 1) {
+                // fold: this lane's column and the period's K half
+#pragma unroll
+                for (int j = 0; j < TN; j++) {
+                    const int c = wn * 64 + j * 32 + (lane & 31);
+                    const float sc = *reinterpret_cast<const float*>(base + 3 * PANEL + 8 * c + 4 * (BS16 ? ks : 0));
+#pragma unroll
+                    for (int i = 0; i < TM; i++)
+#pragma unroll
+                        for (int r = 0; r < 16; r++) acc[i][j][r] = fmaf(sc, part[i][j][r], acc[i][j][r]);
+                }
+            }
+        }
+    };
+
+    const int steps = min(g.sps, g.K / F_K - split * g.sps);
+    int buf = 0;
+    auto one_step = [&](int st, const StageA& ua, const StageB& ub, StageA& la, StageB& lb) {
+        fetch_a((st + 2) * F_K, la);
+        fetch_b((st + 2) * F_K, lb);
+        __builtin_amdgcn_sched_barrier(0);    // issue the requests first
+        step_body(buf, ua, ub);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        buf ^= 1;
+    };
+    auto stage_all = [&](const StageA& sa, const StageB& sb, int b) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) stash_a(sa, b, i);
+        stash_b(sb, b, 0);
+        stash_b(sb, b, 1);
+    };
+    StageA ax, ay;
+    StageB bx, by;
+    int st = 0;
+    if (steps & 1) {
+        fetch_a(0, ax);
+        fetch_b(0, bx);
+        fetch_a(F_K, ay);
+        fetch_b(F_K, by);
+        stage_all(ax, bx, 0);
+        __syncthreads();
+        one_step(0, ay, by, ax, bx);
+        st = 1;
+    } else {
+        fetch_a(0, ay);
+        fetch_b(0, by);
+        fetch_a(F_K, ax);
+        fetch_b(F_K, bx);
+        stage_all(ay, by, 0);
+        __syncthreads();
+    }
+    for (; st < steps; st += 2) {
+        one_step(st, ax, bx, ay, by);
+        one_step(st + 1, ay, by, ax, bx);
+    }
+
+    // epilogue: + bias, float32 store (or the partial, without bias)
+    float* const out = g.part ? g.part + (int64_t)split * g.M * g.N : static_cast<float*>(g.y);
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+        const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+        if (n >= g.N) continue;
+        const float bv = (!g.part && g.bias) ? g.bias[n] : 0.f;
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (m < g.M) out[(int64_t)m * g.N + n] = acc[i][j][r] + bv;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// split-K reduction: Y = sum over the splits of the float32 partials, in
+// split order (deterministic), + bias, rounded to Y's type.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
+                                                            int64_t mn, int N, const float* __restrict__ bias,
+                                                            void* __restrict__ y) {
+    const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < mn; i += stride) {
+        float v[4];
+        if (i + 4 <= mn && (N & 3) == 0) {
+            float4 x = *reinterpret_cast<const float4*>(part + i);
+            for (int sp = 1; sp < splits; sp++) {
+                const float4 z = *reinterpret_cast<const float4*>(part + (int64_t)sp * mn + i);
+                x.x += z.x; x.y += z.y; x.z += z.z; x.w += z.w;
+            }
+            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                v[e] = 0.f;
+                if (i + e < mn) {
+                    float x = part[i + e];
+                    for (int sp = 1; sp < splits; sp++) x += part[(int64_t)sp * mn + i + e];
+                    v[e] = x;
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            if (i + e >= mn) break;
+            const float o = bias ? v[e] + bias[(i + e) % N] : v[e];
+            if constexpr (BF16)
+                static_cast<uint16_t*>(y)[i + e] = f32_to_bf16_rtne(o);
+            else
+                static_cast<float*>(y)[i + e] = o;
+        }
+    }
+}
+
 }  // namespace
 
-int launch_gemm(const Problem& p, hipStream_t s) {
+namespace {
+
+// Which kernel a problem takes, its output tiles and its K split.
+struct Plan {
+    enum Kind { LEGACY_BF16, WIDE, REG256, REG128, F32_INT, LEGACY_F32 } kind;
+    int64_t tiles = 1;
+    int splits = 1, sps = 1;
+    size_t ws = 0;                 // workspace bytes for the split partials
+};
+
+constexpr size_t kMaxWorkspace = size_t(1) << 30;
+
+// Split K only when the output tiles leave resident workgroup slots idle,
+// keeping at least four K steps per split.
+void choose_split(Plan& pl, const Problem& p, int64_t resident, int steps) {
+    pl.splits = 1;
+    pl.sps = steps;
+    if (pl.tiles >= resident) return;
+    int64_t sp = resident / pl.tiles;
+    if (sp > steps / 4) sp = steps / 4;
+    while (sp > 1 && (size_t)sp * (size_t)(p.M * p.N) * 4 > kMaxWorkspace) sp--;
+    if (sp <= 1) return;
+    pl.sps = (int)((steps + sp - 1) / sp);
+    pl.splits = (steps + pl.sps - 1) / pl.sps;
+    if (pl.splits > 1) pl.ws = (size_t)pl.splits * (size_t)(p.M * p.N) * 4;
+}
+
+Plan plan_gemm(const Problem& p) {
+    Plan pl;
+    const int esz = p.bf16 ? 2 : 4;
+    const bool vec_a = ((p.K * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(p.a) & 15) == 0);
+    const int64_t a_bytes = p.M * p.K * esz, b_bytes = p.N * p.col_bytes;
+    const int64_t lim = int64_t(1) << 31;
+    const int64_t cus = device_compute_units();
+    if (p.bf16 && vec_a && (p.K % 8) == 0 && a_bytes + 256 * p.K * esz < lim &&
+        b_bytes + 256 * p.col_bytes < lim && p.M * p.N < lim) {
+        const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+        if (p.M > 128 && p.K % B4_K == 0 && p.K % p.bs == 0) {
+            pl.kind = Plan::WIDE;
+            pl.tiles = big;
+            choose_split(pl, p, cus, (int)(p.K / B4_K));   // one 256 x 256 workgroup per CU
+        } else if (big >= 384) {
+            pl.kind = Plan::REG256;
+            pl.tiles = big;
+        } else {
+            pl.kind = Plan::REG128;
+            pl.tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+        }
+    } else if (p.bf16) {
+        pl.kind = Plan::LEGACY_BF16;
+    } else if (vec_a && p.K % F_K == 0 && p.K % p.bs == 0 && p.M * p.K * 4 + 128 * p.K * 4 < lim &&
+               b_bytes + 128 * p.col_bytes < lim && p.M * p.N < lim) {
+        pl.kind = Plan::F32_INT;
+        pl.tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+        choose_split(pl, p, 2 * cus, (int)(p.K / F_K));    // two 128 x 128 workgroups per CU
+    } else {
+        pl.kind = Plan::LEGACY_F32;
+    }
+    return pl;
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(const Problem& p) { return plan_gemm(p).ws; }
+
+int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
+    Plan pl = plan_gemm(p);
+    if (pl.splits > 1 && (!ws || ws_bytes < pl.ws)) {
+        pl.splits = 1;                                      // no room for partials: one pass
+        pl.sps = (int)(p.K / (pl.kind == Plan::WIDE ? B4_K : F_K));
+    }
     GemmArgs a;
     a.a = p.a; a.b = p.b; a.scales = p.scales; a.zp = p.has_zp ? p.zp : nullptr;
     a.bias = p.bias; a.y = p.y;
@@ -760,42 +1144,67 @@ int launch_gemm(const Problem& p, hipStream_t s) {
     a.nb = p.nb; a.zp_row = p.zp_row; a.bs = p.bs;
     const int esz = p.bf16 ? 2 : 4;
     a.vec_a = ((p.K * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(p.a) & 15) == 0);
-    const int64_t a_bytes = p.M * p.K * esz, b_bytes = p.N * p.col_bytes;
-    const int64_t lim = int64_t(1) << 31;
-    if (p.bf16 && a.vec_a && (p.K % 8) == 0 && a_bytes + 256 * p.K * esz < lim && b_bytes < lim &&
-        p.M * p.N < lim) {
-        Bf16Args b;
-        b.a = p.a; b.b = p.b; b.scales = p.scales; b.zp = p.has_zp ? p.zp : nullptr;
-        b.bias = p.bias; b.y = p.y;
-        b.M = (int)p.M; b.K = (int)p.K; b.N = (int)p.N; b.col_bytes = (int)p.col_bytes;
-        b.k_pad = (int)a.k_pad; b.nb = p.nb; b.zp_row = p.zp_row;
-        int l2 = 0;
-        while ((1 << l2) < p.bs) l2++;
-        b.log2_bs = l2;
-        b.a_bytes = (uint32_t)a_bytes; b.b_bytes = (uint32_t)b_bytes;
-        b.s_bytes = (uint32_t)(p.N * p.nb * 2); b.z_bytes = (uint32_t)(p.N * p.zp_row);
-        // large tiles when they fill the chip, smaller ones otherwise
-        const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-        if (big >= 384 && p.K % B4_K == 0 && p.K % p.bs == 0) {
-            const bool bs16 = p.bs == 16;
+    Bf16Args b;
+    b.a = p.a; b.b = p.b; b.scales = p.scales; b.zp = p.has_zp ? p.zp : nullptr;
+    b.bias = p.bias; b.y = p.y;
+    b.M = (int)p.M; b.K = (int)p.K; b.N = (int)p.N; b.col_bytes = (int)p.col_bytes;
+    b.k_pad = (int)a.k_pad; b.nb = p.nb; b.zp_row = p.zp_row;
+    int l2 = 0;
+    while ((1 << l2) < p.bs) l2++;
+    b.log2_bs = l2;
+    b.a_bytes = (uint32_t)(p.M * p.K * esz); b.b_bytes = (uint32_t)(p.N * p.col_bytes);
+    b.s_bytes = (uint32_t)(p.N * p.nb * esz); b.z_bytes = (uint32_t)(p.N * p.zp_row);
+    b.splits = pl.splits;
+    b.sps = pl.sps;
+    b.part = pl.splits > 1 ? static_cast<float*>(ws) : nullptr;
+    const bool bs16 = p.bs == 16;
+    const unsigned grid = (unsigned)(pl.tiles * pl.splits);
+    switch (pl.kind) {
+        case Plan::WIDE: {
             auto kern = p.has_zp ? (bs16 ? gemm_bf16_wide_kernel<true, true> : gemm_bf16_wide_kernel<true, false>)
                                  : (bs16 ? gemm_bf16_wide_kernel<false, true> : gemm_bf16_wide_kernel<false, false>);
-            hipLaunchKernelGGL(kern, dim3((unsigned)big), dim3(256), 0, s, b);
-        } else if (big >= 384) {
-            hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4>), dim3((unsigned)big), dim3(256), 0, s, b);
-        } else {
-            const int64_t small = ((p.M + 127) / 128) * ((p.N + 127) / 128);
-            hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 8>), dim3((unsigned)small), dim3(512), 0, s, b);
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, b);
+            break;
         }
-    } else if (p.bf16) {
-        const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
-        hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(256), 0, s, a);
-    } else {
-        const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
-        hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(256), 0, s, a);
+        case Plan::REG256:
+            hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4>), dim3(grid), dim3(256), 0, s, b);
+            break;
+        case Plan::REG128:
+            hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 8>), dim3(grid), dim3(512), 0, s, b);
+            break;
+        case Plan::F32_INT: {
+            auto kern = p.has_zp ? (bs16 ? gemm_f32_int_kernel<true, true> : gemm_f32_int_kernel<true, false>)
+                                 : (bs16 ? gemm_f32_int_kernel<false, true> : gemm_f32_int_kernel<false, false>);
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, b);
+            break;
+        }
+        case Plan::LEGACY_BF16:
+        case Plan::LEGACY_F32: {
+            const dim3 g2((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
+            if (pl.kind == Plan::LEGACY_BF16)
+                hipLaunchKernelGGL(gemm_kernel<true>, g2, dim3(256), 0, s, a);
+            else
+                hipLaunchKernelGGL(gemm_kernel<false>, g2, dim3(256), 0, s, a);
+            break;
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MNB_E_HIP, "gemm launch: %s", hipGetErrorString(e));
+    if (pl.splits > 1) {
+        const int64_t mn = p.M * p.N;
+        int64_t blocks = (mn / 4 + 255) / 256;
+        const int64_t cap = (int64_t)device_compute_units() * 8;
+        if (blocks > cap) blocks = cap;
+        if (blocks < 1) blocks = 1;
+        if (p.bf16)
+            hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s,
+                               static_cast<const float*>(ws), pl.splits, mn, (int)p.N, p.bias, p.y);
+        else
+            hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s,
+                               static_cast<const float*>(ws), pl.splits, mn, (int)p.N, p.bias, p.y);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(MNB_E_HIP, "gemm split-K reduction launch: %s", hipGetErrorString(e));
+    }
     return MNB_OK;
 }
 

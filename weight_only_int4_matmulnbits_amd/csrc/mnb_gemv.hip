@@ -437,7 +437,11 @@ GemvFn pick(bool bf16, bool has_zp, int CB, int J, int U, int W) {
                   : (CB == 16 ? pick_cb<false, false, 16>(J, U, W) : pick_cb<false, false, 8>(J, U, W));
 }
 
-int compute_units() {
+int compute_units() { return device_compute_units(); }
+
+}  // namespace
+
+int device_compute_units() {
     static thread_local int cached_dev = -1, cached_cus = 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -450,6 +454,8 @@ int compute_units() {
     }
     return cached_cus;
 }
+
+namespace {
 
 // Workgroups of kernel f with lds bytes of staged activations resident per
 // CU (the compiler's register use and the LDS decide), cached per thread.

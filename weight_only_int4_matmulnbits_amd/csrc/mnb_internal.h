@@ -36,8 +36,12 @@ int launch_pack(int64_t K, int64_t N, int bs, const uint8_t* q,
                 hipStream_t s);
 int launch_dequant(const Problem& p, int out_kind, void* w, hipStream_t s);
 int launch_gemv(const Problem& p, hipStream_t s);
-int launch_gemm(const Problem& p, hipStream_t s);
+// ws: float32 workspace for split-K partials (ws_bytes >= gemm_workspace_bytes
+// to split; NULL or smaller: one pass without splitting).
+int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes);
+size_t gemm_workspace_bytes(const Problem& p);
 int64_t gemv_max_k(int bs);
+int device_compute_units();   // CUs of the current device (cached)
 
 // ---- device helpers ---------------------------------------------------------
 
