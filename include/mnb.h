@@ -23,10 +23,16 @@
  * ---------------------------------------
  * Memory.   Every tensor argument is a DEVICE pointer (memory of the current
  *           HIP device), row-major and contiguous, allocated and owned by the
- *           caller.  The library never allocates device memory, never frees,
- *           and keeps no pointer after a call returns (graph handles, below,
- *           are the one documented exception: they record the pointers given
- *           at creation).
+ *           caller.  The library keeps no pointer to caller memory after a
+ *           call returns (graph handles, below, are the one documented
+ *           exception: they record the pointers given at creation).  Its own
+ *           device memory is a float32 workspace for split-K GEMMs (products
+ *           whose output tiles cannot fill the GPU): one per (device, stream)
+ *           for direct calls, grown on demand outside stream capture and
+ *           kept until the process ends, and one per graph handle, freed by
+ *           mnb_graph_destroy.  A product that cannot get the workspace it
+ *           asks for (inside a capture the caller started, or when hipMalloc
+ *           fails) runs without splitting K.
  * Ordering. Work is enqueued on `stream` (a hipStream_t passed as void*;
  *           NULL is the null stream) and the call returns once it is
  *           enqueued.  Results are valid after the stream is synchronized.
@@ -39,7 +45,7 @@
  *           throws across the ABI.  mnb_last_error() gives a human-readable
  *           detail of the most recent error on the calling thread.
  * Threads.  Calls are reentrant; concurrent calls on different streams are
- *           safe.
+ *           safe (each stream has its own workspace).
  *
  * Data layouts (N-major: every column of B is one contiguous run of bytes)
  * ------------------------------------------------------------------------
@@ -143,11 +149,15 @@ int mnb_gemv(const mnb_desc* d, int64_t M, const void* a,
 
 /* mnb_gemm -- prefill, any M >= 1 ("int4_gemm": activation panels and
  * weight blocks reused on chip).  Same arguments as mnb_gemv with A [M][K]
- * and Y [M][N]; `a` and `b_packed` 16-byte aligned.  Weight tiles are
- * unpacked on chip to exact bfloat16 integers (q - zp); products run on the
- * bf16 matrix cores with float32 accumulation; the per-block scale is applied
- * to the float32 partial sums.  float32 activations are split into two
- * bfloat16 terms (hi + lo) so results stay within float32 tolerance. */
+ * and Y [M][N]; `a` and `b_packed` 16-byte aligned.  Products run on the
+ * bf16 matrix cores with float32 accumulation.  bfloat16 activations meet
+ * weight tiles unpacked on chip to bf16((q - zp) * s) (one rounding of the
+ * exact weight, the bits mnb_dequant's bf16 output gives).  float32
+ * activations are split into two bfloat16 terms (hi + lo) and meet the exact
+ * bfloat16 integers (q - zp); the float32 per-block scale is applied to the
+ * float32 partial sums, so results stay within float32 tolerance.  Products
+ * with too few output tiles to fill the GPU split K across workgroups (see
+ * Memory above); the float32 partials are added in a fixed order. */
 int mnb_gemm(const mnb_desc* d, int64_t M, const void* a,
              const uint8_t* b_packed, const void* scales,
              const uint8_t* zp_packed, const float* bias, void* y,
