@@ -505,9 +505,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(Bf16Args g) {
 
 
 // ---------------------------------------------------------------------------
-// bf16 activations, large grids: 256 x 256 x 64 tiles on 4 wavefronts of
-// 128 x 128 (16 MFMA 32x32x16 tiles each, accumulators in AGPRs; one
-// wavefront per SIMD).
+// bf16 activations, large grids: 256 x 256 x 64 tiles on 8 wavefronts of
+// 128 x 64 (8 MFMA 32x32x16 tiles each), two wavefronts per SIMD so that one
+// multiplies while the other waits on LDS or unpacks weights.
 //
 //  * Both operand panels of a K step live in LDS as bf16, double-buffered
 //    (4 x 32 KiB): the activations as loaded, the weights unpacked to
@@ -517,10 +517,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(Bf16Args g) {
 //  * Global reads run two K steps ahead into registers (plain buffer loads,
 //    so the compiler tracks every one of them and waits precisely); while
 //    step s is multiplied, step s + 1 is moved from registers into the other
-//    LDS buffers, interleaved with the MFMAs.
+//    LDS buffers, a quarter per 16-value sub-step.
 //  * One barrier per K step; the loop body is two steps with the register
 //    stages swapped (a stage copy would wait for loads just issued) and no
-//    exit in the middle (so the accumulators stay in AGPRs).
+//    exit in the middle.
 // Requires K % 64 == 0 and K % block_size == 0 (no partial K step or block).
 // ---------------------------------------------------------------------------
 constexpr int B4_M = 256, B4_N = 256, B4_K = 64;
@@ -529,12 +529,10 @@ constexpr int B4_M = 256, B4_N = 256, B4_K = 64;
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 template <bool HAS_ZP, bool BS16>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
-    constexpr int TM = 4, TN = 4;
+__global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
+    constexpr int TM = 4, TN = 2;
     constexpr int PANEL = 256 * B4_K * 2;               // one K step of one operand: 32 KiB
-    constexpr int AR = 8;                               // activation chunks per thread per step
-    constexpr int BR = 2;                               // packed-weight chunks per thread per step
-    constexpr int NB = BS16 ? 2 : 1;                    // quantization blocks per 32-value chunk
+    constexpr int AR = 4;                               // activation chunks per thread per step
     __shared__ __attribute__((aligned(16))) uint8_t lds[4 * PANEL];
     uint8_t* const As = lds;                            // [2][PANEL]
     uint8_t* const Bs = lds + 2 * PANEL;                // [2][PANEL]
@@ -542,7 +540,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int mt = (g.M + B4_M - 1) / B4_M;
     const int nt = (g.N + B4_N - 1) / B4_N;
     const int tiles = mt * nt;
@@ -561,65 +559,63 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     const __amdgpu_buffer_rsrc_t rz_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(HAS_ZP ? g.zp : g.b), (short)0, (int)(HAS_ZP ? g.z_bytes : 0), 0x00020000);
 
-    // activations: thread t moves chunk t % 8 of rows t / 8 + 32 i (rows past
+    // activations: thread t moves chunk t % 8 of rows t / 8 + 64 i (rows past
     // M read as zeros)
     const int a_r = t >> 3, a_c = t & 7;
     const uint32_t a_off = (uint32_t)(m0 + a_r) * (uint32_t)g.K * 2u + 16u * a_c;
-    const uint32_t a_rows32 = 32u * (uint32_t)g.K * 2u;
+    const uint32_t a_rows64 = 64u * (uint32_t)g.K * 2u;
     struct StageA {
         u32x4 v[AR];
     };
     auto fetch_a = [&](int k0, StageA& st) {
 #pragma unroll
         for (int i = 0; i < AR; i++)
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_off + a_rows32 * i + 2u * (kbase + k0), 0, 0);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_off + a_rows64 * i + 2u * (kbase + k0), 0, 0);
     };
     auto stash_a = [&](const StageA& st, int buf, int i) {
-        *reinterpret_cast<u32x4*>(As + buf * PANEL + swz(a_r + 32 * i, a_c)) = st.v[i];
+        *reinterpret_cast<u32x4*>(As + buf * PANEL + swz(a_r + 64 * i, a_c)) = st.v[i];
     };
 
-    // weights: chunk q = t + 256 i is 16 bytes (32 values) of column q / 2,
-    // K half q % 2 of the step, with its scale(s) and zero point(s); the
-    // loaded values are only read when the step is unpacked, one step later.
-    // zsh: bit offset of the zero-point nibble in its byte.
+    // weights: thread t moves 16 bytes (32 values) of column t / 2, K half
+    // t % 2 of the step, with its scale(s) and zero point(s); the loaded
+    // values are only read when the step is unpacked, one step later.  With
+    // 16-value blocks the chunk spans an even block and the next one: their
+    // two scales are one aligned 32-bit word (K % 64 == 0 makes the blocks
+    // per column even) and their zero points the two nibbles of one byte.
+    // zsh: bit offset of the zero-point nibble in its byte (larger blocks).
+    const int b_col = t >> 1, b_half = t & 1;
     struct StageB {
-        u32x4 b[BR];
-        uint16_t s[BR][NB];
-        uint8_t z[BR][NB];
-        uint32_t zsh[BR][NB];
+        u32x4 b;
+        uint32_t s;
+        uint32_t z;
+        uint32_t zsh;
     };
     auto fetch_b = [&](int k0, StageB& st) {
-#pragma unroll
-        for (int i = 0; i < BR; i++) {
-            const int q = t + 256 * i;
-            const int col = n0 + (q >> 1), half = q & 1;
-            const int kb = kbase + k0 + 32 * half;
-            st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                rb_rs, (uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)kb / 2u, 0, 0);
-#pragma unroll
-            for (int h = 0; h < NB; h++) {
-                const uint32_t blk = (uint32_t)(kb + 16 * h) >> g.log2_bs;
-                st.s[i][h] = __builtin_amdgcn_raw_buffer_load_b16(
-                    rs_rs, 2u * ((uint32_t)col * (uint32_t)g.nb + blk), 0, 0);
-                if constexpr (HAS_ZP) {
-                    st.z[i][h] = __builtin_amdgcn_raw_buffer_load_b8(
-                        rz_rs, (uint32_t)col * (uint32_t)g.zp_row + (blk >> 1), 0, 0);
-                    st.zsh[i][h] = 4u * (blk & 1u);
-                }
-            }
+        const int col = n0 + b_col;
+        const int kb = kbase + k0 + 32 * b_half;
+        st.b = __builtin_amdgcn_raw_buffer_load_b128(
+            rb_rs, (uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)kb / 2u, 0, 0);
+        const uint32_t blk = (uint32_t)kb >> g.log2_bs;
+        const uint32_t s_off = 2u * ((uint32_t)col * (uint32_t)g.nb + blk);
+        if constexpr (BS16)
+            st.s = __builtin_amdgcn_raw_buffer_load_b32(rs_rs, s_off, 0, 0);
+        else
+            st.s = __builtin_amdgcn_raw_buffer_load_b16(rs_rs, s_off, 0, 0);
+        if constexpr (HAS_ZP) {
+            st.z = __builtin_amdgcn_raw_buffer_load_b8(rz_rs, (uint32_t)col * (uint32_t)g.zp_row + (blk >> 1), 0, 0);
+            if constexpr (!BS16) st.zsh = 4u * (blk & 1u);
         }
     };
-    // unpack 8 values (word d of chunk i): (q - zp) * s is exact in float32,
-    // one RTNE rounding to bf16
-    auto stash_b = [&](const StageB& st, int buf, int i, int d) {
-        const int q = t + 256 * i;
-        const int c = q >> 1, half = q & 1;
+    // unpack 8 values (word d of the chunk): (q - zp) * s is exact in
+    // float32, one RTNE rounding to bf16
+    auto stash_b = [&](const StageB& st, int buf, int d) {
         const int h = BS16 ? (d >> 1) : 0;
-        const uint32_t zq = HAS_ZP ? __builtin_amdgcn_ubfe((uint32_t)st.z[i][h], st.zsh[i][h], 4) : 8u;
-        const float sc = __uint_as_float((uint32_t)st.s[i][h] << 16);
+        uint32_t zq = 8u;
+        if constexpr (HAS_ZP) zq = __builtin_amdgcn_ubfe(st.z, BS16 ? 4u * h : st.zsh, 4);
+        const float sc = __uint_as_float(BS16 && h ? (st.s & 0xFFFF0000u) : (st.s << 16));
         const float zs = (float)zq * sc;
-        const uint32_t lo = opaque_and(st.b[i][d], 0x0F0F0F0Fu);
-        const uint32_t hi = opaque_and(st.b[i][d] >> 4, 0x0F0F0F0Fu);
+        const uint32_t lo = opaque_and(st.b[d], 0x0F0F0F0Fu);
+        const uint32_t hi = opaque_and(st.b[d] >> 4, 0x0F0F0F0Fu);
         float v[8];
         v[0] = fmaf(ubyte_to_f32<0>(lo), sc, -zs); v[1] = fmaf(ubyte_to_f32<0>(hi), sc, -zs);
         v[2] = fmaf(ubyte_to_f32<1>(lo), sc, -zs); v[3] = fmaf(ubyte_to_f32<1>(hi), sc, -zs);
@@ -633,7 +629,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
             pr[1] = (__bf16)v[2 * e + 1];
             o[e] = __builtin_bit_cast(uint32_t, pr);
         }
-        *reinterpret_cast<u32x4*>(Bs + buf * PANEL + swz(c, 4 * half + d)) = u32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<u32x4*>(Bs + buf * PANEL + swz(b_col, 4 * b_half + d)) = u32x4{o[0], o[1], o[2], o[3]};
     };
 
     f32x16 acc[TM][TN];
@@ -644,55 +640,29 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    // Multiply the step in LDS buffer buf (4 substeps of 16 MFMAs, operands
-    // of the next substep read ahead) while a quarter of the next step's
-    // activations and weights goes from registers into buffer buf ^ 1 per
-    // substep.
+    // Multiply the step in LDS buffer buf (4 sub-steps of 8 MFMAs) while a
+    // quarter of the next step's activations and weights goes from registers
+    // into buffer buf ^ 1 per sub-step.
     auto step_body = [&](int buf, const StageA& na, const StageB& nb) {
         const uint8_t* a = As + buf * PANEL;
         const uint8_t* b = Bs + buf * PANEL;
-        bf16x8 af[2][TM], bfr[2][TN];
-        auto load_frags = [&](int ks, int p) {
-            const int chunk = 2 * ks + (lane >> 5);
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-                af[p][i] = *reinterpret_cast<const bf16x8*>(a + swz(wm * 128 + i * 32 + (lane & 31), chunk));
-#pragma unroll
-            for (int j = 0; j < TN; j++)
-                bfr[p][j] = *reinterpret_cast<const bf16x8*>(b + swz(wn * 128 + j * 32 + (lane & 31), chunk));
-        };
-        load_frags(0, 0);
-        // the first operands cannot be read before the barrier; fill their
-        // latency with unpacking work
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // 8 LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // 16 VALU
 #pragma unroll
         for (int ks = 0; ks < B4_K / 16; ks++) {
-            const int p = ks & 1;
-            if (ks + 1 < B4_K / 16) load_frags(ks + 1, p ^ 1);
+            const int chunk = 2 * ks + (lane >> 5);
+            bf16x8 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+                af[i] = *reinterpret_cast<const bf16x8*>(a + swz(wm * 128 + i * 32 + (lane & 31), chunk));
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+                bfr[j] = *reinterpret_cast<const bf16x8*>(b + swz(wn * 64 + j * 32 + (lane & 31), chunk));
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
                 for (int j = 0; j < TN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][i], bfr[p][j], acc[i][j], 0, 0, 0);
-            stash_a(na, buf ^ 1, 2 * ks);
-            stash_a(na, buf ^ 1, 2 * ks + 1);
-            stash_b(nb, buf ^ 1, (2 * ks) >> 2, (2 * ks) & 3);
-            stash_b(nb, buf ^ 1, (2 * ks + 1) >> 2, (2 * ks + 1) & 3);
-            // per sub-step: each MFMA followed by an LDS read (the next
-            // sub-step's operands) or write (staging) and unpacking work
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
-            }
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
-                if (q & 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
-            }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            stash_a(na, buf ^ 1, ks);
+            stash_b(nb, buf ^ 1, ks);
         }
     };
 
@@ -717,9 +687,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
 #pragma unroll
         for (int i = 0; i < AR; i++) stash_a(sa, b, i);
 #pragma unroll
-        for (int i = 0; i < BR; i++)
-#pragma unroll
-            for (int d = 0; d < 4; d++) stash_b(sb, b, i, d);
+        for (int d = 0; d < 4; d++) stash_b(sb, b, d);
     };
     StageA ax, ay;
     StageB bx, by;
@@ -752,7 +720,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     float* const part = g.part ? g.part + (int64_t)split * g.M * g.N : nullptr;
 #pragma unroll
     for (int j = 0; j < TN; j++) {
-        const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+        const int n = n0 + wn * 64 + j * 32 + (lane & 31);
         if (n >= g.N) continue;
         const float bv = (!part && g.bias) ? g.bias[n] : 0.f;
 #pragma unroll
@@ -1102,7 +1070,10 @@ Plan plan_gemm(const Problem& p) {
     if (p.bf16 && vec_a && (p.K % 8) == 0 && a_bytes + 256 * p.K * esz < lim &&
         b_bytes + 256 * p.col_bytes < lim && p.M * p.N < lim) {
         const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-        if (p.M > 128 && p.K % B4_K == 0 && p.K % p.bs == 0) {
+        // (16-value blocks: the wide kernel reads a chunk's two scales as one
+        // 32-bit word)
+        const bool s_pairs = p.bs != 16 || (reinterpret_cast<uintptr_t>(p.scales) & 3) == 0;
+        if (p.M > 128 && p.K % B4_K == 0 && p.K % p.bs == 0 && s_pairs) {
             pl.kind = Plan::WIDE;
             pl.tiles = big;
             choose_split(pl, p, cus, (int)(p.K / B4_K));   // one 256 x 256 workgroup per CU
@@ -1163,7 +1134,7 @@ int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
         case Plan::WIDE: {
             auto kern = p.has_zp ? (bs16 ? gemm_bf16_wide_kernel<true, true> : gemm_bf16_wide_kernel<true, false>)
                                  : (bs16 ? gemm_bf16_wide_kernel<false, true> : gemm_bf16_wide_kernel<false, false>);
-            hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, b);
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, s, b);
             break;
         }
         case Plan::REG256:
