@@ -386,3 +386,79 @@ def test_split_k_graph_matches_direct():
                 y.fill_(float("nan"))
     finally:
         seq.close()
+
+
+# ---------------------------------------------------------------------------
+# small M (1 <= M <= 16, K % 32 == 0, block_size >= 32): matrix-core kernel
+# ---------------------------------------------------------------------------
+
+SMALL_M_CASES = [  # (M, K, N): ragged N, K not a multiple of the 128-value span
+    (1, 32, 1), (2, 64, 17), (3, 96, 33), (4, 1024, 4096), (5, 160, 100),
+    (8, 2048, 1024), (15, 3072, 130), (16, 1024, 515), (16, 128, 16), (7, 2560, 260),
+    (9, 9728, 40), (12, 4096, 2049), (6, 224, 31),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("bs", [32, 64, 128, 256])
+def test_small_m_parity_sweep(orc, dt, bs):
+    rng = np.random.default_rng(300 + bs)
+    worst = 0.0
+    for M, K, N in SMALL_M_CASES:
+        zp, bias = bool(rng.integers(2)), bool(rng.integers(2))
+        log(f"small-M {dt} bs={bs} M={M} K={K} N={N} zp={zp} bias={bias}")
+        inp, g = _inputs(K, N, M, bs, dt, zp, bias, seed=M * 11 + K * 3 + N)
+        pw = _packed(g, bs)
+        y = mnb.gemm(g.a, pw.b_packed, pw.scales, pw.zp_packed, pw.bias, K=K, N=N,
+                     block_size=bs)
+        y_ref, S = oracle_ref(orc, inp)
+        worst = max(worst, assert_close(out_f64(y), y_ref, S, dt, f"M={M} K={K} N={N}"))
+    log(f"small-M {dt} bs={bs}: worst err/tol {worst:.3g}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("M", [2, 16])
+def test_small_m_exact_arithmetic_bit_exact(orc, dt, M):
+    for K, N, bs in [(1024, 70, 32), (2560, 33, 128), (352, 17, 64)]:
+        log(f"small-M exact {dt} M={M} K={K} N={N} bs={bs}")
+        q, zp, sc, a, bias = _exact_case(K, N, M, bs, dt, seed=K + 3 * M)
+        pw = mnb.PackedWeight.from_logical(q.to(DEV), sc.to(DEV), zp.to(DEV), bias.to(DEV),
+                                           block_size=bs)
+        y = pw.matmul(a.to(DEV))
+        y_ref, _ = orc.matmul(act_np(a), q.numpy(), zp.numpy(), act_np(sc), bs,
+                              bias=bias.numpy())
+        if dt == "f32":
+            assert np.array_equal(y.cpu().numpy(), orc.round_to_f32(y_ref)), (K, N, M)
+        else:
+            assert np.array_equal(act_np(y), orc.round_to_bf16(y_ref)), (K, N, M)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_small_m_identity_rows_return_dequantized_weights(orc, dt):
+    """A = the first 16 rows of I_K: row m of Y is column m of dequant(B),
+    rounded once (float32, or bfloat16 for bfloat16 activations)."""
+    K, N, bs = 160, 45, 32
+    inp, g = _inputs(K, N, 1, bs, dt, True, False, seed=12)
+    pw = _packed(g, bs)
+    w = orc.dequant(inp.q.numpy(), inp.zp.numpy(), act_np(inp.scales), bs)   # [N][K] exact
+    eye = torch.eye(K, device=DEV)[:16]
+    if dt == "bf16":
+        eye = eye.to(torch.bfloat16)
+    y = mnb.gemm(eye, pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N, block_size=bs)
+    want = orc.round_to_f32(w) if dt == "f32" else orc.round_to_bf16(w)
+    got = y.cpu().numpy() if dt == "f32" else act_np(y)
+    assert np.array_equal(got, want[:, :16].T)
+
+
+@pytest.mark.parametrize("M", [4, 16])
+def test_small_m_fused_launch_bit_identical_to_separate(M):
+    for K, bs, dt in [(1024, 32, "f32"), (2560, 128, "f32"), (2560, 128, "bf16")]:
+        log(f"small-M fusion M={M} K={K} bs={bs} {dt}")
+        _, g1 = _inputs(K, 300, M, bs, dt, True, False, seed=21)
+        _, g2 = _inputs(K, 1700, M, bs, dt, True, False, seed=22)
+        p1, p2 = _packed(g1, bs), _packed(g2, bs)
+        a = g1.a
+        q = torch.cat([g1.q, g2.q])
+        fused = mnb.PackedWeight.from_logical(q, torch.cat([g1.scales, g2.scales]),
+                                              torch.cat([g1.zp, g2.zp]), block_size=bs)
+        assert torch.equal(fused.matmul(a), torch.cat([p1.matmul(a), p2.matmul(a)], 1))

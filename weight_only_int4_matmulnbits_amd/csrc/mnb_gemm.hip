@@ -584,10 +584,12 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     // per column even) and their zero points the two nibbles of one byte.
     // zsh: bit offset of the zero-point nibble in its byte (larger blocks).
     const int b_col = t >> 1, b_half = t & 1;
+    // (z stays a byte: widening it where it is loaded would make the
+    // compiler wait for the load there, ahead of the next step's requests)
     struct StageB {
         u32x4 b;
         uint32_t s;
-        uint32_t z;
+        uint8_t z;
         uint32_t zsh;
     };
     auto fetch_b = [&](int k0, StageB& st) {
@@ -611,7 +613,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     auto stash_b = [&](const StageB& st, int buf, int d) {
         const int h = BS16 ? (d >> 1) : 0;
         uint32_t zq = 8u;
-        if constexpr (HAS_ZP) zq = __builtin_amdgcn_ubfe(st.z, BS16 ? 4u * h : st.zsh, 4);
+        if constexpr (HAS_ZP) zq = __builtin_amdgcn_ubfe((uint32_t)st.z, BS16 ? 4u * h : st.zsh, 4);
         const float sc = __uint_as_float(BS16 && h ? (st.s & 0xFFFF0000u) : (st.s << 16));
         const float zs = (float)zq * sc;
         const uint32_t lo = opaque_and(st.b[d], 0x0F0F0F0Fu);
@@ -640,27 +642,33 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    // Multiply the step in LDS buffer buf (4 sub-steps of 8 MFMAs) while a
-    // quarter of the next step's activations and weights goes from registers
-    // into buffer buf ^ 1 per sub-step.
+    // Multiply the step in LDS buffer buf (4 sub-steps of 8 MFMAs, the
+    // operands of the next sub-step read ahead) while a quarter of the next
+    // step's activations and weights goes from registers into buffer buf ^ 1
+    // per sub-step.
     auto step_body = [&](int buf, const StageA& na, const StageB& nb) {
         const uint8_t* a = As + buf * PANEL;
         const uint8_t* b = Bs + buf * PANEL;
-#pragma unroll
-        for (int ks = 0; ks < B4_K / 16; ks++) {
+        bf16x8 af[2][TM], bfr[2][TN];
+        auto load_frags = [&](int ks, int p) {
             const int chunk = 2 * ks + (lane >> 5);
-            bf16x8 af[TM], bfr[TN];
 #pragma unroll
             for (int i = 0; i < TM; i++)
-                af[i] = *reinterpret_cast<const bf16x8*>(a + swz(wm * 128 + i * 32 + (lane & 31), chunk));
+                af[p][i] = *reinterpret_cast<const bf16x8*>(a + swz(wm * 128 + i * 32 + (lane & 31), chunk));
 #pragma unroll
             for (int j = 0; j < TN; j++)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(b + swz(wn * 64 + j * 32 + (lane & 31), chunk));
+                bfr[p][j] = *reinterpret_cast<const bf16x8*>(b + swz(wn * 64 + j * 32 + (lane & 31), chunk));
+        };
+        load_frags(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < B4_K / 16; ks++) {
+            const int p = ks & 1;
+            if (ks + 1 < B4_K / 16) load_frags(ks + 1, p ^ 1);
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
                 for (int j = 0; j < TN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][i], bfr[p][j], acc[i][j], 0, 0, 0);
             stash_a(na, buf ^ 1, ks);
             stash_b(nb, buf ^ 1, ks);
         }
@@ -1099,9 +1107,10 @@ Plan plan_gemm(const Problem& p) {
 
 }  // namespace
 
-size_t gemm_workspace_bytes(const Problem& p) { return plan_gemm(p).ws; }
+size_t gemm_workspace_bytes(const Problem& p) { return smallm_ok(p) ? 0 : plan_gemm(p).ws; }
 
 int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
+    if (smallm_ok(p)) return launch_smallm(p, s);
     Plan pl = plan_gemm(p);
     if (pl.splits > 1 && (!ws || ws_bytes < pl.ws)) {
         pl.splits = 1;                                      // no room for partials: one pass

@@ -40,6 +40,10 @@ int launch_gemv(const Problem& p, hipStream_t s);
 // to split; NULL or smaller: one pass without splitting).
 int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes);
 size_t gemm_workspace_bytes(const Problem& p);
+// 1 <= M <= 16 on the matrix cores (K % 32 == 0, block_size >= 32, A 16-byte
+// aligned); launch_gemm takes it whenever smallm_ok holds.
+bool smallm_ok(const Problem& p);
+int launch_smallm(const Problem& p, hipStream_t s);
 int64_t gemv_max_k(int bs);
 int device_compute_units();   // CUs of the current device (cached)
 
