@@ -58,6 +58,13 @@ class Oracle:
         L.oracle_dequant_int.argtypes = [i64, i64, i64, vp, vp, vp]
         L.oracle_matmul.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp,
                                     vp, vp, vp, vp, vp, ctypes.c_int]
+        L.oracle_qdq_unpack.argtypes = [i64, vp, vp]
+        L.oracle_qdq_dequant.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp,
+                                         ctypes.c_int, vp, vp]
+        L.oracle_qdq_import.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp,
+                                        i64, vp, vp, vp, vp]
+        L.oracle_silu_mul.argtypes = [i64, vp, vp, vp]
+        L.oracle_argmax.argtypes = [i64, i64, ctypes.c_int, vp, vp]
         for f in ("oracle_pack_weights", "oracle_unpack_weights",
                   "oracle_pack_zero_points", "oracle_unpack_zero_points",
                   "oracle_round_to_f32", "oracle_round_to_bf16",
@@ -187,6 +194,70 @@ class Oracle:
                                self._p(zp), self._p(scales), self._p(bias),
                                self._p(y), self._p(S), int(nthreads))
         return y, S
+
+
+    # -- the QDQ encoding -----------------------------------------------------
+    def qdq_unpack(self, packed: np.ndarray, count: int) -> np.ndarray:
+        """Elements 0..count-1 of a flat low-nibble-first UINT4 stream."""
+        packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        assert packed.size >= (count + 1) // 2
+        out = np.empty(count, np.uint8)
+        self.lib.oracle_qdq_unpack(count, self._p(packed), self._p(out))
+        return out
+
+    def qdq_dequant(self, w_q: np.ndarray, zp_q: Optional[np.ndarray],
+                    scales_q: np.ndarray, K: int, N: int, bs: int,
+                    axis: int) -> np.ndarray:
+        """DequantizeLinear of the QDQ tensors: exact binary64 [K][N]."""
+        w_q = np.ascontiguousarray(w_q, dtype=np.uint8)
+        scales_q = np.ascontiguousarray(scales_q)
+        nb = self.n_blocks(K, bs)
+        assert w_q.size == (K * N + 1) // 2 and scales_q.size == nb * N
+        if zp_q is not None:
+            zp_q = np.ascontiguousarray(zp_q, dtype=np.uint8)
+            assert zp_q.size == (nb * N + 1) // 2
+        out = np.empty((K, N), np.float64)
+        self.lib.oracle_qdq_dequant(K, N, bs, axis, self._p(w_q), self._p(zp_q),
+                                    self._dtype_code(scales_q), self._p(scales_q),
+                                    self._p(out))
+        return out
+
+    def qdq_import(self, w_q: np.ndarray, zp_q: Optional[np.ndarray],
+                   scales_q: np.ndarray, K: int, N: int, bs: int, axis: int):
+        """(b_packed, scales [N][nb], zp_packed) in the MatMulNBits storage."""
+        w_q = np.ascontiguousarray(w_q, dtype=np.uint8)
+        scales_q = np.ascontiguousarray(scales_q)
+        nb = self.n_blocks(K, bs)
+        assert w_q.size == (K * N + 1) // 2 and scales_q.size == nb * N
+        if zp_q is not None:
+            zp_q = np.ascontiguousarray(zp_q, dtype=np.uint8)
+            assert zp_q.size == (nb * N + 1) // 2
+        b = np.empty(N * nb * (bs // 2), np.uint8)
+        s = np.empty((N, nb), scales_q.dtype)
+        z = np.empty(N * ((nb + 1) // 2), np.uint8)
+        self.lib.oracle_qdq_import(K, N, bs, axis, self._p(w_q), self._p(zp_q),
+                                   scales_q.itemsize, self._p(scales_q), self._p(b),
+                                   self._p(s), self._p(z))
+        return b, s, z
+
+    # -- epilogues ----------------------------------------------------------------
+    def silu_mul(self, gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+        gate = np.ascontiguousarray(gate, dtype=np.float64)
+        up = np.ascontiguousarray(up, dtype=np.float64)
+        assert gate.shape == up.shape
+        h = np.empty(gate.shape, np.float64)
+        self.lib.oracle_silu_mul(gate.size, self._p(gate), self._p(up), self._p(h))
+        return h
+
+    def argmax(self, x: np.ndarray) -> np.ndarray:
+        """Row-wise greedy ArgMax of float32 or bfloat16 (uint16 bits) rows."""
+        x = np.ascontiguousarray(x)
+        if x.ndim == 1:
+            x = x[None]
+        M, N = x.shape
+        idx = np.empty(M, np.int64)
+        self.lib.oracle_argmax(M, N, self._dtype_code(x), self._p(x), self._p(idx))
+        return idx
 
 
 _default: Optional[Oracle] = None

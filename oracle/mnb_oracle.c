@@ -233,3 +233,105 @@ void oracle_matmul(int64_t M, int64_t K, int64_t N, int64_t bs, int act_dtype,
         free(wcol);
     }
 }
+
+/* ---- the QDQ encoding (page "Qwen3 CPU Inference Critical Path", "Export
+ * contract", qwen3-int4-qdq) ------------------------------------------------
+ * A logical UINT4 tensor is stored in ONNX row-major element order, two
+ * elements per byte, the even-numbered element in the low nibble.  Scales and
+ * zero points are blocked along one axis of the weight:
+ *   axis 0 (a projection):      W[K][N], scale/zp [nb][N], block of k = k/bs;
+ *   axis 1 (tied embedding/LM): W[N][K], scale/zp [N][nb], block of k = k/bs.
+ * A missing zero-point tensor means zero point 0 (the DequantizeLinear
+ * default), unlike the MatMulNBits default of 8. */
+
+/* element i of a flat packed UINT4 stream */
+static uint8_t qdq_nibble(const uint8_t *packed, int64_t i) {
+    uint8_t byte = packed[i / 2];
+    return (i % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+}
+
+void oracle_qdq_unpack(int64_t count, const uint8_t *packed, uint8_t *out) {
+    for (int64_t i = 0; i < count; i++) out[i] = qdq_nibble(packed, i);
+}
+
+/* flat element index of w[k][n] (the MatMulNBits B[k][n]) in the QDQ tensor */
+static int64_t qdq_w_index(int axis, int64_t K, int64_t N, int64_t k, int64_t n) {
+    return axis == 0 ? k * N + n : n * K + k;
+}
+
+static int64_t qdq_s_index(int axis, int64_t nb, int64_t N, int64_t b, int64_t n) {
+    return axis == 0 ? b * N + n : n * nb + b;
+}
+
+/* DequantizeLinear on the QDQ layout, straight from the definition:
+ * out[k][n] = (w - zp) * scale, exact in binary64. */
+void oracle_qdq_dequant(int64_t K, int64_t N, int64_t bs, int axis,
+                        const uint8_t *w_q, const uint8_t *zp_q,
+                        int scale_dtype, const void *scales_q, double *out) {
+    int64_t nb = oracle_n_blocks(K, bs);
+    for (int64_t k = 0; k < K; k++) {
+        for (int64_t n = 0; n < N; n++) {
+            int64_t b = k / bs;
+            int64_t si = qdq_s_index(axis, nb, N, b, n);
+            int w = qdq_nibble(w_q, qdq_w_index(axis, K, N, k, n));
+            int zero = zp_q ? qdq_nibble(zp_q, si) : 0;
+            out[k * N + n] = (double)(w - zero) * load_value(scale_dtype, scales_q, si);
+        }
+    }
+}
+
+/* The normalization into the MatMulNBits storage: gather the logical
+ * q[n][k] and zp[n][b] from the QDQ tensors, then pack them with the packers
+ * above; scales are moved element by element (scale_size bytes each) into
+ * [N][nb]. */
+void oracle_qdq_import(int64_t K, int64_t N, int64_t bs, int axis,
+                       const uint8_t *w_q, const uint8_t *zp_q,
+                       int64_t scale_size, const void *scales_q,
+                       uint8_t *b_packed, void *scales, uint8_t *zp_packed) {
+    int64_t nb = oracle_n_blocks(K, bs);
+    uint8_t *q = (uint8_t *)malloc((size_t)(N * K));
+    uint8_t *zp = (uint8_t *)malloc((size_t)(N * nb));
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++)
+            q[n * K + k] = qdq_nibble(w_q, qdq_w_index(axis, K, N, k, n));
+        for (int64_t b = 0; b < nb; b++) {
+            int64_t si = qdq_s_index(axis, nb, N, b, n);
+            zp[n * nb + b] = zp_q ? qdq_nibble(zp_q, si) : 0;
+            memcpy((uint8_t *)scales + (n * nb + b) * scale_size,
+                   (const uint8_t *)scales_q + si * scale_size, (size_t)scale_size);
+        }
+    }
+    oracle_pack_weights(K, N, bs, q, b_packed);
+    oracle_pack_zero_points(N, nb, zp, zp_packed);
+    free(q);
+    free(zp);
+}
+
+/* ---- the gated MLP product (page "Qwen3 CPU Inference Critical Path",
+ * "Operator priority": the SiLU-gated MLP, Sigmoid(x) * x times the up
+ * projection) ------------------------------------------------------------- */
+void oracle_silu_mul(int64_t n, const double *gate, const double *up, double *h) {
+    for (int64_t i = 0; i < n; i++) {
+        double g = gate[i];
+        double sig = 1.0 / (1.0 + exp(-g));
+        h[i] = g * sig * up[i];
+    }
+}
+
+/* ---- greedy ArgMax ("final RMSNorm, LM-head GEMV, and greedy ArgMax"):
+ * per row, the first index holding the largest value; a NaN counts as larger
+ * than every number, so the first NaN wins. */
+void oracle_argmax(int64_t M, int64_t N, int dtype, const void *x, int64_t *idx) {
+    for (int64_t m = 0; m < M; m++) {
+        int64_t best = 0;
+        double bv = load_value(dtype, x, m * N);
+        for (int64_t n = 1; n < N && !isnan(bv); n++) {
+            double v = load_value(dtype, x, m * N + n);
+            if (isnan(v) || v > bv) {
+                best = n;
+                bv = v;
+            }
+        }
+        idx[m] = best;
+    }
+}

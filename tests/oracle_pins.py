@@ -427,4 +427,132 @@ def pin_contract_rules(orc):
     assert not orc.contract_ok(64, 0, 4, 32)
 
 
+# ---------------------------------------------------------------------------
+# the QDQ encoding, the gated MLP product and greedy ArgMax
+# ---------------------------------------------------------------------------
+
+QDQ_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "qdq_examples.json")
+
+
+def _qdq_golden():
+    with open(QDQ_GOLDEN) as f:
+        return json.load(f)
+
+
+def pin_qdq_hand_unpack(orc):
+    g = _qdq_golden()["unpack"]
+    got = orc.qdq_unpack(np.array(g["packed"], np.uint8), len(g["values"]))
+    assert got.tolist() == g["values"]
+
+
+def pin_qdq_hand_projection(orc):
+    g = _qdq_golden()["projection_axis0"]
+    K, N, bs = g["K"], g["N"], g["block_size"]
+    w_q = np.array(g["w_q"], np.uint8)
+    zp_q = np.array(g["zp_q"], np.uint8)
+    sc = _f32(g["scales_q_bN"])
+    # the fixture's packed bytes really are the row-major flattening
+    assert orc.qdq_unpack(w_q, K * N).tolist() == sum(g["w_logical_KN"], [])
+    b, s, z = orc.qdq_import(w_q, zp_q, sc, K, N, bs, axis=0)
+    assert b.tolist() == g["b_packed"]
+    assert s.tolist() == g["scales_Nb"]
+    assert z.tolist() == g["zp_packed"]
+    assert orc.qdq_dequant(w_q, zp_q, sc, K, N, bs, axis=0).tolist() == g["dequant_KN"]
+
+
+def pin_qdq_hand_projection_two_blocks(orc):
+    g = _qdq_golden()["projection_axis0_two_blocks"]
+    K, N, bs = g["K"], g["N"], g["block_size"]
+    w_q = np.array(g["w_q"], np.uint8)
+    zp_q = np.array(g["zp_q"], np.uint8)
+    sc = _f32(g["scales_q_bN"])
+    b, s, z = orc.qdq_import(w_q, zp_q, sc, K, N, bs, axis=0)
+    assert b.tolist() == g["b_packed"]
+    assert s.tolist() == g["scales_Nb"]
+    assert z.tolist() == g["zp_packed"]
+    w = orc.qdq_dequant(w_q, zp_q, sc, K, N, bs, axis=0)
+    assert all(w[k].tolist() == g["dequant_rows"]["k_below_16"] for k in range(16))
+    assert all(w[k].tolist() == g["dequant_rows"]["k_from_16"] for k in range(16, K))
+
+
+def pin_qdq_hand_tied(orc):
+    g = _qdq_golden()["tied_axis1"]
+    K, N, bs = g["K"], g["N"], g["block_size"]
+    w_q = np.array(g["w_q"], np.uint8)
+    sc = _f32(g["scales_q_Nb"])
+    assert orc.qdq_unpack(w_q, K * N).tolist() == sum(g["w_logical_NK"], [])
+    b, s, z = orc.qdq_import(w_q, None, sc, K, N, bs, axis=1)
+    assert b.tolist() == g["b_packed"]
+    assert s.tolist() == g["scales_q_Nb"]
+    assert z.tolist() == g["zp_packed"]
+    assert orc.qdq_dequant(w_q, None, sc, K, N, bs, axis=1).tolist() == g["dequant_KN"]
+
+
+def pin_qdq_roundtrip_both_axes(orc):
+    """DequantizeLinear evaluated on the QDQ tensors equals the MatMulNBits
+    dequantization of the normalized tensors (two independent index
+    formulations), for odd sizes, partial blocks, with and without zero
+    points, float32 and bfloat16 scales."""
+    rng = np.random.default_rng(21)
+    for K, N, bs, axis, has_zp, dt in [(37, 5, 16, 0, True, "f32"), (64, 7, 32, 0, False, "bf16"),
+                                       (100, 3, 64, 1, True, "f32"), (33, 9, 16, 1, False, "bf16"),
+                                       (256, 4, 128, 0, True, "bf16"), (17, 1, 256, 1, True, "f32")]:
+        nb = -(-K // bs)
+        w_q = rng.integers(0, 256, (K * N + 1) // 2, dtype=np.uint8)
+        zp_q = rng.integers(0, 256, (nb * N + 1) // 2, dtype=np.uint8) if has_zp else None
+        sc = rng.uniform(0.005, 0.05, nb * N).astype(np.float32)
+        if dt == "bf16":
+            sc = _bf16_bits(sc)
+        ref = orc.qdq_dequant(w_q, zp_q, sc, K, N, bs, axis)
+        b, s, z = orc.qdq_import(w_q, zp_q, sc, K, N, bs, axis)
+        q = orc.unpack_weights(b, K, N, bs)
+        zp = orc.unpack_zero_points(z, N, nb)
+        w = orc.dequant(q, zp, s, bs)                      # [N][K]
+        assert np.array_equal(w.T, ref), (K, N, bs, axis, has_zp, dt)
+        if not has_zp:
+            assert not zp.any()
+
+
+def pin_qdq_tied_is_native_storage(orc):
+    """axis 1 with whole blocks and an even block count: the QDQ bytes already
+    are the MatMulNBits storage (the tied weight needs no copy)."""
+    rng = np.random.default_rng(22)
+    for K, N, bs in [(64, 5, 32), (256, 3, 128), (1024, 2, 32)]:
+        nb = K // bs
+        assert nb % 2 == 0
+        w_q = rng.integers(0, 256, K * N // 2, dtype=np.uint8)
+        zp_q = rng.integers(0, 256, nb * N // 2, dtype=np.uint8)
+        sc = rng.uniform(0.005, 0.05, nb * N).astype(np.float32)
+        b, s, z = orc.qdq_import(w_q, zp_q, sc, K, N, bs, axis=1)
+        assert np.array_equal(b, w_q) and np.array_equal(z, zp_q)
+        assert np.array_equal(s.ravel(), sc)
+
+
+def pin_silu_mul_closed_forms(orc):
+    g = _qdq_golden()["silu_mul"]
+    h = orc.silu_mul(np.array(g["gate"]), np.array(g["up"]))
+    assert np.allclose(h, g["h"], rtol=1e-15, atol=0)
+    x = np.linspace(-30, 30, 61)
+    one = np.ones_like(x)
+    # silu(x) - silu(-x) = x, silu is x for large x, linear in the up value
+    assert np.allclose(orc.silu_mul(x, one) - orc.silu_mul(-x, one), x, rtol=1e-14, atol=1e-14)
+    assert orc.silu_mul(np.array([60.0]), np.array([1.0]))[0] == 60.0
+    assert np.array_equal(orc.silu_mul(x, 3 * one), 3 * orc.silu_mul(x, one))
+
+
+def pin_argmax_hand(orc):
+    g = _qdq_golden()["argmax"]
+    rows = np.array([[float(v) for v in r] for r in g["rows"]], np.float32)
+    assert orc.argmax(rows).tolist() == g["index"]
+    # the same decisions on bfloat16 bit patterns of these exact values
+    assert orc.argmax(_bf16_bits(rows)).tolist() == g["index"]
+
+
+def pin_argmax_bruteforce(orc):
+    rng = np.random.default_rng(23)
+    x = rng.integers(-3, 4, (50, 37)).astype(np.float32)     # many ties
+    want = [int(min(i for i in range(37) if r[i] == r.max())) for r in x]
+    assert orc.argmax(x).tolist() == want
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

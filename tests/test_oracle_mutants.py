@@ -51,6 +51,21 @@ MUTANTS = [
      "out[i] = nextafterf((float)x[i], 0.0f); /* one RTNE rounding */"),
     ("dequant_scale_from_wrong_block", "double s = load_value(scale_dtype, scales, n * nb + b);",
      "double s = load_value(scale_dtype, scales, n * nb + (b == 0 ? 0 : b - 1));"),
+    ("qdq_nibble_order_swapped", "return (i % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
+     "return (i % 2 == 1) ? (byte & 0x0F) : (byte >> 4);"),
+    ("qdq_projection_read_as_tied", "return axis == 0 ? k * N + n : n * K + k;",
+     "return axis == 0 ? n * K + k : n * K + k;"),
+    ("qdq_projection_scales_read_as_tied", "return axis == 0 ? b * N + n : n * nb + b;",
+     "return axis == 0 ? n * nb + b : n * nb + b;"),
+    ("qdq_dequant_default_zero_point_8", "int zero = zp_q ? qdq_nibble(zp_q, si) : 0;",
+     "int zero = zp_q ? qdq_nibble(zp_q, si) : 8;"),
+    ("qdq_import_default_zero_point_8", "zp[n * nb + b] = zp_q ? qdq_nibble(zp_q, si) : 0;",
+     "zp[n * nb + b] = zp_q ? qdq_nibble(zp_q, si) : 8;"),
+    ("silu_sigmoid_sign_flipped", "double sig = 1.0 / (1.0 + exp(-g));",
+     "double sig = 1.0 / (1.0 + exp(g));"),
+    ("silu_gate_factor_dropped", "h[i] = g * sig * up[i];", "h[i] = sig * up[i];"),
+    ("argmax_last_of_ties", "if (isnan(v) || v > bv) {", "if (isnan(v) || v >= bv) {"),
+    ("argmax_nan_ignored", "if (isnan(v) || v > bv) {", "if (v > bv) {"),
 ]
 
 
