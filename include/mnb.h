@@ -183,6 +183,79 @@ int mnb_dequant(const mnb_desc* d, const uint8_t* b_packed, const void* scales,
                 const uint8_t* zp_packed, int32_t out_kind, void* w_nk,
                 void* stream);
 
+/* ---- QDQ import ---------------------------------------------------------------
+ * mnb_import_qdq -- normalizes a weight in the blocked UINT4 DequantizeLinear
+ * encoding into the storage above (page "Qwen3 CPU Inference Critical Path",
+ * "Export contract", qwen3-int4-qdq: a projection is a logical UINT4[K,N]
+ * in row-major, low-nibble-first storage, blocked along axis 0; the tied
+ * embedding / LM-head weight is a logical UINT4[vocabulary,hidden] blocked
+ * along axis 1; another layout is normalized before it is matched).  A
+ * one-time preparation step, like mnb_pack.
+ *   axis        0: W is [K][N] (the MatMul B), scales and zero points [nb][N];
+ *               1: W is [N][K] (N = vocabulary, K = hidden), scales and zero
+ *                  points [N][nb].  nb = ceil(K / block_size).
+ *   w_q         ceil(K*N/2) bytes: W's elements in row-major order, element i
+ *               in byte i/2, the low nibble when i is even.
+ *   scales_q    nb*N elements of act_dtype in the axis's shape.
+ *   zp_q        ceil(nb*N/2) bytes packed like w_q, or NULL: DequantizeLinear
+ *               then uses zero point 0 (not the MatMulNBits default 8), which
+ *               is written to zp_packed explicitly.
+ *   b_packed, scales, zp_packed   outputs in the storage above (sizes from the
+ *               mnb_*_bytes queries; b_packed 16-byte aligned).
+ * d->has_zero_points must be 1 (the result always carries zero points).
+ * Inputs and outputs must not overlap (MNB_E_ARG).  All device pointers. */
+int mnb_import_qdq(const mnb_desc* d, int32_t axis, const uint8_t* w_q,
+                   const void* scales_q, const uint8_t* zp_q,
+                   uint8_t* b_packed, void* scales, uint8_t* zp_packed,
+                   void* stream);
+
+/* Nonzero when an axis-1 QDQ weight with zero points already is the storage
+ * above byte for byte (K % block_size == 0 and an even number of blocks per
+ * row): then w_q, scales_q and zp_q serve every entry point as they are, and
+ * the tied embedding and LM head share one copy ("initializer aliasing": no
+ * duplicated weight).  Host-only; 0 for an invalid descriptor. */
+int mnb_qdq_is_native(const mnb_desc* d, int32_t axis);
+
+/* ---- tied embedding and the LM head -------------------------------------------
+ * mnb_gather_rows -- the embedding lookup on the tied weight (same page,
+ * "Export contract" and "Operator priority", Gather: dequantize only the
+ * selected rows of the tied quantized initializer).  With N = vocabulary and
+ * K = hidden, embedding row v is column v of B:
+ *   out[t][k] = (q[v][k] - zp[v][k / bs]) * s[v][k / bs],  v = ids[t],
+ * rounded once to act_dtype exactly like mnb_dequant (out_kind 0 for float32,
+ * 1 for bfloat16).  ids: int64 [n_ids] (device, 8-byte aligned); a negative
+ * id counts from the end (ids in [-N, N)); a row whose id lies outside that
+ * range is written as NaN and reads no weight.  out: [n_ids][K] act_dtype.
+ * n_ids == 0 does nothing. */
+int mnb_gather_rows(const mnb_desc* d, const int64_t* ids, int64_t n_ids,
+                    const uint8_t* b_packed, const void* scales,
+                    const uint8_t* zp_packed, void* out, void* stream);
+
+/* mnb_argmax -- greedy ArgMax per row (same page, "Phase Q2": final
+ * RMSNorm, LM-head GEMV and greedy ArgMax): idx[m] = the first n holding the
+ * largest x[m][n]; a NaN counts as larger than every number, so the first NaN
+ * wins.  x: [M][N] float32 or bfloat16 (dtype, an mnb_dtype); idx: int64 [M].
+ * One workgroup per row. */
+int mnb_argmax(int32_t dtype, int64_t M, int64_t N, const void* x,
+               int64_t* idx, void* stream);
+
+/* ---- gated MLP epilogue --------------------------------------------------------
+ * mnb_gemv_silu_mul -- the fused gate||up decode projection (same page,
+ * "Operator priority": the SiLU-gated MLP, Sigmoid(x) * x times the up
+ * projection; "Phase Q2": gate projection, SiLU and gate/up multiplication).
+ * B holds N = 2I columns, gate columns 0..I-1 then the matching up columns
+ * I..2I-1 (one concatenated weight, as for the unfused fused-N launch);
+ * bias, when given, has N entries.  With y = a x dequant(B) + bias:
+ *   h[i] = silu(y[i]) * y[I + i],  silu(x) = x / (1 + exp(-x)),
+ * evaluated in float32 on y before any rounding, then stored in act_dtype
+ * (RTNE for bfloat16).  y[i] and y[I + i] are computed exactly as mnb_gemv
+ * computes those columns.  M must be 1, N even and K within the decode kernel
+ * without split-K teams (MNB_E_UNSUPPORTED otherwise); h: [1][I]. */
+int mnb_gemv_silu_mul(const mnb_desc* d, int64_t M, const void* a,
+                      const uint8_t* b_packed, const void* scales,
+                      const uint8_t* zp_packed, const float* bias, void* h,
+                      void* stream);
+
 /* ---- decode-step driver ------------------------------------------------------
  * One projection of a step: mnb_gemv when M == 1 and K <= mnb_gemv_max_k,
  * mnb_gemm otherwise.  A fused QKV or gate||up projection is one entry whose

@@ -158,3 +158,49 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5):
         assert L.mnb_status_string(s).decode().startswith("MNB_")
     assert b"unknown" in L.mnb_status_string(42)
+
+
+def test_import_qdq_argument_errors():
+    L = mnb.lib()
+    dz = mnb.make_desc(64, 8, 32, has_zero_points=True)
+    d = mnb.make_desc(64, 8, 32)
+
+    def imp(desc, axis=0, w=P16, s=0x20000, z=None, b=0x30000, so=0x40000, zo=0x50000):
+        return L.mnb_import_qdq(ctypes.byref(desc), axis, w, s, z, b, so, zo, None)
+
+    assert imp(dz, axis=2) == -1
+    assert imp(d) == -1                              # the result always has zero points
+    assert "has_zero_points" in L.mnb_last_error().decode()
+    assert imp(dz, w=None) == -1
+    assert imp(dz, zo=None) == -1
+    assert imp(dz, b=0x30008) == -3                  # b_packed needs 16-byte alignment
+    assert imp(dz, s=0x20002) == -3                  # float32 scales need 4
+    assert imp(dz, b=P16 + 16) == -1                 # b_packed overlaps w_q (256 bytes)
+    assert "overlap" in L.mnb_last_error().decode()
+
+
+def test_qdq_native_storage_rule():
+    # axis 1, whole blocks, even block count per row, zero points present
+    assert mnb.qdq_is_native(1024, 151936, 32, axis=1)
+    assert mnb.qdq_is_native(2560, 151936, 128, axis=1)
+    assert not mnb.qdq_is_native(1024, 151936, 32, axis=0)      # needs the transpose
+    assert not mnb.qdq_is_native(96, 10, 32, axis=1)            # 3 blocks: zero-point rows straddle
+    assert not mnb.qdq_is_native(100, 10, 32, axis=1)           # partial block: rows straddle
+    assert not mnb.qdq_is_native(1024, 10, 32, axis=1, has_zero_points=False)
+
+
+def test_gather_argmax_silu_argument_errors():
+    L = mnb.lib()
+    d = mnb.make_desc(64, 8, 32)
+    assert L.mnb_gather_rows(ctypes.byref(d), P16, -1, P16, P16, None, P16, None) == -1
+    assert L.mnb_gather_rows(ctypes.byref(d), P16, 0, None, None, None, None, None) == 0   # nothing to do
+    assert L.mnb_gather_rows(ctypes.byref(d), 0x10004, 2, P16, P16, None, P16, None) == -3
+    assert L.mnb_gather_rows(ctypes.byref(d), P16, 2, P16, P16, P16, P16, None) == -1      # zp without flag
+    assert L.mnb_argmax(2, 1, 8, P16, P16, None) == -2
+    assert L.mnb_argmax(0, 0, 8, P16, P16, None) == -1
+    assert L.mnb_argmax(0, 1, 0, P16, P16, None) == -1
+    assert L.mnb_argmax(0, 1, 8, P16, 0x10004, None) == -3
+    odd = mnb.make_desc(64, 7, 32)
+    assert _gemv(odd, fn="mnb_gemv_silu_mul") == -1
+    assert "even" in L.mnb_last_error().decode()
+    assert _gemv(d, M=2, fn="mnb_gemv_silu_mul") == -1

@@ -26,7 +26,8 @@ from ._lib import BF16, F32, Desc, MatmulArgs, MnbError, check, lib  # noqa: F40
 __all__ = [
     "Desc", "MnbError", "make_desc", "validate", "packed_weight_bytes",
     "scale_bytes", "zero_point_bytes", "gemv_max_k", "pack", "gemv", "gemm",
-    "dequant", "PackedWeight", "Sequence", "version",
+    "dequant", "PackedWeight", "Sequence", "version", "import_qdq", "qdq_is_native",
+    "gather_rows", "argmax", "gemv_silu_mul",
 ]
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
@@ -182,6 +183,92 @@ def dequant(b_packed, scales, zp_packed=None, *, K, N, block_size,
 
 
 # ---- prepared plans and step driver ---------------------------------------------
+
+def import_qdq(w_q: torch.Tensor, scales_q: torch.Tensor, zp_q: Optional[torch.Tensor],
+               *, K: int, N: int, block_size: int = 32, axis: int = 0, stream=None
+               ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Normalize a blocked UINT4 DequantizeLinear weight into MatMulNBits
+    storage.  axis 0: W [K][N], scales/zero points [nb][N]; axis 1: W [N][K]
+    (tied embedding / LM head), scales/zero points [N][nb].  w_q and zp_q are
+    flat uint8 streams (row-major elements, low nibble first); zp_q None means
+    zero point 0.  Returns (b_packed, scales [N][nb], zp_packed)."""
+    nb = _nb(K, block_size)
+    d = make_desc(K, N, block_size, scales_q.dtype, True)
+    _need(w_q, "w_q", torch.uint8, numel=(K * N + 1) // 2)
+    _need(scales_q, "scales_q", scales_q.dtype, numel=nb * N)
+    if zp_q is not None:
+        _need(zp_q, "zp_q", torch.uint8, numel=(nb * N + 1) // 2)
+    dev = w_q.device
+    b = torch.empty(packed_weight_bytes(d), dtype=torch.uint8, device=dev)
+    s = torch.empty((N, nb), dtype=scales_q.dtype, device=dev)
+    z = torch.empty(zero_point_bytes(d), dtype=torch.uint8, device=dev)
+    check(lib().mnb_import_qdq(ctypes.byref(d), int(axis), _ptr(w_q), _ptr(scales_q), _ptr(zp_q),
+                               _ptr(b), _ptr(s), _ptr(z), _stream(stream)), "mnb_import_qdq")
+    return b, s, z
+
+
+def qdq_is_native(K: int, N: int, block_size: int = 32, axis: int = 1,
+                  has_zero_points: bool = True) -> bool:
+    """True when the axis-1 QDQ bytes already are MatMulNBits storage."""
+    d = make_desc(K, N, block_size, torch.float32, has_zero_points)
+    return bool(lib().mnb_qdq_is_native(ctypes.byref(d), int(axis)))
+
+
+def gather_rows(ids: torch.Tensor, b_packed, scales, zp_packed=None, *, K: int, N: int,
+                block_size: int, out=None, stream=None) -> torch.Tensor:
+    """Tied-embedding lookup: rows ids of dequant(B)^T, [len(ids)][K] in the
+    scales' dtype (ids int64; negative ids count from the end)."""
+    d = make_desc(K, N, block_size, scales.dtype, zp_packed is not None)
+    _need(ids, "ids", torch.int64)
+    T = ids.numel()
+    _need(b_packed, "b_packed", torch.uint8, numel=packed_weight_bytes(d))
+    _need(scales, "scales", scales.dtype, numel=N * _nb(K, block_size))
+    if zp_packed is not None:
+        _need(zp_packed, "zp_packed", torch.uint8, numel=zero_point_bytes(d))
+    if out is None:
+        out = torch.empty((T, K), dtype=scales.dtype, device=scales.device)
+    _need(out, "out", scales.dtype, shape=(T, K))
+    check(lib().mnb_gather_rows(ctypes.byref(d), _ptr(ids), T, _ptr(b_packed), _ptr(scales),
+                                _ptr(zp_packed), _ptr(out), _stream(stream)), "mnb_gather_rows")
+    return out
+
+
+def argmax(x: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """Row-wise greedy ArgMax (first maximum; a NaN counts as largest) of a
+    float32 or bfloat16 [M][N] (or [N]) tensor; returns int64 [M]."""
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    M, N = x.shape
+    _need(x, "x", x.dtype, shape=(M, N))
+    if out is None:
+        out = torch.empty(M, dtype=torch.int64, device=x.device)
+    _need(out, "out", torch.int64, numel=M)
+    check(lib().mnb_argmax(_code(x.dtype), M, N, _ptr(x), _ptr(out), _stream(stream)), "mnb_argmax")
+    return out
+
+
+def gemv_silu_mul(a, b_packed, scales, zp_packed=None, bias=None, *, K, N, block_size,
+                  out=None, stream=None) -> torch.Tensor:
+    """Fused gate||up decode projection: B has N = 2I columns (gate, then
+    up); returns h [1][I] = silu(y[:I]) * y[I:] with y = a x dequant(B) + bias."""
+    if a.dim() == 1:
+        a = a.view(1, -1)
+    d = make_desc(K, N, block_size, a.dtype, zp_packed is not None)
+    _need(a, "a", a.dtype, shape=(1, K))
+    _need(b_packed, "b_packed", torch.uint8, numel=packed_weight_bytes(d))
+    _need(scales, "scales", a.dtype, numel=N * _nb(K, block_size))
+    if zp_packed is not None:
+        _need(zp_packed, "zp_packed", torch.uint8, numel=zero_point_bytes(d))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, numel=N)
+    if out is None:
+        out = torch.empty((1, N // 2), dtype=a.dtype, device=a.device)
+    _need(out, "out", a.dtype, numel=N // 2)
+    check(lib().mnb_gemv_silu_mul(ctypes.byref(d), 1, _ptr(a), _ptr(b_packed), _ptr(scales),
+                                  _ptr(zp_packed), _ptr(bias), _ptr(out), _stream(stream)),
+          "mnb_gemv_silu_mul")
+    return out
+
 
 class PackedWeight:
     """A prepared weight-only plan: packed weights, scales, optional packed

@@ -27,7 +27,8 @@ EXPORTS = (
     "mnb_zero_point_bytes", "mnb_gemv_max_k", "mnb_pack", "mnb_gemv",
     "mnb_gemm", "mnb_dequant", "mnb_matmul_sequence", "mnb_graph_create",
     "mnb_graph_launch", "mnb_graph_destroy", "mnb_status_string",
-    "mnb_last_error", "mnb_version",
+    "mnb_last_error", "mnb_version", "mnb_import_qdq", "mnb_qdq_is_native",
+    "mnb_gather_rows", "mnb_argmax", "mnb_gemv_silu_mul",
 )
 
 
@@ -100,6 +101,16 @@ def lib() -> ctypes.CDLL:
         getattr(L, f).restype = ctypes.c_int
     L.mnb_dequant.argtypes = [pd, vp, vp, vp, i32, vp, vp]
     L.mnb_dequant.restype = ctypes.c_int
+    L.mnb_import_qdq.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.mnb_import_qdq.restype = ctypes.c_int
+    L.mnb_qdq_is_native.argtypes = [pd, i32]
+    L.mnb_qdq_is_native.restype = ctypes.c_int
+    L.mnb_gather_rows.argtypes = [pd, vp, i64, vp, vp, vp, vp, vp]
+    L.mnb_gather_rows.restype = ctypes.c_int
+    L.mnb_argmax.argtypes = [i32, i64, i64, vp, vp, vp]
+    L.mnb_argmax.restype = ctypes.c_int
+    L.mnb_gemv_silu_mul.argtypes = [pd, i64, vp, vp, vp, vp, vp, vp, vp]
+    L.mnb_gemv_silu_mul.restype = ctypes.c_int
     pa = ctypes.POINTER(MatmulArgs)
     L.mnb_matmul_sequence.argtypes = [pa, i64, vp]
     L.mnb_matmul_sequence.restype = ctypes.c_int

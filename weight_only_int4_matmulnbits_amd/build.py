@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libmnb.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["mnb_api.hip", "mnb_pack.hip", "mnb_gemv.hip", "mnb_gemm.hip", "mnb_smallm.hip"]
+SOURCES = ["mnb_api.hip", "mnb_pack.hip", "mnb_gemv.hip", "mnb_gemm.hip", "mnb_smallm.hip", "mnb_aux.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

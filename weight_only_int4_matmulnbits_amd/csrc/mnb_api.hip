@@ -249,6 +249,100 @@ int mnb_dequant(const mnb_desc* d, const uint8_t* b_packed, const void* scales,
     return launch_dequant(p, out_kind, w_nk, static_cast<hipStream_t>(stream));
 }
 
+namespace {
+
+// [p, p + n) and [q, q + m) share a byte
+bool overlap(const void* p, size_t n, const void* q, size_t m) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return n && m && a < b + m && b < a + n;
+}
+
+}  // namespace
+
+int mnb_import_qdq(const mnb_desc* d, int32_t axis, const uint8_t* w_q, const void* scales_q,
+                   const uint8_t* zp_q, uint8_t* b_packed, void* scales, uint8_t* zp_packed,
+                   void* stream) {
+    int st = check_desc(d, "mnb_import_qdq");
+    if (st != MNB_OK) return st;
+    if (axis != 0 && axis != 1) return fail(MNB_E_ARG, "mnb_import_qdq: axis=%d, must be 0 or 1", axis);
+    if (!d->has_zero_points)
+        return fail(MNB_E_ARG, "mnb_import_qdq: has_zero_points must be 1 (the normalized weight always "
+                               "carries zero points; a missing QDQ zero point means 0)");
+    if (!w_q || !scales_q || !b_packed || !scales || !zp_packed)
+        return fail(MNB_E_ARG, "mnb_import_qdq: w_q, scales_q, b_packed, scales and zp_packed must be non-NULL");
+    const uintptr_t esz = d->act_dtype == MNB_BF16 ? 2 : 4;
+    if (!aligned(b_packed, 16)) return fail(MNB_E_ALIGN, "mnb_import_qdq: b_packed must be 16-byte aligned");
+    if (!aligned(scales_q, esz) || !aligned(scales, esz))
+        return fail(MNB_E_ALIGN, "mnb_import_qdq: scales_q and scales must be %d-byte aligned", (int)esz);
+    Problem p;
+    fill_problem(d, 1, &p);
+    const size_t wq_bytes = (size_t)((d->K * d->N + 1) / 2), zq_bytes = (size_t)((p.nb * d->N + 1) / 2);
+    const size_t s_bytes = (size_t)(p.nb * d->N) * esz, b_bytes = (size_t)(d->N * p.col_bytes),
+                 z_bytes = (size_t)(d->N * p.zp_row);
+    const void* ins[3] = {w_q, scales_q, zp_q};
+    const size_t in_sz[3] = {wq_bytes, s_bytes, zp_q ? zq_bytes : 0};
+    const void* outs[3] = {b_packed, scales, zp_packed};
+    const size_t out_sz[3] = {b_bytes, s_bytes, z_bytes};
+    for (int i = 0; i < 3; i++)
+        for (int j = 0; j < 3; j++)
+            if (overlap(ins[i], in_sz[i], outs[j], out_sz[j]) || (i < j && overlap(outs[i], out_sz[i], outs[j], out_sz[j])))
+                return fail(MNB_E_ARG, "mnb_import_qdq: inputs and outputs must not overlap");
+    p.has_zp = true;
+    return launch_import_qdq(p, axis, w_q, scales_q, zp_q, b_packed, scales, zp_packed,
+                             static_cast<hipStream_t>(stream));
+}
+
+int mnb_qdq_is_native(const mnb_desc* d, int32_t axis) {
+    if (check_desc(d, "mnb_qdq_is_native") != MNB_OK) return 0;
+    const int64_t nb = (d->K + d->block_size - 1) / d->block_size;
+    return axis == 1 && d->has_zero_points && d->K % d->block_size == 0 && nb % 2 == 0;
+}
+
+int mnb_gather_rows(const mnb_desc* d, const int64_t* ids, int64_t n_ids, const uint8_t* b_packed,
+                    const void* scales, const uint8_t* zp_packed, void* out, void* stream) {
+    int st = check_desc(d, "mnb_gather_rows");
+    if (st != MNB_OK) return st;
+    if (n_ids < 0) return fail(MNB_E_ARG, "mnb_gather_rows: n_ids=%lld < 0", (long long)n_ids);
+    if (n_ids == 0) return MNB_OK;
+    if (!ids || !b_packed || !scales || !out)
+        return fail(MNB_E_ARG, "mnb_gather_rows: ids, b_packed, scales and out must be non-NULL");
+    if ((zp_packed != nullptr) != (d->has_zero_points != 0))
+        return fail(MNB_E_ARG, "mnb_gather_rows: zp_packed must be given iff has_zero_points");
+    const uintptr_t esz = d->act_dtype == MNB_BF16 ? 2 : 4;
+    if (!aligned(ids, 8)) return fail(MNB_E_ALIGN, "mnb_gather_rows: ids must be 8-byte aligned");
+    if (!aligned(scales, esz) || !aligned(out, esz))
+        return fail(MNB_E_ALIGN, "mnb_gather_rows: scales and out must be %d-byte aligned", (int)esz);
+    if (n_ids > (int64_t(1) << 40) / d->K)
+        return fail(MNB_E_OVERFLOW, "mnb_gather_rows: n_ids * K too large");
+    Problem p;
+    fill_problem(d, 1, &p);
+    p.a = nullptr; p.b = b_packed; p.scales = scales; p.zp = zp_packed; p.bias = nullptr; p.y = nullptr;
+    return launch_gather_rows(p, ids, n_ids, out, static_cast<hipStream_t>(stream));
+}
+
+int mnb_argmax(int32_t dtype, int64_t M, int64_t N, const void* x, int64_t* idx, void* stream) {
+    if (dtype != MNB_F32 && dtype != MNB_BF16) return fail(MNB_E_UNSUPPORTED, "mnb_argmax: dtype=%d unknown", dtype);
+    if (M < 1 || N < 1) return fail(MNB_E_ARG, "mnb_argmax: M=%lld N=%lld, both must be >= 1", (long long)M, (long long)N);
+    if (M > kMaxDim) return fail(MNB_E_OVERFLOW, "mnb_argmax: M=%lld exceeds 2^31-1", (long long)M);
+    if (!x || !idx) return fail(MNB_E_ARG, "mnb_argmax: x and idx must be non-NULL");
+    if (!aligned(x, dtype == MNB_BF16 ? 2 : 4) || !aligned(idx, 8))
+        return fail(MNB_E_ALIGN, "mnb_argmax: x or idx misaligned");
+    return launch_argmax(dtype == MNB_BF16, M, N, x, idx, static_cast<hipStream_t>(stream));
+}
+
+int mnb_gemv_silu_mul(const mnb_desc* d, int64_t M, const void* a, const uint8_t* b_packed,
+                      const void* scales, const uint8_t* zp_packed, const float* bias, void* h,
+                      void* stream) {
+    Problem p;
+    int st = check_matmul("mnb_gemv_silu_mul", d, M, a, b_packed, scales, zp_packed, bias, h, true, &p);
+    if (st != MNB_OK) return st;
+    if (d->N % 2 != 0)
+        return fail(MNB_E_ARG, "mnb_gemv_silu_mul: N=%lld must be even (gate half, then up half)", (long long)d->N);
+    if (!takes_gemv(p))
+        return fail(MNB_E_UNSUPPORTED, "mnb_gemv_silu_mul: K=%lld beyond the decode kernel", (long long)d->K);
+    return launch_gemv_silu(p, static_cast<hipStream_t>(stream));
+}
+
 static int check_sequence(const mnb_matmul_args* ops, int64_t n_ops, std::vector<Problem>* out) {
     if (n_ops < 0 || (n_ops > 0 && !ops)) return fail(MNB_E_ARG, "sequence: ops NULL or n_ops < 0");
     out->resize((size_t)n_ops);

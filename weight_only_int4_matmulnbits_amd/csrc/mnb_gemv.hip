@@ -52,6 +52,7 @@ struct GemvArgs {
     int64_t K, N, col_bytes, n_groups;
     int nb, zp_row, S, log2_bs, log2_L;
     int a16;                  // K * element size is a multiple of 16 and A is 16-byte aligned
+    int64_t half;             // gated epilogue: columns per half (gate | up); 0 otherwise
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -125,16 +126,19 @@ struct Group {
 // memory instructions on every path.
 constexpr uint32_t kOob = 0x80000000u;    // offset past any resource: reads zero
 
-template <bool BF16, bool HAS_ZP, int CB, int J, int U>
+// Gated epilogue (SILU): the U == 2 groups of an iteration are column group
+// `base` of the gate half and the same group of the up half.
+template <bool BF16, bool HAS_ZP, int CB, int J, int U, bool SILU>
 __device__ __forceinline__ void load_group(const GemvArgs& g, int64_t base, int p, int LT, int G,
                                            int gsub, Group<BF16, HAS_ZP, CB, J, U>& r) {
     constexpr int CK = 2 * CB;
     constexpr int SSZ = BF16 ? 2 : 4;
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        const int64_t gi = base + u;
-        const int64_t col0 = gi * G;
-        const int64_t ncol = gi < g.n_groups ? (g.N - col0 < G ? g.N - col0 : G) : 0;
+        const int64_t gi = SILU ? base : base + u;
+        const int64_t width = SILU ? g.half : g.N;           // columns of this group's half
+        const int64_t col0 = (SILU && u ? g.half : 0) + gi * G;
+        const int64_t ncol = gi < g.n_groups ? (width - gi * G < G ? width - gi * G : G) : 0;
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(g.b) + (ncol ? col0 * g.col_bytes : 0), (short)0,
             (int)(ncol * g.col_bytes), 0x00020000);
@@ -176,12 +180,19 @@ __device__ __forceinline__ void load_group(const GemvArgs& g, int64_t base, int 
 }
 
 // W wavefronts per column team, U column groups per team per iteration.
-template <bool BF16, bool HAS_ZP, int CB, int J, int U, int W>
+// SILU: the gate||up projection with the gated product fused into the
+// epilogue (page "Qwen3 CPU Inference Critical Path", "Phase Q2": gate
+// projection, SiLU and the gate/up multiplication): each iteration takes a
+// gate column group and the matching up group (U == 2), computed exactly as
+// unfused columns, and writes h = silu(gate) * up for the gate columns only.
+template <bool BF16, bool HAS_ZP, int CB, int J, int U, int W, bool SILU = false>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     constexpr int CK = 2 * CB;        // values of K per chunk
     constexpr int NW = CB / 4;        // 32-bit words per chunk
     constexpr int TEAMS = kWavesPerBlock / W;
+    constexpr int UG = SILU ? 1 : U;  // column groups advanced per iteration
     static_assert(W == 1 || U == 1, "split-K teams take one column at a time");
+    static_assert(!SILU || (U == 2 && W == 1), "the gated epilogue pairs two groups of one team");
     __shared__ float red[kWavesPerBlock];
 
     const int lane = threadIdx.x & 63;
@@ -195,9 +206,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     const int gsub = lane >> g.log2_L;
 
     // iteration space: WG-uniform, so barriers (W > 1) are reached by all
-    const int64_t stride = (int64_t)gridDim.x * TEAMS * U;
-    int64_t base = ((int64_t)blockIdx.x * TEAMS + team) * U;
-    const int64_t team0 = (int64_t)blockIdx.x * TEAMS * U;
+    const int64_t stride = (int64_t)gridDim.x * TEAMS * UG;
+    int64_t base = ((int64_t)blockIdx.x * TEAMS + team) * UG;
+    const int64_t team0 = (int64_t)blockIdx.x * TEAMS * UG;
 
     // ---- activations: staged once per workgroup in LDS as they are (float32
     // or bfloat16), one RB-byte row per chunk; the 16-byte pieces of row c sit
@@ -252,8 +263,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     // the first two iterations' weights (the second only if this team has one)
     Group<BF16, HAS_ZP, CB, J, U> g0, g1;
     const bool two = base + stride < g.n_groups;     // wave-uniform
-    load_group(g, base, p, LT, G, gsub, g0);
-    if (two) load_group(g, base + stride, p, LT, G, gsub, g1);
+    load_group<BF16, HAS_ZP, CB, J, U, SILU>(g, base, p, LT, G, gsub, g0);
+    if (two) load_group<BF16, HAS_ZP, CB, J, U, SILU>(g, base + stride, p, LT, G, gsub, g1);
 
     // wait for this wavefront's staging (all memory instructions but the
     // weight loads just issued, and the LDS writes), then meet the others.
@@ -341,7 +352,23 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
             }
             __syncthreads();
         }
-        if (wt == 0 && (lane & (L - 1)) == 0) {
+        if constexpr (SILU) {
+            if ((lane & (L - 1)) == 0) {
+                const int64_t col = gbase * G + gsub;
+                if (gbase < g.n_groups && col < g.half) {
+                    float gate = acc[0], up = acc[1];
+                    if (g.bias) {
+                        gate += __uint_as_float(cur.bias[0]);
+                        up += __uint_as_float(cur.bias[1]);
+                    }
+                    const float h = gate / (1.0f + expf(-gate)) * up;
+                    if constexpr (BF16)
+                        static_cast<uint16_t*>(g.y)[col] = f32_to_bf16_rtne(h);
+                    else
+                        static_cast<float*>(g.y)[col] = h;
+                }
+            }
+        } else if (wt == 0 && (lane & (L - 1)) == 0) {
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int64_t gi = gbase + u;
@@ -362,10 +389,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     // half past the end loads zeros and skips its work.
     for (int64_t it0 = team0; it0 < g.n_groups; it0 += 2 * stride, base += 2 * stride) {
         finish(g0, base);
-        if (base + 2 * stride < g.n_groups) load_group(g, base + 2 * stride, p, LT, G, gsub, g0);
+        if (base + 2 * stride < g.n_groups)
+            load_group<BF16, HAS_ZP, CB, J, U, SILU>(g, base + 2 * stride, p, LT, G, gsub, g0);
         __builtin_amdgcn_sched_barrier(0);
         if (it0 + stride < g.n_groups) finish(g1, base + stride);
-        if (base + 3 * stride < g.n_groups) load_group(g, base + 3 * stride, p, LT, G, gsub, g1);
+        if (base + 3 * stride < g.n_groups)
+            load_group<BF16, HAS_ZP, CB, J, U, SILU>(g, base + 3 * stride, p, LT, G, gsub, g1);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -429,6 +458,25 @@ GemvFn pick_cb(int J, int U, int W) {
     }
 }
 
+template <bool BF16, bool HAS_ZP, int CB>
+GemvFn pick_silu_cb(int J) {
+    switch (J) {
+        case 1: return gemv_kernel<BF16, HAS_ZP, CB, 1, 2, 1, true>;
+        case 2: return gemv_kernel<BF16, HAS_ZP, CB, 2, 2, 1, true>;
+        case 3: return gemv_kernel<BF16, HAS_ZP, CB, 3, 2, 1, true>;
+        case 4: return gemv_kernel<BF16, HAS_ZP, CB, 4, 2, 1, true>;
+        default: return nullptr;
+    }
+}
+
+GemvFn pick_silu(bool bf16, bool has_zp, int CB, int J) {
+    if (bf16)
+        return has_zp ? (CB == 16 ? pick_silu_cb<true, true, 16>(J) : pick_silu_cb<true, true, 8>(J))
+                      : (CB == 16 ? pick_silu_cb<true, false, 16>(J) : pick_silu_cb<true, false, 8>(J));
+    return has_zp ? (CB == 16 ? pick_silu_cb<false, true, 16>(J) : pick_silu_cb<false, true, 8>(J))
+                  : (CB == 16 ? pick_silu_cb<false, false, 16>(J) : pick_silu_cb<false, false, 8>(J));
+}
+
 GemvFn pick(bool bf16, bool has_zp, int CB, int J, int U, int W) {
     if (bf16)
         return has_zp ? (CB == 16 ? pick_cb<true, true, 16>(J, U, W) : pick_cb<true, true, 8>(J, U, W))
@@ -487,7 +535,11 @@ int64_t gemv_max_k(int bs) {
     return s_max * CK;
 }
 
-int launch_gemv(const Problem& p, hipStream_t s) {
+namespace {
+
+// silu: p.N = 2 * half columns (gate half, then up half), y receives half
+// values of silu(gate) * up.
+int launch(const Problem& p, hipStream_t s, bool silu) {
     const int CB = p.bs >= 32 ? 16 : 8;
     const int CK = 2 * CB;
     GemvArgs a;
@@ -497,12 +549,16 @@ int launch_gemv(const Problem& p, hipStream_t s) {
     a.nb = p.nb; a.zp_row = p.zp_row;
     a.S = (int)((p.K + CK - 1) / CK);
     a.log2_bs = ilog2(p.bs);
+    a.half = silu ? p.N / 2 : 0;
     const Geometry geo = geometry(a.S, CB == 16);
     if (geo.J == 0)
         return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld beyond the register kernel", (long long)p.K);
+    if (silu && geo.W != 1)
+        return fail(MNB_E_UNSUPPORTED, "gated gemv: K=%lld needs split-K wavefront teams", (long long)p.K);
     a.log2_L = geo.log2_L;
     const int G = geo.W == 1 ? (64 >> geo.log2_L) : 1;
-    a.n_groups = (p.N + G - 1) / G;
+    const int64_t cols = silu ? a.half : p.N;       // columns whose groups are walked
+    a.n_groups = (cols + G - 1) / G;
     // staged activations: S chunk rows of CK elements
     const int esz = p.bf16 ? 2 : 4;
     a.a16 = ((p.K * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(p.a) & 15) == 0) &&
@@ -515,10 +571,9 @@ int launch_gemv(const Problem& p, hipStream_t s) {
     // groups per iteration costs more in occupancy than it saves.
     const int64_t cus = compute_units();
     const int teams_per_block = kWavesPerBlock / geo.W;
-    const int U = 1;
-    GemvFn f = pick(p.bf16, p.has_zp, CB, geo.J, 1, geo.W);
+    GemvFn f = silu ? pick_silu(p.bf16, p.has_zp, CB, geo.J) : pick(p.bf16, p.has_zp, CB, geo.J, 1, geo.W);
     if (!f) return fail(MNB_E_UNSUPPORTED, "gemv: no kernel for J=%d W=%d", geo.J, geo.W);
-    const int64_t teams = (a.n_groups + U - 1) / U;
+    const int64_t teams = a.n_groups;
     int64_t blocks = (teams + teams_per_block - 1) / teams_per_block;
     const int64_t max_blocks = cus * resident_per_cu(f, lds);
     if (blocks > max_blocks) blocks = max_blocks;
@@ -527,5 +582,11 @@ int launch_gemv(const Problem& p, hipStream_t s) {
     if (e != hipSuccess) return fail(MNB_E_HIP, "gemv launch: %s", hipGetErrorString(e));
     return MNB_OK;
 }
+
+}  // namespace
+
+int launch_gemv(const Problem& p, hipStream_t s) { return launch(p, s, false); }
+
+int launch_gemv_silu(const Problem& p, hipStream_t s) { return launch(p, s, true); }
 
 }  // namespace mnb

@@ -36,6 +36,14 @@ int launch_pack(int64_t K, int64_t N, int bs, const uint8_t* q,
                 hipStream_t s);
 int launch_dequant(const Problem& p, int out_kind, void* w, hipStream_t s);
 int launch_gemv(const Problem& p, hipStream_t s);
+// p.N = 2 * half: the gate half then the up half; y [half] = silu(gate) * up.
+int launch_gemv_silu(const Problem& p, hipStream_t s);
+// QDQ normalization (axis 0: W[K][N], scales/zp [nb][N]; axis 1: W[N][K],
+// scales/zp [N][nb]) into the MatMulNBits storage of p (p.has_zp is true).
+int launch_import_qdq(const Problem& p, int axis, const uint8_t* w_q, const void* scales_q, const uint8_t* zp_q,
+                      uint8_t* b_packed, void* scales, uint8_t* zp_packed, hipStream_t s);
+int launch_gather_rows(const Problem& p, const int64_t* ids, int64_t n_ids, void* out, hipStream_t s);
+int launch_argmax(bool bf16, int64_t M, int64_t N, const void* x, int64_t* idx, hipStream_t s);
 // ws: float32 workspace for split-K partials (ws_bytes >= gemm_workspace_bytes
 // to split; NULL or smaller: one pass without splitting).
 int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes);
