@@ -9,7 +9,10 @@ graph on one stream; inputs are seeded synthetic tensors already resident in
 HBM.  value = packed-weight bytes per step / step time (GB/s).
 
 Also printed in the same JSON line (``extra``): the Qwen3-4B decode step and
-the two prefill steps (TFLOP/s), and the eager (non-graph) decode step time.
+the two prefill steps (TFLOP/s), the eager (non-graph) decode step time, and
+``next_rows``: the 0.6B step with 4 rows (small-M kernel), the tied LM head
+with greedy ArgMax and the embedding gather, the QDQ import, and the fused
+gate||up SiLU GEMV against the unfused pair.
 
 roofline: the only kernel of the headline step is the decode GEMV; its
 algorithmic bytes per launch (packed weights + scales + zero points, averaged
@@ -105,12 +108,16 @@ def cpu_baseline(cfg, budget_s):
 
 
 def measure_config(cfg, steps, warmup, graph=True):
+    from workloads import workload
+    return measure_config_w(workload(cfg), steps, warmup, graph)
+
+
+def measure_config_w(w, steps, warmup, graph=True):
     import torch
     from weight_only_int4_matmulnbits_amd.step import Step
-    from workloads import workload
 
-    w = workload(cfg)
-    log(f"[bench] config {cfg}: {w.title}: building ({len(w.launches)} launches)")
+    cfg = w.cfg
+    log(f"[bench] config {cfg}: {w.title} (M={w.M}): building ({len(w.launches)} launches)")
     step = Step(w, "cuda", seed=0)
     step.run()
     torch.cuda.synchronize()
@@ -128,6 +135,124 @@ def measure_config(cfg, steps, warmup, graph=True):
     del step
     torch.cuda.empty_cache()
     return w, out
+
+
+def graph_time_us(fn, steps, warmup, reps=20):
+    """Average device time of one fn() call: reps calls captured back to back
+    in one graph (a graph of one short kernel is bound by the host's launch
+    rate), replayed; HIP events on the replay stream."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    # capture on the warm-up stream: the library's per-stream workspace (used
+    # by the argmax partials) exists there, and is not allocated in a capture
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(reps):
+            fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (steps * reps)
+
+
+def measure_next_rows(steps, warmup):
+    """One measurement per row beyond the decode / prefill step: the small-M
+    step (a speculative block of 4 rows), the LM head with greedy ArgMax and
+    the tied-embedding gather, the QDQ import, and the fused gate||up SiLU
+    GEMV against its unfused pair."""
+    import torch
+    import weight_only_int4_matmulnbits_amd as mnb
+    from workloads import workload
+    from workloads.generate import random_inputs
+
+    out = {}
+    # f1: the 0.6B decode step with 4 rows per projection
+    w4 = workload(2, M=4)
+    _, r = measure_config_w(w4, steps, warmup)
+    out["small_m"] = {"workload": "Qwen3-0.6B-shaped INT4 step, 4 rows (speculative block)",
+                      "M": 4, "ms_per_step": r["ms_per_step"], "launches": r["launches"],
+                      "weight_GBps": r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9,
+                      "hbm_frac": r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "rows_per_s": 4 / (r["ms_per_step"] * 1e-3)}
+    # f2: LM head (tied weight, N = vocabulary) + greedy token, and the gather
+    K, N, bs = 1024, 151936, 32
+    g = random_inputs(K, N, 1, bs, "f32", True, False, seed=1).to("cuda")
+    pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, block_size=bs)
+    logits = torch.empty(1, N, device="cuda")
+    tok = torch.empty(1, dtype=torch.int64, device="cuda")
+    ids1 = torch.tensor([151935], device="cuda")
+    ids512 = torch.randint(0, N, (512,), device="cuda", generator=torch.Generator("cuda").manual_seed(2))
+    rows1 = torch.empty(1, K, device="cuda")
+    rows512 = torch.empty(512, K, device="cuda")
+    t_lm = graph_time_us(lambda: pw.matmul(g.a, out=logits), steps, warmup)
+    t_lm_arg = graph_time_us(lambda: (pw.matmul(g.a, out=logits), mnb.argmax(logits, out=tok)),
+                             steps, warmup)
+    t_g1 = graph_time_us(lambda: mnb.gather_rows(ids1, pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N,
+                                                 block_size=bs, out=rows1), steps, warmup)
+    t_g512 = graph_time_us(lambda: mnb.gather_rows(ids512, pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N,
+                                                   block_size=bs, out=rows512), steps, warmup)
+    row_read = K // 2 + (K // bs) * 4 + (K // bs + 1) // 2
+    out["lm_head_argmax"] = {
+        "workload": "Qwen3-0.6B tied LM head 1024->151936 (fp32, block 32, zero points) + greedy ArgMax",
+        "lm_head_us": t_lm, "lm_head_GBps": pw.weight_bytes / (t_lm * 1e-6) / 1e9,
+        "lm_head_plus_argmax_us": t_lm_arg, "argmax_added_us": t_lm_arg - t_lm}
+    out["embedding_gather"] = {
+        "workload": "rows of the same packed tied weight, fp32 out",
+        "rows_1_us": t_g1, "rows_512_us": t_g512,
+        "rows_512_GBps": 512 * (row_read + 4 * K) / (t_g512 * 1e-6) / 1e9}
+    del pw, logits, rows512
+    # f3: QDQ import of the 4B gate||up weight (axis 0 -> N-major)
+    K, N, bs = 2560, 19456, 128
+    gen = torch.Generator("cuda").manual_seed(3)
+    w_q = torch.randint(0, 256, (K * N // 2,), dtype=torch.uint8, device="cuda", generator=gen)
+    z_q = torch.randint(0, 256, ((K // bs) * N // 2,), dtype=torch.uint8, device="cuda", generator=gen)
+    s_q = torch.rand((K // bs) * N, device="cuda", generator=gen).to(torch.bfloat16)
+    mnb.import_qdq(w_q, s_q, z_q, K=K, N=N, block_size=bs, axis=0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        mnb.import_qdq(w_q, s_q, z_q, K=K, N=N, block_size=bs, axis=0)
+    e1.record()
+    torch.cuda.synchronize()
+    t_imp = e0.elapsed_time(e1) * 1e3 / 5
+    moved = 2 * (w_q.numel() + z_q.numel() + 2 * s_q.numel())
+    out["qdq_import"] = {"workload": "Qwen3-4B gate||up 2560x19456 QDQ (axis 0, block 128) -> MatMulNBits",
+                         "us": t_imp, "GBps_read_plus_written": moved / (t_imp * 1e-6) / 1e9,
+                         "tied_lm_head_copy_avoided": mnb.qdq_is_native(1024, 151936, 32, axis=1)}
+    del w_q, z_q, s_q
+    # f4: gate||up with silu(gate) * up fused, against the unfused pair
+    fused = {}
+    for name, K, I, bs, dt in (("0.6B", 1024, 3072, 32, "f32"), ("4B", 2560, 9728, 128, "bf16")):
+        g = random_inputs(K, 2 * I, 1, bs, dt, name == "0.6B", False, seed=4).to("cuda")
+        pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, block_size=bs)
+        y = torch.empty(1, 2 * I, dtype=g.a.dtype, device="cuda")
+        h = torch.empty(1, I, dtype=g.a.dtype, device="cuda")
+
+        def unfused():
+            pw.matmul(g.a, out=y)
+            torch.mul(torch.nn.functional.silu(y[:, :I]), y[:, I:], out=h)
+
+        t_u = graph_time_us(unfused, steps, warmup)
+        t_f = graph_time_us(lambda: mnb.gemv_silu_mul(g.a, pw.b_packed, pw.scales, pw.zp_packed, K=K,
+                                                      N=2 * I, block_size=bs, out=h), steps, warmup)
+        fused[name] = {"K": K, "I": I, "unfused_us": t_u, "fused_us": t_f,
+                       "fused_GBps": pw.weight_bytes / (t_f * 1e-6) / 1e9}
+        del pw, y, h, g
+    out["gate_up_silu"] = fused
+    torch.cuda.empty_cache()
+    return out
 
 
 def measured_traffic(cfg, kind):
@@ -260,6 +385,8 @@ def main():
             st = max(3, args.steps // (10 if c == 5 else 2))
             wc, rc = measure_config(c, st, max(2, args.warmup // 2))
             extra[f"config{c}"] = summary(wc, rc)
+        log("[bench] next rows: small M, LM head + argmax, gather, QDQ import, gated gate||up")
+        extra["next_rows"] = measure_next_rows(max(5, args.steps // 5), max(2, args.warmup // 2))
         line["extra"] = extra
     print(json.dumps(line), flush=True)
 

@@ -28,7 +28,8 @@
  *           exception: they record the pointers given at creation).  Its own
  *           device memory is a float32 workspace for split-K GEMMs (products
  *           whose output tiles cannot fill the GPU): one per (device, stream)
- *           for direct calls, grown on demand outside stream capture and
+ *           for direct calls (also holding mnb_argmax's per-segment
+ *           partials), grown on demand outside stream capture and
  *           kept until the process ends, and one per graph handle, freed by
  *           mnb_graph_destroy.  A product that cannot get the workspace it
  *           asks for (inside a capture the caller started, or when hipMalloc
@@ -235,7 +236,10 @@ int mnb_gather_rows(const mnb_desc* d, const int64_t* ids, int64_t n_ids,
  * RMSNorm, LM-head GEMV and greedy ArgMax): idx[m] = the first n holding the
  * largest x[m][n]; a NaN counts as larger than every number, so the first NaN
  * wins.  x: [M][N] float32 or bfloat16 (dtype, an mnb_dtype); idx: int64 [M].
- * One workgroup per row. */
+ * Rows longer than 2048 values are split over up to 256 workgroups whose
+ * partial maxima go to the stream's workspace (see Memory) and are then
+ * reduced per row; without that workspace one workgroup takes a row.  Both
+ * give the same answer (a total order on (value, index)). */
 int mnb_argmax(int32_t dtype, int64_t M, int64_t N, const void* x,
                int64_t* idx, void* stream);
 

@@ -327,7 +327,10 @@ int mnb_argmax(int32_t dtype, int64_t M, int64_t N, const void* x, int64_t* idx,
     if (!x || !idx) return fail(MNB_E_ARG, "mnb_argmax: x and idx must be non-NULL");
     if (!aligned(x, dtype == MNB_BF16 ? 2 : 4) || !aligned(idx, 8))
         return fail(MNB_E_ALIGN, "mnb_argmax: x or idx misaligned");
-    return launch_argmax(dtype == MNB_BF16, M, N, x, idx, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    size_t ws_bytes = 0;
+    void* ws = stream_workspace(s, argmax_workspace_bytes(M, N), &ws_bytes);
+    return launch_argmax(dtype == MNB_BF16, M, N, x, idx, s, ws, ws_bytes);
 }
 
 int mnb_gemv_silu_mul(const mnb_desc* d, int64_t M, const void* a, const uint8_t* b_packed,

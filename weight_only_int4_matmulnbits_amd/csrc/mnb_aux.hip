@@ -147,34 +147,135 @@ __device__ __forceinline__ bool better(float v, int64_t i, float bv, int64_t bi)
     return i < bi;
 }
 
+// Best (value, index) of row m over [n0, n1) by one workgroup: each thread
+// reads 16-byte pieces (4 float32 or 8 bfloat16 values), eight pieces in
+// flight per round, when the row starts 16-byte aligned and has a whole number
+// of pieces (then n0 and n1 are multiples of the piece); otherwise one value
+// at a time.  Every thread of the block returns the block's best.
 template <bool BF16>
-__global__ __launch_bounds__(1024) void argmax_kernel(const void* __restrict__ x, int64_t N,
-                                                      int64_t* __restrict__ idx) {
+__device__ void best_of_range(const void* __restrict__ x, int64_t N, int64_t m, int64_t n0, int64_t n1,
+                              int vec, float& out_v, int64_t& out_i) {
     __shared__ float sv[1024];
     __shared__ int64_t si[1024];
-    const int64_t m = blockIdx.x;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, T = blockDim.x;
     float bv = -INFINITY;
     int64_t bi = kNoIndex;
-    for (int64_t n = t; n < N; n += blockDim.x) {
-        const float v = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(x)[m * N + n])
-                             : static_cast<const float*>(x)[m * N + n];
-        if (better(v, n, bv, bi)) {
-            bv = v;
-            bi = n;
+    if (vec) {
+        constexpr int PER = BF16 ? 8 : 4;        // values per 16-byte piece
+        constexpr int R = 8;                     // pieces in flight per thread
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4* row = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(x) + m * N * (BF16 ? 2 : 4));
+        const int64_t p1 = n1 / PER;
+        for (int64_t p0 = n0 / PER + t; p0 < p1; p0 += (int64_t)R * T) {
+            u32x4 v[R];
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                const int64_t pc = p0 + (int64_t)r * T;
+                v[r] = pc < p1 ? row[pc] : u32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                const int64_t pc = p0 + (int64_t)r * T;
+                if (pc >= p1) break;
+#pragma unroll
+                for (int e = 0; e < PER; e++) {
+                    const uint32_t w = v[r][BF16 ? e / 2 : e];
+                    const float f = BF16 ? __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16)) : __uint_as_float(w);
+                    if (better(f, pc * PER + e, bv, bi)) {
+                        bv = f;
+                        bi = pc * PER + e;
+                    }
+                }
+            }
+        }
+    } else {
+        for (int64_t n = n0 + t; n < n1; n += T) {
+            const float v = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(x)[m * N + n])
+                                 : static_cast<const float*>(x)[m * N + n];
+            if (better(v, n, bv, bi)) {
+                bv = v;
+                bi = n;
+            }
         }
     }
     sv[t] = bv;
     si[t] = bi;
     __syncthreads();
-    for (int s = blockDim.x / 2; s > 0; s >>= 1) {
+    for (int s = T / 2; s > 0; s >>= 1) {
         if (t < s && better(sv[t + s], si[t + s], sv[t], si[t])) {
             sv[t] = sv[t + s];
             si[t] = si[t + s];
         }
         __syncthreads();
     }
+    out_v = sv[0];
+    out_i = si[0];
+}
+
+// One workgroup per row (short rows, or no workspace).
+template <bool BF16>
+__global__ __launch_bounds__(1024) void argmax_kernel(const void* __restrict__ x, int64_t N, int vec,
+                                                      int64_t* __restrict__ idx) {
+    float v;
+    int64_t i;
+    best_of_range<BF16>(x, N, blockIdx.x, 0, N, vec, v, i);
+    if (threadIdx.x == 0) idx[blockIdx.x] = i;
+}
+
+// Long rows: S workgroups per row write the best of their segment (segment
+// boundaries are multiples of 8 values), then one workgroup per row picks
+// the best of the S partials by the same total order.
+struct Partial {
+    float v;
+    int32_t pad;
+    int64_t i;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void argmax_partial_kernel(const void* __restrict__ x, int64_t N, int vec,
+                                                             int64_t seg, Partial* __restrict__ part) {
+    const int64_t m = blockIdx.y, s = blockIdx.x;
+    const int64_t n0 = s * seg, n1 = n0 + seg < N ? n0 + seg : N;
+    float v;
+    int64_t i;
+    best_of_range<BF16>(x, N, m, n0, n1, vec, v, i);
+    if (threadIdx.x == 0) part[m * gridDim.x + s] = Partial{v, 0, i};
+}
+
+__global__ __launch_bounds__(256) void argmax_final_kernel(const Partial* __restrict__ part, int S,
+                                                           int64_t* __restrict__ idx) {
+    __shared__ float sv[256];
+    __shared__ int64_t si[256];
+    const int64_t m = blockIdx.x;
+    const int t = threadIdx.x;
+    float bv = -INFINITY;
+    int64_t bi = kNoIndex;
+    for (int s = t; s < S; s += blockDim.x) {
+        const Partial p = part[m * S + s];
+        if (better(p.v, p.i, bv, bi)) {
+            bv = p.v;
+            bi = p.i;
+        }
+    }
+    sv[t] = bv;
+    si[t] = bi;
+    __syncthreads();
+    for (int h = blockDim.x / 2; h > 0; h >>= 1) {
+        if (t < h && better(sv[t + h], si[t + h], sv[t], si[t])) {
+            sv[t] = sv[t + h];
+            si[t] = si[t + h];
+        }
+        __syncthreads();
+    }
     if (t == 0) idx[m] = si[0];
+}
+
+constexpr int64_t kArgmaxSeg = 2048;     // values per partial workgroup
+constexpr int64_t kArgmaxMaxSeg = 256;   // partials per row
+
+int64_t argmax_segments(int64_t N) {
+    int64_t S = (N + kArgmaxSeg - 1) / kArgmaxSeg;
+    return S > kArgmaxMaxSeg ? kArgmaxMaxSeg : S;
 }
 
 inline unsigned blocks_for(int64_t items, int threads) { return (unsigned)((items + threads - 1) / threads); }
@@ -217,11 +318,37 @@ int launch_gather_rows(const Problem& p, const int64_t* ids, int64_t n_ids, void
     return launched("row gather");
 }
 
-int launch_argmax(bool bf16, int64_t M, int64_t N, const void* x, int64_t* idx, hipStream_t s) {
+size_t argmax_workspace_bytes(int64_t M, int64_t N) {
+    const int64_t S = argmax_segments(N);
+    return S > 1 ? (size_t)(M * S) * sizeof(Partial) : 0;
+}
+
+int launch_argmax(bool bf16, int64_t M, int64_t N, const void* x, int64_t* idx, hipStream_t s, void* ws,
+                  size_t ws_bytes) {
+    const int per = bf16 ? 8 : 4;
+    const int vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0 && N % per == 0;
+    const int64_t S = argmax_segments(N);
+    const size_t need = argmax_workspace_bytes(M, N);
+    if (S > 1 && ws && ws_bytes >= need && M <= 65535) {
+        // segment length: a multiple of 8 values (whole 16-byte pieces)
+        const int64_t seg = ((N + S - 1) / S + 7) / 8 * 8;
+        const int64_t Sused = (N + seg - 1) / seg;
+        Partial* part = static_cast<Partial*>(ws);
+        if (bf16)
+            hipLaunchKernelGGL(argmax_partial_kernel<true>, dim3((unsigned)Sused, (unsigned)M), dim3(256), 0, s, x,
+                               N, vec, seg, part);
+        else
+            hipLaunchKernelGGL(argmax_partial_kernel<false>, dim3((unsigned)Sused, (unsigned)M), dim3(256), 0, s, x,
+                               N, vec, seg, part);
+        int st = launched("argmax partials");
+        if (st != MNB_OK) return st;
+        hipLaunchKernelGGL(argmax_final_kernel, dim3((unsigned)M), dim3(256), 0, s, part, (int)Sused, idx);
+        return launched("argmax");
+    }
     if (bf16)
-        hipLaunchKernelGGL(argmax_kernel<true>, dim3((unsigned)M), dim3(1024), 0, s, x, N, idx);
+        hipLaunchKernelGGL(argmax_kernel<true>, dim3((unsigned)M), dim3(1024), 0, s, x, N, vec, idx);
     else
-        hipLaunchKernelGGL(argmax_kernel<false>, dim3((unsigned)M), dim3(1024), 0, s, x, N, idx);
+        hipLaunchKernelGGL(argmax_kernel<false>, dim3((unsigned)M), dim3(1024), 0, s, x, N, vec, idx);
     return launched("argmax");
 }
 

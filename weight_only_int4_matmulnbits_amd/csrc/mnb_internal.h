@@ -43,7 +43,11 @@ int launch_gemv_silu(const Problem& p, hipStream_t s);
 int launch_import_qdq(const Problem& p, int axis, const uint8_t* w_q, const void* scales_q, const uint8_t* zp_q,
                       uint8_t* b_packed, void* scales, uint8_t* zp_packed, hipStream_t s);
 int launch_gather_rows(const Problem& p, const int64_t* ids, int64_t n_ids, void* out, hipStream_t s);
-int launch_argmax(bool bf16, int64_t M, int64_t N, const void* x, int64_t* idx, hipStream_t s);
+// ws: the stream's workspace for per-segment partials of long rows
+// (argmax_workspace_bytes); NULL or too small: one workgroup per row.
+int launch_argmax(bool bf16, int64_t M, int64_t N, const void* x, int64_t* idx, hipStream_t s, void* ws,
+                  size_t ws_bytes);
+size_t argmax_workspace_bytes(int64_t M, int64_t N);
 // ws: float32 workspace for split-K partials (ws_bytes >= gemm_workspace_bytes
 // to split; NULL or smaller: one pass without splitting).
 int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes);
