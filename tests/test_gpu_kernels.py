@@ -338,6 +338,27 @@ def test_bf16_gemm_large_grid_sampled(orc, M, K, N, bs, zp, bias):
     assert_close(out_f64(ys), y_ref, S, "bf16", f"M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("zp,bias", [(True, True), (False, False)])
+def test_bf16_gemm_tail_split_matches_oracle(orc, zp, bias):
+    """Whole rounds of 256x256 tiles run unsplit; when the last round would
+    leave more than half of the CUs idle, its tiles are split along K and
+    their partials reduced separately.  M = 512, N = 38400: 300 tiles, the
+    last 44 (columns 32768..38399 on a 256-CU device) in the split tail.
+    Sampled columns on both sides of the boundary, all rows; run twice,
+    bit-identical."""
+    M, K, N, bs = 512, 1024, 38400, 128
+    inp, g = _inputs(K, N, M, bs, "bf16", zp, bias, seed=31)
+    pw = _packed(g, bs)
+    y = mnb.gemm(g.a, pw.b_packed, pw.scales, pw.zp_packed, pw.bias, K=K, N=N, block_size=bs)
+    y2 = mnb.gemm(g.a, pw.b_packed, pw.scales, pw.zp_packed, pw.bias, K=K, N=N, block_size=bs)
+    assert torch.equal(y, y2)
+    rng = np.random.default_rng(5)
+    cols = np.unique(np.concatenate([rng.integers(0, 32768, 48), rng.integers(32768, N, 80),
+                                     [0, 32767, 32768, N - 1]]))
+    y_ref, S = oracle_ref(orc, inp, cols=cols)
+    assert_close(out_f64(y[:, torch.as_tensor(cols, device=DEV)]), y_ref, S, "bf16", "tail split")
+
+
 SPLIT_CASES = [
     ("bf16", 512, 4096, 384, 128, True, True),    # 4 tiles of 256x256: 16 K splits
     ("bf16", 300, 1536, 520, 32, False, False),   # ragged M and N: 6 splits

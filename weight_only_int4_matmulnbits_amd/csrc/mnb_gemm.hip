@@ -306,6 +306,11 @@ struct Bf16Args {
     // tile to part[split][M][N] instead of Y (the reduction adds the bias)
     int splits, sps;
     float* part;
+    // tail split (wide kernel): workgroups past full_tiles take the last
+    // tail_tiles tiles, each split into tail_splits parts of tail_sps K steps,
+    // and store float32 partial tiles to tail_part[split][tail tile][256][256]
+    int full_tiles, tail_tiles, tail_splits, tail_sps;
+    float* tail_part;
 };
 
 template <int BM, int BN, int WAVES>
@@ -544,11 +549,24 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     const int mt = (g.M + B4_M - 1) / B4_M;
     const int nt = (g.N + B4_N - 1) / B4_N;
     const int tiles = mt * nt;
-    const int v = xcd_index(blockIdx.x, tiles * g.splits);
-    const int split = v / tiles, tt = v - split * tiles;
+    // whole tiles (remapped so that each XCD takes a contiguous range), then
+    // the tail tiles split along K, dispatched last
+    int split, tt, sps, tail_idx = -1;
+    if (g.tail_tiles && (int)blockIdx.x >= g.full_tiles) {
+        const int w = blockIdx.x - g.full_tiles;
+        tail_idx = w % g.tail_tiles;
+        split = w / g.tail_tiles;
+        tt = g.full_tiles + tail_idx;
+        sps = g.tail_sps;
+    } else {
+        const int v = xcd_index(blockIdx.x, g.tail_tiles ? g.full_tiles : tiles * g.splits);
+        split = v / tiles;
+        tt = v - split * tiles;
+        sps = g.sps;
+    }
     const int m0 = (tt % mt) * B4_M;
     const int n0 = (tt / mt) * B4_N;
-    const int kbase = split * g.sps * B4_K;                // this split's first K value
+    const int kbase = split * sps * B4_K;                   // this split's first K value
 
     const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(g.a), (short)0, (int)g.a_bytes, 0x00020000);
@@ -677,7 +695,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     // One K step st: request step st + 2 (into the `load` stages), multiply
     // step st from LDS buffer st % 2 while moving step st + 1 (the `use`
     // stages, requested one step earlier) into the other buffer, barrier.
-    const int steps = min(g.sps, g.K / B4_K - split * g.sps);
+    const int steps = min(sps, g.K / B4_K - split * sps);
     int buf = 0;
     auto one_step = [&](int st, const StageA& ua, const StageB& ub, StageA& la, StageB& lb) {
         fetch_a((st + 2) * B4_K, la);
@@ -724,7 +742,23 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
         one_step(st + 1, ay, by, ax, bx);
     }
 
-    // epilogue: + bias, RTNE to bf16, store (or the float32 partial)
+    // epilogue: + bias, RTNE to bf16, store (or the float32 partial: of the
+    // whole product for split-K, of the tile for the tail split)
+    if (tail_idx >= 0) {
+        float* const tp = g.tail_part + ((int64_t)split * g.tail_tiles + tail_idx) * (B4_M * B4_N);
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int c = wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int rr = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    tp[rr * B4_N + c] = acc[i][j][r];
+                }
+        }
+        return;
+    }
     float* const part = g.part ? g.part + (int64_t)split * g.M * g.N : nullptr;
 #pragma unroll
     for (int j = 0; j < TN; j++) {
@@ -1039,6 +1073,35 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
+// The tail split's partial tiles: element (r, c) of tail tile t is the sum of
+// its splits in split order, + bias, rounded to bf16; four columns per thread.
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restrict__ tp, int splits, int tail_tiles,
+                                                          int full_tiles, int mt, int M, int N,
+                                                          const float* __restrict__ bias, uint16_t* __restrict__ y) {
+    constexpr int TILE = B4_M * B4_N;
+    const int64_t total = (int64_t)tail_tiles * TILE / 4;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e0 = q * 4;
+        const int t = (int)(e0 / TILE);
+        const int rc = (int)(e0 - (int64_t)t * TILE);
+        const int r = rc / B4_N, c = rc % B4_N;
+        const int tt = full_tiles + t;
+        const int m = (tt % mt) * B4_M + r, n0 = (tt / mt) * B4_N + c;
+        if (m >= M) continue;
+        float4 x = *reinterpret_cast<const float4*>(tp + e0);
+        for (int sp = 1; sp < splits; sp++) {
+            const float4 z = *reinterpret_cast<const float4*>(tp + ((int64_t)sp * tail_tiles) * TILE + e0);
+            x.x += z.x; x.y += z.y; x.z += z.z; x.w += z.w;
+        }
+        const float v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int n = n0 + e;
+            if (n < N) y[(int64_t)m * N + n] = f32_to_bf16_rtne(bias ? v[e] + bias[n] : v[e]);
+        }
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -1048,8 +1111,27 @@ struct Plan {
     enum Kind { LEGACY_BF16, WIDE, REG256, REG128, F32_INT, LEGACY_F32 } kind;
     int64_t tiles = 1;
     int splits = 1, sps = 1;
+    int tail_tiles = 0, tail_splits = 1, tail_sps = 0;   // wide kernel: split of the last round
     size_t ws = 0;                 // workspace bytes for the split partials
 };
+
+// Wide kernel over more than one round of tiles: when the last round would
+// leave more than half of the CUs idle, split its tiles along K (at least
+// four K steps per part) so that it finishes sooner.
+void choose_tail_split(Plan& pl, int64_t cus, int steps) {
+    if (pl.splits > 1 || pl.tiles <= cus) return;
+    const int64_t rem = pl.tiles % cus;
+    if (rem == 0 || rem > cus / 2) return;
+    int ts = (int)(cus / rem);
+    if (ts > 4) ts = 4;
+    if (ts > steps / 4) ts = steps / 4;
+    if (ts < 2) return;
+    pl.tail_sps = (steps + ts - 1) / ts;
+    pl.tail_splits = (steps + pl.tail_sps - 1) / pl.tail_sps;
+    if (pl.tail_splits < 2) return;
+    pl.tail_tiles = (int)rem;
+    pl.ws = (size_t)pl.tail_splits * (size_t)rem * B4_M * B4_N * 4;
+}
 
 constexpr size_t kMaxWorkspace = size_t(1) << 30;
 
@@ -1085,6 +1167,7 @@ Plan plan_gemm(const Problem& p) {
             pl.kind = Plan::WIDE;
             pl.tiles = big;
             choose_split(pl, p, cus, (int)(p.K / B4_K));   // one 256 x 256 workgroup per CU
+            choose_tail_split(pl, cus, (int)(p.K / B4_K));
         } else if (big >= 384) {
             pl.kind = Plan::REG256;
             pl.tiles = big;
@@ -1112,9 +1195,10 @@ size_t gemm_workspace_bytes(const Problem& p) { return smallm_ok(p) ? 0 : plan_g
 int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
     if (smallm_ok(p)) return launch_smallm(p, s);
     Plan pl = plan_gemm(p);
-    if (pl.splits > 1 && (!ws || ws_bytes < pl.ws)) {
+    if (pl.ws && (!ws || ws_bytes < pl.ws)) {
         pl.splits = 1;                                      // no room for partials: one pass
         pl.sps = (int)(p.K / (pl.kind == Plan::WIDE ? B4_K : F_K));
+        pl.tail_tiles = 0;
     }
     GemmArgs a;
     a.a = p.a; a.b = p.b; a.scales = p.scales; a.zp = p.has_zp ? p.zp : nullptr;
@@ -1137,8 +1221,14 @@ int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
     b.splits = pl.splits;
     b.sps = pl.sps;
     b.part = pl.splits > 1 ? static_cast<float*>(ws) : nullptr;
+    b.full_tiles = (int)(pl.tiles - pl.tail_tiles);
+    b.tail_tiles = pl.tail_tiles;
+    b.tail_splits = pl.tail_splits;
+    b.tail_sps = pl.tail_sps;
+    b.tail_part = pl.tail_tiles ? static_cast<float*>(ws) : nullptr;
     const bool bs16 = p.bs == 16;
-    const unsigned grid = (unsigned)(pl.tiles * pl.splits);
+    const unsigned grid = (unsigned)(pl.tail_tiles ? b.full_tiles + (int64_t)pl.tail_tiles * pl.tail_splits
+                                                   : pl.tiles * pl.splits);
     switch (pl.kind) {
         case Plan::WIDE: {
             auto kern = p.has_zp ? (bs16 ? gemm_bf16_wide_kernel<true, true> : gemm_bf16_wide_kernel<true, false>)
@@ -1184,6 +1274,17 @@ int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
                                static_cast<const float*>(ws), pl.splits, mn, (int)p.N, p.bias, p.y);
         e = hipGetLastError();
         if (e != hipSuccess) return fail(MNB_E_HIP, "gemm split-K reduction launch: %s", hipGetErrorString(e));
+    }
+    if (pl.tail_tiles) {
+        const int64_t q = (int64_t)pl.tail_tiles * B4_M * B4_N / 4;
+        int64_t blocks = (q + 255) / 256;
+        const int64_t cap = (int64_t)device_compute_units() * 8;
+        if (blocks > cap) blocks = cap;
+        hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                           static_cast<const float*>(ws), pl.tail_splits, pl.tail_tiles, b.full_tiles,
+                           (int)((p.M + B4_M - 1) / B4_M), (int)p.M, (int)p.N, p.bias, static_cast<uint16_t*>(p.y));
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(MNB_E_HIP, "gemm tail reduction launch: %s", hipGetErrorString(e));
     }
     return MNB_OK;
 }
