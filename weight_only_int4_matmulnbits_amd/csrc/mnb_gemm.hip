@@ -511,27 +511,41 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(Bf16Args g) {
 
 // ---------------------------------------------------------------------------
 // bf16 activations, large grids: 256 x 256 x 64 tiles on 8 wavefronts of
-// 128 x 64 (8 MFMA 32x32x16 tiles each), two wavefronts per SIMD so that one
-// multiplies while the other waits on LDS or unpacks weights.
+// 128 x 64 (8 MFMA 32x32x16 tiles each), in two groups that take turns on
+// the matrix cores (a ping-pong schedule).
 //
 //  * Both operand panels of a K step live in LDS as bf16, double-buffered
 //    (4 x 32 KiB): the activations as loaded, the weights unpacked to
 //    bf16((q - zp) * s).  Rows are 128 bytes (64 K values); the eight
 //    16-byte chunks of row r sit at chunk ^ ((r >> 1) & 7), so the operand
 //    reads of 16 consecutive rows (one 256-byte bank sweep) are conflict-free.
-//  * Global reads run two K steps ahead into registers (plain buffer loads,
-//    so the compiler tracks every one of them and waits precisely); while
-//    step s is multiplied, step s + 1 is moved from registers into the other
-//    LDS buffers, a quarter per 16-value sub-step.
-//  * One barrier per K step; the loop body is two steps with the register
-//    stages swapped (a stage copy would wait for loads just issued) and no
-//    exit in the middle.
+//  * Group g (wavefronts 4g .. 4g + 3, one per SIMD) computes rows 128 g ..
+//    128 g + 127 of the tile and moves half of every K step: activation rows
+//    and weight columns 128 g .. 128 g + 127.  Every step j is "multiply j
+//    from LDS; barrier; write this group's half of step j + 1 + g into the
+//    other buffer and request step j + 2 + g; barrier", with group 1 one
+//    barrier behind group 0.  So on every SIMD one wavefront multiplies
+//    while the other unpacks weights, writes LDS and issues global loads;
+//    both halves of a step are in LDS before group 0 reads it, and no
+//    buffer is written while it is read.
+//  * The barriers wait only for LDS: global loads stay in flight across
+//    them (the compiler tracks every buffer load and waits precisely where
+//    the registers are used, one step later).
+//  * The bf16 tile leaves through LDS (free after the last barrier): each
+//    wavefront writes its 128 x 64 tile as 128-byte rows and stores 16-byte
+//    pieces of whole rows.
 // Requires K % 64 == 0 and K % block_size == 0 (no partial K step or block).
 // ---------------------------------------------------------------------------
 constexpr int B4_M = 256, B4_N = 256, B4_K = 64;
 
 // byte offset of 16-byte chunk c of 128-byte row r
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+// Barrier for LDS traffic only: this wavefront's LDS reads and writes are
+// complete, global loads may still be in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
 
 template <bool HAS_ZP, bool BS16>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
@@ -546,6 +560,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     const int lane = t & 63;
     const int wave = t >> 6;
     const int wm = wave >> 2, wn = wave & 3;
+    const int grp = __builtin_amdgcn_readfirstlane(wm);  // wave-uniform group
+    const int tg = t & 255;                             // thread within the group
     const int mt = (g.M + B4_M - 1) / B4_M;
     const int nt = (g.N + B4_N - 1) / B4_N;
     const int tiles = mt * nt;
@@ -577,40 +593,29 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     const __amdgpu_buffer_rsrc_t rz_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(HAS_ZP ? g.zp : g.b), (short)0, (int)(HAS_ZP ? g.z_bytes : 0), 0x00020000);
 
-    // activations: thread t moves chunk t % 8 of rows t / 8 + 64 i (rows past
-    // M read as zeros)
-    const int a_r = t >> 3, a_c = t & 7;
-    const uint32_t a_off = (uint32_t)(m0 + a_r) * (uint32_t)g.K * 2u + 16u * a_c;
-    const uint32_t a_rows64 = 64u * (uint32_t)g.K * 2u;
-    struct StageA {
-        u32x4 v[AR];
-    };
-    auto fetch_a = [&](int k0, StageA& st) {
-#pragma unroll
-        for (int i = 0; i < AR; i++)
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_off + a_rows64 * i + 2u * (kbase + k0), 0, 0);
-    };
-    auto stash_a = [&](const StageA& st, int buf, int i) {
-        *reinterpret_cast<u32x4*>(As + buf * PANEL + swz(a_r + 64 * i, a_c)) = st.v[i];
-    };
-
-    // weights: thread t moves 16 bytes (32 values) of column t / 2, K half
-    // t % 2 of the step, with its scale(s) and zero point(s); the loaded
-    // values are only read when the step is unpacked, one step later.  With
-    // 16-value blocks the chunk spans an even block and the next one: their
+    // this group's half of a step: activation rows 128 grp + tg / 8 + 32 i,
+    // chunk tg % 8 (rows past M read as zeros); weight column 128 grp + tg / 2,
+    // K half tg % 2, with its scale(s) and zero point(s).  With 16-value
+    // blocks the 32-value chunk spans an even block and the next one: their
     // two scales are one aligned 32-bit word (K % 64 == 0 makes the blocks
     // per column even) and their zero points the two nibbles of one byte.
-    // zsh: bit offset of the zero-point nibble in its byte (larger blocks).
-    const int b_col = t >> 1, b_half = t & 1;
+    const int a_r = 128 * grp + (tg >> 3), a_c = tg & 7;
+    const uint32_t a_off = (uint32_t)(m0 + a_r) * (uint32_t)g.K * 2u + 16u * a_c;
+    const uint32_t a_rows32 = 32u * (uint32_t)g.K * 2u;
+    const int b_col = 128 * grp + (tg >> 1), b_half = tg & 1;
     // (z stays a byte: widening it where it is loaded would make the
     // compiler wait for the load there, ahead of the next step's requests)
-    struct StageB {
+    struct Stage {
+        u32x4 a[AR];
         u32x4 b;
         uint32_t s;
         uint8_t z;
-        uint32_t zsh;
+        uint32_t zsh;   // bit offset of the zero-point nibble (larger blocks)
     };
-    auto fetch_b = [&](int k0, StageB& st) {
+    auto fetch = [&](int k0, Stage& st) {
+#pragma unroll
+        for (int i = 0; i < AR; i++)
+            st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_off + a_rows32 * i + 2u * (kbase + k0), 0, 0);
         const int col = n0 + b_col;
         const int kb = kbase + k0 + 32 * b_half;
         st.b = __builtin_amdgcn_raw_buffer_load_b128(
@@ -626,30 +631,37 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
             if constexpr (!BS16) st.zsh = 4u * (blk & 1u);
         }
     };
-    // unpack 8 values (word d of the chunk): (q - zp) * s is exact in
-    // float32, one RTNE rounding to bf16
-    auto stash_b = [&](const StageB& st, int buf, int d) {
-        const int h = BS16 ? (d >> 1) : 0;
-        uint32_t zq = 8u;
-        if constexpr (HAS_ZP) zq = __builtin_amdgcn_ubfe((uint32_t)st.z, BS16 ? 4u * h : st.zsh, 4);
-        const float sc = __uint_as_float(BS16 && h ? (st.s & 0xFFFF0000u) : (st.s << 16));
-        const float zs = (float)zq * sc;
-        const uint32_t lo = opaque_and(st.b[d], 0x0F0F0F0Fu);
-        const uint32_t hi = opaque_and(st.b[d] >> 4, 0x0F0F0F0Fu);
-        float v[8];
-        v[0] = fmaf(ubyte_to_f32<0>(lo), sc, -zs); v[1] = fmaf(ubyte_to_f32<0>(hi), sc, -zs);
-        v[2] = fmaf(ubyte_to_f32<1>(lo), sc, -zs); v[3] = fmaf(ubyte_to_f32<1>(hi), sc, -zs);
-        v[4] = fmaf(ubyte_to_f32<2>(lo), sc, -zs); v[5] = fmaf(ubyte_to_f32<2>(hi), sc, -zs);
-        v[6] = fmaf(ubyte_to_f32<3>(lo), sc, -zs); v[7] = fmaf(ubyte_to_f32<3>(hi), sc, -zs);
-        uint32_t o[4];
+    // the activations as loaded; the weights unpacked 8 values (one word of
+    // the chunk) at a time: (q - zp) * s is exact in float32, one RTNE
+    // rounding to bf16
+    auto stash = [&](const Stage& st, int buf) {
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            bf16x2 pr;
-            pr[0] = (__bf16)v[2 * e];
-            pr[1] = (__bf16)v[2 * e + 1];
-            o[e] = __builtin_bit_cast(uint32_t, pr);
+        for (int i = 0; i < AR; i++)
+            *reinterpret_cast<u32x4*>(As + buf * PANEL + swz(a_r + 32 * i, a_c)) = st.a[i];
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+            const int h = BS16 ? (d >> 1) : 0;
+            uint32_t zq = 8u;
+            if constexpr (HAS_ZP) zq = __builtin_amdgcn_ubfe((uint32_t)st.z, BS16 ? 4u * h : st.zsh, 4);
+            const float sc = __uint_as_float(BS16 && h ? (st.s & 0xFFFF0000u) : (st.s << 16));
+            const float zs = (float)zq * sc;
+            const uint32_t lo = opaque_and(st.b[d], 0x0F0F0F0Fu);
+            const uint32_t hi = opaque_and(st.b[d] >> 4, 0x0F0F0F0Fu);
+            float v[8];
+            v[0] = fmaf(ubyte_to_f32<0>(lo), sc, -zs); v[1] = fmaf(ubyte_to_f32<0>(hi), sc, -zs);
+            v[2] = fmaf(ubyte_to_f32<1>(lo), sc, -zs); v[3] = fmaf(ubyte_to_f32<1>(hi), sc, -zs);
+            v[4] = fmaf(ubyte_to_f32<2>(lo), sc, -zs); v[5] = fmaf(ubyte_to_f32<2>(hi), sc, -zs);
+            v[6] = fmaf(ubyte_to_f32<3>(lo), sc, -zs); v[7] = fmaf(ubyte_to_f32<3>(hi), sc, -zs);
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                bf16x2 pr;
+                pr[0] = (__bf16)v[2 * e];
+                pr[1] = (__bf16)v[2 * e + 1];
+                o[e] = __builtin_bit_cast(uint32_t, pr);
+            }
+            *reinterpret_cast<u32x4*>(Bs + buf * PANEL + swz(b_col, 4 * b_half + d)) = u32x4{o[0], o[1], o[2], o[3]};
         }
-        *reinterpret_cast<u32x4*>(Bs + buf * PANEL + swz(b_col, 4 * b_half + d)) = u32x4{o[0], o[1], o[2], o[3]};
     };
 
     f32x16 acc[TM][TN];
@@ -660,11 +672,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    // Multiply the step in LDS buffer buf (4 sub-steps of 8 MFMAs, the
-    // operands of the next sub-step read ahead) while a quarter of the next
-    // step's activations and weights goes from registers into buffer buf ^ 1
-    // per sub-step.
-    auto step_body = [&](int buf, const StageA& na, const StageB& nb) {
+    // Multiply the step in LDS buffer buf: 4 sub-steps of 8 MFMAs, the
+    // operands of the next sub-step read ahead, at raised issue priority.
+    auto compute = [&](int buf) {
         const uint8_t* a = As + buf * PANEL;
         const uint8_t* b = Bs + buf * PANEL;
         bf16x8 af[2][TM], bfr[2][TN];
@@ -677,6 +687,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
             for (int j = 0; j < TN; j++)
                 bfr[p][j] = *reinterpret_cast<const bf16x8*>(b + swz(wn * 64 + j * 32 + (lane & 31), chunk));
         };
+        __builtin_amdgcn_s_setprio(1);
         load_frags(0, 0);
 #pragma unroll
         for (int ks = 0; ks < B4_K / 16; ks++) {
@@ -687,82 +698,122 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
 #pragma unroll
                 for (int j = 0; j < TN; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][i], bfr[p][j], acc[i][j], 0, 0, 0);
-            stash_a(na, buf ^ 1, ks);
-            stash_b(nb, buf ^ 1, ks);
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
-    // One K step st: request step st + 2 (into the `load` stages), multiply
-    // step st from LDS buffer st % 2 while moving step st + 1 (the `use`
-    // stages, requested one step earlier) into the other buffer, barrier.
     const int steps = min(sps, g.K / B4_K - split * sps);
-    int buf = 0;
-    auto one_step = [&](int st, const StageA& ua, const StageB& ub, StageA& la, StageB& lb) {
-        fetch_a((st + 2) * B4_K, la);
-        fetch_b((st + 2) * B4_K, lb);
-        __builtin_amdgcn_sched_barrier(0);    // issue the requests first
-        step_body(buf, ua, ub);
-        // the scheduler must not hoist the next step's unpacking (pure
-        // arithmetic) above the barrier, next to the loads that feed it
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        buf ^= 1;
-    };
-    auto stage_all = [&](const StageA& sa, const StageB& sb, int b) {
-#pragma unroll
-        for (int i = 0; i < AR; i++) stash_a(sa, b, i);
-#pragma unroll
-        for (int d = 0; d < 4; d++) stash_b(sb, b, d);
-    };
-    StageA ax, ay;
-    StageB bx, by;
-    int st = 0;
-    if (steps & 1) {
-        // odd step count: peel step 0 so that the loop runs pairs
-        fetch_a(0, ax);
-        fetch_b(0, bx);
-        fetch_a(B4_K, ay);
-        fetch_b(B4_K, by);
-        stage_all(ax, bx, 0);
-        __syncthreads();
-        one_step(0, ay, by, ax, bx);
-        st = 1;
-    } else {
-        fetch_a(0, ay);
-        fetch_b(0, by);
-        fetch_a(B4_K, ax);
-        fetch_b(B4_K, bx);
-        stage_all(ay, by, 0);
-        __syncthreads();
+    // One code path for both groups (divergent paths would double the live
+    // registers), group 1 one barrier behind.  Past the last step the loads
+    // read zeros or unused bytes inside the operands, and the buffer written
+    // is never read again, so neither needs a guard.
+    Stage su, sl;
+    {
+        Stage s0;
+        fetch(0, s0);
+        if (grp) fetch(B4_K, sl);
+        stash(s0, 0);
+        if (grp) stash(sl, 1);
+        fetch((1 + grp) * B4_K, su);
     }
-    // here ax / bx hold step st + 1
-    for (; st < steps; st += 2) {
-        one_step(st, ax, bx, ay, by);
-        one_step(st + 1, ay, by, ax, bx);
+    lds_barrier();
+    if (grp) lds_barrier();
+    auto step = [&](int j, const Stage& use, Stage& ld) {
+        __builtin_amdgcn_sched_barrier(0);
+        compute(j & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        fetch((j + 2 + grp) * B4_K, ld);
+        stash(use, (j + 1 + grp) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int j = 0;
+    for (; j + 1 < steps; j += 2) {
+        step(j, su, sl);
+        step(j + 1, sl, su);
     }
+    if (j < steps) step(j, su, sl);
+    if (!grp) lds_barrier();
+    // every wavefront is past its last LDS access of the operands here
 
-    // epilogue: + bias, RTNE to bf16, store (or the float32 partial: of the
-    // whole product for split-K, of the tile for the tail split)
+    // epilogue: the float32 partial (of the whole product for split-K, of the
+    // tile for the tail split), or + bias and RTNE to bf16
     if (tail_idx >= 0) {
         float* const tp = g.tail_part + ((int64_t)split * g.tail_tiles + tail_idx) * (B4_M * B4_N);
 #pragma unroll
-        for (int j = 0; j < TN; j++) {
-            const int c = wn * 64 + j * 32 + (lane & 31);
+        for (int jj = 0; jj < TN; jj++) {
+            const int c = wn * 64 + jj * 32 + (lane & 31);
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int rr = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    tp[rr * B4_N + c] = acc[i][j][r];
+                    tp[rr * B4_N + c] = acc[i][jj][r];
                 }
         }
         return;
     }
     float* const part = g.part ? g.part + (int64_t)split * g.M * g.N : nullptr;
+    if (!part && (g.N & 1) == 0) {
+        // In the MFMA result a lane holds 16 rows of one column.  Rows R and
+        // R + 1 of a column are packed into one dword and lanes c and c ^ 1
+        // swap halves, so that each lane holds two adjacent columns of one
+        // row.  With N % 8 == 0 these dwords go through this wavefront's own
+        // 16 KiB of LDS (rows of 128 bytes) and leave as 16-byte pieces of
+        // whole rows; otherwise they are stored directly.  Rows past M fall
+        // outside the output buffer and are dropped by its range check (the
+        // whole offset is in the VGPR operand, which the check covers).
+        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+            g.y, (short)0, (int)((uint32_t)g.M * (uint32_t)g.N * 2u), 0x00020000);
+        const bool staged = (g.N & 7) == 0;
+        uint8_t* const wt = lds + wave * 16384;
+        const int odd = lane & 1;
+        const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+        const uint32_t rowb = 2u * (uint32_t)g.N;
 #pragma unroll
-    for (int j = 0; j < TN; j++) {
-        const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+        for (int jj = 0; jj < TN; jj++) {
+            const int c = jj * 32 + (lane & 31);                // column in the wavefront's 64
+            const int n = n0 + wn * 64 + c;
+            const float bv = g.bias && n < g.N ? g.bias[n] : 0.f;
+            const uint32_t vb = (uint32_t)(m0 + wm * 128 + 4 * (lane >> 5) + odd) * rowb + 2u * (uint32_t)(n & ~1);
+            const bool col_ok = (n | 1) < g.N;                  // both columns of the pair
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    bf16x2 pr;
+                    pr[0] = (__bf16)(acc[i][jj][r] + bv);
+                    pr[1] = (__bf16)(acc[i][jj][r + 1] + bv);
+                    const uint32_t own = __builtin_bit_cast(uint32_t, pr);
+                    const uint32_t oth = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
+                    const uint32_t out = __builtin_amdgcn_perm(oth, own, sel);
+                    const int row = i * 32 + 8 * (r >> 2) + (r & 3);   // + 4 (lane >> 5) + odd
+                    if (staged)
+                        *reinterpret_cast<uint32_t*>(wt + (row + 4 * (lane >> 5) + odd) * 128 + 2 * (c & ~1)) = out;
+                    else if (col_ok)
+                        __builtin_amdgcn_raw_buffer_store_b32(out, ry, vb + (uint32_t)row * rowb, 0, 0);
+                }
+        }
+        if (staged) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): this wavefront's LDS writes
+            const int pc = lane & 7;                            // 16-byte piece of a row
+            const int ncol = n0 + wn * 64 + 8 * pc;
+            const uint32_t vb = (uint32_t)(m0 + wm * 128 + (lane >> 3)) * rowb + 2u * (uint32_t)ncol;
+#pragma unroll
+            for (int q = 0; q < 16; q++) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(wt + (8 * q + (lane >> 3)) * 128 + 16 * pc);
+                if (ncol < g.N)
+                    __builtin_amdgcn_raw_buffer_store_b128(v, ry, vb + (uint32_t)(8 * q) * rowb, 0, 0);
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int jj = 0; jj < TN; jj++) {
+        const int n = n0 + wn * 64 + jj * 32 + (lane & 31);
         if (n >= g.N) continue;
         const float bv = (!part && g.bias) ? g.bias[n] : 0.f;
 #pragma unroll
@@ -772,9 +823,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
                 const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (m >= g.M) continue;
                 if (part)
-                    part[(int64_t)m * g.N + n] = acc[i][j][r];
+                    part[(int64_t)m * g.N + n] = acc[i][jj][r];
                 else
-                    static_cast<uint16_t*>(g.y)[(int64_t)m * g.N + n] = f32_to_bf16_rtne(acc[i][j][r] + bv);
+                    static_cast<uint16_t*>(g.y)[(int64_t)m * g.N + n] = f32_to_bf16_rtne(acc[i][jj][r] + bv);
             }
     }
 }
