@@ -93,19 +93,24 @@ __device__ __forceinline__ float add_dpp(float v) {
     return v + __builtin_bit_cast(float, t);
 }
 
-// Sum over aligned groups of 2^log2_L lanes; every lane of a group ends with
-// the same bits.  The tree is fixed: pairs, quads, eights, sixteens,
-// thirty-twos, then the two halves of the wavefront.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float add_dpp_rows(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false);
+    return v + __builtin_bit_cast(float, t);
+}
+
+// Sum over aligned groups of 2^log2_L lanes, valid in the LAST lane of each
+// group.  The tree is fixed and all DPP: pairs, quads, eights, sixteens
+// (after which every lane of a 16-lane row holds the row sum), then the
+// row sums are added by row broadcasts (rows 1 and 3 take the last lane of
+// rows 0 and 2; row 3 then takes the last lane of row 1).
 __device__ __forceinline__ float reduce_lanes(float v, int log2_L) {
-    if (log2_L >= 1) v = add_dpp<0xB1>(v);     // quad_perm [1,0,3,2]
-    if (log2_L >= 2) v = add_dpp<0x4E>(v);     // quad_perm [2,3,0,1]
-    if (log2_L >= 3) v = add_dpp<0x141>(v);    // row_half_mirror
-    if (log2_L >= 4) v = add_dpp<0x140>(v);    // row_mirror
-    if (log2_L >= 5)                           // lanes i, i^16 of each half
-        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
-    if (log2_L >= 6)
-        v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
-            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    if (log2_L >= 1) v = add_dpp<0xB1>(v);            // quad_perm [1,0,3,2]
+    if (log2_L >= 2) v = add_dpp<0x4E>(v);            // quad_perm [2,3,0,1]
+    if (log2_L >= 3) v = add_dpp<0x141>(v);           // row_half_mirror
+    if (log2_L >= 4) v = add_dpp<0x140>(v);           // row_mirror
+    if (log2_L >= 5) v = add_dpp_rows<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+    if (log2_L >= 6) v = add_dpp_rows<0x143, 0x8>(v);  // row_bcast:31 into row 3
     return v;
 }
 
@@ -128,7 +133,7 @@ constexpr uint32_t kOob = 0x80000000u;    // offset past any resource: reads zer
 
 // Gated epilogue (SILU): the U == 2 groups of an iteration are column group
 // `base` of the gate half and the same group of the up half.
-template <bool BF16, bool HAS_ZP, int CB, int J, int U, bool SILU>
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, int U, bool SILU>
 __device__ __forceinline__ void load_group(const GemvArgs& g, int64_t base, int p, int LT, int G,
                                            int gsub, Group<BF16, HAS_ZP, CB, J, U>& r) {
     constexpr int CK = 2 * CB;
@@ -150,7 +155,7 @@ __device__ __forceinline__ void load_group(const GemvArgs& g, int64_t base, int 
         const __amdgpu_buffer_rsrc_t rbias = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float*>(g.bias ? g.bias : reinterpret_cast<const float*>(g.b)) + (ncol && g.bias ? col0 : 0),
             (short)0, g.bias ? (int)(ncol * 4) : 0, 0x00020000);
-        r.bias[u] = __builtin_amdgcn_raw_buffer_load_b32(rbias, (uint32_t)(4 * gsub), 0, 0);
+        r.bias[u] = HAS_BIAS ? __builtin_amdgcn_raw_buffer_load_b32(rbias, (uint32_t)(4 * gsub), 0, 0) : 0u;
         __amdgpu_buffer_rsrc_t rz;
         if constexpr (HAS_ZP)
             rz = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.zp) + (ncol ? col0 * g.zp_row : 0),
@@ -185,7 +190,7 @@ __device__ __forceinline__ void load_group(const GemvArgs& g, int64_t base, int 
 // projection, SiLU and the gate/up multiplication): each iteration takes a
 // gate column group and the matching up group (U == 2), computed exactly as
 // unfused columns, and writes h = silu(gate) * up for the gate columns only.
-template <bool BF16, bool HAS_ZP, int CB, int J, int U, int W, bool SILU = false>
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, int U, int W, bool SILU = false>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     constexpr int CK = 2 * CB;        // values of K per chunk
     constexpr int NW = CB / 4;        // 32-bit words per chunk
@@ -263,14 +268,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     // the first two iterations' weights (the second only if this team has one)
     Group<BF16, HAS_ZP, CB, J, U> g0, g1;
     const bool two = base + stride < g.n_groups;     // wave-uniform
-    load_group<BF16, HAS_ZP, CB, J, U, SILU>(g, base, p, LT, G, gsub, g0);
-    if (two) load_group<BF16, HAS_ZP, CB, J, U, SILU>(g, base + stride, p, LT, G, gsub, g1);
+    load_group<BF16, HAS_ZP, HAS_BIAS, CB, J, U, SILU>(g, base, p, LT, G, gsub, g0);
+    if (two) load_group<BF16, HAS_ZP, HAS_BIAS, CB, J, U, SILU>(g, base + stride, p, LT, G, gsub, g1);
 
     // wait for this wavefront's staging (all memory instructions but the
     // weight loads just issued, and the LDS writes), then meet the others.
     // A plain barrier: a fenced one would also wait for the weights.
     {
-        constexpr int NL = U * (J * (HAS_ZP ? 3 : 2) + 1);     // loads per group
+        constexpr int NL = U * (J * (HAS_ZP ? 3 : 2) + (HAS_BIAS ? 1 : 0));     // loads per group
         static_assert(2 * NL < 64, "vmcnt range");
         constexpr int W1 = (NL & 15) | (7 << 4) | (0 << 8) | ((NL >> 4) << 14);
         constexpr int W2 = ((2 * NL) & 15) | (7 << 4) | (0 << 8) | (((2 * NL) >> 4) << 14);
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
             acc[u] = reduce_lanes(s, g.log2_L);
         }
         if constexpr (W > 1) {
-            if (lane == 0) red[wave] = acc[0];
+            if (lane == 63) red[wave] = acc[0];
             __syncthreads();
             if (wt == 0) {
                 float v = red[team * W];
@@ -353,11 +358,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
             __syncthreads();
         }
         if constexpr (SILU) {
-            if ((lane & (L - 1)) == 0) {
+            if ((lane & (L - 1)) == L - 1) {
                 const int64_t col = gbase * G + gsub;
                 if (gbase < g.n_groups && col < g.half) {
                     float gate = acc[0], up = acc[1];
-                    if (g.bias) {
+                    if (HAS_BIAS) {
                         gate += __uint_as_float(cur.bias[0]);
                         up += __uint_as_float(cur.bias[1]);
                     }
@@ -368,14 +373,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
                         static_cast<float*>(g.y)[col] = h;
                 }
             }
-        } else if (wt == 0 && (lane & (L - 1)) == 0) {
+        } else if (wt == 0 && (lane & (L - 1)) == L - 1) {
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int64_t gi = gbase + u;
                 const int64_t col = gi * G + gsub;
                 if (gi < g.n_groups && col < g.N) {
                     float v = acc[u];
-                    if (g.bias) v += __uint_as_float(cur.bias[u]);
+                    if (HAS_BIAS) v += __uint_as_float(cur.bias[u]);
                     if constexpr (BF16)
                         static_cast<uint16_t*>(g.y)[col] = f32_to_bf16_rtne(v);
                     else
@@ -390,11 +395,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     for (int64_t it0 = team0; it0 < g.n_groups; it0 += 2 * stride, base += 2 * stride) {
         finish(g0, base);
         if (base + 2 * stride < g.n_groups)
-            load_group<BF16, HAS_ZP, CB, J, U, SILU>(g, base + 2 * stride, p, LT, G, gsub, g0);
+            load_group<BF16, HAS_ZP, HAS_BIAS, CB, J, U, SILU>(g, base + 2 * stride, p, LT, G, gsub, g0);
         __builtin_amdgcn_sched_barrier(0);
         if (it0 + stride < g.n_groups) finish(g1, base + stride);
         if (base + 3 * stride < g.n_groups)
-            load_group<BF16, HAS_ZP, CB, J, U, SILU>(g, base + 3 * stride, p, LT, G, gsub, g1);
+            load_group<BF16, HAS_ZP, HAS_BIAS, CB, J, U, SILU>(g, base + 3 * stride, p, LT, G, gsub, g1);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -436,53 +441,41 @@ Geometry geometry(int64_t S, bool allow_split) {
 
 using GemvFn = void (*)(GemvArgs);
 
-template <bool BF16, bool HAS_ZP, int CB, int J>
-GemvFn pick_j(int U, int W) {
-    if (U != 1) return nullptr;
-    if (W == 1) return gemv_kernel<BF16, HAS_ZP, CB, J, 1, 1>;
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J>
+GemvFn pick_j(int W, bool silu) {
+    if (silu) return W == 1 ? gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 2, 1, true> : nullptr;
+    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, 1>;
     if constexpr (CB == 16) {
-        if (W == 2) return gemv_kernel<BF16, HAS_ZP, CB, J, 1, 2>;
-        if (W == 4) return gemv_kernel<BF16, HAS_ZP, CB, J, 1, 4>;
+        if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, 2>;
+        if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, 4>;
     }
     return nullptr;
 }
 
-template <bool BF16, bool HAS_ZP, int CB>
-GemvFn pick_cb(int J, int U, int W) {
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB>
+GemvFn pick_cb(int J, int W, bool silu) {
     switch (J) {
-        case 1: return pick_j<BF16, HAS_ZP, CB, 1>(U, W);
-        case 2: return pick_j<BF16, HAS_ZP, CB, 2>(U, W);
-        case 3: return pick_j<BF16, HAS_ZP, CB, 3>(U, W);
-        case 4: return pick_j<BF16, HAS_ZP, CB, 4>(U, W);
+        case 1: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 1>(W, silu);
+        case 2: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 2>(W, silu);
+        case 3: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 3>(W, silu);
+        case 4: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 4>(W, silu);
         default: return nullptr;
     }
 }
 
-template <bool BF16, bool HAS_ZP, int CB>
-GemvFn pick_silu_cb(int J) {
-    switch (J) {
-        case 1: return gemv_kernel<BF16, HAS_ZP, CB, 1, 2, 1, true>;
-        case 2: return gemv_kernel<BF16, HAS_ZP, CB, 2, 2, 1, true>;
-        case 3: return gemv_kernel<BF16, HAS_ZP, CB, 3, 2, 1, true>;
-        case 4: return gemv_kernel<BF16, HAS_ZP, CB, 4, 2, 1, true>;
-        default: return nullptr;
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS>
+GemvFn pick_b(int CB, int J, int W, bool silu) {
+    return CB == 16 ? pick_cb<BF16, HAS_ZP, HAS_BIAS, 16>(J, W, silu) : pick_cb<BF16, HAS_ZP, HAS_BIAS, 8>(J, W, silu);
+}
+
+// silu: the gated gate||up kernel (two column groups per iteration)
+GemvFn pick(bool bf16, bool has_zp, bool has_bias, int CB, int J, int W, bool silu) {
+    if (bf16) {
+        if (has_zp) return has_bias ? pick_b<true, true, true>(CB, J, W, silu) : pick_b<true, true, false>(CB, J, W, silu);
+        return has_bias ? pick_b<true, false, true>(CB, J, W, silu) : pick_b<true, false, false>(CB, J, W, silu);
     }
-}
-
-GemvFn pick_silu(bool bf16, bool has_zp, int CB, int J) {
-    if (bf16)
-        return has_zp ? (CB == 16 ? pick_silu_cb<true, true, 16>(J) : pick_silu_cb<true, true, 8>(J))
-                      : (CB == 16 ? pick_silu_cb<true, false, 16>(J) : pick_silu_cb<true, false, 8>(J));
-    return has_zp ? (CB == 16 ? pick_silu_cb<false, true, 16>(J) : pick_silu_cb<false, true, 8>(J))
-                  : (CB == 16 ? pick_silu_cb<false, false, 16>(J) : pick_silu_cb<false, false, 8>(J));
-}
-
-GemvFn pick(bool bf16, bool has_zp, int CB, int J, int U, int W) {
-    if (bf16)
-        return has_zp ? (CB == 16 ? pick_cb<true, true, 16>(J, U, W) : pick_cb<true, true, 8>(J, U, W))
-                      : (CB == 16 ? pick_cb<true, false, 16>(J, U, W) : pick_cb<true, false, 8>(J, U, W));
-    return has_zp ? (CB == 16 ? pick_cb<false, true, 16>(J, U, W) : pick_cb<false, true, 8>(J, U, W))
-                  : (CB == 16 ? pick_cb<false, false, 16>(J, U, W) : pick_cb<false, false, 8>(J, U, W));
+    if (has_zp) return has_bias ? pick_b<false, true, true>(CB, J, W, silu) : pick_b<false, true, false>(CB, J, W, silu);
+    return has_bias ? pick_b<false, false, true>(CB, J, W, silu) : pick_b<false, false, false>(CB, J, W, silu);
 }
 
 int compute_units() { return device_compute_units(); }
@@ -568,14 +561,19 @@ int launch(const Problem& p, hipStream_t s, bool silu) {
         return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld needs %zu bytes of LDS", (long long)p.K, lds);
     // Fill the chip with resident teams of W wavefronts (the kernel's real
     // occupancy), one column group per team per iteration: unrolling several
-    // groups per iteration costs more in occupancy than it saves.
+    // groups per iteration costs more in occupancy than it saves.  When two
+    // workgroups per CU already leave each team at most 2.5 groups, use only
+    // those: a team with two groups has the second in flight while it reduces
+    // the first, which measured 2-7 % faster than one group per team on the
+    // few-MB decode projections (and slower on the large ones).
     const int64_t cus = compute_units();
     const int teams_per_block = kWavesPerBlock / geo.W;
-    GemvFn f = silu ? pick_silu(p.bf16, p.has_zp, CB, geo.J) : pick(p.bf16, p.has_zp, CB, geo.J, 1, geo.W);
+    GemvFn f = pick(p.bf16, p.has_zp, p.bias != nullptr, CB, geo.J, geo.W, silu);
     if (!f) return fail(MNB_E_UNSUPPORTED, "gemv: no kernel for J=%d W=%d", geo.J, geo.W);
     const int64_t teams = a.n_groups;
     int64_t blocks = (teams + teams_per_block - 1) / teams_per_block;
-    const int64_t max_blocks = cus * resident_per_cu(f, lds);
+    int64_t max_blocks = cus * resident_per_cu(f, lds);
+    if (max_blocks > 2 * cus && 2 * teams <= 5 * (2 * cus * teams_per_block)) max_blocks = 2 * cus;
     if (blocks > max_blocks) blocks = max_blocks;
     hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(64 * kWavesPerBlock), lds, s, a);
     const hipError_t e = hipGetLastError();
