@@ -63,8 +63,9 @@ def time_steps(step, steps, warmup, graph):
 
 
 def cpu_baseline(cfg, budget_s):
-    """The oracle (as it is) on the host cores: launches of the step in order
-    until the time budget is used; returns a dict in the metric's unit."""
+    """The oracle (as it is) on the host cores: the step's launches in order,
+    repeated, until the time budget is used (input generation is not timed);
+    returns a dict in the metric's unit."""
     import oracle
     from workloads import workload
     from workloads.generate import projection_inputs
@@ -76,33 +77,46 @@ def cpu_baseline(cfg, budget_s):
     cores = len(os.sched_getaffinity(0))
     done_bytes = done_flops = 0
     spent = 0.0
-    names = []
+    calls = 0
+    first, last = None, None
     rows = w.M if w.M == 1 else 2
-    for i, L in enumerate(w.launches):
-        inp = projection_inputs(w, i, 0, "cpu")
-        a = inp.a[:rows]
-        act = (a.numpy() if w.act_dtype == "f32"
-               else a.view(torch.int16).numpy().view(np.uint16))
-        sc = (inp.scales.numpy() if w.act_dtype == "f32"
-              else inp.scales.view(torch.int16).numpy().view(np.uint16))
-        t0 = time.perf_counter()
-        orc.matmul(act, inp.q.numpy(), None if inp.zp is None else inp.zp.numpy(), sc,
-                   w.block_size, bias=None if inp.bias is None else inp.bias.numpy(),
-                   nthreads=cores)
-        spent += time.perf_counter() - t0
-        done_bytes += w.weight_bytes(L)
-        done_flops += 2 * rows * L.K * L.N
-        names.append(L.name)
-        if spent >= budget_s:
-            break
+    cache, cached = {}, 0
+    passes = 0
+    while spent < budget_s:
+        for i, L in enumerate(w.launches):
+            if i in cache:
+                args = cache[i]
+            else:
+                inp = projection_inputs(w, i, 0, "cpu")
+                a = inp.a[:rows]
+                act = (a.numpy() if w.act_dtype == "f32"
+                       else a.view(torch.int16).numpy().view(np.uint16))
+                sc = (inp.scales.numpy() if w.act_dtype == "f32"
+                      else inp.scales.view(torch.int16).numpy().view(np.uint16))
+                args = (act, inp.q.numpy(), None if inp.zp is None else inp.zp.numpy(), sc,
+                        None if inp.bias is None else inp.bias.numpy())
+                if cached + args[1].nbytes < (2 << 30):     # keep inputs for the next pass
+                    cache[i] = args
+                    cached += args[1].nbytes
+            t0 = time.perf_counter()
+            orc.matmul(args[0], args[1], args[2], args[3], w.block_size, bias=args[4], nthreads=cores)
+            spent += time.perf_counter() - t0
+            done_bytes += w.weight_bytes(L)
+            done_flops += 2 * rows * L.K * L.N
+            calls += 1
+            first = first or L.name
+            last = L.name
+            if spent >= budget_s:
+                break
+        passes += 1
+    n = len(w.launches)
+    what = f"{calls} launches ({calls / n:.2f} passes over the step's {n}, {first}..{last})"
     if w.M == 1:
         val, unit = done_bytes / spent / 1e9, "GB/s"
-        sample = (f"{len(names)} of {len(w.launches)} launches of the step "
-                  f"({names[0]}..{names[-1]}), full columns, M=1")
+        sample = f"{what}, full columns, M=1"
     else:
         val, unit = done_flops / spent / 1e12, "TFLOP/s"
-        sample = (f"{len(names)} launches ({names[0]}..{names[-1]}), "
-                  f"{rows} of {w.M} rows")
+        sample = f"{what}, {rows} of {w.M} rows"
     return {"value": val, "unit": unit, "cores": cores, "kind": "oracle",
             "sample": sample, "seconds": round(spent, 2)}
 
@@ -314,6 +328,153 @@ def summary(w, r):
     return s
 
 
+# ---- rocprofv3 summaries (run on the CSV output of the commands in
+# profiles/; nothing here touches the GPU) ----
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _library_rows(rows):
+    # dispatches of this library's matmul kernels (packing excluded)
+    return [r for r in rows if "mnb::" in r["Kernel_Name"] and "pack_" not in r["Kernel_Name"]]
+
+
+def _short(name):
+    name = name.replace("mnb::(anonymous namespace)::", "").replace("(GemvArgs)", "").replace("(Bf16Args)", "")
+    return name.replace("void ", "")
+
+
+def summarize_trace(trace_dir, cfg, steps, warmup):
+    """Per-kernel statistics and the timed graph-replayed steps of one
+    `bench.py --config cfg --steps steps --warmup warmup` run under
+    `rocprofv3 --kernel-trace --stats`."""
+    from workloads import workload
+    import statistics
+    w = workload(cfg)
+    n = len(w.launches)
+    rows = _library_rows(_read_csv(os.path.join(trace_dir, "run_kernel_trace.csv")))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    stats = _read_csv(os.path.join(trace_dir, "run_kernel_stats.csv"))
+    out = ["kernel statistics (run_kernel_stats.csv, library matmul kernels):"]
+    for r in stats:
+        if "mnb::" in r["Name"] and "pack_" not in r["Name"]:
+            out.append(f"  {_short(r['Name']):<62} calls {int(r['Calls']):6d}  avg {float(r['AverageNs']) / 1e3:9.3f} us"
+                       f"  min {float(r['MinNs']) / 1e3:8.3f}  max {float(r['MaxNs']) / 1e3:8.3f}")
+    # the run: one eager step, `warmup` + `steps` graph replays (+ the same
+    # again eagerly for a decode step); kernels per step = dispatches / steps
+    total_steps = 1 + warmup + steps + ((warmup + steps) if w.M == 1 else 0)
+    per_step = len(rows) // total_steps
+    out.append(f"library dispatches in trace: {len(rows)} ({total_steps} steps x {per_step})")
+    def span_stats(rng):
+        sums, spans, durs = [], [], []
+        for k in rng:
+            st = rows[k * per_step:(k + 1) * per_step]
+            d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in st]
+            sums.append(sum(d))
+            durs.extend(d)
+            spans.append(int(st[-1]["End_Timestamp"]) - int(st[0]["Start_Timestamp"]))
+        return statistics.median(sums), statistics.median(spans), statistics.mean(durs) / 1e3
+    timed = range(1 + warmup, 1 + warmup + steps)
+    s_sum, s_span, avg = span_stats(timed)
+    out.append(f"timed graph-replayed steps: median sum of kernel durations {s_sum / 1e3:.1f} us, "
+               f"first-start to last-end {s_span / 1e3:.1f} us")
+    if w.M == 1:
+        # Back to back in a replayed graph, the tracer stamps about half of
+        # the kernels as starting exactly when the previous one ends and puts
+        # ~3.7 us gaps before the others, so those durations are not a
+        # kernel's own.  In the eager steps every kernel runs alone (host
+        # launch gaps of several us), which gives its duration undisturbed.
+        e_timed = range(1 + 2 * warmup + steps, 1 + 2 * warmup + 2 * steps)
+        e_sum, e_span, e_avg = span_stats(e_timed)
+        out.append(f"timed eager steps: median sum of kernel durations {e_sum / 1e3:.1f} us "
+                   f"(first-start to last-end {e_span / 1e3:.1f} us, host launch gaps included)")
+        per = w.step_weight_bytes() / n
+        out.append(f"average kernel duration, eager steps: {e_avg:.3f} us over {n} launches per step -> "
+                   f"{per / (e_avg * 1e-6) / 1e9:.1f} GB/s of algorithmic bytes per launch")
+        out.append(f"average kernel duration, graph-replayed steps (tracer-stamped): {avg:.3f} us")
+    else:
+        # per projection: the GEMM plus its reduction, medians over the timed steps
+        names = [L.name.split(".")[-1] for L in w.launches]
+        kinds = sorted(set(names), key=names.index)
+        k0 = 1 + warmup
+        per = {}
+        for k in timed:
+            st = rows[k * per_step:(k + 1) * per_step]
+            i = 0
+            for L, nm in zip(w.launches, names):
+                g = int(st[i]["End_Timestamp"]) - int(st[i]["Start_Timestamp"])
+                i += 1
+                red = 0
+                while i < len(st) and "reduce" in st[i]["Kernel_Name"]:
+                    red += int(st[i]["End_Timestamp"]) - int(st[i]["Start_Timestamp"])
+                    i += 1
+                per.setdefault(nm, []).append((g, red, 2 * w.M * L.K * L.N))
+        for nm in kinds:
+            v = per[nm]
+            g = statistics.median(x[0] for x in v) / 1e3
+            r = statistics.median(x[1] for x in v) / 1e3
+            fl = v[0][2]
+            out.append(f"  {nm:<8} GEMM {g:9.1f} us ({fl / (g * 1e-6) / 1e12:7.1f} TFLOP/s)  reduction {r:6.1f} us")
+        out.append(f"average launch (GEMM + reduction) {s_sum / 1e3 / n:.3f} us over {n} launches per step")
+    return "\n".join(out)
+
+
+def traffic_from(fetch_dir, write_dir, cfg, copy_mib, kind="gemv"):
+    """HBM bytes per library dispatch from `--pmc FETCH_SIZE` and `--pmc
+    WRITE_SIZE` runs of `bench.py --config cfg --copy-calibration copy_mib`:
+    each counter is scaled by known bytes / its reading for the plain copy
+    kernel of the same run.  Updates profiles/traffic.json (with the hash of
+    the kernel sources the counters were taken with) and returns the text."""
+    import hashlib
+    known = copy_mib << 20
+    res, lines = {}, []
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _read_csv(os.path.join(d, "run_counter_collection.csv")) if r["Counter_Name"] == name]
+        cal = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        lib = [float(r["Counter_Value"]) for r in _library_rows(rows)]
+        factor = known / (max(cal) * 1024.0)
+        per = sum(lib) / len(lib) * 1024.0 * factor
+        res[name] = (per, factor)
+        lines.append(f"{name}: copy of {copy_mib} MiB: counter {max(cal):.1f} KiB -> factor {factor:.3f}; "
+                     f"{len(lib)} dispatches, {sum(lib) / len(lib):.1f} KiB raw -> {per / 1e6:.4f} MB per dispatch")
+    from workloads import workload
+    w = workload(cfg)
+    alg = w.step_weight_bytes() / len(w.launches)
+    tot = res["FETCH_SIZE"][0] + res["WRITE_SIZE"][0]
+    lines.append(f"HBM traffic per launch {tot / 1e6:.4f} MB vs algorithmic {alg / 1e6:.4f} MB ({tot / alg:.3f}x)")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    srcs = {"gemv": ["weight_only_int4_matmulnbits_amd/csrc/mnb_gemv.hip",
+                     "weight_only_int4_matmulnbits_amd/csrc/mnb_internal.h"]}[kind]
+    h = hashlib.sha256()
+    for src in srcs:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    ent = rec.get(kind, {})
+    if ent.get("kernel_sha256") != h.hexdigest():
+        ent = {}
+    ent.update({"kernel_sha256": h.hexdigest(), "sources": srcs})
+    ent[f"config{cfg}"] = {"traffic_bytes_per_launch": tot, "fetch_bytes_per_launch": res["FETCH_SIZE"][0],
+                           "write_bytes_per_launch": res["WRITE_SIZE"][0], "fetch_factor": res["FETCH_SIZE"][1],
+                           "write_factor": res["WRITE_SIZE"][1]}
+    rec[kind] = ent
+    rec["note"] = ("HBM bytes per library dispatch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs "
+                   "(KiB per dispatch, averaged over the run's dispatches), each scaled by known bytes / the "
+                   "counter's reading for one plain device-to-device copy (__amd_rocclr_copyBuffer) in the same "
+                   "run.  Valid only while the kernel sources hash to kernel_sha256; written by "
+                   "bench.py --traffic-from.")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,7 +487,21 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one plain device-to-device copy of MIB MiB, the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print the summary of a rocprofv3 --kernel-trace --stats run of this "
+                         "bench (same --config/--steps/--warmup) and exit; no GPU is used")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="derive HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                         "runs of this bench (same --config, --copy-calibration), update "
+                         "profiles/traffic.json and exit; no GPU is used")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.config, args.steps, args.warmup))
+        return
+    if args.traffic_from:
+        print(traffic_from(args.traffic_from[0], args.traffic_from[1], args.config,
+                           args.copy_calibration or 256))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
               "supported (the path has no multi-GPU sharding)", file=sys.stderr)
