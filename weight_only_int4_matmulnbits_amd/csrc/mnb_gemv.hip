@@ -160,6 +160,8 @@ __device__ __forceinline__ void load_group(const GemvArgs& g, int64_t base, int 
         if constexpr (HAS_ZP)
             rz = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.zp) + (ncol ? col0 * g.zp_row : 0),
                                                    (short)0, (int)(ncol * g.zp_row), 0x00020000);
+        // scales and zero points first: loads complete in order, so they are
+        // in registers by the time the weights arrive
 #pragma unroll
         for (int j = 0; j < J; j++) {
             const int c = p + j * LT;
@@ -167,6 +169,17 @@ __device__ __forceinline__ void load_group(const GemvArgs& g, int64_t base, int 
             // so that every lane issues the same single load)
             const uint32_t out = c < g.S ? 0u : kOob;
             const int blk = (c * CK) >> g.log2_bs;
+            const uint32_t os = (uint32_t)((gsub * g.nb + blk) * SSZ) | out;
+            r.sc[u][j] = BF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0)
+                              : __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
+            if constexpr (HAS_ZP)
+                r.zb[u][j] = __builtin_amdgcn_raw_buffer_load_b8(
+                    rz, (uint32_t)(gsub * g.zp_row + (blk >> 1)) | out, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < J; j++) {
+            const int c = p + j * LT;
+            const uint32_t out = c < g.S ? 0u : kOob;
             const uint32_t ow = (uint32_t)(gsub * g.col_bytes + c * CB) | out;
             if constexpr (CB == 16) {
                 r.w[u][j] = __builtin_amdgcn_raw_buffer_load_b128(rb, ow, 0, 0);
@@ -174,12 +187,6 @@ __device__ __forceinline__ void load_group(const GemvArgs& g, int64_t base, int 
                 const uint64_t x = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rb, ow, 0, 0));
                 r.w[u][j] = u32x2{(uint32_t)x, (uint32_t)(x >> 32)};
             }
-            const uint32_t os = (uint32_t)((gsub * g.nb + blk) * SSZ) | out;
-            r.sc[u][j] = BF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0)
-                              : __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
-            if constexpr (HAS_ZP)
-                r.zb[u][j] = __builtin_amdgcn_raw_buffer_load_b8(
-                    rz, (uint32_t)(gsub * g.zp_row + (blk >> 1)) | out, 0, 0);
         }
     }
 }
