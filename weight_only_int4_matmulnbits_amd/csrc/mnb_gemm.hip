@@ -693,11 +693,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
         for (int ks = 0; ks < B4_K / 16; ks++) {
             const int p = ks & 1;
             if (ks + 1 < B4_K / 16) load_frags(ks + 1, p ^ 1);
+            // keep the next sub-step's reads ahead of this sub-step's MFMAs:
+            // left alone, the scheduler sinks each read to just before its
+            // first use and the MFMAs then wait for LDS
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
                 for (int j = 0; j < TN; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][i], bfr[p][j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
     };
