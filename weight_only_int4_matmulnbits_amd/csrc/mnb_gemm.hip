@@ -1246,9 +1246,10 @@ Plan plan_gemm(const Problem& p) {
 
 }  // namespace
 
-size_t gemm_workspace_bytes(const Problem& p) { return smallm_ok(p) ? 0 : plan_gemm(p).ws; }
+size_t gemm_workspace_bytes(const Problem& p) { return gemv_rows_ok(p) || smallm_ok(p) ? 0 : plan_gemm(p).ws; }
 
 int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
+    if (gemv_rows_ok(p)) return launch_gemv_rows(p, s);
     if (smallm_ok(p)) return launch_smallm(p, s);
     Plan pl = plan_gemm(p);
     if (pl.ws && (!ws || ws_bytes < pl.ws)) {

@@ -53,6 +53,7 @@ struct GemvArgs {
     int nb, zp_row, S, log2_bs, log2_L;
     int a16;                  // K * element size is a multiple of 16 and A is 16-byte aligned
     int64_t half;             // gated epilogue: columns per half (gate | up); 0 otherwise
+    int M;                    // rows of A and Y (1 for the decode GEMV; up to MR)
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -85,6 +86,31 @@ __device__ __forceinline__ float dot_words(const uint32_t (&w)[NW], const float*
         dd = fmaf(av[8 * d + 7], ubyte_to_f32<3>(hi), dd);
     }
     return de + dd;
+}
+
+// The same for MR rows of activations: each weight is unpacked once and
+// multiplied into every row (per row the additions are those of dot_words).
+template <int NW, int MR>
+__device__ __forceinline__ void dot_words_rows(const uint32_t (&w)[NW], const float (*av)[32], float (&out)[MR]) {
+    float de[MR], dd[MR];
+#pragma unroll
+    for (int r = 0; r < MR; r++) de[r] = dd[r] = 0.f;
+#pragma unroll
+    for (int d = 0; d < NW; d++) {
+        const uint32_t lo = opaque_and(w[d], 0x0F0F0F0Fu);
+        const uint32_t hi = opaque_and(w[d], 0xF0F0F0F0u);
+        const float q[8] = {ubyte_to_f32<0>(lo), ubyte_to_f32<0>(hi), ubyte_to_f32<1>(lo), ubyte_to_f32<1>(hi),
+                            ubyte_to_f32<2>(lo), ubyte_to_f32<2>(hi), ubyte_to_f32<3>(lo), ubyte_to_f32<3>(hi)};
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+#pragma unroll
+            for (int r = 0; r < MR; r++) {
+                de[r] = fmaf(av[r][8 * d + e], q[e], de[r]);
+                dd[r] = fmaf(av[r][8 * d + e + 1], q[e + 1], dd[r]);
+            }
+    }
+#pragma unroll
+    for (int r = 0; r < MR; r++) out[r] = de[r] + dd[r];
 }
 
 template <int CTRL>
@@ -197,7 +223,10 @@ __device__ __forceinline__ void load_group(const GemvArgs& g, int64_t base, int 
 // projection, SiLU and the gate/up multiplication): each iteration takes a
 // gate column group and the matching up group (U == 2), computed exactly as
 // unfused columns, and writes h = silu(gate) * up for the gate columns only.
-template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, int U, int W, bool SILU = false>
+// MR > 1: rows 0 .. M - 1 of A (M <= MR; the rows past M read zeros) with
+// one chunk of K per lane (J == 1, or 2 for two rows): every weight byte is
+// still read and unpacked once and serves all rows.
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, int U, int W, bool SILU = false, int MR = 1>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     constexpr int CK = 2 * CB;        // values of K per chunk
     constexpr int NW = CB / 4;        // 32-bit words per chunk
@@ -205,7 +234,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     constexpr int UG = SILU ? 1 : U;  // column groups advanced per iteration
     static_assert(W == 1 || U == 1, "split-K teams take one column at a time");
     static_assert(!SILU || (U == 2 && W == 1), "the gated epilogue pairs two groups of one team");
-    __shared__ float red[kWavesPerBlock];
+    static_assert(MR == 1 || (!SILU && U == 1 && J * MR <= 4 && CB == 16), "row kernel: one team column, <= 4 row chunks");
+    __shared__ float red[kWavesPerBlock * MR];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -234,20 +264,25 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     constexpr int RPS = 256 / RB;                // rows per 256-byte bank sweep
     extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];
     const int nthr = 64 * kWavesPerBlock;
+    const int nreq = (g.S * RB + 1023) / 1024;   // 1 KiB requests per row of A
     if (g.a16) {
-        // LDS-direct loads: request r puts 64 pieces (1 KiB) at a_lds + 1024 r;
-        // lane l fills row r * 64 / NV + l / NV, position l % NV, with the
-        // piece that the swizzle assigns there; reads past K return zeros
-        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<void*>(g.a), (short)0, (int)(g.K * ESZ), 0x00020000);
-        const int nreq = (g.S * RB + 1023) / 1024;
-        for (int r = wave; r < nreq; r += kWavesPerBlock) {
-            const int row = r * (64 / NV) + lane / NV;
-            const int pos = lane % NV;
-            const int piece = pos ^ ((row / RPS) % NV);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (void __attribute__((address_space(3)))*)(a_lds + 1024 * r), 16,
-                (uint32_t)(row * RB + 16 * piece), 0, 0, 0);
+        // LDS-direct loads: request r of row m puts 64 pieces (1 KiB) at
+        // a_lds + 1024 (m nreq + r); lane l fills chunk row r * 64 / NV + l / NV,
+        // position l % NV, with the piece that the swizzle assigns there;
+        // reads past K (and rows past M) return zeros
+#pragma unroll
+        for (int m = 0; m < MR; m++) {
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                static_cast<uint8_t*>(const_cast<void*>(g.a)) + (m < g.M ? (int64_t)m * g.K * ESZ : 0), (short)0,
+                m < g.M ? (int)(g.K * ESZ) : 0, 0x00020000);
+            for (int r = wave; r < nreq; r += kWavesPerBlock) {
+                const int row = r * (64 / NV) + lane / NV;
+                const int pos = lane % NV;
+                const int piece = pos ^ ((row / RPS) % NV);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ra, (void __attribute__((address_space(3)))*)(a_lds + 1024 * (m * nreq + r)), 16,
+                    (uint32_t)(row * RB + 16 * piece), 0, 0, 0);
+            }
         }
     } else {
         // K * element size not a multiple of 16: element-wise loads
@@ -293,36 +328,38 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
         asm volatile("s_barrier" : : : "memory");
     }
     // this lane's chunks of A in registers (odd k pre-scaled by 1/16) and
-    // the chunk sums of the unscaled values
-    float av[J][CK];
-    float asum[J];
+    // the chunk sums of the unscaled values, for each row
+    float av[MR * J][CK];
+    float asum[MR * J];
 #pragma unroll
-    for (int j = 0; j < J; j++) {
+    for (int mj = 0; mj < MR * J; mj++) {          // [chunk j][row m]
+        const int j = mj / MR, m = mj % MR;
         const int c = p + j * LT;
         if (c < g.S) {
 #pragma unroll
             for (int v = 0; v < NV; v++) {
-                const u32x4 x = *reinterpret_cast<const u32x4*>(a_lds + c * RB + 16 * (v ^ ((c / RPS) % NV)));
+                const u32x4 x = *reinterpret_cast<const u32x4*>(a_lds + 1024 * m * nreq + c * RB +
+                                                                16 * (v ^ ((c / RPS) % NV)));
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     if constexpr (BF16) {
-                        av[j][8 * v + 2 * e] = __uint_as_float(x[e] << 16);
-                        av[j][8 * v + 2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
+                        av[mj][8 * v + 2 * e] = __uint_as_float(x[e] << 16);
+                        av[mj][8 * v + 2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
                     } else {
-                        av[j][4 * v + e] = __uint_as_float(x[e]);
+                        av[mj][4 * v + e] = __uint_as_float(x[e]);
                     }
                 }
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < CK; i++) av[j][i] = 0.f;
+            for (int i = 0; i < CK; i++) av[mj][i] = 0.f;
         }
         float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < CK; i++) s += av[j][i];
-        asum[j] = s;
+        for (int i = 0; i < CK; i++) s += av[mj][i];
+        asum[mj] = s;
 #pragma unroll
-        for (int i = 1; i < CK; i += 2) av[j][i] *= 0.0625f;
+        for (int i = 1; i < CK; i += 2) av[mj][i] *= 0.0625f;
     }
 
     // Two register stages used alternately (copying a stage would make the
@@ -330,16 +367,22 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     // iteration is reduced, the next one's weights are in flight, and its
     // own stage is refilled with the iteration after.
     auto finish = [&](const Group<BF16, HAS_ZP, CB, J, U>& cur, int64_t gbase) {
-        float acc[U];
+        float acc[U][MR];
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            float s = 0.f;
+            float s[MR];
+#pragma unroll
+            for (int r = 0; r < MR; r++) s[r] = 0.f;
 #pragma unroll
             for (int j = 0; j < J; j++) {
                 uint32_t words[NW];
 #pragma unroll
                 for (int d = 0; d < NW; d++) words[d] = cur.w[u][j][d];
-                const float dot = dot_words<NW>(words, av[j]);
+                float dot[MR];
+                if constexpr (MR == 1)
+                    dot[0] = dot_words<NW>(words, av[j]);
+                else
+                    dot_words_rows<NW, MR>(words, &av[j * MR], dot);
                 float zf = 8.f;
                 if constexpr (HAS_ZP) {
                     const int blk = ((p + j * LT) * CK) >> g.log2_bs;
@@ -348,19 +391,29 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
                 }
                 const float sc = BF16 ? __uint_as_float(cur.sc[u][j] << 16)
                                       : __uint_as_float(cur.sc[u][j]);
-                const float t = fmaf(-zf, asum[j], dot);
-                s = fmaf(sc, t, s);
+#pragma unroll
+                for (int r = 0; r < MR; r++) {
+                    const float t = fmaf(-zf, asum[j * MR + r], dot[r]);
+                    s[r] = fmaf(sc, t, s[r]);
+                }
             }
-            acc[u] = reduce_lanes(s, g.log2_L);
+#pragma unroll
+            for (int r = 0; r < MR; r++) acc[u][r] = reduce_lanes(s[r], g.log2_L);
         }
         if constexpr (W > 1) {
-            if (lane == 63) red[wave] = acc[0];
+            if (lane == 63) {
+#pragma unroll
+                for (int r = 0; r < MR; r++) red[wave * MR + r] = acc[0][r];
+            }
             __syncthreads();
             if (wt == 0) {
-                float v = red[team * W];
 #pragma unroll
-                for (int w2 = 1; w2 < W; w2++) v += red[team * W + w2];
-                acc[0] = v;
+                for (int r = 0; r < MR; r++) {
+                    float v = red[team * W * MR + r];
+#pragma unroll
+                    for (int w2 = 1; w2 < W; w2++) v += red[(team * W + w2) * MR + r];
+                    acc[0][r] = v;
+                }
             }
             __syncthreads();
         }
@@ -368,7 +421,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
             if ((lane & (L - 1)) == L - 1) {
                 const int64_t col = gbase * G + gsub;
                 if (gbase < g.n_groups && col < g.half) {
-                    float gate = acc[0], up = acc[1];
+                    float gate = acc[0][0], up = acc[1][0];
                     if (HAS_BIAS) {
                         gate += __uint_as_float(cur.bias[0]);
                         up += __uint_as_float(cur.bias[1]);
@@ -386,12 +439,16 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
                 const int64_t gi = gbase + u;
                 const int64_t col = gi * G + gsub;
                 if (gi < g.n_groups && col < g.N) {
-                    float v = acc[u];
-                    if (HAS_BIAS) v += __uint_as_float(cur.bias[u]);
-                    if constexpr (BF16)
-                        static_cast<uint16_t*>(g.y)[col] = f32_to_bf16_rtne(v);
-                    else
-                        static_cast<float*>(g.y)[col] = v;
+#pragma unroll
+                    for (int r = 0; r < MR; r++) {
+                        if (r >= g.M) break;
+                        float v = acc[u][r];
+                        if (HAS_BIAS) v += __uint_as_float(cur.bias[u]);
+                        if constexpr (BF16)
+                            static_cast<uint16_t*>(g.y)[r * g.N + col] = f32_to_bf16_rtne(v);
+                        else
+                            static_cast<float*>(g.y)[r * g.N + col] = v;
+                    }
                 }
             }
         }
@@ -422,9 +479,10 @@ struct Geometry {
 };
 
 // Lanes per wavefront, chunks per lane and wavefronts per column: a function
-// of S = ceil(K / CK) only.  Highest lane efficiency S / (L*W*J) first, then
-// fewer wavefronts, then fewer chunks per lane.  J == 0: no register kernel.
-Geometry geometry(int64_t S, bool allow_split) {
+// of S = ceil(K / CK) (and of the chunks a lane may hold) only.  Highest lane
+// efficiency S / (L*W*J) first, then fewer wavefronts, then fewer chunks per
+// lane.  J == 0: no register kernel.
+Geometry geometry(int64_t S, bool allow_split, int jmax = kJMax) {
     Geometry best{0, 0, 0};
     double best_eff = -1.0;
     for (int W = 1; W <= (allow_split ? kWMax : 1); W *= 2) {
@@ -433,7 +491,7 @@ Geometry geometry(int64_t S, bool allow_split) {
             const int64_t LT = (int64_t(1) << lL) * W;
             if (LT > 2 * S && lL > 0) continue; // more than twice the lanes needed
             const int64_t J = (S + LT - 1) / LT;
-            if (J > kJMax) continue;
+            if (J > jmax) continue;
             const double eff = (double)S / (double)(LT * J);
             const bool better = eff > best_eff + 1e-9 ||
                                 (eff > best_eff - 1e-9 && (W < best.W || (W == best.W && J < best.J)));
@@ -473,6 +531,32 @@ GemvFn pick_cb(int J, int W, bool silu) {
 template <bool BF16, bool HAS_ZP, bool HAS_BIAS>
 GemvFn pick_b(int CB, int J, int W, bool silu) {
     return CB == 16 ? pick_cb<BF16, HAS_ZP, HAS_BIAS, 16>(J, W, silu) : pick_cb<BF16, HAS_ZP, HAS_BIAS, 8>(J, W, silu);
+}
+
+// MR rows of A (block >= 32, so 16-byte chunks), J * MR <= 4
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int MR, int J>
+GemvFn pick_rows_j(int W) {
+    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 1, 1, false, MR>;
+    if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 1, 2, false, MR>;
+    if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 1, 4, false, MR>;
+    return nullptr;
+}
+
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS>
+GemvFn pick_rows_b(int MR, int J, int W) {
+    if (MR == 2) return J == 1 ? pick_rows_j<BF16, HAS_ZP, HAS_BIAS, 2, 1>(W)
+                               : J == 2 ? pick_rows_j<BF16, HAS_ZP, HAS_BIAS, 2, 2>(W) : nullptr;
+    if (MR == 4 && J == 1) return pick_rows_j<BF16, HAS_ZP, HAS_BIAS, 4, 1>(W);
+    return nullptr;
+}
+
+GemvFn pick_rows(bool bf16, bool has_zp, bool has_bias, int MR, int J, int W) {
+    if (bf16) {
+        if (has_zp) return has_bias ? pick_rows_b<true, true, true>(MR, J, W) : pick_rows_b<true, true, false>(MR, J, W);
+        return has_bias ? pick_rows_b<true, false, true>(MR, J, W) : pick_rows_b<true, false, false>(MR, J, W);
+    }
+    if (has_zp) return has_bias ? pick_rows_b<false, true, true>(MR, J, W) : pick_rows_b<false, true, false>(MR, J, W);
+    return has_bias ? pick_rows_b<false, false, true>(MR, J, W) : pick_rows_b<false, false, false>(MR, J, W);
 }
 
 // silu: the gated gate||up kernel (two column groups per iteration)
@@ -537,9 +621,21 @@ int64_t gemv_max_k(int bs) {
 
 namespace {
 
+// Rows per launch of the row kernel for M rows (2 <= M <= 4), and whether
+// it takes the problem: 16-byte chunks (block >= 32), activations staged with
+// LDS-direct loads, one chunk per lane and row (two for M == 2), and the MR
+// rows' staged activations within kMaxLds.
+int rows_mr(int64_t M) { return M <= 2 ? 2 : 4; }
+
+size_t rows_lds(const Problem& p, int MR) {
+    const int esz = p.bf16 ? 2 : 4;
+    const int64_t S = (p.K + 31) / 32;
+    return (size_t)MR * (size_t)((S * 32 * esz + 1023) / 1024) * 1024;
+}
+
 // silu: p.N = 2 * half columns (gate half, then up half), y receives half
-// values of silu(gate) * up.
-int launch(const Problem& p, hipStream_t s, bool silu) {
+// values of silu(gate) * up.  MR > 1: the row kernel (p.M rows, p.M <= MR).
+int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1) {
     const int CB = p.bs >= 32 ? 16 : 8;
     const int CK = 2 * CB;
     GemvArgs a;
@@ -550,7 +646,8 @@ int launch(const Problem& p, hipStream_t s, bool silu) {
     a.S = (int)((p.K + CK - 1) / CK);
     a.log2_bs = ilog2(p.bs);
     a.half = silu ? p.N / 2 : 0;
-    const Geometry geo = geometry(a.S, CB == 16);
+    a.M = (int)p.M;
+    const Geometry geo = MR == 1 ? geometry(a.S, CB == 16) : geometry(a.S, true, 4 / MR);
     if (geo.J == 0)
         return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld beyond the register kernel", (long long)p.K);
     if (silu && geo.W != 1)
@@ -563,7 +660,8 @@ int launch(const Problem& p, hipStream_t s, bool silu) {
     const int esz = p.bf16 ? 2 : 4;
     a.a16 = ((p.K * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(p.a) & 15) == 0) &&
             p.K * esz < (int64_t(1) << 31);
-    const size_t lds = (size_t)a.S * CK * esz;
+    // (the row kernel stages row m at m * ceil(S * CK * esz / 1 KiB) KiB)
+    const size_t lds = MR == 1 ? (size_t)a.S * CK * esz : rows_lds(p, MR);
     if (lds > kMaxLds)
         return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld needs %zu bytes of LDS", (long long)p.K, lds);
     // Fill the chip with resident teams of W wavefronts (the kernel's real
@@ -575,7 +673,8 @@ int launch(const Problem& p, hipStream_t s, bool silu) {
     // few-MB decode projections (and slower on the large ones).
     const int64_t cus = compute_units();
     const int teams_per_block = kWavesPerBlock / geo.W;
-    GemvFn f = pick(p.bf16, p.has_zp, p.bias != nullptr, CB, geo.J, geo.W, silu);
+    GemvFn f = MR == 1 ? pick(p.bf16, p.has_zp, p.bias != nullptr, CB, geo.J, geo.W, silu)
+                       : pick_rows(p.bf16, p.has_zp, p.bias != nullptr, MR, geo.J, geo.W);
     if (!f) return fail(MNB_E_UNSUPPORTED, "gemv: no kernel for J=%d W=%d", geo.J, geo.W);
     const int64_t teams = a.n_groups;
     int64_t blocks = (teams + teams_per_block - 1) / teams_per_block;
@@ -591,6 +690,17 @@ int launch(const Problem& p, hipStream_t s, bool silu) {
 }  // namespace
 
 int launch_gemv(const Problem& p, hipStream_t s) { return launch(p, s, false); }
+
+bool gemv_rows_ok(const Problem& p) {
+    if (p.M < 2 || p.M > 4 || p.bs < 32) return false;
+    const int esz = p.bf16 ? 2 : 4;
+    if ((p.K * esz) % 16 != 0 || (reinterpret_cast<uintptr_t>(p.a) & 15) != 0 || p.M * p.K * esz >= (int64_t(1) << 31))
+        return false;
+    const int MR = rows_mr(p.M);
+    return geometry((p.K + 31) / 32, true, 4 / MR).J > 0 && rows_lds(p, MR) <= kMaxLds;
+}
+
+int launch_gemv_rows(const Problem& p, hipStream_t s) { return launch(p, s, false, rows_mr(p.M)); }
 
 int launch_gemv_silu(const Problem& p, hipStream_t s) { return launch(p, s, true); }
 
