@@ -159,14 +159,18 @@ int mnb_gemv(const mnb_desc* d, int64_t M, const void* a,
  * float32 partial sums, so results stay within float32 tolerance.  Products
  * with too few output tiles to fill the GPU split K across workgroups (see
  * Memory above); the float32 partials are added in a fixed order.
- * Short row blocks (1 <= M <= 16, K % 32 == 0, block_size >= 32, K up to
- * 3072 for float32 and 4096 for bfloat16 activations; page "Qwen3 CPU
- * Inference Critical Path", int4_small_m) take a matrix-core kernel that
- * unpacks every weight once for all rows: the exact integers (q - zp) meet
- * the activations (float32 as bf16 head + tail) and each 32-value partial
- * sum is scaled in float32; no workspace.  There, as in mnb_gemv, a column's
- * float32 summation order depends only on K, so concatenated launches are
- * bit-identical to separate ones. */
+ * Short row blocks (page "Qwen3 CPU Inference Critical Path", int4_small_m)
+ * unpack every weight once for all rows, with no workspace.  2 <= M <= 4
+ * (block_size >= 32, K * element size a multiple of 16, A 16-byte aligned;
+ * K up to 8192 for two rows and 4096 for three or four with float32
+ * activations, twice that with bfloat16) go through the decode GEMV: each
+ * unpacked weight feeds one float32 FMA per row.  Otherwise 1 <= M <= 16
+ * (K % 32 == 0, block_size >= 32, K up to 3072 for float32 and 4096 for
+ * bfloat16 activations) take a matrix-core kernel: the exact integers
+ * (q - zp) meet the activations (float32 as bf16 head + tail) and each
+ * 32-value partial sum is scaled in float32.  In both, as in mnb_gemv, a
+ * column's float32 summation order depends only on K (and the row count
+ * class), so concatenated launches are bit-identical to separate ones. */
 int mnb_gemm(const mnb_desc* d, int64_t M, const void* a,
              const uint8_t* b_packed, const void* scales,
              const uint8_t* zp_packed, const float* bias, void* y,
