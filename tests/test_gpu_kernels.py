@@ -213,6 +213,28 @@ def test_identity_and_one_hot_return_dequantized_weights(orc):
         assert np.array_equal(yv.cpu().numpy()[0], w[:, k]), k
 
 
+@pytest.mark.parametrize("bs,zp", [(16, True), (32, True), (32, False), (128, True)])
+def test_f32_gemm_large_tiles_matches_oracle(orc, bs, zp):
+    """Float32 products with at least two 128 x 128 output tiles per CU take
+    the 128 x 128 tile kernel (short ones take 64 x 64 tiles): every output
+    of a ragged shape against the oracle, and identity rows return the
+    float32 dequantized weights bit for bit."""
+    M, K, N = 130, 320, 256 * 128 + 37
+    log(f"f32 large tiles M={M} K={K} N={N} bs={bs} zp={zp}")
+    inp, g = _inputs(K, N, M, bs, "f32", zp, not zp, seed=bs * 7 + zp)
+    pw = _packed(g, bs)
+    y = pw.matmul(g.a)
+    y_ref, S = oracle_ref(orc, inp)
+    assert_close(out_f64(y), y_ref, S, "f32", f"large tiles bs={bs} zp={zp}")
+    Ki = 256
+    inp, g = _inputs(Ki, N, 1, bs, "f32", zp, False, seed=bs + 3)
+    pw = _packed(g, bs)
+    w = orc.round_to_f32(orc.dequant(inp.q.numpy(), None if inp.zp is None else inp.zp.numpy(),
+                                     inp.scales.numpy(), bs))
+    y = pw.matmul(torch.eye(Ki, device=DEV))
+    assert np.array_equal(y.cpu().numpy(), w.T)
+
+
 @pytest.mark.parametrize("M", [1, 64])
 def test_fused_launch_bit_identical_to_separate(M):
     """gate||up in one launch == the two launches; any column permutation of
@@ -362,8 +384,8 @@ def test_bf16_gemm_tail_split_matches_oracle(orc, zp, bias):
 SPLIT_CASES = [
     ("bf16", 512, 4096, 384, 128, True, True),    # 4 tiles of 256x256: 16 K splits
     ("bf16", 300, 1536, 520, 32, False, False),   # ragged M and N: 6 splits
-    ("f32", 256, 2048, 256, 32, True, True),      # 4 tiles of 128x128: 16 splits
-    ("f32", 200, 1024, 136, 16, True, False),     # block 16, ragged: 8 splits
+    ("f32", 256, 2048, 256, 32, True, True),      # 16 tiles of 64x64: 4 splits
+    ("f32", 200, 1024, 136, 16, True, False),     # block 16, ragged: 4 splits
 ]
 
 

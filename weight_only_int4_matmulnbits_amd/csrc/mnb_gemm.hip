@@ -848,18 +848,22 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
 // one output column, so that is one scale per lane.  With A the identity
 // the result is float32((q - zp) * s), the dequantized weight, exactly.
 //
-// Tiles of 128 x 128 x 32 on 4 wavefronts of 64 x 64 (2 x 2 MFMA 32x32x16
-// tiles); the three panels (A hi, A lo, B) and the step's scales sit in LDS,
-// double-buffered (2 x 24.5 KiB), so several workgroups fit on a CU.  Rows
-// are 64 bytes (32 K values) with the four 16-byte pieces of row r at
-// piece ^ ((r >> 2) & 3), so the operand reads of 16 consecutive rows are
-// conflict-free.  Activations (full 128-byte lines per row and K step) and
-// packed weights are read two K steps ahead into registers and staged one
-// step ahead, interleaved with the MFMAs; one barrier per K step; a
-// two-step loop body with alternating register stages.
+// Tiles of BT x BT x 32 on 4 wavefronts of BT/2 x BT/2 (T x T MFMA 32x32x16
+// tiles each, BT = 64 T): T = 2 for large products, T = 1 for short ones,
+// whose 64 x 64 tiles give four times as many workgroups (more of them per
+// CU, far fewer K splits).  The three panels (A hi, A lo, B) and the step's
+// scales sit in LDS, double-buffered (2 x 24.5 KiB for T = 2, 2 x 12.5 KiB
+// for T = 1).  Rows are 64 bytes (32 K values) with the four 16-byte pieces
+// of row r at piece ^ ((r >> 2) & 3), so the operand reads of 16 consecutive
+// rows are conflict-free.  Activations (full 128-byte lines per row and K
+// step) and packed weights are read two K steps ahead into registers and
+// staged one step ahead, interleaved with the MFMAs; one barrier per K step;
+// a two-step loop body with alternating register stages.
 // Requires K % 32 == 0 and K % block_size == 0.
 // ---------------------------------------------------------------------------
 constexpr int F_K = 32;
+
+template <int V> struct IntC { static constexpr int value = V; };
 
 __device__ __forceinline__ int swz64(int r, int piece) { return r * 64 + ((piece ^ ((r >> 2) & 3)) << 4); }
 
@@ -883,11 +887,14 @@ __device__ __forceinline__ void split4(const u32x4& x, uint2& hi, uint2& lo) {
     lo = make_uint2(l[0], l[1]);
 }
 
-template <bool HAS_ZP, bool BS16>
-__global__ __launch_bounds__(256, 2) void gemm_f32_int_kernel(Bf16Args g) {
-    constexpr int TM = 2, TN = 2;
-    constexpr int PANEL = 128 * F_K * 2;                // one K step of one operand: 8 KiB
-    constexpr int SPAN = 128 * 8;                       // the step's scales: 2 per column
+template <bool HAS_ZP, bool BS16, int T>
+__global__ __launch_bounds__(256, T == 2 ? 2 : 4) void gemm_f32_int_kernel(Bf16Args g) {
+    constexpr int TM = T, TN = T;
+    constexpr int BT = 64 * T;                          // tile rows and columns
+    constexpr int PANEL = BT * F_K * 2;                 // one K step of one operand
+    constexpr int SPAN = BT * 8;                        // the step's scales: 2 per column
+    constexpr int AP = BT / 32;                         // activation rows per thread and step
+    constexpr int BQ = 256 / BT;                        // threads per weight column and step
     constexpr int BUF = 3 * PANEL + SPAN;               // A hi, A lo, B, scales
     constexpr int NS = BS16 ? 2 : 1;                    // scale periods per K step
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
@@ -896,13 +903,13 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_int_kernel(Bf16Args g) {
     const int lane = t & 63;
     const int wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int mt = (g.M + 127) / 128;
-    const int nt = (g.N + 127) / 128;
+    const int mt = (g.M + BT - 1) / BT;
+    const int nt = (g.N + BT - 1) / BT;
     const int tiles = mt * nt;
     const int v = xcd_index(blockIdx.x, tiles * g.splits);
     const int split = v / tiles, tt = v - split * tiles;
-    const int m0 = (tt % mt) * 128;
-    const int n0 = (tt / mt) * 128;
+    const int m0 = (tt % mt) * BT;
+    const int n0 = (tt / mt) * BT;
     const int kbase = split * g.sps * F_K;                 // this split's first K value
 
     const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -919,11 +926,11 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_int_kernel(Bf16Args g) {
     const uint32_t a_off = (uint32_t)(m0 + a_r) * (uint32_t)g.K * 4u + 16u * a_c;
     const uint32_t a_rows32 = 32u * (uint32_t)g.K * 4u;
     struct StageA {
-        u32x4 v[4];
+        u32x4 v[AP];
     };
     auto fetch_a = [&](int k0, StageA& st) {
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < AP; i++)
             st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_off + a_rows32 * i + 4u * (kbase + k0), 0, 0);
     };
     auto stash_a = [&](const StageA& st, int buf, int i) {
@@ -934,9 +941,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_int_kernel(Bf16Args g) {
         *reinterpret_cast<uint2*>(lds + buf * BUF + PANEL + off) = lo;
     };
 
-    // weights: thread t takes 16 values (8 bytes) of column t / 2, K half
-    // t % 2, which lie in one quantization block
-    const int b_c = t >> 1, b_h = t & 1;
+    // weights: thread t takes 32 / BQ values (16 or 8) of column t / BQ, part
+    // t % BQ of the step, which lie in one quantization block
+    const int b_c = t / BQ, b_h = t % BQ;
     struct StageB {
         uint2 b;
         uint32_t s;
@@ -945,32 +952,43 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_int_kernel(Bf16Args g) {
     };
     auto fetch_b = [&](int k0, StageB& st) {
         const int col = n0 + b_c;
-        const int kb = kbase + k0 + 16 * b_h;
-        st.b = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                             rb_rs, (uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)kb / 2u, 0, 0));
-        const uint32_t blk = (uint32_t)kb >> g.log2_bs;
+        const uint32_t kq = (uint32_t)(kbase + k0);        // the step's first K value
+        const uint32_t boff = (uint32_t)col * (uint32_t)g.col_bytes + kq / 2u + (16u / BQ) * (uint32_t)b_h;
+        if constexpr (BQ == 2)
+            st.b = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rb_rs, boff, 0, 0));
+        else
+            st.b.x = __builtin_amdgcn_raw_buffer_load_b32(rb_rs, boff, 0, 0);
+        // a block of 32 or more values holds the whole step (one block index
+        // for the workgroup); 16-value blocks split it in two
+        const uint32_t blk = BS16 ? (kq + (32u / BQ) * (uint32_t)b_h) >> 4 : kq >> g.log2_bs;
         st.s = __builtin_amdgcn_raw_buffer_load_b32(rs_rs, 4u * ((uint32_t)col * (uint32_t)g.nb + blk), 0, 0);
         if constexpr (HAS_ZP) {
             st.z = __builtin_amdgcn_raw_buffer_load_b8(rz_rs, (uint32_t)col * (uint32_t)g.zp_row + (blk >> 1), 0, 0);
             st.zsh = 4u * (blk & 1u);
         }
     };
-    // word d (8 values) of a staged weight as the exact bf16 integers q - zp;
-    // the half's scale goes to the step's scale row
+    // word d (8 values) of a staged weight as the exact bf16 integers q - zp
+    // (piece BQ == 2 ? 2 h + d : h of the column): even and odd nibbles
+    // masked into bytes, v_cvt_f32_ubyte, the zero point subtracted in
+    // float32 (exact), the upper halves of two results packed in one v_perm.
+    // The part's scale goes to the step's scale row (slot 1 for the second
+    // 16 values; with larger blocks both slots hold the same scale).
     auto stash_b = [&](const StageB& st, int buf, int d) {
-        const int zq = HAS_ZP ? (int)__builtin_amdgcn_ubfe((uint32_t)st.z, st.zsh, 4) : 8;
+        const float zf = HAS_ZP ? (float)__builtin_amdgcn_ubfe((uint32_t)st.z, st.zsh, 4) : 8.f;
         const uint32_t word = d ? st.b.y : st.b.x;
+        const uint32_t lo = opaque_and(word, 0x0F0F0F0Fu);
+        const uint32_t hi = opaque_and(word >> 4, 0x0F0F0F0Fu);
+        const float w[8] = {ubyte_to_f32<0>(lo) - zf, ubyte_to_f32<0>(hi) - zf, ubyte_to_f32<1>(lo) - zf,
+                            ubyte_to_f32<1>(hi) - zf, ubyte_to_f32<2>(lo) - zf, ubyte_to_f32<2>(hi) - zf,
+                            ubyte_to_f32<3>(lo) - zf, ubyte_to_f32<3>(hi) - zf};
         uint32_t v[4];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const uint32_t byte = (word >> (8 * e)) & 0xFFu;
-            const float w0 = (float)((int)(byte & 0xFu) - zq);
-            const float w1 = (float)((int)(byte >> 4) - zq);
-            v[e] = (__float_as_uint(w0) >> 16) | (__float_as_uint(w1) & 0xFFFF0000u);   // exact
-        }
-        *reinterpret_cast<u32x4*>(lds + buf * BUF + 2 * PANEL + swz64(b_c, 2 * b_h + d)) =
+        for (int e = 0; e < 4; e++)
+            v[e] = __builtin_amdgcn_perm(__float_as_uint(w[2 * e + 1]), __float_as_uint(w[2 * e]), 0x07060302u);
+        *reinterpret_cast<u32x4*>(lds + buf * BUF + 2 * PANEL + swz64(b_c, BQ == 2 ? 2 * b_h + d : b_h)) =
             u32x4{v[0], v[1], v[2], v[3]};
-        if (d == 0) *reinterpret_cast<uint32_t*>(lds + buf * BUF + 3 * PANEL + 8 * b_c + 4 * b_h) = st.s;
+        if (d == 0)
+            *reinterpret_cast<uint32_t*>(lds + buf * BUF + 3 * PANEL + 8 * b_c + 4 * (BQ == 2 ? b_h : b_h >> 1)) = st.s;
     };
 
     f32x16 acc[TM][TN], part[TM][TN];
@@ -993,18 +1011,18 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_int_kernel(Bf16Args g) {
             bf16x8 ah[TM], al[TM], bw[TN];
 #pragma unroll
             for (int i = 0; i < TM; i++) {
-                const int r = wm * 64 + i * 32 + (lane & 31);
+                const int r = wm * (32 * TM) + i * 32 + (lane & 31);
                 ah[i] = *reinterpret_cast<const bf16x8*>(base + swz64(r, piece));
                 al[i] = *reinterpret_cast<const bf16x8*>(base + PANEL + swz64(r, piece));
             }
 #pragma unroll
             for (int j = 0; j < TN; j++) {
-                const int c = wn * 64 + j * 32 + (lane & 31);
+                const int c = wn * (32 * TN) + j * 32 + (lane & 31);
                 bw[j] = *reinterpret_cast<const bf16x8*>(base + 2 * PANEL + swz64(c, piece));
             }
-            stash_a(na, buf ^ 1, 2 * ks);
-            stash_a(na, buf ^ 1, 2 * ks + 1);
-            stash_b(nb, buf ^ 1, ks);
+#pragma unroll
+            for (int i = 0; i < AP / 2; i++) stash_a(na, buf ^ 1, (AP / 2) * ks + i);
+            if (BQ == 2 || ks == 0) stash_b(nb, buf ^ 1, ks);
             const bool first = BS16 || ks == 0;
 #pragma unroll
             for (int i = 0; i < TM; i++)
@@ -1017,7 +1035,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_int_kernel(Bf16Args g) {
                 // fold: this lane's column and the period's K half
 #pragma unroll
                 for (int j = 0; j < TN; j++) {
-                    const int c = wn * 64 + j * 32 + (lane & 31);
+                    const int c = wn * (32 * TN) + j * 32 + (lane & 31);
                     const float sc = *reinterpret_cast<const float*>(base + 3 * PANEL + 8 * c + 4 * (BS16 ? ks : 0));
 #pragma unroll
                     for (int i = 0; i < TM; i++)
@@ -1029,10 +1047,13 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_int_kernel(Bf16Args g) {
     };
 
     const int steps = min(g.sps, g.K / F_K - split * g.sps);
+    // D register stages: step st stages step st + 1 (requested D - 1 steps
+    // earlier) into LDS and requests step st + D into the stage it frees
+    constexpr int D = 2;
     int buf = 0;
     auto one_step = [&](int st, const StageA& ua, const StageB& ub, StageA& la, StageB& lb) {
-        fetch_a((st + 2) * F_K, la);
-        fetch_b((st + 2) * F_K, lb);
+        fetch_a((st + D) * F_K, la);
+        fetch_b((st + D) * F_K, lb);
         __builtin_amdgcn_sched_barrier(0);    // issue the requests first
         step_body(buf, ua, ub);
         __builtin_amdgcn_sched_barrier(0);
@@ -1040,49 +1061,56 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_int_kernel(Bf16Args g) {
         __builtin_amdgcn_sched_barrier(0);
         buf ^= 1;
     };
-    auto stage_all = [&](const StageA& sa, const StageB& sb, int b) {
+    // Step j's data lives in stage (j - r) mod D, r = steps mod D: the loop
+    // then runs whole groups of D steps with fixed stage roles (no tail,
+    // whose conditional steps would keep every stage live past the loop);
+    // the r leading steps run before it.
+    StageA sa[D];
+    StageB sb[D];
+    auto lead = [&](auto rc) {
+        constexpr int R = decltype(rc)::value;
 #pragma unroll
-        for (int i = 0; i < 4; i++) stash_a(sa, b, i);
-        stash_b(sb, b, 0);
-        stash_b(sb, b, 1);
+        for (int j = 0; j < D; j++) {
+            fetch_a(j * F_K, sa[(j - R + D) % D]);
+            fetch_b(j * F_K, sb[(j - R + D) % D]);
+        }
+#pragma unroll
+        for (int i = 0; i < AP; i++) stash_a(sa[(D - R) % D], 0, i);
+        stash_b(sb[(D - R) % D], 0, 0);
+        if (BQ == 2) stash_b(sb[(D - R) % D], 0, 1);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < R; j++)
+            one_step(j, sa[(j + 1 - R + D) % D], sb[(j + 1 - R + D) % D], sa[(j - R + D) % D], sb[(j - R + D) % D]);
     };
-    StageA ax, ay;
-    StageB bx, by;
-    int st = 0;
-    if (steps & 1) {
-        fetch_a(0, ax);
-        fetch_b(0, bx);
-        fetch_a(F_K, ay);
-        fetch_b(F_K, by);
-        stage_all(ax, bx, 0);
-        __syncthreads();
-        one_step(0, ay, by, ax, bx);
-        st = 1;
+    const int r = steps % D;
+    if (D == 2) {
+        if (r == 0) lead(IntC<0>{}); else lead(IntC<1>{});
     } else {
-        fetch_a(0, ay);
-        fetch_b(0, by);
-        fetch_a(F_K, ax);
-        fetch_b(F_K, bx);
-        stage_all(ay, by, 0);
-        __syncthreads();
+        switch (r) {
+            case 0: lead(IntC<0>{}); break;
+            case 1: lead(IntC<1 % D>{}); break;
+            case 2: lead(IntC<2 % D>{}); break;
+            default: lead(IntC<3 % D>{}); break;
+        }
     }
-    for (; st < steps; st += 2) {
-        one_step(st, ax, bx, ay, by);
-        one_step(st + 1, ay, by, ax, bx);
+    for (int st = r; st < steps; st += D) {
+#pragma unroll
+        for (int u = 0; u < D; u++) one_step(st + u, sa[(u + 1) % D], sb[(u + 1) % D], sa[u], sb[u]);
     }
 
     // epilogue: + bias, float32 store (or the partial, without bias)
     float* const out = g.part ? g.part + (int64_t)split * g.M * g.N : static_cast<float*>(g.y);
 #pragma unroll
     for (int j = 0; j < TN; j++) {
-        const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+        const int n = n0 + wn * (32 * TN) + j * 32 + (lane & 31);
         if (n >= g.N) continue;
         const float bv = (!g.part && g.bias) ? g.bias[n] : 0.f;
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int m = m0 + wm * (32 * TM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (m < g.M) out[(int64_t)m * g.N + n] = acc[i][j][r] + bv;
             }
     }
@@ -1166,6 +1194,7 @@ namespace {
 struct Plan {
     enum Kind { LEGACY_BF16, WIDE, REG256, REG128, F32_INT, LEGACY_F32 } kind;
     int64_t tiles = 1;
+    int f32_t = 2;                 // F32_INT: MFMA tiles per wavefront side (tile 64 f32_t)
     int splits = 1, sps = 1;
     int tail_tiles = 0, tail_splits = 1, tail_sps = 0;   // wide kernel: split of the last round
     size_t ws = 0;                 // workspace bytes for the split partials
@@ -1192,13 +1221,14 @@ void choose_tail_split(Plan& pl, int64_t cus, int steps) {
 constexpr size_t kMaxWorkspace = size_t(1) << 30;
 
 // Split K only when the output tiles leave resident workgroup slots idle,
-// keeping at least four K steps per split.
-void choose_split(Plan& pl, const Problem& p, int64_t resident, int steps) {
+// keeping at least four K steps per split and at most max_sp splits.
+void choose_split(Plan& pl, const Problem& p, int64_t resident, int steps, int64_t max_sp = 1 << 20) {
     pl.splits = 1;
     pl.sps = steps;
     if (pl.tiles >= resident) return;
     int64_t sp = resident / pl.tiles;
     if (sp > steps / 4) sp = steps / 4;
+    if (sp > max_sp) sp = max_sp;
     while (sp > 1 && (size_t)sp * (size_t)(p.M * p.N) * 4 > kMaxWorkspace) sp--;
     if (sp <= 1) return;
     pl.sps = (int)((steps + sp - 1) / sp);
@@ -1236,8 +1266,16 @@ Plan plan_gemm(const Problem& p) {
     } else if (vec_a && p.K % F_K == 0 && p.K % p.bs == 0 && p.M * p.K * 4 + 128 * p.K * 4 < lim &&
                b_bytes + 128 * p.col_bytes < lim && p.M * p.N < lim) {
         pl.kind = Plan::F32_INT;
-        pl.tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
-        choose_split(pl, p, 2 * cus, (int)(p.K / F_K));    // two 128 x 128 workgroups per CU
+        const int64_t big = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+        if (big >= 2 * cus) {                               // two 128 x 128 workgroups per CU
+            pl.f32_t = 2;
+            pl.tiles = big;
+            choose_split(pl, p, 2 * cus, (int)(p.K / F_K));
+        } else {                                            // 64 x 64 tiles, at most 4 K splits
+            pl.f32_t = 1;
+            pl.tiles = ((p.M + 63) / 64) * ((p.N + 63) / 64);
+            choose_split(pl, p, 2 * cus, (int)(p.K / F_K), 4);
+        }
     } else {
         pl.kind = Plan::LEGACY_F32;
     }
@@ -1300,8 +1338,11 @@ int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
             hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 8>), dim3(grid), dim3(512), 0, s, b);
             break;
         case Plan::F32_INT: {
-            auto kern = p.has_zp ? (bs16 ? gemm_f32_int_kernel<true, true> : gemm_f32_int_kernel<true, false>)
-                                 : (bs16 ? gemm_f32_int_kernel<false, true> : gemm_f32_int_kernel<false, false>);
+            auto kern = pl.f32_t == 2
+                ? (p.has_zp ? (bs16 ? gemm_f32_int_kernel<true, true, 2> : gemm_f32_int_kernel<true, false, 2>)
+                            : (bs16 ? gemm_f32_int_kernel<false, true, 2> : gemm_f32_int_kernel<false, false, 2>))
+                : (p.has_zp ? (bs16 ? gemm_f32_int_kernel<true, true, 1> : gemm_f32_int_kernel<true, false, 1>)
+                            : (bs16 ? gemm_f32_int_kernel<false, true, 1> : gemm_f32_int_kernel<false, false, 1>));
             hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, b);
             break;
         }
