@@ -18,15 +18,14 @@
 // consecutive chunks: fully coalesced 16-byte-per-lane loads, marked
 // non-temporal (each weight byte is read once).
 //
-// Inner product in float32 on the vector ALU, about 2.25 instructions per
-// weight: per 32-bit word (8 nibbles) one AND keeps the even nibbles and one
-// AND keeps the odd nibbles in place (16*q), v_cvt_f32_ubyte{0..3} turn each
-// byte into a float, and one FMA per weight accumulates; odd-k activations
-// are held pre-multiplied by 1/16 so that (16q)(a/16) = q*a exactly.  Per
-// chunk a lane forms dot = sum a_k q_k and t = dot - zp * sum a_k, then
-// acc += s * t.  The L partial sums of a wavefront meet in
-// a fixed DPP tree (quad_perm, row_half_mirror, row_mirror, ds_swizzle,
-// readlane); the W wavefront sums meet in LDS in wavefront order.  Grid
+// Inner product in float32 on the vector ALU, about 1.9 instructions per
+// weight: per 32-bit word (8 nibbles) three ALU operations mask the even
+// and the odd nibbles into bytes, four v_cvt_pk_f32_fp8 turn the eight bytes
+// into the floats q * 2^-9 (the fp8 encoding of 0x00..0x0F is linear), and
+// one FMA per weight accumulates.  Per chunk a lane forms
+// dot = sum a_k q_k (the FMA sum times 512, exact) and t = dot - zp * sum a_k,
+// then acc += s * t.  The L partial sums of a wavefront meet in a fixed
+// all-DPP tree; the W wavefront sums meet in LDS in wavefront order.  Grid
 // size, unroll and prefetch only change which wavefront handles a column,
 // never the arithmetic: (L, J, W) depend only on (K, block_size), so the
 // float32 summation order of a column is the same whatever N is and wherever
@@ -67,23 +66,35 @@ template <>
 struct ChunkT<8> { using type = u32x2; };
 
 // One 32-bit word of a chunk holds values 8d..8d+7, two per byte, the even
-// one in the low nibble.  av[] holds the chunk's activations with the odd
-// ones pre-multiplied by 1/16.
+// one in the low nibble.  Masked into bytes 0x0q, a nibble read as an OCP
+// fp8 e4m3 value is exactly q * 2^-9 (a subnormal for q < 8, a normal value
+// above: the encoding is linear over 0..15), so one v_cvt_pk_f32_fp8
+// converts two weights and the sum returned is 2^-9 times the chunk's
+// integer dot product (exactly: scaling by a power of two).
+__device__ __forceinline__ void nibble_bytes(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    lo = w & 0x0F0F0F0Fu;            // q(8d), q(8d+2), q(8d+4), q(8d+6)
+    hi = (w >> 4) & 0x0F0F0F0Fu;     // q(8d+1), q(8d+3), ...
+}
+
 template <int NW>
 __device__ __forceinline__ float dot_words(const uint32_t (&w)[NW], const float* av) {
     float de = 0.f, dd = 0.f;
 #pragma unroll
     for (int d = 0; d < NW; d++) {
-        const uint32_t lo = opaque_and(w[d], 0x0F0F0F0Fu);   // q(8d), q(8d+2), ...
-        const uint32_t hi = opaque_and(w[d], 0xF0F0F0F0u);   // 16*q(8d+1), ...
-        de = fmaf(av[8 * d + 0], ubyte_to_f32<0>(lo), de);
-        dd = fmaf(av[8 * d + 1], ubyte_to_f32<0>(hi), dd);
-        de = fmaf(av[8 * d + 2], ubyte_to_f32<1>(lo), de);
-        dd = fmaf(av[8 * d + 3], ubyte_to_f32<1>(hi), dd);
-        de = fmaf(av[8 * d + 4], ubyte_to_f32<2>(lo), de);
-        dd = fmaf(av[8 * d + 5], ubyte_to_f32<2>(hi), dd);
-        de = fmaf(av[8 * d + 6], ubyte_to_f32<3>(lo), de);
-        dd = fmaf(av[8 * d + 7], ubyte_to_f32<3>(hi), dd);
+        uint32_t lo, hi;
+        nibble_bytes(w[d], lo, hi);
+        const auto e0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+        const auto e1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+        const auto o0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+        const auto o1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+        de = fmaf(av[8 * d + 0], e0[0], de);
+        dd = fmaf(av[8 * d + 1], o0[0], dd);
+        de = fmaf(av[8 * d + 2], e0[1], de);
+        dd = fmaf(av[8 * d + 3], o0[1], dd);
+        de = fmaf(av[8 * d + 4], e1[0], de);
+        dd = fmaf(av[8 * d + 5], o1[0], dd);
+        de = fmaf(av[8 * d + 6], e1[1], de);
+        dd = fmaf(av[8 * d + 7], o1[1], dd);
     }
     return de + dd;
 }
@@ -97,10 +108,13 @@ __device__ __forceinline__ void dot_words_rows(const uint32_t (&w)[NW], const fl
     for (int r = 0; r < MR; r++) de[r] = dd[r] = 0.f;
 #pragma unroll
     for (int d = 0; d < NW; d++) {
-        const uint32_t lo = opaque_and(w[d], 0x0F0F0F0Fu);
-        const uint32_t hi = opaque_and(w[d], 0xF0F0F0F0u);
-        const float q[8] = {ubyte_to_f32<0>(lo), ubyte_to_f32<0>(hi), ubyte_to_f32<1>(lo), ubyte_to_f32<1>(hi),
-                            ubyte_to_f32<2>(lo), ubyte_to_f32<2>(hi), ubyte_to_f32<3>(lo), ubyte_to_f32<3>(hi)};
+        uint32_t lo, hi;
+        nibble_bytes(w[d], lo, hi);
+        const auto e0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+        const auto e1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+        const auto o0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+        const auto o1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+        const float q[8] = {e0[0], o0[0], e0[1], o0[1], e1[0], o1[0], e1[1], o1[1]};
 #pragma unroll
         for (int e = 0; e < 8; e += 2)
 #pragma unroll
@@ -327,8 +341,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
             __builtin_amdgcn_s_waitcnt(W1);
         asm volatile("s_barrier" : : : "memory");
     }
-    // this lane's chunks of A in registers (odd k pre-scaled by 1/16) and
-    // the chunk sums of the unscaled values, for each row
+    // this lane's chunks of A in registers and their chunk sums, for each row
     float av[MR * J][CK];
     float asum[MR * J];
 #pragma unroll
@@ -358,8 +371,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
 #pragma unroll
         for (int i = 0; i < CK; i++) s += av[mj][i];
         asum[mj] = s;
-#pragma unroll
-        for (int i = 1; i < CK; i += 2) av[mj][i] *= 0.0625f;
     }
 
     // Two register stages used alternately (copying a stage would make the
@@ -393,7 +404,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
                                       : __uint_as_float(cur.sc[u][j]);
 #pragma unroll
                 for (int r = 0; r < MR; r++) {
-                    const float t = fmaf(-zf, asum[j * MR + r], dot[r]);
+                    const float t = fmaf(-zf, asum[j * MR + r], dot[r] * 512.f);   // exact rescaling
                     s[r] = fmaf(sc, t, s[r]);
                 }
             }
