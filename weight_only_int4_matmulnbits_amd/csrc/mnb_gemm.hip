@@ -1123,26 +1123,47 @@ __global__ __launch_bounds__(256, T == 2 ? 2 : 4) void gemm_f32_int_kernel(Bf16A
 template <bool BF16>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
                                                             int64_t mn, int N, const float* __restrict__ bias,
-                                                            void* __restrict__ y) {
+                                                            void* __restrict__ y, int vec) {
     const int64_t stride = (int64_t)gridDim.x * 256 * 4;
     for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < mn; i += stride) {
         float v[4];
-        if (i + 4 <= mn && (N & 3) == 0) {
+        if (vec && i + 4 <= mn) {
+            // four columns of one row (N % 4 == 0); the slices are requested
+            // ahead of the additions, which stay in split order
             float4 x = *reinterpret_cast<const float4*>(part + i);
-            for (int sp = 1; sp < splits; sp++) {
+            int sp = 1;
+            for (; sp + 1 < splits; sp += 2) {
+                const float4 z0 = *reinterpret_cast<const float4*>(part + (int64_t)sp * mn + i);
+                const float4 z1 = *reinterpret_cast<const float4*>(part + (int64_t)(sp + 1) * mn + i);
+                x.x += z0.x; x.y += z0.y; x.z += z0.z; x.w += z0.w;
+                x.x += z1.x; x.y += z1.y; x.z += z1.z; x.w += z1.w;
+            }
+            if (sp < splits) {
                 const float4 z = *reinterpret_cast<const float4*>(part + (int64_t)sp * mn + i);
                 x.x += z.x; x.y += z.y; x.z += z.z; x.w += z.w;
             }
             v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-        } else {
+            if (bias) {
+                const int c = (int)(i % N);
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                v[e] = 0.f;
-                if (i + e < mn) {
-                    float x = part[i + e];
-                    for (int sp = 1; sp < splits; sp++) x += part[(int64_t)sp * mn + i + e];
-                    v[e] = x;
-                }
+                for (int e = 0; e < 4; e++) v[e] += bias[c + e];
+            }
+            if constexpr (BF16) {
+                const uint32_t lo = (uint32_t)f32_to_bf16_rtne(v[0]) | ((uint32_t)f32_to_bf16_rtne(v[1]) << 16);
+                const uint32_t hi = (uint32_t)f32_to_bf16_rtne(v[2]) | ((uint32_t)f32_to_bf16_rtne(v[3]) << 16);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + i) = make_uint2(lo, hi);
+            } else {
+                *reinterpret_cast<float4*>(static_cast<float*>(y) + i) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+            continue;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            v[e] = 0.f;
+            if (i + e < mn) {
+                float x = part[i + e];
+                for (int sp = 1; sp < splits; sp++) x += part[(int64_t)sp * mn + i + e];
+                v[e] = x;
             }
         }
 #pragma unroll
@@ -1161,7 +1182,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // its splits in split order, + bias, rounded to bf16; four columns per thread.
 __global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restrict__ tp, int splits, int tail_tiles,
                                                           int full_tiles, int mt, int M, int N,
-                                                          const float* __restrict__ bias, uint16_t* __restrict__ y) {
+                                                          const float* __restrict__ bias, uint16_t* __restrict__ y,
+                                                          int vec) {
     constexpr int TILE = B4_M * B4_N;
     const int64_t total = (int64_t)tail_tiles * TILE / 4;
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
@@ -1178,6 +1200,14 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restric
             x.x += z.x; x.y += z.y; x.z += z.z; x.w += z.w;
         }
         const float v[4] = {x.x, x.y, x.z, x.w};
+        if (vec && n0 + 4 <= N) {          // four bf16 in one 8-byte store
+            uint16_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) o[e] = f32_to_bf16_rtne(bias ? v[e] + bias[n0 + e] : v[e]);
+            *reinterpret_cast<uint2*>(y + (int64_t)m * N + n0) =
+                make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+            continue;
+        }
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             const int n = n0 + e;
@@ -1364,12 +1394,15 @@ int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
         const int64_t cap = (int64_t)device_compute_units() * 8;
         if (blocks > cap) blocks = cap;
         if (blocks < 1) blocks = 1;
+        // whole vectors of four: N % 4 == 0 and Y aligned to four elements
+        // (the workspace slices are)
+        const int vec = (p.N % 4 == 0) && (reinterpret_cast<uintptr_t>(p.y) % (p.bf16 ? 8 : 16) == 0);
         if (p.bf16)
             hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s,
-                               static_cast<const float*>(ws), pl.splits, mn, (int)p.N, p.bias, p.y);
+                               static_cast<const float*>(ws), pl.splits, mn, (int)p.N, p.bias, p.y, vec);
         else
             hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s,
-                               static_cast<const float*>(ws), pl.splits, mn, (int)p.N, p.bias, p.y);
+                               static_cast<const float*>(ws), pl.splits, mn, (int)p.N, p.bias, p.y, vec);
         e = hipGetLastError();
         if (e != hipSuccess) return fail(MNB_E_HIP, "gemm split-K reduction launch: %s", hipGetErrorString(e));
     }
@@ -1380,7 +1413,8 @@ int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
         if (blocks > cap) blocks = cap;
         hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                            static_cast<const float*>(ws), pl.tail_splits, pl.tail_tiles, b.full_tiles,
-                           (int)((p.M + B4_M - 1) / B4_M), (int)p.M, (int)p.N, p.bias, static_cast<uint16_t*>(p.y));
+                           (int)((p.M + B4_M - 1) / B4_M), (int)p.M, (int)p.N, p.bias, static_cast<uint16_t*>(p.y),
+                           (int)(p.N % 4 == 0 && reinterpret_cast<uintptr_t>(p.y) % 8 == 0));
         e = hipGetLastError();
         if (e != hipSuccess) return fail(MNB_E_HIP, "gemm tail reduction launch: %s", hipGetErrorString(e));
     }
