@@ -862,6 +862,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
 // Requires K % 32 == 0 and K % block_size == 0.
 // ---------------------------------------------------------------------------
 constexpr int F_K = 32;
+#ifndef F32_SMALL_KS
+#define F32_SMALL_KS 64
+#endif
 
 template <int V> struct IntC { static constexpr int value = V; };
 
@@ -887,16 +890,27 @@ __device__ __forceinline__ void split4(const u32x4& x, uint2& hi, uint2& lo) {
     lo = make_uint2(l[0], l[1]);
 }
 
-template <bool HAS_ZP, bool BS16, int T>
-__global__ __launch_bounds__(256, T == 2 ? 2 : 4) void gemm_f32_int_kernel(Bf16Args g) {
+template <int KS>
+__device__ __forceinline__ int swz_k(int r, int piece) {
+    if constexpr (KS == 32) return swz64(r, piece);
+    else return r * 128 + ((piece ^ ((r >> 1) & 7)) << 4);
+}
+
+template <bool HAS_ZP, int KS, int P, int T>
+__global__ __launch_bounds__(256, T == 2 ? 2 : KS == 64 ? 3 : 4) void gemm_f32_int_kernel(Bf16Args g) {
     constexpr int TM = T, TN = T;
     constexpr int BT = 64 * T;                          // tile rows and columns
-    constexpr int PANEL = BT * F_K * 2;                 // one K step of one operand
-    constexpr int SPAN = BT * 8;                        // the step's scales: 2 per column
-    constexpr int AP = BT / 32;                         // activation rows per thread and step
+    constexpr int PANEL = BT * KS * 2;                  // one K step of one operand
+    constexpr int SPAN = BT * 16;                       // the step's scales: up to 4 per column
+    constexpr int CPR = KS / 4;                         // 16-byte activation chunks per row
+    constexpr int RPP = 256 / CPR;                      // activation rows per pass
+    constexpr int AP = BT / RPP;                        // activation chunks per thread and step
     constexpr int BQ = 256 / BT;                        // threads per weight column and step
+    constexpr int VPT = BT * KS / 256;                  // weights per thread and step
+    constexpr int NWB = VPT / 8;                        // 32-bit weight words per thread and step
+    constexpr int NSUB = KS / 16;                       // MFMA sub-steps per K step
     constexpr int BUF = 3 * PANEL + SPAN;               // A hi, A lo, B, scales
-    constexpr int NS = BS16 ? 2 : 1;                    // scale periods per K step
+    static_assert(AP % NSUB == 0 || NSUB % AP == 0, "activation chunks per sub-step");
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
 
     const int t = threadIdx.x;
@@ -910,7 +924,7 @@ __global__ __launch_bounds__(256, T == 2 ? 2 : 4) void gemm_f32_int_kernel(Bf16A
     const int split = v / tiles, tt = v - split * tiles;
     const int m0 = (tt % mt) * BT;
     const int n0 = (tt / mt) * BT;
-    const int kbase = split * g.sps * F_K;                 // this split's first K value
+    const int kbase = split * g.sps * KS;                  // this split's first K value
 
     const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(g.a), (short)0, (int)g.a_bytes, 0x00020000);
@@ -921,46 +935,48 @@ __global__ __launch_bounds__(256, T == 2 ? 2 : 4) void gemm_f32_int_kernel(Bf16A
     const __amdgpu_buffer_rsrc_t rz_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(HAS_ZP ? g.zp : g.b), (short)0, (int)(HAS_ZP ? g.z_bytes : 0), 0x00020000);
 
-    // activations: thread t moves four floats (chunk t % 8) of rows t / 8 + 32 i
-    const int a_r = t >> 3, a_c = t & 7;
+    // activations: thread t moves four floats (chunk t % CPR) of rows
+    // t / CPR + RPP i
+    const int a_r = t / CPR, a_c = t % CPR;
     const uint32_t a_off = (uint32_t)(m0 + a_r) * (uint32_t)g.K * 4u + 16u * a_c;
-    const uint32_t a_rows32 = 32u * (uint32_t)g.K * 4u;
+    const uint32_t a_rows = (uint32_t)RPP * (uint32_t)g.K * 4u;
     struct StageA {
         u32x4 v[AP];
     };
     auto fetch_a = [&](int k0, StageA& st) {
 #pragma unroll
         for (int i = 0; i < AP; i++)
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_off + a_rows32 * i + 4u * (kbase + k0), 0, 0);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_off + a_rows * i + 4u * (kbase + k0), 0, 0);
     };
     auto stash_a = [&](const StageA& st, int buf, int i) {
         uint2 hi, lo;
         split4(st.v[i], hi, lo);
-        const int off = swz64(a_r + 32 * i, a_c >> 1) + 8 * (a_c & 1);
+        const int off = swz_k<KS>(a_r + RPP * i, a_c >> 1) + 8 * (a_c & 1);
         *reinterpret_cast<uint2*>(lds + buf * BUF + off) = hi;
         *reinterpret_cast<uint2*>(lds + buf * BUF + PANEL + off) = lo;
     };
 
-    // weights: thread t takes 32 / BQ values (16 or 8) of column t / BQ, part
+    // weights: thread t takes VPT values (NWB words) of column t / BQ, part
     // t % BQ of the step, which lie in one quantization block
     const int b_c = t / BQ, b_h = t % BQ;
     struct StageB {
-        uint2 b;
+        uint32_t b[NWB];
         uint32_t s;
         uint8_t z;
         uint32_t zsh;
     };
     auto fetch_b = [&](int k0, StageB& st) {
         const int col = n0 + b_c;
-        const uint32_t kq = (uint32_t)(kbase + k0);        // the step's first K value
-        const uint32_t boff = (uint32_t)col * (uint32_t)g.col_bytes + kq / 2u + (16u / BQ) * (uint32_t)b_h;
-        if constexpr (BQ == 2)
-            st.b = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rb_rs, boff, 0, 0));
-        else
-            st.b.x = __builtin_amdgcn_raw_buffer_load_b32(rb_rs, boff, 0, 0);
-        // a block of 32 or more values holds the whole step (one block index
-        // for the workgroup); 16-value blocks split it in two
-        const uint32_t blk = BS16 ? (kq + (32u / BQ) * (uint32_t)b_h) >> 4 : kq >> g.log2_bs;
+        const uint32_t kq = (uint32_t)(kbase + k0) + (uint32_t)(VPT * b_h);   // first K value of the part
+        const uint32_t boff = (uint32_t)col * (uint32_t)g.col_bytes + kq / 2u;
+        if constexpr (NWB == 2) {
+            const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rb_rs, boff, 0, 0));
+            st.b[0] = x.x;
+            st.b[1] = x.y;
+        } else {
+            st.b[0] = __builtin_amdgcn_raw_buffer_load_b32(rb_rs, boff, 0, 0);
+        }
+        const uint32_t blk = kq >> g.log2_bs;
         st.s = __builtin_amdgcn_raw_buffer_load_b32(rs_rs, 4u * ((uint32_t)col * (uint32_t)g.nb + blk), 0, 0);
         if constexpr (HAS_ZP) {
             st.z = __builtin_amdgcn_raw_buffer_load_b8(rz_rs, (uint32_t)col * (uint32_t)g.zp_row + (blk >> 1), 0, 0);
@@ -968,14 +984,14 @@ __global__ __launch_bounds__(256, T == 2 ? 2 : 4) void gemm_f32_int_kernel(Bf16A
         }
     };
     // word d (8 values) of a staged weight as the exact bf16 integers q - zp
-    // (piece BQ == 2 ? 2 h + d : h of the column): even and odd nibbles
-    // masked into bytes, v_cvt_f32_ubyte, the zero point subtracted in
-    // float32 (exact), the upper halves of two results packed in one v_perm.
-    // The part's scale goes to the step's scale row (slot 1 for the second
-    // 16 values; with larger blocks both slots hold the same scale).
+    // (piece NWB h + d of the column): even and odd nibbles masked into
+    // bytes, v_cvt_f32_ubyte, the zero point subtracted in float32 (exact),
+    // the upper halves of two results packed in one v_perm.  The part's scale
+    // goes to its scale period's slot of the step's scale row (parts of one
+    // period write the same value).
     auto stash_b = [&](const StageB& st, int buf, int d) {
         const float zf = HAS_ZP ? (float)__builtin_amdgcn_ubfe((uint32_t)st.z, st.zsh, 4) : 8.f;
-        const uint32_t word = d ? st.b.y : st.b.x;
+        const uint32_t word = st.b[d];
         const uint32_t lo = opaque_and(word, 0x0F0F0F0Fu);
         const uint32_t hi = opaque_and(word >> 4, 0x0F0F0F0Fu);
         const float w[8] = {ubyte_to_f32<0>(lo) - zf, ubyte_to_f32<0>(hi) - zf, ubyte_to_f32<1>(lo) - zf,
@@ -985,10 +1001,10 @@ __global__ __launch_bounds__(256, T == 2 ? 2 : 4) void gemm_f32_int_kernel(Bf16A
 #pragma unroll
         for (int e = 0; e < 4; e++)
             v[e] = __builtin_amdgcn_perm(__float_as_uint(w[2 * e + 1]), __float_as_uint(w[2 * e]), 0x07060302u);
-        *reinterpret_cast<u32x4*>(lds + buf * BUF + 2 * PANEL + swz64(b_c, BQ == 2 ? 2 * b_h + d : b_h)) =
+        *reinterpret_cast<u32x4*>(lds + buf * BUF + 2 * PANEL + swz_k<KS>(b_c, NWB * b_h + d)) =
             u32x4{v[0], v[1], v[2], v[3]};
         if (d == 0)
-            *reinterpret_cast<uint32_t*>(lds + buf * BUF + 3 * PANEL + 8 * b_c + 4 * (BQ == 2 ? b_h : b_h >> 1)) = st.s;
+            *reinterpret_cast<uint32_t*>(lds + buf * BUF + 3 * PANEL + 16 * b_c + 4 * ((VPT * b_h) / (16 * P))) = st.s;
     };
 
     f32x16 acc[TM][TN], part[TM][TN];
@@ -1006,24 +1022,24 @@ __global__ __launch_bounds__(256, T == 2 ? 2 : 4) void gemm_f32_int_kernel(Bf16A
     auto step_body = [&](int buf, const StageA& na, const StageB& nb) {
         const uint8_t* base = lds + buf * BUF;
 #pragma unroll
-        for (int ks = 0; ks < F_K / 16; ks++) {
+        for (int ks = 0; ks < NSUB; ks++) {
             const int piece = 2 * ks + (lane >> 5);
             bf16x8 ah[TM], al[TM], bw[TN];
 #pragma unroll
             for (int i = 0; i < TM; i++) {
                 const int r = wm * (32 * TM) + i * 32 + (lane & 31);
-                ah[i] = *reinterpret_cast<const bf16x8*>(base + swz64(r, piece));
-                al[i] = *reinterpret_cast<const bf16x8*>(base + PANEL + swz64(r, piece));
+                ah[i] = *reinterpret_cast<const bf16x8*>(base + swz_k<KS>(r, piece));
+                al[i] = *reinterpret_cast<const bf16x8*>(base + PANEL + swz_k<KS>(r, piece));
             }
 #pragma unroll
             for (int j = 0; j < TN; j++) {
                 const int c = wn * (32 * TN) + j * 32 + (lane & 31);
-                bw[j] = *reinterpret_cast<const bf16x8*>(base + 2 * PANEL + swz64(c, piece));
+                bw[j] = *reinterpret_cast<const bf16x8*>(base + 2 * PANEL + swz_k<KS>(c, piece));
             }
 #pragma unroll
-            for (int i = 0; i < AP / 2; i++) stash_a(na, buf ^ 1, (AP / 2) * ks + i);
-            if (BQ == 2 || ks == 0) stash_b(nb, buf ^ 1, ks);
-            const bool first = BS16 || ks == 0;
+            for (int i = 0; i < AP / NSUB; i++) stash_a(na, buf ^ 1, (AP / NSUB) * ks + i);
+            if (ks < NWB) stash_b(nb, buf ^ 1, ks);
+            const bool first = ks % P == 0;
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
@@ -1031,12 +1047,12 @@ __global__ __launch_bounds__(256, T == 2 ? 2 : 4) void gemm_f32_int_kernel(Bf16A
                     part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], first ? zero : part[i][j], 0, 0, 0);
                     part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], part[i][j], 0, 0, 0);
                 }
-            if (BS16 || ks == F_K / 16 - 1) {
-                // fold: this lane's column and the period's K half
+            if (ks % P == P - 1) {
+                // fold: this lane's column and the period's scale
 #pragma unroll
                 for (int j = 0; j < TN; j++) {
                     const int c = wn * (32 * TN) + j * 32 + (lane & 31);
-                    const float sc = *reinterpret_cast<const float*>(base + 3 * PANEL + 8 * c + 4 * (BS16 ? ks : 0));
+                    const float sc = *reinterpret_cast<const float*>(base + 3 * PANEL + 16 * c + 4 * (ks / P));
 #pragma unroll
                     for (int i = 0; i < TM; i++)
 #pragma unroll
@@ -1046,14 +1062,14 @@ __global__ __launch_bounds__(256, T == 2 ? 2 : 4) void gemm_f32_int_kernel(Bf16A
         }
     };
 
-    const int steps = min(g.sps, g.K / F_K - split * g.sps);
+    const int steps = min(g.sps, g.K / KS - split * g.sps);
     // D register stages: step st stages step st + 1 (requested D - 1 steps
     // earlier) into LDS and requests step st + D into the stage it frees
     constexpr int D = 2;
     int buf = 0;
     auto one_step = [&](int st, const StageA& ua, const StageB& ub, StageA& la, StageB& lb) {
-        fetch_a((st + D) * F_K, la);
-        fetch_b((st + D) * F_K, lb);
+        fetch_a((st + D) * KS, la);
+        fetch_b((st + D) * KS, lb);
         __builtin_amdgcn_sched_barrier(0);    // issue the requests first
         step_body(buf, ua, ub);
         __builtin_amdgcn_sched_barrier(0);
@@ -1071,13 +1087,13 @@ __global__ __launch_bounds__(256, T == 2 ? 2 : 4) void gemm_f32_int_kernel(Bf16A
         constexpr int R = decltype(rc)::value;
 #pragma unroll
         for (int j = 0; j < D; j++) {
-            fetch_a(j * F_K, sa[(j - R + D) % D]);
-            fetch_b(j * F_K, sb[(j - R + D) % D]);
+            fetch_a(j * KS, sa[(j - R + D) % D]);
+            fetch_b(j * KS, sb[(j - R + D) % D]);
         }
 #pragma unroll
         for (int i = 0; i < AP; i++) stash_a(sa[(D - R) % D], 0, i);
-        stash_b(sb[(D - R) % D], 0, 0);
-        if (BQ == 2) stash_b(sb[(D - R) % D], 0, 1);
+#pragma unroll
+        for (int d = 0; d < NWB; d++) stash_b(sb[(D - R) % D], 0, d);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < R; j++)
@@ -1225,6 +1241,7 @@ struct Plan {
     enum Kind { LEGACY_BF16, WIDE, REG256, REG128, F32_INT, LEGACY_F32 } kind;
     int64_t tiles = 1;
     int f32_t = 2;                 // F32_INT: MFMA tiles per wavefront side (tile 64 f32_t)
+    int f32_ks = F_K;              // F32_INT: K values per step (32 or 64)
     int splits = 1, sps = 1;
     int tail_tiles = 0, tail_splits = 1, tail_sps = 0;   // wide kernel: split of the last round
     size_t ws = 0;                 // workspace bytes for the split partials
@@ -1303,8 +1320,11 @@ Plan plan_gemm(const Problem& p) {
             choose_split(pl, p, 2 * cus, (int)(p.K / F_K));
         } else {                                            // 64 x 64 tiles, at most 4 K splits
             pl.f32_t = 1;
+            // 64-value K steps where the blocks allow (a block of 32 or
+            // more values holds each thread's 16 weights of a step)
+            pl.f32_ks = (p.K % 64 == 0 && p.bs >= 32) ? F32_SMALL_KS : F_K;
             pl.tiles = ((p.M + 63) / 64) * ((p.N + 63) / 64);
-            choose_split(pl, p, 2 * cus, (int)(p.K / F_K), 4);
+            choose_split(pl, p, 2 * cus, (int)(p.K / pl.f32_ks), 4);
         }
     } else {
         pl.kind = Plan::LEGACY_F32;
@@ -1322,7 +1342,7 @@ int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
     Plan pl = plan_gemm(p);
     if (pl.ws && (!ws || ws_bytes < pl.ws)) {
         pl.splits = 1;                                      // no room for partials: one pass
-        pl.sps = (int)(p.K / (pl.kind == Plan::WIDE ? B4_K : F_K));
+        pl.sps = (int)(p.K / (pl.kind == Plan::WIDE ? B4_K : pl.kind == Plan::F32_INT ? pl.f32_ks : F_K));
         pl.tail_tiles = 0;
     }
     GemmArgs a;
@@ -1368,11 +1388,17 @@ int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
             hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 8>), dim3(grid), dim3(512), 0, s, b);
             break;
         case Plan::F32_INT: {
-            auto kern = pl.f32_t == 2
-                ? (p.has_zp ? (bs16 ? gemm_f32_int_kernel<true, true, 2> : gemm_f32_int_kernel<true, false, 2>)
-                            : (bs16 ? gemm_f32_int_kernel<false, true, 2> : gemm_f32_int_kernel<false, false, 2>))
-                : (p.has_zp ? (bs16 ? gemm_f32_int_kernel<true, true, 1> : gemm_f32_int_kernel<true, false, 1>)
-                            : (bs16 ? gemm_f32_int_kernel<false, true, 1> : gemm_f32_int_kernel<false, false, 1>));
+            // P: 16-value MFMA sub-steps per scale period
+            decltype(&gemm_f32_int_kernel<true, 32, 1, 2>) kern;
+            if (pl.f32_t == 2)
+                kern = p.has_zp ? (bs16 ? gemm_f32_int_kernel<true, 32, 1, 2> : gemm_f32_int_kernel<true, 32, 2, 2>)
+                                : (bs16 ? gemm_f32_int_kernel<false, 32, 1, 2> : gemm_f32_int_kernel<false, 32, 2, 2>);
+            else if (pl.f32_ks == 64)
+                kern = p.has_zp ? (p.bs == 32 ? gemm_f32_int_kernel<true, 64, 2, 1> : gemm_f32_int_kernel<true, 64, 4, 1>)
+                                : (p.bs == 32 ? gemm_f32_int_kernel<false, 64, 2, 1> : gemm_f32_int_kernel<false, 64, 4, 1>);
+            else
+                kern = p.has_zp ? (bs16 ? gemm_f32_int_kernel<true, 32, 1, 1> : gemm_f32_int_kernel<true, 32, 2, 1>)
+                                : (bs16 ? gemm_f32_int_kernel<false, 32, 1, 1> : gemm_f32_int_kernel<false, 32, 2, 1>);
             hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, b);
             break;
         }
