@@ -128,6 +128,7 @@ GEMM_CASES = [  # (M, K, N)
     (1, 64, 64), (2, 33, 5), (3, 257, 129), (17, 1000, 63), (64, 128, 128),
     (65, 129, 130), (128, 256, 256), (130, 512, 200), (257, 320, 300),
     (512, 1024, 257), (33, 2560, 96), (40, 9728, 64), (7, 16, 1), (300, 1, 9),
+    (96, 544, 200),   # K % 64 == 32: float32 products keep 32-value K steps
 ]
 
 
