@@ -848,23 +848,22 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
 // one output column, so that is one scale per lane.  With A the identity
 // the result is float32((q - zp) * s), the dequantized weight, exactly.
 //
-// Tiles of BT x BT x 32 on 4 wavefronts of BT/2 x BT/2 (T x T MFMA 32x32x16
+// Tiles of BT x BT x KS on 4 wavefronts of BT/2 x BT/2 (T x T MFMA 32x32x16
 // tiles each, BT = 64 T): T = 2 for large products, T = 1 for short ones,
 // whose 64 x 64 tiles give four times as many workgroups (more of them per
-// CU, far fewer K splits).  The three panels (A hi, A lo, B) and the step's
-// scales sit in LDS, double-buffered (2 x 24.5 KiB for T = 2, 2 x 12.5 KiB
-// for T = 1).  Rows are 64 bytes (32 K values) with the four 16-byte pieces
-// of row r at piece ^ ((r >> 2) & 3), so the operand reads of 16 consecutive
-// rows are conflict-free.  Activations (full 128-byte lines per row and K
-// step) and packed weights are read two K steps ahead into registers and
-// staged one step ahead, interleaved with the MFMAs; one barrier per K step;
-// a two-step loop body with alternating register stages.
-// Requires K % 32 == 0 and K % block_size == 0.
+// CU, far fewer K splits).  K steps of KS = 32 values, or 64 for T = 1 when
+// K and the blocks allow (half the barriers per K); P 16-value sub-steps
+// make one scale period.  The three panels (A hi, A lo, B) and the step's
+// scales sit in LDS, double-buffered.  Rows are 2 KS bytes with the 16-byte
+// pieces of row r XOR-swizzled (piece ^ ((r >> 2) & 3) for 64-byte rows,
+// piece ^ ((r >> 1) & 7) for 128-byte rows), so the operand reads of 16
+// consecutive rows are conflict-free.  Activations (full 128-byte lines)
+// and packed weights are read two K steps ahead into registers and staged
+// one step ahead, interleaved with the MFMAs; one barrier per K step; a
+// two-step loop body with alternating register stages.
+// Requires K % KS == 0 and K % block_size == 0.
 // ---------------------------------------------------------------------------
 constexpr int F_K = 32;
-#ifndef F32_SMALL_KS
-#define F32_SMALL_KS 64
-#endif
 
 template <int V> struct IntC { static constexpr int value = V; };
 
@@ -1322,7 +1321,7 @@ Plan plan_gemm(const Problem& p) {
             pl.f32_t = 1;
             // 64-value K steps where the blocks allow (a block of 32 or
             // more values holds each thread's 16 weights of a step)
-            pl.f32_ks = (p.K % 64 == 0 && p.bs >= 32) ? F32_SMALL_KS : F_K;
+            pl.f32_ks = (p.K % 64 == 0 && p.bs >= 32) ? 64 : F_K;
             pl.tiles = ((p.M + 63) / 64) * ((p.N + 63) / 64);
             choose_split(pl, p, 2 * cus, (int)(p.K / pl.f32_ks), 4);
         }
