@@ -147,6 +147,42 @@ __device__ __forceinline__ bool better(float v, int64_t i, float bv, int64_t bi)
     return i < bi;
 }
 
+// The best (value, index) pair of a wavefront, in every lane: an XOR
+// butterfly under the total order above (the result does not depend on the
+// pairing).
+__device__ __forceinline__ void wave_best(float& v, int64_t& i) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(v, off, 64);
+        const int64_t oi = __shfl_xor(i, off, 64);
+        if (better(ov, oi, v, i)) {
+            v = ov;
+            i = oi;
+        }
+    }
+}
+
+// The best pair of a workgroup (blockDim.x a multiple of 64, at most 1024):
+// per wavefront, then the wavefronts' bests in order; every thread returns it.
+__device__ __forceinline__ void block_best(float& v, int64_t& i) {
+    __shared__ float sv[16];
+    __shared__ int64_t si[16];
+    wave_best(v, i);
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        sv[w] = v;
+        si[w] = i;
+    }
+    __syncthreads();
+    v = sv[0];
+    i = si[0];
+    for (int k = 1; k < nw; k++)
+        if (better(sv[k], si[k], v, i)) {
+            v = sv[k];
+            i = si[k];
+        }
+}
+
 // Best (value, index) of row m over [n0, n1) by one workgroup: each thread
 // reads 16-byte pieces (4 float32 or 8 bfloat16 values), eight pieces in
 // flight per round, when the row starts 16-byte aligned and has a whole number
@@ -155,8 +191,6 @@ __device__ __forceinline__ bool better(float v, int64_t i, float bv, int64_t bi)
 template <bool BF16>
 __device__ void best_of_range(const void* __restrict__ x, int64_t N, int64_t m, int64_t n0, int64_t n1,
                               int vec, float& out_v, int64_t& out_i) {
-    __shared__ float sv[1024];
-    __shared__ int64_t si[1024];
     const int t = threadIdx.x, T = blockDim.x;
     float bv = -INFINITY;
     int64_t bi = kNoIndex;
@@ -198,18 +232,9 @@ __device__ void best_of_range(const void* __restrict__ x, int64_t N, int64_t m, 
             }
         }
     }
-    sv[t] = bv;
-    si[t] = bi;
-    __syncthreads();
-    for (int s = T / 2; s > 0; s >>= 1) {
-        if (t < s && better(sv[t + s], si[t + s], sv[t], si[t])) {
-            sv[t] = sv[t + s];
-            si[t] = si[t + s];
-        }
-        __syncthreads();
-    }
-    out_v = sv[0];
-    out_i = si[0];
+    block_best(bv, bi);
+    out_v = bv;
+    out_i = bi;
 }
 
 // One workgroup per row (short rows, or no workspace).
@@ -244,8 +269,6 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const void* __restr
 
 __global__ __launch_bounds__(256) void argmax_final_kernel(const Partial* __restrict__ part, int S,
                                                            int64_t* __restrict__ idx) {
-    __shared__ float sv[256];
-    __shared__ int64_t si[256];
     const int64_t m = blockIdx.x;
     const int t = threadIdx.x;
     float bv = -INFINITY;
@@ -257,17 +280,8 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const Partial* __rest
             bi = p.i;
         }
     }
-    sv[t] = bv;
-    si[t] = bi;
-    __syncthreads();
-    for (int h = blockDim.x / 2; h > 0; h >>= 1) {
-        if (t < h && better(sv[t + h], si[t + h], sv[t], si[t])) {
-            sv[t] = sv[t + h];
-            si[t] = si[t + h];
-        }
-        __syncthreads();
-    }
-    if (t == 0) idx[m] = si[0];
+    block_best(bv, bi);
+    if (t == 0) idx[m] = bi;
 }
 
 constexpr int64_t kArgmaxSeg = 2048;     // values per partial workgroup
