@@ -18,13 +18,14 @@
 // consecutive chunks: fully coalesced 16-byte-per-lane loads, marked
 // non-temporal (each weight byte is read once).
 //
-// Inner product in float32 on the vector ALU, about 1.9 instructions per
-// weight: per 32-bit word (8 nibbles) three ALU operations mask the even
-// and the odd nibbles into bytes, four v_cvt_pk_f32_fp8 turn the eight bytes
-// into the floats q * 2^-9 (the fp8 encoding of 0x00..0x0F is linear), and
-// one FMA per weight accumulates.  Per chunk a lane forms
-// dot = sum a_k q_k (the FMA sum times 512, exact) and t = dot - zp * sum a_k,
-// then acc += s * t.  The L partial sums of a wavefront meet in a fixed
+// Inner product in float32 on the vector ALU, about 2.1 instructions per
+// weight: per 32-bit word (8 nibbles) one shift and four masks build f16
+// pairs 1024 + q (1024 + 16 q for odd k), one packed f16 addition per pair
+// leaves the exact integers q - zp (16 (q - zp)), and one mixed-precision FMA
+// (f16 weight, float32 activation and sum; odd-k activations times 1/16) per
+// weight accumulates.  Per chunk a lane forms
+// t = sum a_k (q_k - zp), then acc += s * t; a weight equal to its zero point
+// adds exactly nothing.  The L partial sums of a wavefront meet in a fixed
 // all-DPP tree; the W wavefront sums meet in LDS in wavefront order.  Grid
 // size, unroll and prefetch only change which wavefront handles a column,
 // never the arithmetic: (L, J, W) depend only on (K, block_size), so the
@@ -66,35 +67,64 @@ template <>
 struct ChunkT<8> { using type = u32x2; };
 
 // One 32-bit word of a chunk holds values 8d..8d+7, two per byte, the even
-// one in the low nibble.  Masked into bytes 0x0q, a nibble read as an OCP
-// fp8 e4m3 value is exactly q * 2^-9 (a subnormal for q < 8, a normal value
-// above: the encoding is linear over 0..15), so one v_cvt_pk_f32_fp8
-// converts two weights and the sum returned is 2^-9 times the chunk's
-// integer dot product (exactly: scaling by a power of two).
-__device__ __forceinline__ void nibble_bytes(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    lo = w & 0x0F0F0F0Fu;            // q(8d), q(8d+2), q(8d+4), q(8d+6)
-    hi = (w >> 4) & 0x0F0F0F0Fu;     // q(8d+1), q(8d+3), ...
+// one in the low nibble.  Two nibbles 16 bits apart are masked into the
+// mantissas of a packed f16 pair with one v_and_or_b32: nibbles at bits 0..3
+// of a half give 1024 + q, nibbles at bits 4..7 give 1024 + 16 q.  One
+// v_pk_add_f16 of -(1024 + zp), respectively -(1024 + 16 zp), leaves the
+// exact integers q - zp, respectively 16 (q - zp), and v_fma_mix_f32
+// multiplies each f16 half into a float32 FMA; odd-k activations are held
+// times 1/16, so every product is exactly a (q - zp).  A weight equal to its
+// zero point thus adds exactly nothing, and the chunk sum is the float32 sum
+// of the products a_k (q_k - zp) (about 2.1 instructions per weight).
+// zc holds the two subtrahends: -(1024 + zp) in the low half, -(1024 + 16 zp)
+// in the high half.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// The masks and the f16 exponent pattern live in VGPRs whose values the
+// compiler cannot see, so (w & mask) | magic becomes one v_and_or_b32 (gfx9
+// VOP3 encodings take no literal constants) without an opaque asm statement
+// at every use.
+struct NibbleMasks {
+    uint32_t lo, hi, magic;      // 0x000F000F, 0x00F000F0, 0x64006400
+};
+
+__device__ __forceinline__ NibbleMasks nibble_masks() {
+    NibbleMasks k{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+    asm volatile("" : "+v"(k.lo), "+v"(k.hi), "+v"(k.magic));
+    return k;
+}
+
+__device__ __forceinline__ half2_t nibble_pair(uint32_t w, uint32_t mask, uint32_t magic, uint32_t zc) {
+    const uint32_t m = (w & mask) | magic;
+    return __builtin_bit_cast(half2_t, m) + __builtin_bit_cast(half2_t, zc);
+}
+
+// the two subtrahend pairs of a zero point: {even, odd} nibble positions
+__device__ __forceinline__ void zero_point_pairs(uint32_t zp, uint32_t& ze, uint32_t& zo) {
+    const uint32_t he = 0xE400u | zp, ho = 0xE400u | (zp << 4);   // f16 -(1024 + zp), -(1024 + 16 zp)
+    ze = he | (he << 16);
+    zo = ho | (ho << 16);
 }
 
 template <int NW>
-__device__ __forceinline__ float dot_words(const uint32_t (&w)[NW], const float* av) {
+__device__ __forceinline__ float dot_words(const uint32_t (&w)[NW], const float* av, uint32_t ze, uint32_t zo,
+                                           const NibbleMasks& k) {
     float de = 0.f, dd = 0.f;
 #pragma unroll
     for (int d = 0; d < NW; d++) {
-        uint32_t lo, hi;
-        nibble_bytes(w[d], lo, hi);
-        const auto e0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-        const auto e1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-        const auto o0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-        const auto o1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-        de = fmaf(av[8 * d + 0], e0[0], de);
-        dd = fmaf(av[8 * d + 1], o0[0], dd);
-        de = fmaf(av[8 * d + 2], e0[1], de);
-        dd = fmaf(av[8 * d + 3], o0[1], dd);
-        de = fmaf(av[8 * d + 4], e1[0], de);
-        dd = fmaf(av[8 * d + 5], o1[0], dd);
-        de = fmaf(av[8 * d + 6], e1[1], de);
-        dd = fmaf(av[8 * d + 7], o1[1], dd);
+        const uint32_t w8 = w[d] >> 8;
+        const half2_t p0 = nibble_pair(w[d], k.lo, k.magic, ze);   // values 8d + 0, 8d + 4
+        const half2_t p1 = nibble_pair(w[d], k.hi, k.magic, zo);   // 8d + 1, 8d + 5 (times 16)
+        const half2_t p2 = nibble_pair(w8, k.lo, k.magic, ze);     // 8d + 2, 8d + 6
+        const half2_t p3 = nibble_pair(w8, k.hi, k.magic, zo);     // 8d + 3, 8d + 7 (times 16)
+        de = fmaf(av[8 * d + 0], (float)p0[0], de);
+        dd = fmaf(av[8 * d + 1], (float)p1[0], dd);
+        de = fmaf(av[8 * d + 2], (float)p2[0], de);
+        dd = fmaf(av[8 * d + 3], (float)p3[0], dd);
+        de = fmaf(av[8 * d + 4], (float)p0[1], de);
+        dd = fmaf(av[8 * d + 5], (float)p1[1], dd);
+        de = fmaf(av[8 * d + 6], (float)p2[1], de);
+        dd = fmaf(av[8 * d + 7], (float)p3[1], dd);
     }
     return de + dd;
 }
@@ -102,19 +132,20 @@ __device__ __forceinline__ float dot_words(const uint32_t (&w)[NW], const float*
 // The same for MR rows of activations: each weight is unpacked once and
 // multiplied into every row (per row the additions are those of dot_words).
 template <int NW, int MR>
-__device__ __forceinline__ void dot_words_rows(const uint32_t (&w)[NW], const float (*av)[32], float (&out)[MR]) {
+__device__ __forceinline__ void dot_words_rows(const uint32_t (&w)[NW], const float (*av)[32], uint32_t ze,
+                                               uint32_t zo, const NibbleMasks& k, float (&out)[MR]) {
     float de[MR], dd[MR];
 #pragma unroll
     for (int r = 0; r < MR; r++) de[r] = dd[r] = 0.f;
 #pragma unroll
     for (int d = 0; d < NW; d++) {
-        uint32_t lo, hi;
-        nibble_bytes(w[d], lo, hi);
-        const auto e0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-        const auto e1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-        const auto o0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-        const auto o1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-        const float q[8] = {e0[0], o0[0], e0[1], o0[1], e1[0], o1[0], e1[1], o1[1]};
+        const uint32_t w8 = w[d] >> 8;
+        const half2_t p0 = nibble_pair(w[d], k.lo, k.magic, ze);
+        const half2_t p1 = nibble_pair(w[d], k.hi, k.magic, zo);
+        const half2_t p2 = nibble_pair(w8, k.lo, k.magic, ze);
+        const half2_t p3 = nibble_pair(w8, k.hi, k.magic, zo);
+        const float q[8] = {(float)p0[0], (float)p1[0], (float)p2[0], (float)p3[0],
+                            (float)p0[1], (float)p1[1], (float)p2[1], (float)p3[1]};
 #pragma unroll
         for (int e = 0; e < 8; e += 2)
 #pragma unroll
@@ -341,9 +372,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
             __builtin_amdgcn_s_waitcnt(W1);
         asm volatile("s_barrier" : : : "memory");
     }
-    // this lane's chunks of A in registers and their chunk sums, for each row
+    const NibbleMasks nk = nibble_masks();
+    // this lane's chunks of A in registers (odd k times 1/16), for each row
     float av[MR * J][CK];
-    float asum[MR * J];
 #pragma unroll
     for (int mj = 0; mj < MR * J; mj++) {          // [chunk j][row m]
         const int j = mj / MR, m = mj % MR;
@@ -367,10 +398,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
 #pragma unroll
             for (int i = 0; i < CK; i++) av[mj][i] = 0.f;
         }
-        float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < CK; i++) s += av[mj][i];
-        asum[mj] = s;
+        for (int i = 1; i < CK; i += 2) av[mj][i] *= 0.0625f;
     }
 
     // Two register stages used alternately (copying a stage would make the
@@ -389,24 +418,23 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
                 uint32_t words[NW];
 #pragma unroll
                 for (int d = 0; d < NW; d++) words[d] = cur.w[u][j][d];
-                float dot[MR];
-                if constexpr (MR == 1)
-                    dot[0] = dot_words<NW>(words, av[j]);
-                else
-                    dot_words_rows<NW, MR>(words, &av[j * MR], dot);
-                float zf = 8.f;
+                uint32_t zq = 8u;
                 if constexpr (HAS_ZP) {
                     const int blk = ((p + j * LT) * CK) >> g.log2_bs;
                     const uint32_t zb = cur.zb[u][j];
-                    zf = (float)((blk & 1) ? (zb >> 4) : (zb & 0xF));
+                    zq = (blk & 1) ? ((zb >> 4) & 0xFu) : (zb & 0xFu);
                 }
+                uint32_t ze, zo;
+                zero_point_pairs(zq, ze, zo);
+                float dot[MR];
+                if constexpr (MR == 1)
+                    dot[0] = dot_words<NW>(words, av[j], ze, zo, nk);
+                else
+                    dot_words_rows<NW, MR>(words, &av[j * MR], ze, zo, nk, dot);
                 const float sc = BF16 ? __uint_as_float(cur.sc[u][j] << 16)
                                       : __uint_as_float(cur.sc[u][j]);
 #pragma unroll
-                for (int r = 0; r < MR; r++) {
-                    const float t = fmaf(-zf, asum[j * MR + r], dot[r] * 512.f);   // exact rescaling
-                    s[r] = fmaf(sc, t, s[r]);
-                }
+                for (int r = 0; r < MR; r++) s[r] = fmaf(sc, dot[r], s[r]);
             }
 #pragma unroll
             for (int r = 0; r < MR; r++) acc[u][r] = reduce_lanes(s[r], g.log2_L);
