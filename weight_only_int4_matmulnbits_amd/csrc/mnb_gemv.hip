@@ -20,10 +20,9 @@
 //
 // Inner product in float32 on the vector ALU, about 2.1 instructions per
 // weight: per 32-bit word (8 nibbles) one shift and four masks build f16
-// pairs 1024 + q (1024 + 16 q for odd k), one packed f16 addition per pair
-// leaves the exact integers q - zp (16 (q - zp)), and one mixed-precision FMA
-// (f16 weight, float32 activation and sum; odd-k activations times 1/16) per
-// weight accumulates.  Per chunk a lane forms
+// pairs 1024 + q (1024 + 16 q for odd k), one packed f16 addition or FMA per
+// pair leaves the exact integers q - zp, and one mixed-precision FMA (f16
+// weight, float32 activation and sum) per weight accumulates.  Per chunk a lane forms
 // t = sum a_k (q_k - zp), then acc += s * t; a weight equal to its zero point
 // adds exactly nothing.  The L partial sums of a wavefront meet in a fixed
 // all-DPP tree; the W wavefront sums meet in LDS in wavefront order.  Grid
@@ -69,15 +68,14 @@ struct ChunkT<8> { using type = u32x2; };
 // One 32-bit word of a chunk holds values 8d..8d+7, two per byte, the even
 // one in the low nibble.  Two nibbles 16 bits apart are masked into the
 // mantissas of a packed f16 pair with one v_and_or_b32: nibbles at bits 0..3
-// of a half give 1024 + q, nibbles at bits 4..7 give 1024 + 16 q.  One
-// v_pk_add_f16 of -(1024 + zp), respectively -(1024 + 16 zp), leaves the
-// exact integers q - zp, respectively 16 (q - zp), and v_fma_mix_f32
-// multiplies each f16 half into a float32 FMA; odd-k activations are held
-// times 1/16, so every product is exactly a (q - zp).  A weight equal to its
-// zero point thus adds exactly nothing, and the chunk sum is the float32 sum
-// of the products a_k (q_k - zp) (about 2.1 instructions per weight).
-// zc holds the two subtrahends: -(1024 + zp) in the low half, -(1024 + 16 zp)
-// in the high half.
+// of a half give 1024 + q, nibbles at bits 4..7 give 1024 + 16 q.  One packed
+// f16 operation leaves the exact integers q - zp: v_pk_add_f16 of
+// -(1024 + zp) for the first kind, v_pk_fma_f16 times 1/16 plus -(64 + zp)
+// for the second.  v_fma_mix_f32 multiplies each f16 half into a float32 FMA,
+// so every product is exactly a (q - zp) before the FMA rounding, a weight
+// equal to its zero point adds exactly nothing, and the chunk sum is the
+// float32 sum of the products a_k (q_k - zp) (about 2.1 instructions per
+// weight).  ze holds -(1024 + zp) and zo holds -(64 + zp) in both halves.
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 // The masks and the f16 exponent pattern live in VGPRs whose values the
@@ -94,14 +92,22 @@ __device__ __forceinline__ NibbleMasks nibble_masks() {
     return k;
 }
 
-__device__ __forceinline__ half2_t nibble_pair(uint32_t w, uint32_t mask, uint32_t magic, uint32_t zc) {
+// nibbles at bits 0..3 of each half: q - zp
+__device__ __forceinline__ half2_t nibble_pair(uint32_t w, uint32_t mask, uint32_t magic, uint32_t ze) {
     const uint32_t m = (w & mask) | magic;
-    return __builtin_bit_cast(half2_t, m) + __builtin_bit_cast(half2_t, zc);
+    return __builtin_bit_cast(half2_t, m) + __builtin_bit_cast(half2_t, ze);
 }
 
-// the two subtrahend pairs of a zero point: {even, odd} nibble positions
+// nibbles at bits 4..7 of each half: (1024 + 16 q) / 16 - (64 + zp) = q - zp
+__device__ __forceinline__ half2_t nibble_pair_hi(uint32_t w, uint32_t mask, uint32_t magic, uint32_t zo) {
+    const uint32_t m = (w & mask) | magic;
+    const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    return __builtin_elementwise_fma(__builtin_bit_cast(half2_t, m), sixteenth, __builtin_bit_cast(half2_t, zo));
+}
+
+// f16 pairs -(1024 + zp) and -(64 + zp)
 __device__ __forceinline__ void zero_point_pairs(uint32_t zp, uint32_t& ze, uint32_t& zo) {
-    const uint32_t he = 0xE400u | zp, ho = 0xE400u | (zp << 4);   // f16 -(1024 + zp), -(1024 + 16 zp)
+    const uint32_t he = 0xE400u | zp, ho = 0xD400u | (zp << 4);
     ze = he | (he << 16);
     zo = ho | (ho << 16);
 }
@@ -114,9 +120,9 @@ __device__ __forceinline__ float dot_words(const uint32_t (&w)[NW], const float*
     for (int d = 0; d < NW; d++) {
         const uint32_t w8 = w[d] >> 8;
         const half2_t p0 = nibble_pair(w[d], k.lo, k.magic, ze);   // values 8d + 0, 8d + 4
-        const half2_t p1 = nibble_pair(w[d], k.hi, k.magic, zo);   // 8d + 1, 8d + 5 (times 16)
+        const half2_t p1 = nibble_pair_hi(w[d], k.hi, k.magic, zo);   // 8d + 1, 8d + 5
         const half2_t p2 = nibble_pair(w8, k.lo, k.magic, ze);     // 8d + 2, 8d + 6
-        const half2_t p3 = nibble_pair(w8, k.hi, k.magic, zo);     // 8d + 3, 8d + 7 (times 16)
+        const half2_t p3 = nibble_pair_hi(w8, k.hi, k.magic, zo);     // 8d + 3, 8d + 7
         de = fmaf(av[8 * d + 0], (float)p0[0], de);
         dd = fmaf(av[8 * d + 1], (float)p1[0], dd);
         de = fmaf(av[8 * d + 2], (float)p2[0], de);
@@ -141,9 +147,9 @@ __device__ __forceinline__ void dot_words_rows(const uint32_t (&w)[NW], const fl
     for (int d = 0; d < NW; d++) {
         const uint32_t w8 = w[d] >> 8;
         const half2_t p0 = nibble_pair(w[d], k.lo, k.magic, ze);
-        const half2_t p1 = nibble_pair(w[d], k.hi, k.magic, zo);
+        const half2_t p1 = nibble_pair_hi(w[d], k.hi, k.magic, zo);
         const half2_t p2 = nibble_pair(w8, k.lo, k.magic, ze);
-        const half2_t p3 = nibble_pair(w8, k.hi, k.magic, zo);
+        const half2_t p3 = nibble_pair_hi(w8, k.hi, k.magic, zo);
         const float q[8] = {(float)p0[0], (float)p1[0], (float)p2[0], (float)p3[0],
                             (float)p0[1], (float)p1[1], (float)p2[1], (float)p3[1]};
 #pragma unroll
@@ -373,7 +379,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
         asm volatile("s_barrier" : : : "memory");
     }
     const NibbleMasks nk = nibble_masks();
-    // this lane's chunks of A in registers (odd k times 1/16), for each row
+    // this lane's chunks of A in registers, for each row
     float av[MR * J][CK];
 #pragma unroll
     for (int mj = 0; mj < MR * J; mj++) {          // [chunk j][row m]
@@ -398,8 +404,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
 #pragma unroll
             for (int i = 0; i < CK; i++) av[mj][i] = 0.f;
         }
-#pragma unroll
-        for (int i = 1; i < CK; i += 2) av[mj][i] *= 0.0625f;
     }
 
     // Two register stages used alternately (copying a stage would make the
