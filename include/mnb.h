@@ -139,10 +139,12 @@ int mnb_pack(const mnb_desc* d, const uint8_t* q_nk, const uint8_t* zp_nb,
  *   zp_packed   packed zero points or NULL (iff !has_zero_points).
  *   bias        float32 [N] or NULL.
  *   y           [1][N] act_dtype, aligned to its element size.
- * M must be 1 (MNB_E_ARG otherwise).  For a given (K, block_size) the
- * float32 summation order of a column does not depend on N or on the
- * column's position, so a launch over concatenated weights (fused QKV,
- * gate||up) is bit-identical to separate launches. */
+ * M must be 1 (MNB_E_ARG otherwise).  Each product is a * (q - zp) with the
+ * exact integer q - zp, so weights equal to their zero points contribute
+ * exactly nothing.  For a given (K, block_size) the float32 summation order
+ * of a column does not depend on N or on the column's position, so a launch
+ * over concatenated weights (fused QKV, gate||up) is bit-identical to
+ * separate launches. */
 int mnb_gemv(const mnb_desc* d, int64_t M, const void* a,
              const uint8_t* b_packed, const void* scales,
              const uint8_t* zp_packed, const float* bias, void* y,
