@@ -503,7 +503,7 @@ def main():
                            args.copy_calibration or 256))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+        print(f"bench.py: the library computes on exactly one GPU; --gpus {args.gpus} is not "
               "supported (the path has no multi-GPU sharding)", file=sys.stderr)
         sys.exit(2)
 

@@ -53,7 +53,7 @@
 
 int64_t oracle_n_blocks(int64_t K, int64_t bs) { return (K + bs - 1) / bs; }
 
-/* The contract this build accepts: 4-bit weights, K >= 1, N >= 1, and a
+/* The accepted contract: 4-bit weights, K >= 1, N >= 1, and a
  * block size that is a power of two from 16 to 256 (the pages use 32 and
  * 128; the public MatMulNBits schema requires a power of two >= 16). */
 int oracle_contract_ok(int64_t K, int64_t N, int64_t bits, int64_t bs) {
