@@ -259,8 +259,11 @@ int mnb_argmax(int32_t dtype, int64_t M, int64_t N, const void* x,
  *   h[i] = silu(y[i]) * y[I + i],  silu(x) = x / (1 + exp(-x)),
  * evaluated in float32 on y before any rounding, then stored in act_dtype
  * (RTNE for bfloat16).  y[i] and y[I + i] are computed exactly as mnb_gemv
- * computes those columns.  M must be 1, N even and K within the decode kernel
- * without split-K teams (MNB_E_UNSUPPORTED otherwise); h: [1][I]. */
+ * computes those columns when mnb_gemv holds at most four 32-value chunks
+ * of K per lane; where it takes five (K = 2560, for one) their float32
+ * summation orders differ, each within the same tolerance.  M must be 1,
+ * N even and K within the decode kernel without split-K teams
+ * (MNB_E_UNSUPPORTED otherwise); h: [1][I]. */
 int mnb_gemv_silu_mul(const mnb_desc* d, int64_t M, const void* a,
                       const uint8_t* b_packed, const void* scales,
                       const uint8_t* zp_packed, const float* bias, void* h,

@@ -149,7 +149,7 @@ def test_gemm_parity_sweep(orc, dt, bs):
     log(f"gemm {dt} bs={bs}: worst err/tol {worst:.3g}")
 
 
-@pytest.mark.parametrize("K,bs", [(4096, 16), (4096 + 16, 16), (14560, 32),
+@pytest.mark.parametrize("K,bs", [(5120, 16), (5120 + 16, 16), (14560, 32),
                                   (14560 + 32, 32), (12288, 128), (16384 + 100, 256)])
 def test_gemv_long_k_and_beyond_register_limit(orc, K, bs):
     """Split-K across wavefronts up to mnb_gemv_max_k; K above it is served

@@ -36,7 +36,11 @@
 namespace mnb {
 namespace {
 
-constexpr int kJMax = 4;          // chunks per lane held in registers
+constexpr int kJMax = 5;          // chunks per lane held in registers
+// The gated kernel holds two column groups (gate and up) at once: five
+// chunks each would take all 256 VGPRs (one wavefront per SIMD) and, with
+// zero points and bias, more loads per iteration than the waits can count.
+constexpr int kJGated = 4;
 constexpr int kWMax = 4;          // wavefronts per column (split-K)
 constexpr int kWavesPerBlock = 4;
 constexpr size_t kMaxLds = 64 * 1024;    // staged activations per workgroup
@@ -551,7 +555,11 @@ using GemvFn = void (*)(GemvArgs);
 
 template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J>
 GemvFn pick_j(int W, bool silu) {
-    if (silu) return W == 1 ? gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 2, 1, true> : nullptr;
+    if constexpr (J <= kJGated) {
+        if (silu) return W == 1 ? gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 2, 1, true> : nullptr;
+    } else {
+        if (silu) return nullptr;
+    }
     if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, 1>;
     if constexpr (CB == 16) {
         if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, 2>;
@@ -567,6 +575,7 @@ GemvFn pick_cb(int J, int W, bool silu) {
         case 2: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 2>(W, silu);
         case 3: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 3>(W, silu);
         case 4: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 4>(W, silu);
+        case 5: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 5>(W, silu);
         default: return nullptr;
     }
 }
@@ -690,7 +699,7 @@ int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1) {
     a.log2_bs = ilog2(p.bs);
     a.half = silu ? p.N / 2 : 0;
     a.M = (int)p.M;
-    const Geometry geo = MR == 1 ? geometry(a.S, CB == 16) : geometry(a.S, true, 4 / MR);
+    const Geometry geo = MR == 1 ? geometry(a.S, CB == 16, silu ? kJGated : kJMax) : geometry(a.S, true, 4 / MR);
     if (geo.J == 0)
         return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld beyond the register kernel", (long long)p.K);
     if (silu && geo.W != 1)
