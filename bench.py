@@ -1,25 +1,32 @@
 """Benchmark of the weight-only block-INT4 MatMul on one MI355X.
 
-Headline workload: the Qwen3-0.6B-shaped INT4 decode step (M = 1, fp32
-activations, block 32, per-block zero points): 28 layers x {fused QKV
-1024->4096, o 2048->1024, gate||up 1024->6144, down 3072->1024} + LM head
-1024->151936 = 113 launches over 381,802,496 bytes of packed weights, scales
-and zero points.  One step = that whole sequence, replayed as one captured HIP
-graph on one stream; inputs are seeded synthetic tensors already resident in
-HBM.  value = packed-weight bytes per step / step time (GB/s).
+Headline workload: the Qwen3-4B-shaped INT4 decode step (M = 1, fp32
+activations, block 128, default zero point 8): 36 layers x {fused QKV
+2560->6144, o 4096->2560, gate||up 2560->19456, down 9728->2560} + LM head
+2560->151936 = 145 launches over 2,136,832,000 bytes of packed weights and
+scales.  One step = that whole sequence, replayed as one captured HIP graph on
+one stream; inputs are seeded synthetic tensors already resident in HBM (the
+step streams 2.1 GB, more than the 256 MB last-level cache, so every step is
+cold).  value = packed-weight bytes per step / step time (GB/s).
 
-Also printed in the same JSON line (``extra``): the Qwen3-4B decode step and
-the two prefill steps (TFLOP/s), the eager (non-graph) decode step time, and
-``next_rows``: the 0.6B step with 4 rows (small-M kernel), the tied LM head
-with greedy ArgMax and the embedding gather, the QDQ import, and the fused
-gate||up SiLU GEMV against the unfused pair.
+The timed region is exactly --steps graph replays between two HIP events on
+the launch stream, bracketed by device synchronizations; a second pass of at
+least 60 replays, each between its own pair of events, gives the p50 / min /
+max and the raw samples.  The same protocol times the other workloads in
+``extra``: the Qwen3-4B prefill step (2048 bf16 rows, the MFMA bar) with its
+own roofline block, the Qwen3-0.6B decode and prefill steps, the single
+1024->3072 GEMV cold (rotating over 512 copies, 1 GB) and hot, the plain
+streaming read of 1 GB (achievable HBM, the control arm), and ``next_rows``:
+small M (4, 8, 16 rows), the tied LM head with greedy ArgMax and the
+embedding gather, the QDQ import, and the fused gate||up SiLU GEMV against the
+unfused pair.
 
-roofline: the only kernel of the headline step is the decode GEMV; its
+roofline: every launch of the headline step is the decode GEMV; its
 algorithmic bytes per launch (packed weights + scales + zero points, averaged
 over the step's launches) are divided by its average launch duration, the
-event-timed step time (HIP events on the launch stream around the timed graph
-replays) over the number of launches.  cpu_baseline: the CPU oracle timed on
-the host cores on a bounded sample of the same step.
+event-timed step over the number of launches.  cpu_baseline: the CPU oracle
+(fp64, as it is) timed on the host on a bounded sample of the same step, on
+all the cores the process may use and on one core, with the CPU model.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C]
 """
@@ -29,6 +36,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -36,18 +44,32 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak, TFLOP/s
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s (datasheet)
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak, TFLOP/s (datasheet)
 METRIC = "INT4 GEMV weight GB/s (% HBM peak) at M=1; prefill TFLOP/s (% MFMA peak)"
+MIN_SAMPLES = 60
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_steps(step, steps, warmup, graph):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_runs(run, steps, warmup, samples=MIN_SAMPLES):
+    """Exactly `steps` calls of run() between two HIP events on the current
+    stream (device synchronized before and after), then `samples` calls each
+    between its own pair of events.  Returns ms per call and the samples."""
     import torch
-    run = step.replay if graph else step.run
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -59,212 +81,119 @@ def time_steps(step, steps, warmup, graph):
     e1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    return e0.elapsed_time(e1) / steps, wall
+    ms = e0.elapsed_time(e1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(samples + 1)]
+    ev[0].record()
+    for i in range(samples):
+        run()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    raw = [ev[i].elapsed_time(ev[i + 1]) for i in range(samples)]
+    return ms, wall, raw
 
 
-def cpu_baseline(cfg, budget_s):
-    """The oracle (as it is) on the host cores: the step's launches in order,
-    repeated, until the time budget is used (input generation is not timed);
-    returns a dict in the metric's unit."""
-    import oracle
-    from workloads import workload
-    from workloads.generate import projection_inputs
+def sample_stats(raw, digits=5):
+    return {"n": len(raw), "p50_ms": round(statistics.median(raw), digits),
+            "min_ms": round(min(raw), digits), "max_ms": round(max(raw), digits),
+            "raw_ms": [round(x, digits) for x in raw]}
+
+
+# ---- CPU baseline: the oracle as it stands, timed on the host ----------------
+
+def _oracle_args(w, i, rows):
     import numpy as np
     import torch
+    from workloads.generate import projection_inputs
+    inp = projection_inputs(w, i, 0, "cpu")
+    a = inp.a[:rows] if rows is not None else inp.a
+    f32 = w.act_dtype == "f32"
+    act = a.numpy() if f32 else a.view(torch.int16).numpy().view(np.uint16)
+    sc = inp.scales.numpy() if f32 else inp.scales.view(torch.int16).numpy().view(np.uint16)
+    return (act, inp.q.numpy(), None if inp.zp is None else inp.zp.numpy(), sc,
+            None if inp.bias is None else inp.bias.numpy())
+
+
+def cpu_baseline(cfg, budget_s, threads, rows=None):
+    """The oracle on `threads` host threads: the step's launches in order,
+    repeated until `budget_s` of oracle time is spent (input generation is not
+    timed).  Decode steps: full columns, every row.  Prefill steps: `rows` of
+    the M rows, the rate extrapolated to all M rows (labelled so)."""
+    import oracle
+    from workloads import workload
 
     w = workload(cfg)
     orc = oracle.get()
-    cores = len(os.sched_getaffinity(0))
+    r = w.M if rows is None else min(rows, w.M)
     done_bytes = done_flops = 0
     spent = 0.0
     calls = 0
-    first, last = None, None
-    rows = w.M if w.M == 1 else 2
+    first = last = None
     cache, cached = {}, 0
-    passes = 0
     while spent < budget_s:
         for i, L in enumerate(w.launches):
-            if i in cache:
-                args = cache[i]
-            else:
-                inp = projection_inputs(w, i, 0, "cpu")
-                a = inp.a[:rows]
-                act = (a.numpy() if w.act_dtype == "f32"
-                       else a.view(torch.int16).numpy().view(np.uint16))
-                sc = (inp.scales.numpy() if w.act_dtype == "f32"
-                      else inp.scales.view(torch.int16).numpy().view(np.uint16))
-                args = (act, inp.q.numpy(), None if inp.zp is None else inp.zp.numpy(), sc,
-                        None if inp.bias is None else inp.bias.numpy())
-                if cached + args[1].nbytes < (2 << 30):     # keep inputs for the next pass
-                    cache[i] = args
-                    cached += args[1].nbytes
+            args = cache.get(i) or _oracle_args(w, i, r)
+            if i not in cache and cached + args[1].nbytes < (2 << 30):
+                cache[i] = args
+                cached += args[1].nbytes
             t0 = time.perf_counter()
-            orc.matmul(args[0], args[1], args[2], args[3], w.block_size, bias=args[4], nthreads=cores)
+            orc.matmul(args[0], args[1], args[2], args[3], w.block_size, bias=args[4], nthreads=threads)
             spent += time.perf_counter() - t0
             done_bytes += w.weight_bytes(L)
-            done_flops += 2 * rows * L.K * L.N
+            done_flops += 2 * r * L.K * L.N
             calls += 1
             first = first or L.name
             last = L.name
             if spent >= budget_s:
                 break
-        passes += 1
     n = len(w.launches)
     what = f"{calls} launches ({calls / n:.2f} passes over the step's {n}, {first}..{last})"
     if w.M == 1:
-        val, unit = done_bytes / spent / 1e9, "GB/s"
-        sample = f"{what}, full columns, M=1"
-    else:
-        val, unit = done_flops / spent / 1e12, "TFLOP/s"
-        sample = f"{what}, {rows} of {w.M} rows"
-    return {"value": val, "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": sample, "seconds": round(spent, 2)}
+        return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": f"{what}, full columns, M=1", "seconds": round(spent, 2)}
+    return {"value": done_flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}, {r} of {w.M} rows, full columns; rate extrapolated to all {w.M} rows "
+                      f"(the oracle's cost is linear in rows)", "extrapolated": True,
+            "seconds": round(spent, 2)}
 
 
-def measure_config(cfg, steps, warmup, graph=True):
-    from workloads import workload
-    return measure_config_w(workload(cfg), steps, warmup, graph)
+def cpu_baselines(cfg, budget_s, rows=None):
+    """All cores the process may use, and one core; with the CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    log(f"[bench] cpu baseline config {cfg}: oracle on {cores} threads, then 1")
+    allc = cpu_baseline(cfg, budget_s, cores, rows)
+    one = cpu_baseline(cfg, budget_s, 1, rows)
+    allc["one_core"] = {k: one[k] for k in ("value", "unit", "sample", "seconds")}
+    allc["cpu_model"] = cpu_model()
+    allc["host_cpus_visible"] = os.cpu_count()
+    return allc
 
 
-def measure_config_w(w, steps, warmup, graph=True):
+# ---- GPU measurements -------------------------------------------------------
+
+def measure_step(w, steps, warmup, samples=MIN_SAMPLES):
+    """Build one step of workload w (weights packed on the GPU), capture it
+    as one graph and time its replays; for a decode step also the eager
+    (sequence driver) step.  The launch order of a traced run is: one eager
+    step, warmup + steps + samples graph replays, then (decode) warmup +
+    steps eager steps."""
     import torch
     from weight_only_int4_matmulnbits_amd.step import Step
 
-    cfg = w.cfg
-    log(f"[bench] config {cfg}: {w.title} (M={w.M}): building ({len(w.launches)} launches)")
+    log(f"[bench] {w.title} (M={w.M}): building ({len(w.launches)} launches)")
     step = Step(w, "cuda", seed=0)
     step.run()
     torch.cuda.synchronize()
-    if graph:
-        step.capture()
-    ms, wall = time_steps(step, steps, warmup, graph)
-    log(f"[bench] config {cfg}: {ms:.4f} ms/step (graph={graph})")
-    out = {"ms_per_step": ms, "wall_ms_per_step": wall, "launches": step.launches,
-           "weight_bytes": step.weight_bytes, "flops": w.step_flops(),
-           "pack_ms": step.pack_seconds * 1e3}
+    step.capture()
+    ms, wall, raw = time_runs(step.replay, steps, warmup, samples)
+    log(f"[bench] {w.title}: {ms:.4f} ms/step graph-replayed (p50 {statistics.median(raw):.4f})")
+    out = {"ms_per_step": ms, "wall_ms_per_step": wall, "samples": sample_stats(raw),
+           "launches": step.launches, "weight_bytes": step.weight_bytes, "flops": w.step_flops(),
+           "pack_ms": step.pack_seconds * 1e3, "workspace_bytes": step.sequence.workspace_bytes}
     if w.M == 1:
-        ms_eager, _ = time_steps(step, steps, warmup, False)
-        out["eager_ms_per_step"] = ms_eager
+        ms_e, _, _ = time_runs(step.run, steps, warmup, 0)
+        out["eager_ms_per_step"] = ms_e
     step.close()
     del step
-    torch.cuda.empty_cache()
-    return w, out
-
-
-def graph_time_us(fn, steps, warmup, reps=20):
-    """Average device time of one fn() call: reps calls captured back to back
-    in one graph (a graph of one short kernel is bound by the host's launch
-    rate), replayed; HIP events on the replay stream."""
-    import torch
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        fn()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    # capture on the warm-up stream: the library's per-stream workspace (used
-    # by the argmax partials) exists there, and is not allocated in a capture
-    with torch.cuda.graph(g, stream=s):
-        for _ in range(reps):
-            fn()
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (steps * reps)
-
-
-def measure_next_rows(steps, warmup):
-    """One measurement per row beyond the decode / prefill step: the small-M
-    step (a speculative block of 4 rows), the LM head with greedy ArgMax and
-    the tied-embedding gather, the QDQ import, and the fused gate||up SiLU
-    GEMV against its unfused pair."""
-    import torch
-    import weight_only_int4_matmulnbits_amd as mnb
-    from workloads import workload
-    from workloads.generate import random_inputs
-
-    out = {}
-    # f1: the 0.6B decode step with 4 rows per projection
-    w4 = workload(2, M=4)
-    _, r = measure_config_w(w4, steps, warmup)
-    out["small_m"] = {"workload": "Qwen3-0.6B-shaped INT4 step, 4 rows (speculative block)",
-                      "M": 4, "ms_per_step": r["ms_per_step"], "launches": r["launches"],
-                      "weight_GBps": r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9,
-                      "hbm_frac": r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                      "rows_per_s": 4 / (r["ms_per_step"] * 1e-3)}
-    # f2: LM head (tied weight, N = vocabulary) + greedy token, and the gather
-    K, N, bs = 1024, 151936, 32
-    g = random_inputs(K, N, 1, bs, "f32", True, False, seed=1).to("cuda")
-    pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, block_size=bs)
-    logits = torch.empty(1, N, device="cuda")
-    tok = torch.empty(1, dtype=torch.int64, device="cuda")
-    ids1 = torch.tensor([151935], device="cuda")
-    ids512 = torch.randint(0, N, (512,), device="cuda", generator=torch.Generator("cuda").manual_seed(2))
-    rows1 = torch.empty(1, K, device="cuda")
-    rows512 = torch.empty(512, K, device="cuda")
-    t_lm = graph_time_us(lambda: pw.matmul(g.a, out=logits), steps, warmup)
-    t_lm_arg = graph_time_us(lambda: (pw.matmul(g.a, out=logits), mnb.argmax(logits, out=tok)),
-                             steps, warmup)
-    t_g1 = graph_time_us(lambda: mnb.gather_rows(ids1, pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N,
-                                                 block_size=bs, out=rows1), steps, warmup)
-    t_g512 = graph_time_us(lambda: mnb.gather_rows(ids512, pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N,
-                                                   block_size=bs, out=rows512), steps, warmup)
-    row_read = K // 2 + (K // bs) * 4 + (K // bs + 1) // 2
-    out["lm_head_argmax"] = {
-        "workload": "Qwen3-0.6B tied LM head 1024->151936 (fp32, block 32, zero points) + greedy ArgMax",
-        "lm_head_us": t_lm, "lm_head_GBps": pw.weight_bytes / (t_lm * 1e-6) / 1e9,
-        "lm_head_plus_argmax_us": t_lm_arg, "argmax_added_us": t_lm_arg - t_lm}
-    out["embedding_gather"] = {
-        "workload": "rows of the same packed tied weight, fp32 out",
-        "rows_1_us": t_g1, "rows_512_us": t_g512,
-        "rows_512_GBps": 512 * (row_read + 4 * K) / (t_g512 * 1e-6) / 1e9}
-    del pw, logits, rows512
-    # f3: QDQ import of the 4B gate||up weight (axis 0 -> N-major)
-    K, N, bs = 2560, 19456, 128
-    gen = torch.Generator("cuda").manual_seed(3)
-    w_q = torch.randint(0, 256, (K * N // 2,), dtype=torch.uint8, device="cuda", generator=gen)
-    z_q = torch.randint(0, 256, ((K // bs) * N // 2,), dtype=torch.uint8, device="cuda", generator=gen)
-    s_q = torch.rand((K // bs) * N, device="cuda", generator=gen).to(torch.bfloat16)
-    mnb.import_qdq(w_q, s_q, z_q, K=K, N=N, block_size=bs, axis=0)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        mnb.import_qdq(w_q, s_q, z_q, K=K, N=N, block_size=bs, axis=0)
-    e1.record()
-    torch.cuda.synchronize()
-    t_imp = e0.elapsed_time(e1) * 1e3 / 5
-    moved = 2 * (w_q.numel() + z_q.numel() + 2 * s_q.numel())
-    out["qdq_import"] = {"workload": "Qwen3-4B gate||up 2560x19456 QDQ (axis 0, block 128) -> MatMulNBits",
-                         "us": t_imp, "GBps_read_plus_written": moved / (t_imp * 1e-6) / 1e9,
-                         "tied_lm_head_copy_avoided": mnb.qdq_is_native(1024, 151936, 32, axis=1)}
-    del w_q, z_q, s_q
-    # f4: gate||up with silu(gate) * up fused, against the unfused pair
-    fused = {}
-    for name, K, I, bs, dt in (("0.6B", 1024, 3072, 32, "f32"), ("4B", 2560, 9728, 128, "bf16")):
-        g = random_inputs(K, 2 * I, 1, bs, dt, name == "0.6B", False, seed=4).to("cuda")
-        pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, block_size=bs)
-        y = torch.empty(1, 2 * I, dtype=g.a.dtype, device="cuda")
-        h = torch.empty(1, I, dtype=g.a.dtype, device="cuda")
-
-        def unfused():
-            pw.matmul(g.a, out=y)
-            torch.mul(torch.nn.functional.silu(y[:, :I]), y[:, I:], out=h)
-
-        t_u = graph_time_us(unfused, steps, warmup)
-        t_f = graph_time_us(lambda: mnb.gemv_silu_mul(g.a, pw.b_packed, pw.scales, pw.zp_packed, K=K,
-                                                      N=2 * I, block_size=bs, out=h), steps, warmup)
-        fused[name] = {"K": K, "I": I, "unfused_us": t_u, "fused_us": t_f,
-                       "fused_GBps": pw.weight_bytes / (t_f * 1e-6) / 1e9}
-        del pw, y, h, g
-    out["gate_up_silu"] = fused
     torch.cuda.empty_cache()
     return out
 
@@ -290,11 +219,11 @@ def measured_traffic(cfg, kind):
 
 
 def roofline_for(w, r):
-    """The step is nothing but launches of one kernel (the decode GEMV, or the
-    prefill GEMM), so its average launch duration is the event-timed step time
-    over the launches of the step; this includes the gaps between launches
-    inside the replayed graph, which rocprofv3's kernel trace of the same
-    command shows to be small."""
+    """Decode: every launch of the step is the decode GEMV, so its average
+    launch duration is the event-timed step over the step's launches, and
+    its algorithmic bytes per launch are the step's weight bytes over the
+    same count.  Prefill: the same with 2*M*K*N flop, a launch being one
+    projection (the GEMM and, where K is split, its reduction)."""
     avg_s = r["ms_per_step"] * 1e-3 / r["launches"]
     if w.M == 1:
         per_launch = r["weight_bytes"] / r["launches"]
@@ -302,21 +231,21 @@ def roofline_for(w, r):
         return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.cfg, "gemv"),
                 "kernel": "gemv_kernel (every launch of the step)",
-                "algorithmic_bytes_per_launch": per_launch,
-                "avg_launch_us": avg_s * 1e6}
+                "algorithmic_bytes_per_launch": per_launch, "avg_launch_us": avg_s * 1e6}
     per_launch = r["flops"] / r["launches"]
     achieved = per_launch / avg_s / 1e12
     return {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
             "traffic": measured_traffic(w.cfg, "gemm"),
-            "kernel": "gemm_kernel (every launch of the step)",
-            "algorithmic_flops_per_launch": per_launch,
-            "avg_launch_us": avg_s * 1e6}
+            "kernel": ("gemm_bf16_wide_kernel + split-K/tail reductions (every projection of the step)"
+                       if w.act_dtype == "bf16" else
+                       "gemm_f32_int_kernel + split-K reductions (every projection of the step)"),
+            "algorithmic_flops_per_launch": per_launch, "avg_launch_us": avg_s * 1e6}
 
 
-def summary(w, r):
-    s = {"workload": w.title, "ms_per_step": round(r["ms_per_step"], 5),
-         "launches": r["launches"]}
+def summary(w, r, with_samples=True):
+    s = {"workload": w.title, "config_index": w.cfg, "M": w.M, "ms_per_step": round(r["ms_per_step"], 5),
+         "launches": r["launches"], "workspace_bytes": r["workspace_bytes"]}
     if w.M == 1:
         s["weight_GBps"] = r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
         s["hbm_frac"] = s["weight_GBps"] / HBM_PEAK_GBS
@@ -325,7 +254,198 @@ def summary(w, r):
         s["TFLOPs"] = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
         s["mfma_frac"] = s["TFLOPs"] / BF16_PEAK_TFLOPS
     s["avg_launch_us"] = r["ms_per_step"] * 1e3 / r["launches"]
+    if with_samples:
+        s["samples"] = r["samples"]
+    s["roofline"] = roofline_for(w, r)
     return s
+
+
+def probe_lib():
+    import ctypes
+    import torch  # noqa: F401  -- the HIP runtime torch loaded comes first
+    path = os.path.join(ROOT, "weight_only_int4_matmulnbits_amd", "libmnb_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build first")
+    L = ctypes.CDLL(path)
+    L.mnb_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    L.mnb_probe_stream_read.restype = ctypes.c_int
+    return L
+
+
+def measure_control_read(steps, warmup, nbytes=1 << 30):
+    """Achievable HBM: a plain 16-byte non-temporal streaming read of 1 GiB
+    (libmnb_probe), the same protocol as the steps."""
+    import ctypes
+    import torch
+    L = probe_lib()
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run():
+        rc = L.mnb_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), st)
+        if rc != 0:
+            raise RuntimeError(f"probe read failed: {rc}")
+
+    ms, _, raw = time_runs(run, steps, warmup)
+    del buf, sink
+    torch.cuda.empty_cache()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "plain streaming read of 1 GiB, 16-byte non-temporal loads (libmnb_probe)",
+            "bytes": nbytes, "ms": ms, "GBps": gbs, "frac_of_datasheet_peak": gbs / HBM_PEAK_GBS,
+            "samples": {k: v for k, v in sample_stats(raw).items() if k != "raw_ms"}}
+
+
+def measure_config1(steps, warmup, copies=512):
+    """The single 1024->3072 GEMV: cold, one graph of `copies` launches each
+    on its own copy of the weights (1 GB in all, more than the last-level
+    cache), and hot, the same launches on one copy."""
+    import torch
+    import weight_only_int4_matmulnbits_amd as mnb
+    from workloads import workload
+    from workloads.generate import projection_inputs
+
+    w = workload(1)
+    inp = projection_inputs(w, 0, 0, "cuda")
+    pw = mnb.PackedWeight.from_logical(inp.q, inp.scales, inp.zp, inp.bias, block_size=w.block_size)
+    y = torch.empty(1, 3072, device="cuda")
+    cold = [mnb.PackedWeight(pw.K, pw.N, pw.block_size, pw.act_dtype, pw.b_packed.clone(), pw.scales.clone())
+            for _ in range(copies)]
+    out = {"workload": f"{w.title} (fp32, block 32, default zero point)", "weight_bytes": pw.weight_bytes}
+    for name, ws in (("cold", cold), ("hot", [pw] * copies)):
+        seq = mnb.Sequence([(x, inp.a, y) for x in ws])
+        seq.capture()
+        ms, _, raw = time_runs(seq.replay, max(3, steps // 10), max(2, warmup // 2), 10)
+        us = ms * 1e3 / copies
+        out[name] = {"us_per_launch": us, "GBps": pw.weight_bytes / (us * 1e-6) / 1e9,
+                     "launches_per_graph": copies,
+                     "copies": len({id(x) for x in ws}),
+                     "p50_us_per_launch": statistics.median(raw) * 1e3 / copies}
+        seq.close()
+    out["hbm_frac_cold"] = out["cold"]["GBps"] / HBM_PEAK_GBS
+    del cold, pw
+    torch.cuda.empty_cache()
+    return out
+
+
+def graph_time_us(fn, steps, warmup, reps=20):
+    """Average device time of one fn() call: reps calls captured back to back
+    in one graph (a graph of one short kernel is bound by the host's launch
+    rate), replayed; HIP events on the replay stream."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(reps):
+            fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (steps * reps)
+
+
+def measure_next_rows(steps, warmup):
+    """One measurement per row beyond the decode / prefill step: the small-M
+    steps (speculative blocks of 4, 8 and 16 rows), the LM head with greedy
+    ArgMax and the tied-embedding gather, the QDQ import, and the fused
+    gate||up SiLU GEMV against its unfused pair."""
+    import torch
+    import weight_only_int4_matmulnbits_amd as mnb
+    from workloads import workload
+    from workloads.generate import random_inputs
+
+    out = {}
+    # f1: the 0.6B decode step with 4, 8 and 16 rows per projection
+    sm = {}
+    for M in (4, 8, 16):
+        wm = workload(2, M=M)
+        r = measure_step(wm, steps, warmup, 20)
+        gbs = r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+        sm[f"M{M}"] = {"workload": f"Qwen3-0.6B-shaped INT4 step, {M} rows (speculative block)",
+                       "ms_per_step": r["ms_per_step"], "p50_ms": r["samples"]["p50_ms"],
+                       "launches": r["launches"], "weight_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                       "rows_per_s": M / (r["ms_per_step"] * 1e-3)}
+    out["small_m"] = sm
+    # f2: LM head (tied weight, N = vocabulary) + greedy token, and the gather
+    K, N, bs = 1024, 151936, 32
+    g = random_inputs(K, N, 1, bs, "f32", True, False, seed=1).to("cuda")
+    pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, block_size=bs)
+    logits = torch.empty(1, N, device="cuda")
+    tok = torch.empty(1, dtype=torch.int64, device="cuda")
+    aws = mnb.workspace(mnb.argmax_workspace_bytes(1, N))
+    ids1 = torch.tensor([151935], device="cuda")
+    ids512 = torch.randint(0, N, (512,), device="cuda", generator=torch.Generator("cuda").manual_seed(2))
+    rows1 = torch.empty(1, K, device="cuda")
+    rows512 = torch.empty(512, K, device="cuda")
+    t_lm = graph_time_us(lambda: pw.matmul(g.a, out=logits), steps, warmup)
+    t_lm_arg = graph_time_us(lambda: (pw.matmul(g.a, out=logits), mnb.argmax(logits, out=tok, workspace=aws)),
+                             steps, warmup)
+    t_g1 = graph_time_us(lambda: mnb.gather_rows(ids1, pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N,
+                                                 block_size=bs, out=rows1), steps, warmup)
+    t_g512 = graph_time_us(lambda: mnb.gather_rows(ids512, pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N,
+                                                   block_size=bs, out=rows512), steps, warmup)
+    row_read = K // 2 + (K // bs) * 4 + (K // bs + 1) // 2
+    out["lm_head_argmax"] = {
+        "workload": "Qwen3-0.6B tied LM head 1024->151936 (fp32, block 32, zero points) + greedy ArgMax",
+        "lm_head_us": t_lm, "lm_head_GBps": pw.weight_bytes / (t_lm * 1e-6) / 1e9,
+        "lm_head_plus_argmax_us": t_lm_arg, "argmax_added_us": t_lm_arg - t_lm}
+    out["embedding_gather"] = {
+        "workload": "rows of the same packed tied weight, fp32 out",
+        "rows_1_us": t_g1, "rows_512_us": t_g512,
+        "rows_512_GBps": 512 * (row_read + 4 * K) / (t_g512 * 1e-6) / 1e9}
+    del pw, logits, rows512, aws
+    # f3: QDQ import of the 4B gate||up weight (axis 0 -> N-major)
+    K, N, bs = 2560, 19456, 128
+    gen = torch.Generator("cuda").manual_seed(3)
+    w_q = torch.randint(0, 256, (K * N // 2,), dtype=torch.uint8, device="cuda", generator=gen)
+    z_q = torch.randint(0, 256, ((K // bs) * N // 2,), dtype=torch.uint8, device="cuda", generator=gen)
+    s_q = torch.rand((K // bs) * N, device="cuda", generator=gen).to(torch.bfloat16)
+    mnb.import_qdq(w_q, s_q, z_q, K=K, N=N, block_size=bs, axis=0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        mnb.import_qdq(w_q, s_q, z_q, K=K, N=N, block_size=bs, axis=0)
+    e1.record()
+    torch.cuda.synchronize()
+    t_imp = e0.elapsed_time(e1) * 1e3 / 5
+    moved = 2 * (w_q.numel() + z_q.numel() + 2 * s_q.numel())
+    out["qdq_import"] = {"workload": "Qwen3-4B gate||up 2560x19456 QDQ (axis 0, block 128) -> MatMulNBits",
+                         "us": t_imp, "GBps_read_plus_written": moved / (t_imp * 1e-6) / 1e9,
+                         "tied_lm_head_copy_avoided": mnb.qdq_is_native(1024, 151936, 32, axis=1)}
+    del w_q, z_q, s_q
+    # f4: gate||up with silu(gate) * up fused, against the unfused pair
+    fused = {}
+    for name, K, I, bs, dt in (("0.6B", 1024, 3072, 32, "f32"), ("4B", 2560, 9728, 128, "f32")):
+        g = random_inputs(K, 2 * I, 1, bs, dt, name == "0.6B", False, seed=4).to("cuda")
+        pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, block_size=bs)
+        y = torch.empty(1, 2 * I, dtype=g.a.dtype, device="cuda")
+        h = torch.empty(1, I, dtype=g.a.dtype, device="cuda")
+
+        def unfused():
+            pw.matmul(g.a, out=y)
+            torch.mul(torch.nn.functional.silu(y[:, :I]), y[:, I:], out=h)
+
+        t_u = graph_time_us(unfused, steps, warmup)
+        t_f = graph_time_us(lambda: mnb.gemv_silu_mul(g.a, pw.b_packed, pw.scales, pw.zp_packed, K=K,
+                                                      N=2 * I, block_size=bs, out=h), steps, warmup)
+        fused[name] = {"K": K, "I": I, "dtype": dt, "unfused_us": t_u, "fused_us": t_f,
+                       "fused_GBps": pw.weight_bytes / (t_f * 1e-6) / 1e9}
+        del pw, y, h, g
+    out["gate_up_silu"] = fused
+    torch.cuda.empty_cache()
+    return out
 
 
 # ---- rocprofv3 summaries (run on the CSV output of the commands in
@@ -347,10 +467,12 @@ def _short(name):
     return name.replace("void ", "")
 
 
-def summarize_trace(trace_dir, cfg, steps, warmup):
+def summarize_trace(trace_dir, cfg, steps, warmup, samples=MIN_SAMPLES, bench_json=None):
     """Per-kernel statistics and the timed graph-replayed steps of one
-    `bench.py --config cfg --steps steps --warmup warmup` run under
-    `rocprofv3 --kernel-trace --stats`."""
+    `bench.py --config cfg --steps steps --warmup warmup --samples samples
+    --no-extra` run under `rocprofv3 --kernel-trace --stats`; with the JSON
+    line that run printed, the tracer's overhead against its untraced
+    event-timed step."""
     from workloads import workload
     import statistics
     w = workload(cfg)
@@ -363,9 +485,10 @@ def summarize_trace(trace_dir, cfg, steps, warmup):
         if "mnb::" in r["Name"] and "pack_" not in r["Name"]:
             out.append(f"  {_short(r['Name']):<62} calls {int(r['Calls']):6d}  avg {float(r['AverageNs']) / 1e3:9.3f} us"
                        f"  min {float(r['MinNs']) / 1e3:8.3f}  max {float(r['MaxNs']) / 1e3:8.3f}")
-    # the run: one eager step, `warmup` + `steps` graph replays (+ the same
-    # again eagerly for a decode step); kernels per step = dispatches / steps
-    total_steps = 1 + warmup + steps + ((warmup + steps) if w.M == 1 else 0)
+    # the run (measure_step): one eager step, `warmup` + `steps` + `samples`
+    # graph replays, then for a decode step `warmup` + `steps` eager steps;
+    # kernels per step = dispatches / steps
+    total_steps = 1 + warmup + steps + samples + ((warmup + steps) if w.M == 1 else 0)
     per_step = len(rows) // total_steps
     out.append(f"library dispatches in trace: {len(rows)} ({total_steps} steps x {per_step})")
     def span_stats(rng):
@@ -387,7 +510,7 @@ def summarize_trace(trace_dir, cfg, steps, warmup):
         # ~3.7 us gaps before the others, so those durations are not a
         # kernel's own.  In the eager steps every kernel runs alone (host
         # launch gaps of several us), which gives its duration undisturbed.
-        e_timed = range(1 + 2 * warmup + steps, 1 + 2 * warmup + 2 * steps)
+        e_timed = range(1 + 2 * warmup + steps + samples, 1 + 2 * warmup + 2 * steps + samples)
         e_sum, e_span, e_avg = span_stats(e_timed)
         out.append(f"timed eager steps: median sum of kernel durations {e_sum / 1e3:.1f} us "
                    f"(first-start to last-end {e_span / 1e3:.1f} us, host launch gaps included)")
@@ -419,6 +542,14 @@ def summarize_trace(trace_dir, cfg, steps, warmup):
             fl = v[0][2]
             out.append(f"  {nm:<8} GEMM {g:9.1f} us ({fl / (g * 1e-6) / 1e12:7.1f} TFLOP/s)  reduction {r:6.1f} us")
         out.append(f"average launch (GEMM + reduction) {s_sum / 1e3 / n:.3f} us over {n} launches per step")
+    if bench_json:
+        with open(bench_json) as f:
+            rec = json.loads([l for l in f if l.startswith("{")][-1])
+        un = rec["ms_per_step"] * 1e3
+        out.append(f"same run, untraced event timing (bench JSON): {un:.1f} us per graph-replayed step; "
+                   f"traced median sum of kernel durations {s_sum / 1e3:.1f} us "
+                   f"({'within' if s_sum / 1e3 <= un else 'above'} it: tracer overhead "
+                   f"{max(0.0, s_sum / 1e3 - un):.1f} us per step, {100 * (s_sum / 1e3 / un - 1):+.1f} %)")
     return "\n".join(out)
 
 
@@ -442,9 +573,17 @@ def traffic_from(fetch_dir, write_dir, cfg, copy_mib, kind="gemv"):
                      f"{len(lib)} dispatches, {sum(lib) / len(lib):.1f} KiB raw -> {per / 1e6:.4f} MB per dispatch")
     from workloads import workload
     w = workload(cfg)
-    alg = w.step_weight_bytes() / len(w.launches)
     tot = res["FETCH_SIZE"][0] + res["WRITE_SIZE"][0]
-    lines.append(f"HBM traffic per launch {tot / 1e6:.4f} MB vs algorithmic {alg / 1e6:.4f} MB ({tot / alg:.3f}x)")
+    if w.M == 1:
+        alg = w.step_weight_bytes() / len(w.launches)
+        lines.append(f"HBM traffic per launch {tot / 1e6:.4f} MB vs algorithmic {alg / 1e6:.4f} MB "
+                     f"({tot / alg:.3f}x)")
+    else:
+        # a prefill projection must read A and the packed weight once and write Y once
+        esz = 4 if w.act_dtype == "f32" else 2
+        alg = sum(w.weight_bytes(L) + esz * w.M * (L.K + L.N) for L in w.launches) / len(w.launches)
+        lines.append(f"HBM traffic per dispatch {tot / 1e6:.4f} MB; per projection the minimum "
+                     f"(A + packed weight read once, Y written once) averages {alg / 1e6:.4f} MB")
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -452,6 +591,8 @@ def traffic_from(fetch_dir, write_dir, cfg, copy_mib, kind="gemv"):
     except (OSError, ValueError):
         rec = {}
     srcs = {"gemv": ["weight_only_int4_matmulnbits_amd/csrc/mnb_gemv.hip",
+                     "weight_only_int4_matmulnbits_amd/csrc/mnb_internal.h"],
+            "gemm": ["weight_only_int4_matmulnbits_amd/csrc/mnb_gemm.hip",
                      "weight_only_int4_matmulnbits_amd/csrc/mnb_internal.h"]}[kind]
     h = hashlib.sha256()
     for src in srcs:
@@ -478,33 +619,43 @@ def traffic_from(fetch_dir, write_dir, cfg, copy_mib, kind="gemv"):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--samples", type=int, default=MIN_SAMPLES,
+                    help="individually timed replays for p50/min/max (at least 60 by default)")
     ap.add_argument("--no-extra", action="store_true", help="headline config only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=6.0,
+                    help="seconds of oracle time per policy (all cores, one core) for the headline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one plain device-to-device copy of MIB MiB, the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print the summary of a rocprofv3 --kernel-trace --stats run of this "
-                         "bench (same --config/--steps/--warmup) and exit; no GPU is used")
+                         "bench (same --config/--steps/--warmup/--samples) and exit; no GPU is used")
+    ap.add_argument("--bench-json", metavar="FILE",
+                    help="with --summarize-trace: the JSON line the traced run printed, to state "
+                         "the tracer's overhead against the same run's untraced timing")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="derive HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
                          "runs of this bench (same --config, --copy-calibration), update "
                          "profiles/traffic.json and exit; no GPU is used")
     args = ap.parse_args()
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace, args.config, args.steps, args.warmup))
+        print(summarize_trace(args.summarize_trace, args.config, args.steps, args.warmup, args.samples,
+                              args.bench_json))
         return
     if args.traffic_from:
+        from workloads import workload
+        kind = "gemv" if workload(args.config).M == 1 else "gemm"
         print(traffic_from(args.traffic_from[0], args.traffic_from[1], args.config,
-                           args.copy_calibration or 256))
+                           args.copy_calibration or 256, kind))
         return
     if args.gpus != 1:
-        print(f"bench.py: the library computes on exactly one GPU; --gpus {args.gpus} is not "
-              "supported (the path has no multi-GPU sharding)", file=sys.stderr)
+        print(f"bench.py: this build computes on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (the path has no multi-GPU sharding: every box here has one GPU)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -512,6 +663,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    from workloads import workload
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -523,7 +675,8 @@ def main():
         log(f"[bench] copy calibration: {n} bytes read, {n} bytes written")
         del src, dst
 
-    w, r = measure_config(args.config, args.steps, args.warmup)
+    w = workload(args.config)
+    r = measure_step(w, args.steps, args.warmup, args.samples)
     dec = w.M == 1
     value = (r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 if dec
              else r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12)
@@ -545,23 +698,33 @@ def main():
                    "projections": w.n_projections, "weight_bytes": r["weight_bytes"],
                    "flops": r["flops"], "graph_replay": True},
         "roofline": roofline_for(w, r),
+        "samples": r["samples"],
+        "wall_ms_per_step": r["wall_ms_per_step"],
+        "pack_ms": r["pack_ms"],
     }
-    line["pack_ms"] = r["pack_ms"]
     if dec:
         line["eager_ms_per_step"] = r["eager_ms_per_step"]
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baselines(args.config, args.cpu_budget, rows=None if dec else 2)
     if not args.no_extra:
         extra = {}
-        for c in (4, 3, 5):
+        for c in (5, 3, 2):
             if c == args.config:
                 continue
-            st = max(3, args.steps // (10 if c == 5 else 2))
-            wc, rc = measure_config(c, st, max(2, args.warmup // 2))
+            wc = workload(c)
+            rc = measure_step(wc, args.steps, args.warmup, args.samples)
             extra[f"config{c}"] = summary(wc, rc)
+            if c in (5, 3) and not args.no_cpu_baseline:
+                extra[f"config{c}"]["cpu_baseline"] = cpu_baselines(c, 3.0, rows=2)
+        log("[bench] config 1 (cold and hot), the 1 GiB streaming-read control arm")
+        extra["config1"] = measure_config1(args.steps, args.warmup)
+        extra["control_read"] = measure_control_read(args.steps, args.warmup)
+        ach = extra["control_read"]["GBps"]
+        line["roofline"]["achievable_GBps_control"] = ach if dec else None
+        if dec:
+            line["roofline"]["frac_of_achievable"] = line["roofline"]["achieved"] / ach
         log("[bench] next rows: small M, LM head + argmax, gather, QDQ import, gated gate||up")
-        extra["next_rows"] = measure_next_rows(max(5, args.steps // 5), max(2, args.warmup // 2))
+        extra["next_rows"] = measure_next_rows(max(10, args.steps // 3), max(2, args.warmup // 2))
         line["extra"] = extra
     print(json.dumps(line), flush=True)
 

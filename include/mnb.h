@@ -23,17 +23,25 @@
  * ---------------------------------------
  * Memory.   Every tensor argument is a DEVICE pointer (memory of the current
  *           HIP device), row-major and contiguous, allocated and owned by the
- *           caller.  The library keeps no pointer to caller memory after a
- *           call returns (graph handles, below, are the one documented
- *           exception: they record the pointers given at creation).  Its own
- *           device memory is a float32 workspace for split-K GEMMs (products
- *           whose output tiles cannot fill the GPU): one per (device, stream)
- *           for direct calls (also holding mnb_argmax's per-segment
- *           partials), grown on demand outside stream capture and
- *           kept until the process ends, and one per graph handle, freed by
- *           mnb_graph_destroy.  A product that cannot get the workspace it
- *           asks for (inside a capture the caller started, or when hipMalloc
- *           fails) runs without splitting K.
+ *           caller.  The library allocates no device memory and keeps no
+ *           pointer to caller memory after a call returns (graph handles,
+ *           below, are the one documented exception: they record the
+ *           pointers given at creation).  Products that split K across
+ *           workgroups (too few output tiles to fill the GPU) and ArgMax over
+ *           long rows keep partial results in a caller-provided WORKSPACE
+ *           ("Prepared weight-only plan": the plan captures a bounded
+ *           workspace): its size is a pure function of the shape, returned
+ *           by mnb_workspace_bytes / mnb_argmax_workspace_bytes /
+ *           mnb_sequence_workspace_bytes on the host before any HIP call;
+ *           0 means none is needed and NULL may be passed.  A workspace must
+ *           be 256-byte aligned and at least that size, else the call
+ *           returns MNB_E_ARG (MNB_E_ALIGN) and launches nothing; its
+ *           contents on entry do not matter and are undefined on return.
+ *           Calls that may overlap on the device (different streams, or a
+ *           graph replayed beside eager calls) must not share a workspace.
+ *           The choice of kernel and K split depends on the shape alone
+ *           (never on the workspace offered, the pointers, or the device's
+ *           compute-unit count), so results are a function of the inputs.
  * Ordering. Work is enqueued on `stream` (a hipStream_t passed as void*;
  *           NULL is the null stream) and the call returns once it is
  *           enqueued.  Results are valid after the stream is synchronized.
@@ -45,8 +53,9 @@
  *           output buffers are undefined.  No call aborts the process or
  *           throws across the ABI.  mnb_last_error() gives a human-readable
  *           detail of the most recent error on the calling thread.
- * Threads.  Calls are reentrant; concurrent calls on different streams are
- *           safe (each stream has its own workspace).
+ * Threads.  The library holds no mutable global state: calls are
+ *           reentrant, and concurrent calls on different streams are safe
+ *           when they do not share output buffers or a workspace.
  *
  * Data layouts (N-major: every column of B is one contiguous run of bytes)
  * ------------------------------------------------------------------------
@@ -116,7 +125,7 @@ size_t mnb_zero_point_bytes(const mnb_desc* d);
 
 /* Largest K that mnb_gemv serves with its register-resident decode kernel
  * for this descriptor's block size; larger K is served, with the same
- * results contract, by the tiled prefill kernel at M = 1. */
+ * results contract, by mnb_gemm at M = 1 (the tiled prefill kernel). */
 int64_t mnb_gemv_max_k(const mnb_desc* d);
 
 /* mnb_pack -- the preparation step ("Prepared weight-only plan": packed
@@ -139,7 +148,9 @@ int mnb_pack(const mnb_desc* d, const uint8_t* q_nk, const uint8_t* zp_nb,
  *   zp_packed   packed zero points or NULL (iff !has_zero_points).
  *   bias        float32 [N] or NULL.
  *   y           [1][N] act_dtype, aligned to its element size.
- * M must be 1 (MNB_E_ARG otherwise).  Each product is a * (q - zp) with the
+ * M must be 1 (MNB_E_ARG otherwise) and K at most mnb_gemv_max_k
+ * (MNB_E_UNSUPPORTED otherwise; mnb_gemm serves any K).  No workspace.
+ * Each product is a * (q - zp) with the
  * exact integer q - zp, so weights equal to their zero points contribute
  * exactly nothing.  For a given (K, block_size) the float32 summation order
  * of a column does not depend on N or on the column's position, so a launch
@@ -150,33 +161,41 @@ int mnb_gemv(const mnb_desc* d, int64_t M, const void* a,
              const uint8_t* zp_packed, const float* bias, void* y,
              void* stream);
 
+/* Bytes of workspace mnb_gemm needs for this descriptor and M (0: none;
+ * 0 also for an invalid descriptor or M).  Host-only, no HIP call; a
+ * function of the shape alone. */
+size_t mnb_workspace_bytes(const mnb_desc* d, int64_t M);
+
 /* mnb_gemm -- prefill, any M >= 1 ("int4_gemm": activation panels and
  * weight blocks reused on chip).  Same arguments as mnb_gemv with A [M][K]
- * and Y [M][N]; `a` and `b_packed` 16-byte aligned.  Products run on the
- * bf16 matrix cores with float32 accumulation.  bfloat16 activations meet
- * weight tiles unpacked on chip to bf16((q - zp) * s) (one rounding of the
- * exact weight, the bits mnb_dequant's bf16 output gives).  float32
- * activations are split into two bfloat16 terms (hi + lo) and meet the exact
- * bfloat16 integers (q - zp); the float32 per-block scale is applied to the
- * float32 partial sums, so results stay within float32 tolerance.  Products
- * with too few output tiles to fill the GPU split K across workgroups (see
- * Memory above); the float32 partials are added in a fixed order.
+ * and Y [M][N]; `a` and `b_packed` 16-byte aligned (bfloat16 scales of
+ * 16-value blocks 4-byte aligned), plus the workspace: at least
+ * mnb_workspace_bytes(d, M) bytes, 256-byte aligned (NULL when that is 0).
+ * Products run on the bf16 matrix cores with float32 accumulation.
+ * bfloat16 activations meet weight tiles unpacked on chip to
+ * bf16((q - zp) * s) (one rounding of the exact weight, the bits
+ * mnb_dequant's bf16 output gives).  float32 activations are split into two
+ * bfloat16 terms (hi + lo) and meet the exact bfloat16 integers (q - zp); the
+ * float32 per-block scale is applied to the float32 partial sums, so results
+ * stay within float32 tolerance.  Products with too few output tiles to fill
+ * the GPU split K across workgroups, keep the float32 partials in the
+ * workspace and add them in a fixed order.
  * Short row blocks (page "Qwen3 CPU Inference Critical Path", int4_small_m)
  * unpack every weight once for all rows, with no workspace.  2 <= M <= 4
- * (block_size >= 32, K * element size a multiple of 16, A 16-byte aligned;
- * K up to 8192 for two rows and 4096 for three or four with float32
- * activations, twice that with bfloat16) go through the decode GEMV: each
- * unpacked weight feeds one float32 FMA per row.  Otherwise 1 <= M <= 16
- * (K % 32 == 0, block_size >= 32, K up to 3072 for float32 and 4096 for
- * bfloat16 activations) take a matrix-core kernel: the exact integers
- * (q - zp) meet the activations (float32 as bf16 head + tail) and each
- * 32-value partial sum is scaled in float32.  In both, as in mnb_gemv, a
- * column's float32 summation order depends only on K (and the row count
- * class), so concatenated launches are bit-identical to separate ones. */
+ * (block_size >= 32, K * element size a multiple of 16; K up to 8192 for
+ * two rows and 4096 for three or four with float32 activations, twice that
+ * with bfloat16) go through the decode GEMV: each unpacked weight feeds one
+ * float32 FMA per row.  Otherwise 1 <= M <= 16 (K % 32 == 0,
+ * block_size >= 32, K up to 3072 for float32 and 4096 for bfloat16
+ * activations) take a matrix-core kernel: the exact integers (q - zp) meet
+ * the activations (float32 as bf16 head + tail) and each 32-value partial
+ * sum is scaled in float32.  In both, as in mnb_gemv, a column's float32
+ * summation order depends only on K (and the row count class), so
+ * concatenated launches are bit-identical to separate ones. */
 int mnb_gemm(const mnb_desc* d, int64_t M, const void* a,
              const uint8_t* b_packed, const void* scales,
              const uint8_t* zp_packed, const float* bias, void* y,
-             void* stream);
+             void* workspace, size_t workspace_bytes, void* stream);
 
 /* mnb_dequant -- test hook: writes the dequantized weights w[N][K] (the
  * transposed logical B) so they can be compared bit-for-bit.
@@ -238,16 +257,23 @@ int mnb_gather_rows(const mnb_desc* d, const int64_t* ids, int64_t n_ids,
                     const uint8_t* b_packed, const void* scales,
                     const uint8_t* zp_packed, void* out, void* stream);
 
-/* mnb_argmax -- greedy ArgMax per row (same page, "Phase Q2": final
- * RMSNorm, LM-head GEMV and greedy ArgMax): idx[m] = the first n holding the
- * largest x[m][n]; a NaN counts as larger than every number, so the first NaN
- * wins.  x: [M][N] float32 or bfloat16 (dtype, an mnb_dtype); idx: int64 [M].
- * Rows longer than 2048 values are split over up to 256 workgroups whose
- * partial maxima go to the stream's workspace (see Memory) and are then
- * reduced per row; without that workspace one workgroup takes a row.  Both
- * give the same answer (a total order on (value, index)). */
+/* Bytes of workspace mnb_argmax needs for M rows of N values (0: none, or
+ * invalid sizes).  Host-only. */
+size_t mnb_argmax_workspace_bytes(int64_t M, int64_t N);
+
+/* mnb_argmax -- greedy ArgMax per row (same page, "Phase Q5: scheduling and
+ * fusion": the final RMSNorm, LM-head GEMV and greedy ArgMax chain):
+ * idx[m] = the first n holding the largest x[m][n]; a NaN counts as larger
+ * than every number, so the first NaN wins.  x: [M][N] float32 or bfloat16
+ * (dtype, an mnb_dtype); idx: int64 [M].  Rows longer than 2048 values (and
+ * at most 65,535 rows) are split over up to 256 workgroups whose partial
+ * maxima go to the workspace (at least mnb_argmax_workspace_bytes(M, N),
+ * 256-byte aligned; NULL when that is 0) and are then reduced per row;
+ * otherwise one workgroup takes a row.  Comparisons use a total order on
+ * (value, index), so the answer does not depend on the split. */
 int mnb_argmax(int32_t dtype, int64_t M, int64_t N, const void* x,
-               int64_t* idx, void* stream);
+               int64_t* idx, void* workspace, size_t workspace_bytes,
+               void* stream);
 
 /* ---- gated MLP epilogue --------------------------------------------------------
  * mnb_gemv_silu_mul -- the fused gate||up decode projection (same page,
@@ -272,7 +298,10 @@ int mnb_gemv_silu_mul(const mnb_desc* d, int64_t M, const void* a,
 /* ---- decode-step driver ------------------------------------------------------
  * One projection of a step: mnb_gemv when M == 1 and K <= mnb_gemv_max_k,
  * mnb_gemm otherwise.  A fused QKV or gate||up projection is one entry whose
- * weights are concatenated along N. */
+ * weights are concatenated along N.  (Page "Qwen3 CPU Inference Critical
+ * Path", "Phase Q1": the plan-owned packed weights serve every token; the
+ * decode GEMV and the prefill GEMM are the two algorithms of "INT4 MatMul is
+ * first".) */
 typedef struct mnb_matmul_args {
     mnb_desc desc;
     int64_t M;
@@ -284,17 +313,26 @@ typedef struct mnb_matmul_args {
     void* y;
 } mnb_matmul_args;
 
-/* Validates every entry first (nothing is launched if one is invalid; the
- * error detail names the entry), then enqueues them in order on `stream`. */
+/* Workspace bytes a sequence needs: the largest any entry needs (its
+ * entries run in order on one stream and share it).  0 when none is needed
+ * or an entry is invalid.  Host-only. */
+size_t mnb_sequence_workspace_bytes(const mnb_matmul_args* ops, int64_t n_ops);
+
+/* Validates every entry and the workspace first (nothing is launched if one
+ * is invalid; the error detail names the entry), then enqueues them in order
+ * on `stream`. */
 int mnb_matmul_sequence(const mnb_matmul_args* ops, int64_t n_ops,
+                        void* workspace, size_t workspace_bytes,
                         void* stream);
 
 /* A captured HIP graph of a sequence, replayed with one launch.  The handle
- * records the pointers in `ops`; the caller keeps those buffers alive until
- * mnb_graph_destroy.  Creation captures on a private stream of default
- * priority and launches nothing on the device. */
+ * records the pointers in `ops` and the workspace; the caller keeps those
+ * buffers alive until mnb_graph_destroy, and does not use that workspace
+ * for other work that may run while a replay does.  Creation captures on a
+ * private stream of default priority and launches nothing on the device. */
 typedef struct mnb_graph mnb_graph;
 int mnb_graph_create(const mnb_matmul_args* ops, int64_t n_ops,
+                     void* workspace, size_t workspace_bytes,
                      mnb_graph** out);
 int mnb_graph_launch(mnb_graph* g, void* stream);
 int mnb_graph_destroy(mnb_graph* g);

@@ -25,6 +25,24 @@ def test_header_declares_the_binding_exports():
     assert _declared_functions() == sorted(_lib.EXPORTS)
 
 
+def test_probe_library_exports_its_header():
+    """The benchmark's control-arm library (not part of libmnb) exports
+    exactly what include/mnb_probe.h declares, and refuses bad arguments on
+    the host."""
+    import torch  # noqa: F401
+    hdr = os.path.join(os.path.dirname(HEADER), "mnb_probe.h")
+    text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(mnb_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["mnb_probe_stream_read"]
+    L = ctypes.CDLL(os.path.join(os.path.dirname(_lib.LIB_PATH), "libmnb_probe.so"))
+    f = L.mnb_probe_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 16, P16, None) == -1
+    assert f(P16, 17, P16, None) == -1
+    assert f(P16 + 8, 16, P16, None) == -1
+    assert f(P16, 16, None, None) == -1
+
+
 def test_library_exports_every_declared_symbol():
     L = mnb.lib()
     for name in _declared_functions():
@@ -89,8 +107,10 @@ P16 = 0x10000          # fake, never dereferenced: each call below fails validat
 P_MIS = 0x10008        # 8-byte aligned only
 
 
-def _gemv(d, M=1, a=P16, b=P16, s=P16, zp=None, bias=None, y=P16, fn="mnb_gemv"):
+def _gemv(d, M=1, a=P16, b=P16, s=P16, zp=None, bias=None, y=P16, fn="mnb_gemv", ws=None, ws_bytes=0):
     f = getattr(mnb.lib(), fn)
+    if fn == "mnb_gemm":
+        return f(ctypes.byref(d), M, a, b, s, zp, bias, y, ws, ws_bytes, None)
     return f(ctypes.byref(d), M, a, b, s, zp, bias, y, None)
 
 
@@ -142,15 +162,16 @@ def test_sequence_validates_every_entry_before_launching():
                           scales=P16, zp_packed=None, bias=None, y=P16)
     arr = (_lib.MatmulArgs * 2)(good, bad)
     # the invalid second entry stops the call before the first is launched
-    assert L.mnb_matmul_sequence(arr, 2, None) == -2
+    assert L.mnb_matmul_sequence(arr, 2, None, 0, None) == -2
     assert "entry 1" in L.mnb_last_error().decode()
     g = ctypes.c_void_p()
-    assert L.mnb_graph_create(arr, 2, ctypes.byref(g)) == -2
+    assert L.mnb_graph_create(arr, 2, None, 0, ctypes.byref(g)) == -2
     assert not g.value
-    assert L.mnb_graph_create(arr, 2, None) == -1
+    assert L.mnb_graph_create(arr, 2, None, 0, None) == -1
     assert L.mnb_graph_launch(None, None) == -1
     assert L.mnb_graph_destroy(None) == 0
-    assert L.mnb_matmul_sequence(arr, -1, None) == -1
+    assert L.mnb_matmul_sequence(arr, -1, None, 0, None) == -1
+    assert L.mnb_sequence_workspace_bytes(arr, 2) == 0          # invalid entry
 
 
 def test_status_strings():
@@ -196,11 +217,101 @@ def test_gather_argmax_silu_argument_errors():
     assert L.mnb_gather_rows(ctypes.byref(d), P16, 0, None, None, None, None, None) == 0   # nothing to do
     assert L.mnb_gather_rows(ctypes.byref(d), 0x10004, 2, P16, P16, None, P16, None) == -3
     assert L.mnb_gather_rows(ctypes.byref(d), P16, 2, P16, P16, P16, P16, None) == -1      # zp without flag
-    assert L.mnb_argmax(2, 1, 8, P16, P16, None) == -2
-    assert L.mnb_argmax(0, 0, 8, P16, P16, None) == -1
-    assert L.mnb_argmax(0, 1, 0, P16, P16, None) == -1
-    assert L.mnb_argmax(0, 1, 8, P16, 0x10004, None) == -3
+    assert L.mnb_argmax(2, 1, 8, P16, P16, None, 0, None) == -2
+    assert L.mnb_argmax(0, 0, 8, P16, P16, None, 0, None) == -1
+    assert L.mnb_argmax(0, 1, 0, P16, P16, None, 0, None) == -1
+    assert L.mnb_argmax(0, 1, 8, P16, 0x10004, None, 0, None) == -3
     odd = mnb.make_desc(64, 7, 32)
     assert _gemv(odd, fn="mnb_gemv_silu_mul") == -1
     assert "even" in L.mnb_last_error().decode()
     assert _gemv(d, M=2, fn="mnb_gemv_silu_mul") == -1
+
+
+# ---- caller-provided workspace ("Prepared weight-only plan": a bounded
+# workspace is part of the plan) ---------------------------------------------
+
+def _ws(K, N, M, bs, dt="f32", zp=True):
+    import torch
+    adt = torch.float32 if dt == "f32" else torch.bfloat16
+    return mnb.workspace_bytes(mnb.make_desc(K, N, bs, adt, zp), M)
+
+
+def test_workspace_sizes_are_a_function_of_the_shape():
+    """The K split (and so the workspace) follows from the shape alone, sized
+    for 256 CUs: float32 partial slices of M x N for split products, of the
+    last round's 256 x 256 tiles for a split tail, none for the decode,
+    row and small-M kernels."""
+    MB = 2048 * 2560 * 4
+    # Qwen3-4B prefill, 2048 bf16 rows, block 128: o and down (80 tiles of
+    # 256 x 256) split K three ways; gate||up (608 tiles) splits its last
+    # 96 tiles two ways; qkv (192 tiles) and the LM head run unsplit
+    assert _ws(4096, 2560, 2048, 128, "bf16") == 3 * MB
+    assert _ws(9728, 2560, 2048, 128, "bf16") == 3 * MB
+    assert _ws(2560, 19456, 2048, 128, "bf16") == 2 * 96 * 256 * 256 * 4
+    assert _ws(2560, 6144, 2048, 128, "bf16") == 0
+    assert _ws(2560, 151936, 2048, 128, "bf16") == 0
+    # Qwen3-0.6B prefill, 512 float32 rows, block 32: o and down (128 tiles
+    # of 64 x 64) take four splits; qkv, gate||up and the LM head none
+    assert _ws(2048, 1024, 512, 32) == 4 * 512 * 1024 * 4
+    assert _ws(3072, 1024, 512, 32) == 4 * 512 * 1024 * 4
+    assert _ws(1024, 4096, 512, 32) == 0
+    assert _ws(1024, 6144, 512, 32) == 0
+    assert _ws(1024, 151936, 512, 32) == 0
+    # decode, 2-4 rows, small M: no workspace
+    for M in (1, 2, 3, 4, 8, 16):
+        assert _ws(2560, 151936, M, 128) == 0
+    # invalid descriptor or M
+    assert mnb.workspace_bytes(mnb.make_desc(64, 8, 24), 600) == 0
+    assert mnb.workspace_bytes(mnb.make_desc(64, 8, 32), 0) == 0
+
+
+def test_gemm_refuses_a_missing_or_short_workspace():
+    d = mnb.make_desc(2048, 1024, 32, has_zero_points=True)
+    need = mnb.workspace_bytes(d, 512)
+    assert need > 0
+    L = mnb.lib()
+    assert _gemv(d, M=512, zp=P16, fn="mnb_gemm") == -1
+    assert "workspace" in L.mnb_last_error().decode()
+    assert _gemv(d, M=512, zp=P16, fn="mnb_gemm", ws=0x100000, ws_bytes=need - 1) == -1
+    assert _gemv(d, M=512, zp=P16, fn="mnb_gemm", ws=0x100010, ws_bytes=need) == -3   # 256-byte aligned
+    # a product that needs none ignores what is offered
+    d1 = mnb.make_desc(1024, 4096, 32, has_zero_points=True)
+    assert mnb.workspace_bytes(d1, 512) == 0
+
+
+def test_bf16_block16_scales_need_word_alignment_in_gemm():
+    import torch
+    d = mnb.make_desc(64, 8, 16, torch.bfloat16)
+    assert _gemv(d, M=300, s=0x10002, fn="mnb_gemm") == -3
+    assert "4-byte" in mnb.lib().mnb_last_error().decode()
+
+
+def test_gemv_refuses_k_beyond_the_register_kernel():
+    d = mnb.make_desc(20000, 8, 32)
+    assert 20000 > mnb.gemv_max_k(d)
+    assert _gemv(d) == -2
+    assert "mnb_gemm" in mnb.lib().mnb_last_error().decode()
+
+
+def test_argmax_workspace_rule():
+    assert mnb.argmax_workspace_bytes(1, 2048) == 0          # one segment: one workgroup per row
+    one = mnb.argmax_workspace_bytes(1, 151936)
+    assert one > 0 and mnb.argmax_workspace_bytes(3, 151936) == 3 * one
+    assert mnb.argmax_workspace_bytes(70000, 151936) == 0    # beyond grid.y: one workgroup per row
+    assert mnb.argmax_workspace_bytes(0, 10) == 0
+    L = mnb.lib()
+    assert L.mnb_argmax(0, 1, 151936, P16, P16, None, 0, None) == -1
+    assert L.mnb_argmax(0, 1, 151936, P16, P16, 0x100000, one - 1, None) == -1
+
+
+def test_sequence_workspace_is_the_largest_entry():
+    L = mnb.lib()
+    mk = lambda K, N, M: _lib.MatmulArgs(desc=mnb.make_desc(K, N, 32, has_zero_points=True), M=M,  # noqa: E731
+                                         a=P16, b_packed=P16, scales=P16, zp_packed=P16, bias=None, y=P16)
+    arr = (_lib.MatmulArgs * 3)(mk(1024, 4096, 512), mk(2048, 1024, 512), mk(1024, 4096, 1))
+    assert L.mnb_sequence_workspace_bytes(arr, 3) == 4 * 512 * 1024 * 4
+    assert L.mnb_matmul_sequence(arr, 3, None, 0, None) == -1
+    assert L.mnb_matmul_sequence(arr, 3, 0x100000, 4 * 512 * 1024 * 4 - 4, None) == -1
+    g = ctypes.c_void_p()
+    assert L.mnb_graph_create(arr, 3, None, 0, ctypes.byref(g)) == -1
+    assert not g.value

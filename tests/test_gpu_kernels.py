@@ -345,10 +345,10 @@ def test_bf16_gemm_identity_returns_bf16_dequant(orc, K, N, bs, zp):
                                               (2048, 128, 12288, 128, False, False),
                                               (1030, 320, 24600, 32, True, False)])
 def test_bf16_gemm_large_grid_sampled(orc, M, K, N, bs, zp, bias):
-    """Grids of >= 384 tiles of 256x256 take the 256x256x64 prefill kernel
-    without splitting K (K a multiple of 64 and of the block size); ragged M
-    and N, an odd number of K steps; sampled rows x columns against the
-    oracle."""
+    """bfloat16, more than 128 rows, K a multiple of 64 and of the block size:
+    the 256 x 256 x 64 wide kernel over many rounds of tiles (no K split);
+    ragged M and N, an odd number of K steps; sampled rows x columns against
+    the oracle."""
     log(f"large bf16 gemm M={M} K={K} N={N} bs={bs} zp={zp} bias={bias}")
     inp, g = _inputs(K, N, M, bs, "bf16", zp, bias, seed=M + K + N)
     pw = _packed(g, bs)
@@ -356,6 +356,29 @@ def test_bf16_gemm_large_grid_sampled(orc, M, K, N, bs, zp, bias):
     rng = np.random.default_rng(M)
     rows = sorted({0, M - 1, 255, 256, *rng.choice(M, 12, replace=False).tolist()})
     cols = sorted({0, N - 1, 255, 256, N - 257, *rng.choice(N, 40, replace=False).tolist()})
+    y_ref, S = oracle_ref(orc, inp, rows, cols)
+    ys = y[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)]
+    assert_close(out_f64(ys), y_ref, S, "bf16", f"M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M,K,N,bs,zp,bias", [(64, 2560, 151936, 128, True, True),
+                                              (17, 1024, 98305, 32, False, True),
+                                              (300, 1056, 49200, 32, True, False)])
+def test_bf16_gemm_128_tiles_wide_n_sampled(orc, M, K, N, bs, zp, bias):
+    """bfloat16 products the wide kernel does not take -- 17..128 rows (a
+    64-token prefill through the 151,936-column LM head), or K not a multiple
+    of 64 (K = 1056) -- run on the 128 x 128 tile kernel however many tiles
+    the grid has.  Random weights, zero points and bias; all rows of the
+    short products, sampled rows otherwise, x sampled columns including the
+    ragged last tile, against the oracle."""
+    log(f"bf16 128-tile gemm M={M} K={K} N={N} bs={bs} zp={zp} bias={bias}")
+    inp, g = _inputs(K, N, M, bs, "bf16", zp, bias, seed=M * 5 + K + N)
+    pw = _packed(g, bs)
+    y = mnb.gemm(g.a, pw.b_packed, pw.scales, pw.zp_packed, pw.bias, K=K, N=N, block_size=bs)
+    rng = np.random.default_rng(M + 1)
+    rows = list(range(M)) if M <= 64 else sorted({0, M - 1, 127, 128, *rng.choice(M, 10, replace=False).tolist()})
+    last = (N - 1) // 128 * 128
+    cols = sorted({0, 127, 128, last - 1, *range(last, N), *rng.choice(N, 48, replace=False).tolist()})
     y_ref, S = oracle_ref(orc, inp, rows, cols)
     ys = y[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)]
     assert_close(out_f64(ys), y_ref, S, "bf16", f"M={M} K={K} N={N}")
@@ -393,22 +416,55 @@ SPLIT_CASES = [
 @pytest.mark.parametrize("dt,M,K,N,bs,zp,bias", SPLIT_CASES)
 def test_split_k_gemm_matches_oracle(orc, dt, M, K, N, bs, zp, bias):
     """Few output tiles: K is split across workgroups and the float32
-    partials are added in split order (+ bias); every output against the
-    oracle, twice (the second call reuses the stream's workspace)."""
+    partials (in the caller's workspace) are added in split order (+ bias);
+    every output against the oracle, twice (the second call reuses the same
+    workspace, left holding the first call's partials)."""
     log(f"split-K gemm {dt} M={M} K={K} N={N} bs={bs} zp={zp} bias={bias}")
     inp, g = _inputs(K, N, M, bs, dt, zp, bias, seed=M * 3 + K + N)
     pw = _packed(g, bs)
+    need = mnb.workspace_bytes(pw.desc, M)
+    assert need > 0
+    ws = mnb.workspace(need)
     y_ref, S = oracle_ref(orc, inp)
-    y1 = pw.matmul(g.a).clone()
-    y2 = pw.matmul(g.a)
+    y1 = pw.matmul(g.a, workspace=ws).clone()
+    y2 = pw.matmul(g.a, workspace=ws)
     assert_close(out_f64(y1), y_ref, S, dt, f"{dt} M={M} K={K} N={N}")
     assert torch.equal(y1, y2)
 
 
+def test_split_k_captured_in_callers_graph_before_any_eager_call():
+    """A split product whose first call ever is inside a graph the caller
+    captures (torch.cuda.graph, workspace from the caller) gives the bits of
+    the same product run eagerly afterwards, on every replay, with eager
+    work between the replays."""
+    dt, M, K, N, bs, zp, bias = "f32", 192, 3072, 200, 32, True, True
+    _, g = _inputs(K, N, M, bs, dt, zp, bias, seed=77)
+    pw = _packed(g, bs)
+    ws_graph = mnb.workspace(mnb.workspace_bytes(pw.desc, M))
+    y = torch.empty(M, N, device=DEV)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        pw.matmul(g.a, out=y, workspace=ws_graph)
+    ws_eager = mnb.workspace(mnb.workspace_bytes(pw.desc, M))
+    replays = []
+    for rep in range(3):
+        y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        replays.append(y.clone())
+        pw.matmul(g.a, workspace=ws_eager)       # eager work between replays
+        torch.cuda.synchronize()
+    eager = pw.matmul(g.a, workspace=ws_eager)
+    for rep, r in enumerate(replays):
+        assert torch.equal(r, eager), rep
+
+
 def test_split_k_graph_matches_direct():
-    """A captured sequence of split products (its own workspace) gives the
-    bits of the same products run directly (the stream's workspace), on
-    every replay."""
+    """A captured sequence of split products (the sequence's graph
+    workspace) gives the bits of the same products run directly (its eager
+    workspace), on every replay."""
     items = []
     for i, (dt, M, K, N, bs, zp, bias) in enumerate(SPLIT_CASES):
         _, g = _inputs(K, N, M, bs, dt, zp, bias, seed=100 + i)
@@ -435,6 +491,43 @@ def test_split_k_graph_matches_direct():
 # ---------------------------------------------------------------------------
 # small M (1 <= M <= 16, K % 32 == 0, block_size >= 32): matrix-core kernel
 # ---------------------------------------------------------------------------
+
+# 2..4 rows through the decode GEMV with split-K wavefront teams (W = 2 or 4
+# wavefronts per column): K beyond one wavefront's 64 lanes x 4 / MR chunks.
+ROW_TEAM_CASES = [  # (M, K, dt)
+    (3, 2560, "f32"), (4, 2560, "f32"), (3, 3072, "f32"), (4, 3072, "f32"),
+    (3, 4096, "f32"), (4, 4096, "f32"), (2, 6144, "f32"), (2, 8192, "f32"),
+    (3, 2560, "bf16"), (4, 3072, "bf16"), (4, 4096, "bf16"), (4, 8192, "bf16"),
+    (2, 16384, "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,K,dt", ROW_TEAM_CASES)
+def test_row_gemv_split_k_teams_random_weights(orc, M, K, dt):
+    """Random weights, zero points, scales and bias (on and off) through the
+    2-4-row GEMV where a column takes a team of several wavefronts (their
+    partial sums meet in LDS per row): every output of a ragged N against
+    the oracle, for block sizes 32 and 128."""
+    worst = 0.0
+    for bs, zp, bias in ((32, True, True), (128, False, False), (128, True, False)):
+        N = 257
+        log(f"row-team gemv {dt} M={M} K={K} N={N} bs={bs} zp={zp} bias={bias}")
+        inp, g = _inputs(K, N, M, bs, dt, zp, bias, seed=M * 1000 + K + bs)
+        pw = _packed(g, bs)
+        assert mnb.workspace_bytes(pw.desc, M) == 0
+        y = mnb.gemm(g.a, pw.b_packed, pw.scales, pw.zp_packed, pw.bias, K=K, N=N, block_size=bs)
+        y_ref, S = oracle_ref(orc, inp)
+        worst = max(worst, assert_close(out_f64(y), y_ref, S, dt, f"M={M} K={K} bs={bs}"))
+        # each row alone through the decode GEMV: same tolerance, and the
+        # rows do not disturb one another (a row of zeros gives the bias)
+        a0 = g.a.clone()
+        a0[1:] = 0
+        y0 = mnb.gemm(a0, pw.b_packed, pw.scales, pw.zp_packed, pw.bias, K=K, N=N, block_size=bs)
+        want = torch.zeros(N, device=DEV) if pw.bias is None else pw.bias
+        for r in range(1, M):
+            assert torch.equal(y0[r].float(), want.to(y0.dtype).float()), r
+    log(f"row-team gemv {dt} M={M} K={K}: worst err/tol {worst:.3g}")
+
 
 SMALL_M_CASES = [  # (M, K, N): ragged N, K not a multiple of the 128-value span
     (1, 32, 1), (2, 64, 17), (3, 96, 33), (4, 1024, 4096), (5, 160, 100),

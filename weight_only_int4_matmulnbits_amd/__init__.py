@@ -27,7 +27,8 @@ __all__ = [
     "Desc", "MnbError", "make_desc", "validate", "packed_weight_bytes",
     "scale_bytes", "zero_point_bytes", "gemv_max_k", "pack", "gemv", "gemm",
     "dequant", "PackedWeight", "Sequence", "version", "import_qdq", "qdq_is_native",
-    "gather_rows", "argmax", "gemv_silu_mul",
+    "gather_rows", "argmax", "gemv_silu_mul", "workspace_bytes",
+    "argmax_workspace_bytes", "workspace",
 ]
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
@@ -66,6 +67,34 @@ def zero_point_bytes(desc: Desc) -> int:
 
 def gemv_max_k(desc: Desc) -> int:
     return int(lib().mnb_gemv_max_k(ctypes.byref(desc)))
+
+
+def workspace_bytes(desc: Desc, M: int) -> int:
+    """Workspace bytes mnb_gemm needs for (desc, M); 0 when none."""
+    return int(lib().mnb_workspace_bytes(ctypes.byref(desc), int(M)))
+
+
+def argmax_workspace_bytes(M: int, N: int) -> int:
+    return int(lib().mnb_argmax_workspace_bytes(int(M), int(N)))
+
+
+def workspace(nbytes: int, device="cuda") -> Optional[torch.Tensor]:
+    """A caller-owned workspace of at least nbytes (None when nbytes is 0).
+    torch's allocator returns 256-byte aligned blocks, as the library needs."""
+    if nbytes <= 0:
+        return None
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
+def _ws(t: Optional[torch.Tensor], need: int, device):
+    """(pointer, size) of the given workspace, or of a fresh one when none is
+    given (the library itself never allocates)."""
+    if need <= 0:
+        return None, 0, t
+    if t is None:
+        t = workspace(need, device)
+    _need(t, "workspace", torch.uint8)
+    return ctypes.c_void_p(t.data_ptr()), t.numel(), t
 
 
 def version() -> str:
@@ -127,7 +156,7 @@ def pack(q: torch.Tensor, zp: Optional[torch.Tensor] = None, block_size: int = 3
 def _matmul(fn: str, a: torch.Tensor, b_packed: torch.Tensor, scales: torch.Tensor,
             zp_packed: Optional[torch.Tensor], bias: Optional[torch.Tensor],
             K: int, N: int, block_size: int, out: Optional[torch.Tensor],
-            stream) -> torch.Tensor:
+            stream, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     if a.dim() == 1:
         a = a.view(1, -1)
     M = a.shape[0]
@@ -143,8 +172,15 @@ def _matmul(fn: str, a: torch.Tensor, b_packed: torch.Tensor, scales: torch.Tens
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     _need(out, "out", a.dtype, shape=(M, N))
     f = getattr(lib(), fn)
-    check(f(ctypes.byref(d), M, _ptr(a), _ptr(b_packed), _ptr(scales), _ptr(zp_packed),
-            _ptr(bias), _ptr(out), _stream(stream)), fn)
+    if fn == "mnb_gemm":
+        wp, wn, keep = _ws(ws, workspace_bytes(d, M), a.device)
+        check(f(ctypes.byref(d), M, _ptr(a), _ptr(b_packed), _ptr(scales), _ptr(zp_packed),
+                _ptr(bias), _ptr(out), wp, wn, _stream(stream)), fn)
+        if keep is not None and ws is None and stream is not None:
+            keep.record_stream(stream)     # freed only after the work on that stream
+    else:
+        check(f(ctypes.byref(d), M, _ptr(a), _ptr(b_packed), _ptr(scales), _ptr(zp_packed),
+                _ptr(bias), _ptr(out), _stream(stream)), fn)
     return out
 
 
@@ -156,10 +192,12 @@ def gemv(a, b_packed, scales, zp_packed=None, bias=None, *, K, N, block_size,
 
 
 def gemm(a, b_packed, scales, zp_packed=None, bias=None, *, K, N, block_size,
-         out=None, stream=None) -> torch.Tensor:
-    """Prefill GEMM: a is [M][K]; returns y [M][N] in a's dtype."""
+         out=None, stream=None, workspace=None) -> torch.Tensor:
+    """Prefill GEMM: a is [M][K]; returns y [M][N] in a's dtype.  workspace:
+    a uint8 device tensor of at least workspace_bytes(desc, M) bytes, or None
+    to have one allocated through torch for this call."""
     return _matmul("mnb_gemm", a, b_packed, scales, zp_packed, bias, K, N, block_size,
-                   out, stream)
+                   out, stream, workspace)
 
 
 DEQUANT_F32, DEQUANT_BF16, DEQUANT_INT8 = 0, 1, 2
@@ -233,9 +271,10 @@ def gather_rows(ids: torch.Tensor, b_packed, scales, zp_packed=None, *, K: int, 
     return out
 
 
-def argmax(x: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+def argmax(x: torch.Tensor, out=None, stream=None, workspace=None) -> torch.Tensor:
     """Row-wise greedy ArgMax (first maximum; a NaN counts as largest) of a
-    float32 or bfloat16 [M][N] (or [N]) tensor; returns int64 [M]."""
+    float32 or bfloat16 [M][N] (or [N]) tensor; returns int64 [M].
+    workspace: at least argmax_workspace_bytes(M, N) bytes, or None."""
     if x.dim() == 1:
         x = x.view(1, -1)
     M, N = x.shape
@@ -243,7 +282,11 @@ def argmax(x: torch.Tensor, out=None, stream=None) -> torch.Tensor:
     if out is None:
         out = torch.empty(M, dtype=torch.int64, device=x.device)
     _need(out, "out", torch.int64, numel=M)
-    check(lib().mnb_argmax(_code(x.dtype), M, N, _ptr(x), _ptr(out), _stream(stream)), "mnb_argmax")
+    wp, wn, keep = _ws(workspace, argmax_workspace_bytes(M, N), x.device)
+    check(lib().mnb_argmax(_code(x.dtype), M, N, _ptr(x), _ptr(out), wp, wn, _stream(stream)),
+          "mnb_argmax")
+    if keep is not None and workspace is None and stream is not None:
+        keep.record_stream(stream)
     return out
 
 
@@ -301,10 +344,17 @@ class PackedWeight:
         return (self.b_packed.numel() + self.scales.numel() * self.scales.element_size()
                 + (0 if self.zp_packed is None else self.zp_packed.numel()))
 
-    def matmul(self, a: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
-        fn = gemv if (a.dim() == 1 or a.shape[0] == 1) else gemm
-        return fn(a, self.b_packed, self.scales, self.zp_packed, self.bias, K=self.K,
-                  N=self.N, block_size=self.block_size, out=out, stream=stream)
+    def matmul(self, a: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None,
+               workspace: Optional[torch.Tensor] = None):
+        """y = a x dequant(B) (+ bias): the decode GEMV for one row within the
+        register kernel's K, the prefill GEMM otherwise."""
+        one = a.dim() == 1 or a.shape[0] == 1
+        if one and self.K <= gemv_max_k(self.desc):
+            return gemv(a, self.b_packed, self.scales, self.zp_packed, self.bias, K=self.K,
+                        N=self.N, block_size=self.block_size, out=out, stream=stream)
+        return gemm(a, self.b_packed, self.scales, self.zp_packed, self.bias, K=self.K,
+                    N=self.N, block_size=self.block_size, out=out, stream=stream,
+                    workspace=workspace)
 
     def args(self, a: torch.Tensor, y: torch.Tensor) -> MatmulArgs:
         M = 1 if a.dim() == 1 else a.shape[0]
@@ -321,7 +371,10 @@ class PackedWeight:
 class Sequence:
     """An ordered list of projections run back to back on one stream (a decode
     or prefill step), either eagerly or as one captured HIP graph.  The caller
-    keeps every tensor alive while the sequence exists."""
+    keeps every tensor alive while the sequence exists.  The sequence owns
+    one workspace for its split products (sized by the library's query) for
+    eager runs, and a second one for its captured graph, so that a replay and
+    eager runs never share partial sums."""
 
     def __init__(self, items: TSeq[Tuple[PackedWeight, torch.Tensor, torch.Tensor]]):
         self._keep: List = list(items)
@@ -331,14 +384,25 @@ class Sequence:
             self._args[i] = w.args(a, y)
         self.n = n
         self._graph = None
+        self.workspace_bytes = int(lib().mnb_sequence_workspace_bytes(self._args, n))
+        dev = self._keep[0][1].device if n else "cuda"
+        self._ws = workspace(self.workspace_bytes, dev)
+        self._graph_ws = None
+
+    @staticmethod
+    def _wsargs(t):
+        return (None, 0) if t is None else (ctypes.c_void_p(t.data_ptr()), t.numel())
 
     def run(self, stream=None) -> None:
-        check(lib().mnb_matmul_sequence(self._args, self.n, _stream(stream)),
+        check(lib().mnb_matmul_sequence(self._args, self.n, *self._wsargs(self._ws), _stream(stream)),
               "mnb_matmul_sequence")
 
     def capture(self) -> None:
         g = ctypes.c_void_p()
-        check(lib().mnb_graph_create(self._args, self.n, ctypes.byref(g)), "mnb_graph_create")
+        if self._graph_ws is None and self.workspace_bytes:
+            self._graph_ws = workspace(self.workspace_bytes, self._keep[0][1].device)
+        check(lib().mnb_graph_create(self._args, self.n, *self._wsargs(self._graph_ws), ctypes.byref(g)),
+              "mnb_graph_create")
         self._graph = g
 
     def replay(self, stream=None) -> None:

@@ -29,6 +29,8 @@ EXPORTS = (
     "mnb_graph_launch", "mnb_graph_destroy", "mnb_status_string",
     "mnb_last_error", "mnb_version", "mnb_import_qdq", "mnb_qdq_is_native",
     "mnb_gather_rows", "mnb_argmax", "mnb_gemv_silu_mul",
+    "mnb_workspace_bytes", "mnb_argmax_workspace_bytes",
+    "mnb_sequence_workspace_bytes",
 )
 
 
@@ -96,9 +98,15 @@ def lib() -> ctypes.CDLL:
     L.mnb_gemv_max_k.restype = i64
     L.mnb_pack.argtypes = [pd, vp, vp, vp, vp, vp]
     L.mnb_pack.restype = ctypes.c_int
-    for f in ("mnb_gemv", "mnb_gemm"):
-        getattr(L, f).argtypes = [pd, i64, vp, vp, vp, vp, vp, vp, vp]
-        getattr(L, f).restype = ctypes.c_int
+    sz = ctypes.c_size_t
+    L.mnb_gemv.argtypes = [pd, i64, vp, vp, vp, vp, vp, vp, vp]
+    L.mnb_gemv.restype = ctypes.c_int
+    L.mnb_gemm.argtypes = [pd, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.mnb_gemm.restype = ctypes.c_int
+    L.mnb_workspace_bytes.argtypes = [pd, i64]
+    L.mnb_workspace_bytes.restype = sz
+    L.mnb_argmax_workspace_bytes.argtypes = [i64, i64]
+    L.mnb_argmax_workspace_bytes.restype = sz
     L.mnb_dequant.argtypes = [pd, vp, vp, vp, i32, vp, vp]
     L.mnb_dequant.restype = ctypes.c_int
     L.mnb_import_qdq.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -107,14 +115,16 @@ def lib() -> ctypes.CDLL:
     L.mnb_qdq_is_native.restype = ctypes.c_int
     L.mnb_gather_rows.argtypes = [pd, vp, i64, vp, vp, vp, vp, vp]
     L.mnb_gather_rows.restype = ctypes.c_int
-    L.mnb_argmax.argtypes = [i32, i64, i64, vp, vp, vp]
+    L.mnb_argmax.argtypes = [i32, i64, i64, vp, vp, vp, sz, vp]
     L.mnb_argmax.restype = ctypes.c_int
     L.mnb_gemv_silu_mul.argtypes = [pd, i64, vp, vp, vp, vp, vp, vp, vp]
     L.mnb_gemv_silu_mul.restype = ctypes.c_int
     pa = ctypes.POINTER(MatmulArgs)
-    L.mnb_matmul_sequence.argtypes = [pa, i64, vp]
+    L.mnb_sequence_workspace_bytes.argtypes = [pa, i64]
+    L.mnb_sequence_workspace_bytes.restype = sz
+    L.mnb_matmul_sequence.argtypes = [pa, i64, vp, sz, vp]
     L.mnb_matmul_sequence.restype = ctypes.c_int
-    L.mnb_graph_create.argtypes = [pa, i64, ctypes.POINTER(vp)]
+    L.mnb_graph_create.argtypes = [pa, i64, vp, sz, ctypes.POINTER(vp)]
     L.mnb_graph_create.restype = ctypes.c_int
     L.mnb_graph_launch.argtypes = [vp, vp]
     L.mnb_graph_launch.restype = ctypes.c_int

@@ -19,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmnb.so")
+# the benchmark's bandwidth control arm, a separate library (include/mnb_probe.h)
+PROBE_LIB = os.path.join(PKG, "libmnb_probe.so")
+PROBE_SOURCE = "mnb_probe.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -49,9 +52,10 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     cmds = []
-    for src in SOURCES:
+    for src in SOURCES + [PROBE_SOURCE]:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        objs.append(obj)
+        if src != PROBE_SOURCE:
+            objs.append(obj)
         cmds.append([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), 4)) as ex:
         for log in ex.map(_run, cmds):
@@ -60,6 +64,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+          os.path.join(BUILD, PROBE_SOURCE.replace(".hip", ".o"))])
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

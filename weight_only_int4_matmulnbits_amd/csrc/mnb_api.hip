@@ -5,7 +5,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <mutex>
 #include <new>
 #include <vector>
 
@@ -82,73 +81,34 @@ int check_matmul(const char* who, const mnb_desc* d, int64_t M, const void* a,
     if (!aligned(scales, esz)) return fail(MNB_E_ALIGN, "%s: scales must be %d-byte aligned", who, (int)esz);
     if (!aligned(y, esz)) return fail(MNB_E_ALIGN, "%s: y must be %d-byte aligned", who, (int)esz);
     if (bias && !aligned(bias, 4)) return fail(MNB_E_ALIGN, "%s: bias must be 4-byte aligned", who);
+    // the prefill kernel reads the two bfloat16 scales of a 16-value block
+    // pair as one 32-bit word
+    if (!gemv && esz == 2 && d->block_size == 16 && !aligned(scales, 4))
+        return fail(MNB_E_ALIGN, "%s: bfloat16 scales of 16-value blocks must be 4-byte aligned", who);
     fill_problem(d, M, p);
     p->a = a; p->b = b; p->scales = scales; p->zp = zp; p->bias = bias; p->y = y;
     return MNB_OK;
 }
 
-// Split-K partials of direct calls live in one workspace per (device,
-// stream), grown on demand (never while the stream is being captured: a
-// captured launch then runs without splitting) and kept until the process
-// ends.  Calls on one stream are ordered, so they can share it.
-struct StreamWorkspace {
-    int dev;
-    hipStream_t stream;
-    void* ptr;
-    size_t bytes;
-};
-std::mutex g_ws_mutex;
-std::vector<StreamWorkspace> g_ws;
-
-void* stream_workspace(hipStream_t s, size_t bytes, size_t* have) {
-    *have = 0;
-    if (bytes == 0) return nullptr;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    StreamWorkspace* e = nullptr;
-    for (auto& w : g_ws)
-        if (w.dev == dev && w.stream == s) e = &w;
-    if (e && e->bytes >= bytes) {
-        *have = e->bytes;
-        return e->ptr;
-    }
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-    const size_t want = (bytes + (size_t(32) << 20) - 1) / (size_t(32) << 20) * (size_t(32) << 20);
-    if (e) {
-        // earlier launches on this stream may still use the old buffer
-        if (hipStreamSynchronize(s) != hipSuccess) return nullptr;
-        (void)hipFree(e->ptr);
-        e->ptr = nullptr;
-        e->bytes = 0;
-    }
-    void* ptr = nullptr;
-    if (hipMalloc(&ptr, want) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    if (e) {
-        e->ptr = ptr;
-        e->bytes = want;
-    } else {
-        g_ws.push_back(StreamWorkspace{dev, s, ptr, want});
-    }
-    *have = want;
-    return ptr;
-}
-
 bool takes_gemv(const Problem& p) { return p.M == 1 && p.K <= gemv_max_k(p.bs); }
 
-// ws == nullptr: the stream's own workspace
-int run_gemm(const Problem& p, hipStream_t s, void* ws = nullptr, size_t ws_bytes = 0) {
-    if (!ws) ws = stream_workspace(s, gemm_workspace_bytes(p), &ws_bytes);
-    return launch_gemm(p, s, ws, ws_bytes);
+size_t workspace_of(const Problem& p) { return takes_gemv(p) ? 0 : gemm_workspace_bytes(p); }
+
+// The caller's workspace must hold what the product's plan needs: a split
+// never changes with the workspace offered, so results depend on the shape
+// alone.
+int check_workspace(const char* who, size_t need, const void* ws, size_t ws_bytes) {
+    if (need == 0) return MNB_OK;
+    if (!ws || ws_bytes < need)
+        return fail(MNB_E_ARG, "%s: needs a workspace of %zu bytes (given %zu%s)", who, need,
+                    ws ? ws_bytes : (size_t)0, ws ? "" : ", NULL");
+    if (!aligned(ws, 256)) return fail(MNB_E_ALIGN, "%s: workspace must be 256-byte aligned", who);
+    return MNB_OK;
 }
 
-int run(const Problem& p, hipStream_t s, void* ws = nullptr, size_t ws_bytes = 0) {
+int run(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
     if (takes_gemv(p)) return launch_gemv(p, s);
-    return run_gemm(p, s, ws, ws_bytes);
+    return launch_gemm(p, s, ws, ws_bytes);
 }
 
 }  // namespace
@@ -159,7 +119,6 @@ using namespace mnb;
 struct mnb_graph {
     hipGraph_t graph;
     hipGraphExec_t exec;
-    void* ws;          // split-K partials of the captured products (owned)
 };
 
 extern "C" {
@@ -218,16 +177,31 @@ int mnb_gemv(const mnb_desc* d, int64_t M, const void* a, const uint8_t* b_packe
     Problem p;
     int st = check_matmul("mnb_gemv", d, M, a, b_packed, scales, zp_packed, bias, y, true, &p);
     if (st != MNB_OK) return st;
-    return run(p, static_cast<hipStream_t>(stream));
+    if (!takes_gemv(p))
+        return fail(MNB_E_UNSUPPORTED, "mnb_gemv: K=%lld exceeds mnb_gemv_max_k=%lld (use mnb_gemm)",
+                    (long long)p.K, (long long)gemv_max_k(p.bs));
+    return launch_gemv(p, static_cast<hipStream_t>(stream));
+}
+
+size_t mnb_workspace_bytes(const mnb_desc* d, int64_t M) {
+    if (mnb_validate(d, M) != MNB_OK) return 0;
+    // the choice of kernel depends on the shape alone (A's 16-byte alignment
+    // is a precondition of every product)
+    Problem p;
+    fill_problem(d, M, &p);
+    p.a = nullptr; p.b = nullptr; p.scales = nullptr; p.zp = nullptr; p.bias = nullptr; p.y = nullptr;
+    return gemm_workspace_bytes(p);
 }
 
 int mnb_gemm(const mnb_desc* d, int64_t M, const void* a, const uint8_t* b_packed,
              const void* scales, const uint8_t* zp_packed, const float* bias, void* y,
-             void* stream) {
+             void* workspace, size_t workspace_bytes, void* stream) {
     Problem p;
     int st = check_matmul("mnb_gemm", d, M, a, b_packed, scales, zp_packed, bias, y, false, &p);
     if (st != MNB_OK) return st;
-    return run_gemm(p, static_cast<hipStream_t>(stream));
+    st = check_workspace("mnb_gemm", gemm_workspace_bytes(p), workspace, workspace_bytes);
+    if (st != MNB_OK) return st;
+    return launch_gemm(p, static_cast<hipStream_t>(stream), workspace, workspace_bytes);
 }
 
 int mnb_dequant(const mnb_desc* d, const uint8_t* b_packed, const void* scales,
@@ -320,17 +294,23 @@ int mnb_gather_rows(const mnb_desc* d, const int64_t* ids, int64_t n_ids, const 
     return launch_gather_rows(p, ids, n_ids, out, static_cast<hipStream_t>(stream));
 }
 
-int mnb_argmax(int32_t dtype, int64_t M, int64_t N, const void* x, int64_t* idx, void* stream) {
+size_t mnb_argmax_workspace_bytes(int64_t M, int64_t N) {
+    if (M < 1 || N < 1 || M > kMaxDim) return 0;
+    return argmax_workspace_bytes(M, N);
+}
+
+int mnb_argmax(int32_t dtype, int64_t M, int64_t N, const void* x, int64_t* idx, void* workspace,
+               size_t workspace_bytes, void* stream) {
     if (dtype != MNB_F32 && dtype != MNB_BF16) return fail(MNB_E_UNSUPPORTED, "mnb_argmax: dtype=%d unknown", dtype);
     if (M < 1 || N < 1) return fail(MNB_E_ARG, "mnb_argmax: M=%lld N=%lld, both must be >= 1", (long long)M, (long long)N);
     if (M > kMaxDim) return fail(MNB_E_OVERFLOW, "mnb_argmax: M=%lld exceeds 2^31-1", (long long)M);
     if (!x || !idx) return fail(MNB_E_ARG, "mnb_argmax: x and idx must be non-NULL");
     if (!aligned(x, dtype == MNB_BF16 ? 2 : 4) || !aligned(idx, 8))
         return fail(MNB_E_ALIGN, "mnb_argmax: x or idx misaligned");
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    size_t ws_bytes = 0;
-    void* ws = stream_workspace(s, argmax_workspace_bytes(M, N), &ws_bytes);
-    return launch_argmax(dtype == MNB_BF16, M, N, x, idx, s, ws, ws_bytes);
+    int st = check_workspace("mnb_argmax", argmax_workspace_bytes(M, N), workspace, workspace_bytes);
+    if (st != MNB_OK) return st;
+    return launch_argmax(dtype == MNB_BF16, M, N, x, idx, static_cast<hipStream_t>(stream), workspace,
+                         workspace_bytes);
 }
 
 int mnb_gemv_silu_mul(const mnb_desc* d, int64_t M, const void* a, const uint8_t* b_packed,
@@ -362,7 +342,29 @@ static int check_sequence(const mnb_matmul_args* ops, int64_t n_ops, std::vector
     return MNB_OK;
 }
 
-int mnb_matmul_sequence(const mnb_matmul_args* ops, int64_t n_ops, void* stream) {
+// The products of a sequence run in order on one stream, so they share one
+// workspace: the largest any of them needs.
+static size_t sequence_workspace(const std::vector<Problem>& probs) {
+    size_t need = 0;
+    for (const Problem& p : probs) {
+        const size_t b = workspace_of(p);
+        if (b > need) need = b;
+    }
+    return need;
+}
+
+size_t mnb_sequence_workspace_bytes(const mnb_matmul_args* ops, int64_t n_ops) {
+    std::vector<Problem> probs;
+    try {
+        if (check_sequence(ops, n_ops, &probs) != MNB_OK) return 0;
+    } catch (const std::bad_alloc&) {
+        return 0;
+    }
+    return sequence_workspace(probs);
+}
+
+int mnb_matmul_sequence(const mnb_matmul_args* ops, int64_t n_ops, void* workspace, size_t workspace_bytes,
+                        void* stream) {
     std::vector<Problem> probs;
     int st;
     try {
@@ -371,15 +373,18 @@ int mnb_matmul_sequence(const mnb_matmul_args* ops, int64_t n_ops, void* stream)
         return fail(MNB_E_ARG, "sequence: out of host memory");
     }
     if (st != MNB_OK) return st;
+    st = check_workspace("mnb_matmul_sequence", sequence_workspace(probs), workspace, workspace_bytes);
+    if (st != MNB_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (size_t i = 0; i < probs.size(); i++) {
-        st = run(probs[i], s);
+        st = run(probs[i], s, workspace, workspace_bytes);
         if (st != MNB_OK) return st;
     }
     return MNB_OK;
 }
 
-int mnb_graph_create(const mnb_matmul_args* ops, int64_t n_ops, mnb_graph** out) {
+int mnb_graph_create(const mnb_matmul_args* ops, int64_t n_ops, void* workspace, size_t workspace_bytes,
+                     mnb_graph** out) {
     if (!out) return fail(MNB_E_ARG, "mnb_graph_create: out is NULL");
     *out = nullptr;
     std::vector<Problem> probs;
@@ -390,42 +395,23 @@ int mnb_graph_create(const mnb_matmul_args* ops, int64_t n_ops, mnb_graph** out)
         return fail(MNB_E_ARG, "mnb_graph_create: out of host memory");
     }
     if (st != MNB_OK) return st;
-    // the graph's own workspace for split-K partials, allocated before the
-    // capture (the products run in order, so they share it)
-    size_t need = 0;
-    for (const Problem& p : probs)
-        if (!takes_gemv(p)) {
-            const size_t b = gemm_workspace_bytes(p);
-            if (b > need) need = b;
-        }
-    void* gws = nullptr;
-    if (need && hipMalloc(&gws, need) != hipSuccess) {
-        (void)hipGetLastError();
-        gws = nullptr;               // no room: the products run without splitting
-    }
+    st = check_workspace("mnb_graph_create", sequence_workspace(probs), workspace, workspace_bytes);
+    if (st != MNB_OK) return st;
     hipStream_t cs;
     hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
-    if (e != hipSuccess) {
-        if (gws) (void)hipFree(gws);
-        return fail(MNB_E_HIP, "mnb_graph_create: stream: %s", hipGetErrorString(e));
-    }
+    if (e != hipSuccess) return fail(MNB_E_HIP, "mnb_graph_create: stream: %s", hipGetErrorString(e));
     e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) {
         (void)hipStreamDestroy(cs);
-        if (gws) (void)hipFree(gws);
         return fail(MNB_E_HIP, "mnb_graph_create: begin capture: %s", hipGetErrorString(e));
     }
-    // without a workspace, pass a non-NULL zero-size one so that no product
-    // reaches for the (capturing) stream's
-    static char none;
     for (size_t i = 0; i < probs.size() && st == MNB_OK; i++)
-        st = run(probs[i], cs, gws ? gws : &none, gws ? need : 0);
+        st = run(probs[i], cs, workspace, workspace_bytes);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
     (void)hipStreamDestroy(cs);
     if (st != MNB_OK || e != hipSuccess) {
         if (graph) (void)hipGraphDestroy(graph);
-        if (gws) (void)hipFree(gws);
         if (st != MNB_OK) return st;
         return fail(MNB_E_HIP, "mnb_graph_create: end capture: %s", hipGetErrorString(e));
     }
@@ -433,14 +419,12 @@ int mnb_graph_create(const mnb_matmul_args* ops, int64_t n_ops, mnb_graph** out)
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
     if (e != hipSuccess) {
         (void)hipGraphDestroy(graph);
-        if (gws) (void)hipFree(gws);
         return fail(MNB_E_HIP, "mnb_graph_create: instantiate: %s", hipGetErrorString(e));
     }
-    mnb_graph* g = new (std::nothrow) mnb_graph{graph, exec, gws};
+    mnb_graph* g = new (std::nothrow) mnb_graph{graph, exec};
     if (!g) {
         (void)hipGraphExecDestroy(exec);
         (void)hipGraphDestroy(graph);
-        if (gws) (void)hipFree(gws);
         return fail(MNB_E_ARG, "mnb_graph_create: out of host memory");
     }
     *out = g;
@@ -458,11 +442,6 @@ int mnb_graph_destroy(mnb_graph* g) {
     if (!g) return MNB_OK;
     hipError_t e1 = hipGraphExecDestroy(g->exec);
     hipError_t e2 = hipGraphDestroy(g->graph);
-    // hipFree waits for the device, so a replay still running keeps its memory
-    if (g->ws) {
-        const hipError_t e3 = hipFree(g->ws);
-        if (e1 == hipSuccess && e2 == hipSuccess) e1 = e3;
-    }
     delete g;
     if (e1 != hipSuccess || e2 != hipSuccess)
         return fail(MNB_E_HIP, "mnb_graph_destroy: %s",

@@ -332,9 +332,12 @@ int launch_gather_rows(const Problem& p, const int64_t* ids, int64_t n_ids, void
     return launched("row gather");
 }
 
+// Rows longer than one segment (up to 65,535 rows: grid.y) keep their
+// per-segment partials in the caller's workspace; otherwise one workgroup
+// takes a row and no workspace is used.
 size_t argmax_workspace_bytes(int64_t M, int64_t N) {
     const int64_t S = argmax_segments(N);
-    return S > 1 ? (size_t)(M * S) * sizeof(Partial) : 0;
+    return S > 1 && M <= 65535 ? (size_t)(M * S) * sizeof(Partial) : 0;
 }
 
 int launch_argmax(bool bf16, int64_t M, int64_t N, const void* x, int64_t* idx, hipStream_t s, void* ws,
@@ -343,7 +346,7 @@ int launch_argmax(bool bf16, int64_t M, int64_t N, const void* x, int64_t* idx, 
     const int vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0 && N % per == 0;
     const int64_t S = argmax_segments(N);
     const size_t need = argmax_workspace_bytes(M, N);
-    if (S > 1 && ws && ws_bytes >= need && M <= 65535) {
+    if (need > 0 && ws && ws_bytes >= need) {
         // segment length: a multiple of 8 values (whole 16-byte pieces)
         const int64_t seg = ((N + S - 1) / S + 7) / 8 * 8;
         const int64_t Sused = (N + seg - 1) / seg;

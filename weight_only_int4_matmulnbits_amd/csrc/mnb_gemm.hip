@@ -1237,7 +1237,7 @@ namespace {
 
 // Which kernel a problem takes, its output tiles and its K split.
 struct Plan {
-    enum Kind { LEGACY_BF16, WIDE, REG256, REG128, F32_INT, LEGACY_F32 } kind;
+    enum Kind { LEGACY_BF16, WIDE, REG128, F32_INT, LEGACY_F32 } kind;
     int64_t tiles = 1;
     int f32_t = 2;                 // F32_INT: MFMA tiles per wavefront side (tile 64 f32_t)
     int f32_ks = F_K;              // F32_INT: K values per step (32 or 64)
@@ -1282,27 +1282,28 @@ void choose_split(Plan& pl, const Problem& p, int64_t resident, int steps, int64
     if (pl.splits > 1) pl.ws = (size_t)pl.splits * (size_t)(p.M * p.N) * 4;
 }
 
+// The plan is a function of the problem's shape alone (the ABI layer has
+// checked the alignment of A and of the scales), sized for the 256 CUs of an
+// MI355X whatever the device reports: the K split fixes the float32
+// summation order, so results do not depend on the partition mode, and the
+// workspace a caller must provide is known on the host before any HIP call.
+constexpr int64_t kPlanCUs = 256;
+
 Plan plan_gemm(const Problem& p) {
     Plan pl;
     const int esz = p.bf16 ? 2 : 4;
-    const bool vec_a = ((p.K * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(p.a) & 15) == 0);
+    const bool vec_a = (p.K * esz) % 16 == 0;
     const int64_t a_bytes = p.M * p.K * esz, b_bytes = p.N * p.col_bytes;
     const int64_t lim = int64_t(1) << 31;
-    const int64_t cus = device_compute_units();
+    const int64_t cus = kPlanCUs;
     if (p.bf16 && vec_a && (p.K % 8) == 0 && a_bytes + 256 * p.K * esz < lim &&
         b_bytes + 256 * p.col_bytes < lim && p.M * p.N < lim) {
         const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-        // (16-value blocks: the wide kernel reads a chunk's two scales as one
-        // 32-bit word)
-        const bool s_pairs = p.bs != 16 || (reinterpret_cast<uintptr_t>(p.scales) & 3) == 0;
-        if (p.M > 128 && p.K % B4_K == 0 && p.K % p.bs == 0 && s_pairs) {
+        if (p.M > 128 && p.K % B4_K == 0 && p.K % p.bs == 0) {
             pl.kind = Plan::WIDE;
             pl.tiles = big;
             choose_split(pl, p, cus, (int)(p.K / B4_K));   // one 256 x 256 workgroup per CU
             choose_tail_split(pl, cus, (int)(p.K / B4_K));
-        } else if (big >= 384) {
-            pl.kind = Plan::REG256;
-            pl.tiles = big;
         } else {
             pl.kind = Plan::REG128;
             pl.tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
@@ -1338,12 +1339,9 @@ size_t gemm_workspace_bytes(const Problem& p) { return gemv_rows_ok(p) || smallm
 int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
     if (gemv_rows_ok(p)) return launch_gemv_rows(p, s);
     if (smallm_ok(p)) return launch_smallm(p, s);
-    Plan pl = plan_gemm(p);
-    if (pl.ws && (!ws || ws_bytes < pl.ws)) {
-        pl.splits = 1;                                      // no room for partials: one pass
-        pl.sps = (int)(p.K / (pl.kind == Plan::WIDE ? B4_K : pl.kind == Plan::F32_INT ? pl.f32_ks : F_K));
-        pl.tail_tiles = 0;
-    }
+    const Plan pl = plan_gemm(p);
+    if (pl.ws && (!ws || ws_bytes < pl.ws))                 // the ABI layer checked this
+        return fail(MNB_E_ARG, "gemm: workspace of %zu bytes, %zu needed", ws ? ws_bytes : (size_t)0, pl.ws);
     GemmArgs a;
     a.a = p.a; a.b = p.b; a.scales = p.scales; a.zp = p.has_zp ? p.zp : nullptr;
     a.bias = p.bias; a.y = p.y;
@@ -1380,9 +1378,6 @@ int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
             hipLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, s, b);
             break;
         }
-        case Plan::REG256:
-            hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4>), dim3(grid), dim3(256), 0, s, b);
-            break;
         case Plan::REG128:
             hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 8>), dim3(grid), dim3(512), 0, s, b);
             break;

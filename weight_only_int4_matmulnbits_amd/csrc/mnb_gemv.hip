@@ -712,8 +712,10 @@ int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1) {
     const int esz = p.bf16 ? 2 : 4;
     a.a16 = ((p.K * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(p.a) & 15) == 0) &&
             p.K * esz < (int64_t(1) << 31);
-    // (the row kernel stages row m at m * ceil(S * CK * esz / 1 KiB) KiB)
-    const size_t lds = MR == 1 ? (size_t)a.S * CK * esz : rows_lds(p, MR);
+    // The staging writes whole 1 KiB requests (nreq per row in the kernel),
+    // so every row is rounded up to a whole KiB of LDS; the row kernel stages
+    // row m at m * ceil(S * CK * esz / 1 KiB) KiB.
+    const size_t lds = MR == 1 ? (size_t)(((int64_t)a.S * CK * esz + 1023) / 1024) * 1024 : rows_lds(p, MR);
     if (lds > kMaxLds)
         return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld needs %zu bytes of LDS", (long long)p.K, lds);
     // Fill the chip with resident teams of W wavefronts (the kernel's real
@@ -746,7 +748,7 @@ int launch_gemv(const Problem& p, hipStream_t s) { return launch(p, s, false); }
 bool gemv_rows_ok(const Problem& p) {
     if (p.M < 2 || p.M > 4 || p.bs < 32) return false;
     const int esz = p.bf16 ? 2 : 4;
-    if ((p.K * esz) % 16 != 0 || (reinterpret_cast<uintptr_t>(p.a) & 15) != 0 || p.M * p.K * esz >= (int64_t(1) << 31))
+    if ((p.K * esz) % 16 != 0 || p.M * p.K * esz >= (int64_t(1) << 31))
         return false;
     const int MR = rows_mr(p.M);
     return geometry((p.K + 31) / 32, true, 4 / MR).J > 0 && rows_lds(p, MR) <= kMaxLds;

@@ -47,13 +47,14 @@ int launch_gemv_silu(const Problem& p, hipStream_t s);
 int launch_import_qdq(const Problem& p, int axis, const uint8_t* w_q, const void* scales_q, const uint8_t* zp_q,
                       uint8_t* b_packed, void* scales, uint8_t* zp_packed, hipStream_t s);
 int launch_gather_rows(const Problem& p, const int64_t* ids, int64_t n_ids, void* out, hipStream_t s);
-// ws: the stream's workspace for per-segment partials of long rows
-// (argmax_workspace_bytes); NULL or too small: one workgroup per row.
+// ws: the caller's workspace for per-segment partials of long rows, at least
+// argmax_workspace_bytes (the ABI layer checks it).
 int launch_argmax(bool bf16, int64_t M, int64_t N, const void* x, int64_t* idx, hipStream_t s, void* ws,
                   size_t ws_bytes);
 size_t argmax_workspace_bytes(int64_t M, int64_t N);
-// ws: float32 workspace for split-K partials (ws_bytes >= gemm_workspace_bytes
-// to split; NULL or smaller: one pass without splitting).
+// ws: the caller's float32 workspace for split-K partials, at least
+// gemm_workspace_bytes (a function of the shape alone; the ABI layer checks
+// it, and launch_gemm refuses a smaller one).
 int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes);
 size_t gemm_workspace_bytes(const Problem& p);
 // 1 <= M <= 16 on the matrix cores (K % 32 == 0, block_size >= 32, A 16-byte
@@ -61,7 +62,7 @@ size_t gemm_workspace_bytes(const Problem& p);
 bool smallm_ok(const Problem& p);
 int launch_smallm(const Problem& p, hipStream_t s);
 int64_t gemv_max_k(int bs);
-int device_compute_units();   // CUs of the current device (cached)
+int device_compute_units();   // CUs of the current device (cached); sizes grids only
 
 // ---- device helpers ---------------------------------------------------------
 

@@ -328,7 +328,7 @@ bool smallm_ok(const Problem& p) {
     const int64_t lim = int64_t(1) << 31;
     return p.M >= 1 && p.M <= 16 && p.K % 32 == 0 && p.bs >= 32 &&
            spans_per_wave(p.K) <= (p.bf16 ? kMaxP16 : kMaxP32) &&
-           (reinterpret_cast<uintptr_t>(p.a) & 15) == 0 && p.M * p.K * esz < lim &&
+           p.M * p.K * esz < lim &&
            p.N * p.col_bytes < lim && (int64_t)p.N * p.nb * esz < lim;
 }
 
