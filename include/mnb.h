@@ -23,8 +23,10 @@
  * ---------------------------------------
  * Memory.   Every tensor argument is a DEVICE pointer (memory of the current
  *           HIP device), row-major and contiguous, allocated and owned by the
- *           caller.  The library allocates no device memory and keeps no
- *           pointer to caller memory after a call returns (graph handles,
+ *           caller.  The library allocates no device memory (apart from the
+ *           static array behind mnb_gemm_noalloc, loaded with the library's
+ *           device code) and keeps no pointer to caller memory after a call
+ *           returns (graph handles,
  *           below, are the one documented exception: they record the
  *           pointers given at creation).  Products that split K across
  *           workgroups (too few output tiles to fill the GPU) and ArgMax over
@@ -53,9 +55,11 @@
  *           output buffers are undefined.  No call aborts the process or
  *           throws across the ABI.  mnb_last_error() gives a human-readable
  *           detail of the most recent error on the calling thread.
- * Threads.  The library holds no mutable global state: calls are
- *           reentrant, and concurrent calls on different streams are safe
- *           when they do not share output buffers or a workspace.
+ * Threads.  The library's only mutable global state is the per-device
+ *           address of mnb_gemm_noalloc's array (looked up once, under a
+ *           lock): calls are reentrant, and concurrent calls on different
+ *           streams are safe when they do not share output buffers or a
+ *           workspace (mnb_gemm_noalloc calls on one GPU share one).
  *
  * Data layouts (N-major: every column of B is one contiguous run of bytes)
  * ------------------------------------------------------------------------
@@ -196,6 +200,26 @@ int mnb_gemm(const mnb_desc* d, int64_t M, const void* a,
              const uint8_t* b_packed, const void* scales,
              const uint8_t* zp_packed, const float* bias, void* y,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/* mnb_gemm_noalloc -- mnb_gemm for callers that cannot allocate device
+ * memory (code under HIP graph capture that must not call hipMalloc, tight
+ * serving loops, harnesses that forbid allocation): the same kernels, plan
+ * and results as mnb_gemm, but the split-K partials live in a static device
+ * array of MNB_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held
+ * from the library's first use on that GPU until the process ends) instead
+ * of a caller workspace.  Arguments and validation as for mnb_gemm, without
+ * the workspace.  A product needing more than MNB_NOALLOC_SCRATCH_BYTES
+ * returns MNB_E_UNSUPPORTED (no current plan does: a K split never holds
+ * more than 256 float32 tiles of 256 x 256 = 64 MiB).  The call itself
+ * allocates nothing; the first call on a device looks up that device's array
+ * (hipGetSymbolAddress).  Every call on one GPU shares its array: calls that
+ * may overlap on the device (different streams, graphs replayed beside other
+ * work) race on it and must be ordered by the caller. */
+#define MNB_NOALLOC_SCRATCH_BYTES (64u << 20)
+int mnb_gemm_noalloc(const mnb_desc* d, int64_t M, const void* a,
+                     const uint8_t* b_packed, const void* scales,
+                     const uint8_t* zp_packed, const float* bias, void* y,
+                     void* stream);
 
 /* mnb_dequant -- test hook: writes the dequantized weights w[N][K] (the
  * transposed logical B) so they can be compared bit-for-bit.

@@ -28,7 +28,7 @@ __all__ = [
     "scale_bytes", "zero_point_bytes", "gemv_max_k", "pack", "gemv", "gemm",
     "dequant", "PackedWeight", "Sequence", "version", "import_qdq", "qdq_is_native",
     "gather_rows", "argmax", "gemv_silu_mul", "workspace_bytes",
-    "argmax_workspace_bytes", "workspace",
+    "argmax_workspace_bytes", "workspace", "gemm_noalloc",
 ]
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
@@ -172,7 +172,10 @@ def _matmul(fn: str, a: torch.Tensor, b_packed: torch.Tensor, scales: torch.Tens
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     _need(out, "out", a.dtype, shape=(M, N))
     f = getattr(lib(), fn)
-    if fn == "mnb_gemm":
+    if fn == "mnb_gemm_noalloc":
+        check(f(ctypes.byref(d), M, _ptr(a), _ptr(b_packed), _ptr(scales), _ptr(zp_packed),
+                _ptr(bias), _ptr(out), _stream(stream)), fn)
+    elif fn == "mnb_gemm":
         wp, wn, keep = _ws(ws, workspace_bytes(d, M), a.device)
         check(f(ctypes.byref(d), M, _ptr(a), _ptr(b_packed), _ptr(scales), _ptr(zp_packed),
                 _ptr(bias), _ptr(out), wp, wn, _stream(stream)), fn)
@@ -198,6 +201,16 @@ def gemm(a, b_packed, scales, zp_packed=None, bias=None, *, K, N, block_size,
     to have one allocated through torch for this call."""
     return _matmul("mnb_gemm", a, b_packed, scales, zp_packed, bias, K, N, block_size,
                    out, stream, workspace)
+
+
+def gemm_noalloc(a, b_packed, scales, zp_packed=None, bias=None, *, K, N, block_size,
+                 out=None, stream=None) -> torch.Tensor:
+    """mnb_gemm_noalloc: the prefill GEMM with its split-K partials in the
+    library's static per-GPU array (no workspace; calls that may overlap on
+    one GPU race on that array).  `out` should be given by callers that must
+    not allocate."""
+    return _matmul("mnb_gemm_noalloc", a, b_packed, scales, zp_packed, bias, K, N, block_size,
+                   out, stream)
 
 
 DEQUANT_F32, DEQUANT_BF16, DEQUANT_INT8 = 0, 1, 2

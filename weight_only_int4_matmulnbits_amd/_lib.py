@@ -30,7 +30,7 @@ EXPORTS = (
     "mnb_last_error", "mnb_version", "mnb_import_qdq", "mnb_qdq_is_native",
     "mnb_gather_rows", "mnb_argmax", "mnb_gemv_silu_mul",
     "mnb_workspace_bytes", "mnb_argmax_workspace_bytes",
-    "mnb_sequence_workspace_bytes",
+    "mnb_sequence_workspace_bytes", "mnb_gemm_noalloc",
 )
 
 
@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
     L.mnb_gemv.restype = ctypes.c_int
     L.mnb_gemm.argtypes = [pd, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.mnb_gemm.restype = ctypes.c_int
+    L.mnb_gemm_noalloc.argtypes = [pd, i64, vp, vp, vp, vp, vp, vp, vp]
+    L.mnb_gemm_noalloc.restype = ctypes.c_int
     L.mnb_workspace_bytes.argtypes = [pd, i64]
     L.mnb_workspace_bytes.restype = sz
     L.mnb_argmax_workspace_bytes.argtypes = [i64, i64]

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -116,6 +117,42 @@ int run(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
 
 using namespace mnb;
 
+// ---- the workspace of mnb_gemm_noalloc ---------------------------------------
+// A file-scope device array: each GPU the library runs on holds its own copy
+// from module load until the process ends.  Host code never passes its name to
+// a kernel (on the host it is only a stand-in for the symbol): its device
+// address is looked up once per device with hipGetSymbolAddress and that
+// pointer is what the kernels get.
+static __device__ __align__(256) unsigned char scratch[MNB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];      // device address of `scratch`, per device
+
+// The current device's copy of `scratch`; looked up on the first call on
+// that device (the device is current), then cached.
+int scratch_for_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MNB_E_HIP, "mnb_gemm_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MNB_E_UNSUPPORTED, "mnb_gemm_noalloc: device %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(MNB_E_HIP, "mnb_gemm_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MNB_OK;
+}
+
+}  // namespace
+
 struct mnb_graph {
     hipGraph_t graph;
     hipGraphExec_t exec;
@@ -202,6 +239,25 @@ int mnb_gemm(const mnb_desc* d, int64_t M, const void* a, const uint8_t* b_packe
     st = check_workspace("mnb_gemm", gemm_workspace_bytes(p), workspace, workspace_bytes);
     if (st != MNB_OK) return st;
     return launch_gemm(p, static_cast<hipStream_t>(stream), workspace, workspace_bytes);
+}
+
+int mnb_gemm_noalloc(const mnb_desc* d, int64_t M, const void* a, const uint8_t* b_packed,
+                     const void* scales, const uint8_t* zp_packed, const float* bias, void* y,
+                     void* stream) {
+    Problem p;
+    int st = check_matmul("mnb_gemm_noalloc", d, M, a, b_packed, scales, zp_packed, bias, y, false, &p);
+    if (st != MNB_OK) return st;
+    const size_t need = gemm_workspace_bytes(p);
+    if (need > (size_t)MNB_NOALLOC_SCRATCH_BYTES)
+        return fail(MNB_E_UNSUPPORTED,
+                    "mnb_gemm_noalloc: this product needs %zu bytes of workspace, beyond the %u-byte static "
+                    "scratch (use mnb_gemm with a caller workspace)", need, (unsigned)MNB_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != MNB_OK) return st;
+    // the split partials are written in full before they are read: nothing in
+    // the scratch needs clearing between calls
+    return launch_gemm(p, static_cast<hipStream_t>(stream), ws, (size_t)MNB_NOALLOC_SCRATCH_BYTES);
 }
 
 int mnb_dequant(const mnb_desc* d, const uint8_t* b_packed, const void* scales,
