@@ -616,6 +616,38 @@ def traffic_from(fetch_dir, write_dir, cfg, copy_mib, kind="gemv"):
     return "\n".join(lines)
 
 
+def counters_from(dirs, cus=256):
+    """Per-kernel averages of the counters of one or more rocprofv3 `--pmc`
+    runs (run_counter_collection.csv), library kernels only, plus the derived
+    fractions that need them: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
+    (GRBM_GUI_ACTIVE x CUs x 4 SIMDs), wait = SQ_WAIT_INST_ANY /
+    SQ_WAVE_CYCLES, LDS bank conflicts per LDS instruction."""
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in dirs:
+        for r in _read_csv(os.path.join(d, "run_counter_collection.csv")):
+            if "mnb::" not in r["Kernel_Name"] or "pack_" in r["Kernel_Name"]:
+                continue
+            per[_short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = []
+    for k, cs in sorted(per.items(), key=lambda kv: -len(next(iter(kv[1].values())))):
+        n = max(len(v) for v in cs.values())
+        avg = {c: sum(v) / len(v) for c, v in cs.items()}
+        out.append(f"{k}  ({n} dispatches)")
+        for c in sorted(avg):
+            out.append(f"    {c:<28} {avg[c]:16.1f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg and avg["GRBM_GUI_ACTIVE"] > 0:
+            out.append(f"    -> MFMA busy {100 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (avg['GRBM_GUI_ACTIVE'] * cus * 4):.1f} % "
+                       f"of {cus} CUs x 4 SIMDs over the kernel's GPU-active cycles")
+        if "SQ_WAIT_INST_ANY" in avg and avg.get("SQ_WAVE_CYCLES", 0) > 0:
+            out.append(f"    -> waiting on any instruction {100 * avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.1f} % "
+                       f"of wave cycles")
+        if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_INSTS_LDS", 0) > 0:
+            out.append(f"    -> {avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_INSTS_LDS']:.3f} LDS bank-conflict cycles "
+                       f"per LDS instruction")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -637,6 +669,8 @@ def main():
     ap.add_argument("--bench-json", metavar="FILE",
                     help="with --summarize-trace: the JSON line the traced run printed, to state "
                          "the tracer's overhead against the same run's untraced timing")
+    ap.add_argument("--counters-from", nargs="+", metavar="DIR",
+                    help="per-kernel averages of rocprofv3 --pmc runs of this bench and exit; no GPU")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="derive HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
                          "runs of this bench (same --config, --copy-calibration), update "
@@ -645,6 +679,9 @@ def main():
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.config, args.steps, args.warmup, args.samples,
                               args.bench_json))
+        return
+    if args.counters_from:
+        print(counters_from(args.counters_from))
         return
     if args.traffic_from:
         from workloads import workload

@@ -8,26 +8,32 @@
 //
 // Mapping on CDNA4.  One v_mfma_f32_16x16x32_bf16 multiplies 16 rows of A (rows
 // past M are zeros) by 32 K values of 16 columns (a "column group").  K is cut
-// into spans of 128 values; wavefront w of a workgroup owns spans w, w + WV,
-// ... (P of them) and keeps their activations in registers as MFMA operands.
-// The workgroup then walks over column groups (grid-stride, the next groups'
-// weights in flight in two register stages).  For a span, lane l = c + 16 g
-// reads the 16 packed bytes (32 values, K offset 32 g of the span) of column c
-// of the group; a 4 x 4 word transpose across the four 16-lane rows
-// (v_permlane32_swap, v_permlane16_swap) gives lane (c, g) word t = values
-// 32 t + 8 g .. 32 t + 8 g + 7: exactly the B operand of MFMA t, whose 32
-// values all lie in one quantization block (block_size >= 32, K % 32 == 0).
+// into spans of 128 values (four MFMA slices of 32).  A workgroup of WV
+// wavefronts stages A once in LDS, already in the MFMA operand layout
+// (float32 activations as a bf16 head and tail, a = hi + lo), for as many
+// spans as fit (a "pass"; longer K is staged pass by pass).  It then walks
+// over "group sets" of up to four column groups; wavefront w takes spans w,
+// w + WV, ... of every column group of the set, so each weight byte is read by
+// exactly one wavefront and one staged activation slice serves the whole set.
+// Weights stream through two register stages (the next item's loads are in
+// flight while one is multiplied).  For a span, lane l = c + 16 g reads the 16
+// packed bytes (32 values, K offset 32 g of the span) of column c; a 4 x 4
+// word transpose across the four 16-lane rows (v_permlane32_swap,
+// v_permlane16_swap) gives lane (c, g) word t = values 32 t + 8 g ..
+// 32 t + 8 g + 7: exactly the B operand of slice t, whose 32 values all lie
+// in one quantization block (block_size >= 32, K % 32 == 0).  The wavefronts'
+// partial sums of a set meet in LDS once, at the end of the set.
 //
 // Arithmetic.  The B operand holds the exact integers q - zp (|q - zp| <= 15
-// is exact in bf16).  float32 activations are split into a bf16 head and
-// tail (a = hi + lo), two MFMAs; bfloat16 activations are one term.  Each
-// MFMA starts from zero and its float32 result, one column per lane, is
-// folded into the accumulators with that column's block scale:
-// acc += s * partial.  The wavefronts' partial sums meet in LDS and are added
-// in wavefront order.  P and WV depend only on K, so a column's summation
-// order does not depend on N or on the column's position: concatenated
-// launches (fused QKV, gate||up) are bit-identical to separate ones.  No
-// atomics, no workspace.
+// is exact in bf16).  Each slice's MFMA (two for float32: head, then tail)
+// starts from zero and its float32 result, one column per lane, is folded
+// into the accumulators with that column's block scale: acc += s * partial,
+// slice by slice in K order within a wavefront; the WV wavefront sums are
+// then added in wavefront order.  WV depends only on K, so a column's
+// summation order does not depend on N or on the column's position:
+// concatenated launches (fused QKV, gate||up) are bit-identical to separate
+// ones.  With one nonzero activation the result is float32((q - zp) * s)
+// exactly.  No atomics, no workspace.
 #include "mnb_internal.h"
 
 namespace mnb {
@@ -37,9 +43,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSpan = 128;          // K values per span
-constexpr int kMaxWaves = 8;        // wavefronts per workgroup (split K)
-constexpr uint32_t kOob = 0x80000000u;    // offset past any resource: reads zero
+constexpr int kSpan = 128;                  // K values per span
+constexpr int kNG = 4;                      // column groups per set (at most)
+constexpr int kMaxWV = 8;                   // wavefronts per workgroup
+constexpr int kStageMax = 128 * 1024;       // LDS for staged activations
+constexpr uint32_t kOob = 0x80000000u;      // offset past any resource: reads zero
 
 struct SmallArgs {
     const void* a;
@@ -50,58 +58,121 @@ struct SmallArgs {
     void* y;
     int M, K, N;
     int col_bytes, nb, zp_row, log2_bs;
-    int spans, n_groups;
+    int spans;              // ceil(K / 128)
+    int ngw;                // column groups per set (1 .. kNG)
+    int n_sets;             // ceil(ceil(N / 16) / ngw)
+    int pass_spans;         // spans staged per pass, a multiple of WV
+    int passes;             // ceil(spans / pass_spans)
+    int ipw;                // items per wavefront per set: ceil(spans / WV)
+    int ipp;                // items per wavefront per pass: pass_spans / WV
+    int log2_mr;            // rows of A staged: 8 (M <= 8) or 16
     uint32_t a_bytes, b_bytes, s_bytes, z_bytes;
 };
 
-// The weight loads of one column group over a wavefront's P spans, kept raw
-// (decoding here would make the wavefront wait for the loads it just issued).
-template <int NG, int P>
-struct Stage {
-    u32x4 w[NG][P];              // 32 packed values per lane, group and span
-    uint32_t s[NG][P][4];        // scale bits of slice t
-    uint8_t z[NG][P][4];         // zero-point byte of slice t
-    uint32_t bias;               // wavefront u < NG: float32 bits of the bias of
-                                 // group u's column c (0 without a bias)
+// NSB distinct scale blocks per span (4 for 32-value blocks, 2 for 64, 1 for
+// larger), NZB zero-point bytes per span (two blocks per byte).  With SV the
+// NSB scales of a span are one aligned vector load and its zero-point bytes
+// one load (nb a multiple of NSB); otherwise one load each.
+template <int NG, int NSB>
+struct Item {
+    static constexpr int NZB = (NSB + 1) / 2;
+    u32x4 w[NG];             // 32 packed values per lane and group
+    uint32_t s[NG][NSB];     // scale bits
+    uint32_t z[NG][NZB];     // zero-point bytes
+    uint32_t bias;           // float32 bits of the bias of column c of group `wave`
 };
 
-// groups gi .. gi + NG - 1 (those past the last read zeros)
-template <bool BF16, bool HAS_ZP, int NG, int P>
-__device__ __forceinline__ void load_stage(const SmallArgs& g, int64_t gi, int wave, int WV, int lane,
-                                           __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rs,
-                                           __amdgpu_buffer_rsrc_t rz, __amdgpu_buffer_rsrc_t rbias,
-                                           Stage<NG, P>& st) {
+struct Res {
+    __amdgpu_buffer_rsrc_t a, b, s, z, bias;
+};
+
+// The loads of item f of this wavefront: set r = f / ipw of this workgroup,
+// span wave + (f % ipw) * WV, every column group of the set.  Items past the
+// last set or span, values past K and columns past N read zeros (offsets
+// forced past the resources), so every lane issues the same loads whatever
+// the shape.
+template <bool BF16, bool HAS_ZP, int NG, int NSB, bool SV>
+__device__ __forceinline__ void load_item(const SmallArgs& g, const Res& rr, int f, int wave, int WV, int lane,
+                                          Item<NG, NSB>& it) {
     constexpr int ESZ = BF16 ? 2 : 4;
+    constexpr int SPB = 4 / NSB;                 // slices per scale block
     const int c = lane & 15, grp = lane >> 4;
-    // the bias goes with the weights: a load issued late and consumed at once
-    // would wait for every load in flight (they complete in order)
+    const int r = f / g.ipw;
+    const int span = wave + (f - r * g.ipw) * WV;
+    const int set = (int)blockIdx.x + r * (int)gridDim.x;
+    const uint32_t set_out = set < g.n_sets ? 0u : kOob;
+    const uint32_t span_out = span < g.spans ? 0u : kOob;
     {
-        const int col = (int)(gi + (wave < NG ? wave : 0)) * 16 + c;
-        st.bias = __builtin_amdgcn_raw_buffer_load_b32(rbias, (uint32_t)col * 4u | (col < g.N ? 0u : kOob), 0, 0);
+        const int col = (set * g.ngw + (wave < g.ngw ? wave : 0)) * 16 + c;
+        it.bias = __builtin_amdgcn_raw_buffer_load_b32(rr.bias, (uint32_t)col * 4u | set_out | (col < g.N ? 0u : kOob),
+                                                       0, 0);
     }
 #pragma unroll
     for (int u = 0; u < NG; u++) {
-    const int col = (int)(gi + u) * 16 + c;
-    const uint32_t c_out = col < g.N ? 0u : kOob;
-#pragma unroll
-    for (int j = 0; j < P; j++) {
-        const int sp = wave + j * WV;
-        const uint32_t w_out = (sp * kSpan + 32 * grp < g.K ? 0u : kOob) | c_out;
-        st.w[u][j] = __builtin_amdgcn_raw_buffer_load_b128(
-            rb, ((uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)(sp * 64 + 16 * grp)) | w_out, 0, 0);
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            const int k0 = sp * kSpan + 32 * t;
-            const uint32_t out = (k0 < g.K ? 0u : kOob) | c_out;
+        const int col = (set * g.ngw + u) * 16 + c;
+        const uint32_t o = ((u < g.ngw && col < g.N) ? set_out : kOob) | span_out;
+        const uint32_t kw = (span * kSpan + 32 * grp < g.K) ? 0u : kOob;
+        it.w[u] = __builtin_amdgcn_raw_buffer_load_b128(
+            rr.b, ((uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)(span * 64 + 16 * grp)) | o | kw, 0, 0);
+        if constexpr (SV) {
+            // the span's NSB consecutive scales and NZB consecutive zero-point
+            // bytes, each as one load (aligned: nb is a multiple of NSB)
+            const int k0 = span * kSpan;
             const uint32_t blk = (uint32_t)k0 >> g.log2_bs;
-            const uint32_t os = (((uint32_t)col * (uint32_t)g.nb + blk) * ESZ) | out;
-            st.s[u][j][t] = BF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0)
-                                 : __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
-            if constexpr (HAS_ZP)
-                st.z[u][j][t] = __builtin_amdgcn_raw_buffer_load_b8(
-                    rz, ((uint32_t)col * (uint32_t)g.zp_row + (blk >> 1)) | out, 0, 0);
+            const uint32_t os = (((uint32_t)col * (uint32_t)g.nb + blk) * ESZ) | o | (k0 < g.K ? 0u : kOob);
+            if constexpr (NSB * ESZ == 16) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rr.s, os, 0, 0);
+#pragma unroll
+                for (int b = 0; b < 4; b++) it.s[u][b] = v[b];
+            } else if constexpr (NSB * ESZ == 8) {
+                const uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rr.s, os, 0, 0));
+                if constexpr (BF16) {
+#pragma unroll
+                    for (int b = 0; b < 4; b++) it.s[u][b] = (uint32_t)(v >> (16 * b)) & 0xFFFFu;
+                } else {
+                    it.s[u][0] = (uint32_t)v;
+                    it.s[u][1] = (uint32_t)(v >> 32);
+                }
+            } else if constexpr (NSB * ESZ == 4) {
+                const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rr.s, os, 0, 0);
+                if constexpr (BF16 && NSB == 2) {
+                    it.s[u][0] = v & 0xFFFFu;
+                    it.s[u][1] = v >> 16;
+                } else {
+                    it.s[u][0] = v;
+                }
+            } else {
+                it.s[u][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rr.s, os, 0, 0);
+            }
+            if constexpr (HAS_ZP) {
+                const uint32_t oz = ((uint32_t)col * (uint32_t)g.zp_row + (blk >> 1)) | o | (k0 < g.K ? 0u : kOob);
+                if constexpr (Item<NG, NSB>::NZB == 2) {
+                    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b16(rr.z, oz, 0, 0);
+                    it.z[u][0] = v & 0xFFu;
+                    it.z[u][1] = v >> 8;
+                } else {
+                    it.z[u][0] = __builtin_amdgcn_raw_buffer_load_b8(rr.z, oz, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < NSB; b++) {
+                const int k0 = span * kSpan + 32 * SPB * b;
+                const uint32_t blk = (uint32_t)k0 >> g.log2_bs;
+                const uint32_t os = (((uint32_t)col * (uint32_t)g.nb + blk) * ESZ) | o | (k0 < g.K ? 0u : kOob);
+                it.s[u][b] = BF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rr.s, os, 0, 0)
+                                  : __builtin_amdgcn_raw_buffer_load_b32(rr.s, os, 0, 0);
+            }
+            if constexpr (HAS_ZP) {
+#pragma unroll
+                for (int b = 0; b < Item<NG, NSB>::NZB; b++) {
+                    const int k0 = span * kSpan + 64 * SPB * b;
+                    const uint32_t blk = (uint32_t)k0 >> g.log2_bs;
+                    it.z[u][b] = __builtin_amdgcn_raw_buffer_load_b8(
+                        rr.z, ((uint32_t)col * (uint32_t)g.zp_row + (blk >> 1)) | o | (k0 < g.K ? 0u : kOob), 0, 0);
+                }
+            }
         }
-    }
     }
 }
 
@@ -115,188 +186,268 @@ __device__ __forceinline__ void transpose_rows(u32x4& w) {
     w = u32x4{q01[0], q01[1], q23[0], q23[1]};
 }
 
-template <bool BF16, bool HAS_ZP, int NG, int P>
-__global__ __launch_bounds__(64 * kMaxWaves) void smallm_kernel(SmallArgs g) {
-    __shared__ f32x4 red[2][NG][kMaxWaves * 64];    // partial sums, two buffers in turn
+// Stages the activations of the pass's spans into LDS: for the first mr
+// rows (8 when M <= 8, else 16), slice j (32 values) of the pass at
+// hi[(j * 4 + g) * mr + row] (and lo): values 8 g .. 8 g + 7 of the slice for
+// that row, the A operand of MFMA lane row + 16 g; rows past M and values
+// past K are zeros (rows past mr are never stored: their lanes read zeros).  Each thread requests kStageU pieces before it
+// converts any (a load consumed at once would serialize the round trips).
+constexpr int kStageU = 8;
 
+template <bool BF16>
+struct StageRegs {
+    u32x4 x[kStageU][BF16 ? 1 : 2];
+};
+
+// Requests pieces base .. of the pass into registers.
+template <bool BF16>
+__device__ __forceinline__ void stage_issue(const SmallArgs& g, const Res& rr, int pass, int base, StageRegs<BF16>& st) {
+    constexpr int ESZ = BF16 ? 2 : 4;
+    constexpr int AV = BF16 ? 1 : 2;             // 16-byte loads per piece
+    const int n = (g.pass_spans * 16) << g.log2_mr;
+    const int mr = 1 << g.log2_mr;
+#pragma unroll
+    for (int j = 0; j < kStageU; j++) {
+        const int idx = base + j * (int)blockDim.x + (int)threadIdx.x;
+        const int sl = idx >> (g.log2_mr + 2), rem = idx & (4 * mr - 1);
+        const int row = rem & (mr - 1);
+        const int k0 = (pass * g.pass_spans * 4 + sl) * 32 + 8 * (rem >> g.log2_mr);
+        const uint32_t out = (idx < n && row < g.M && k0 < g.K) ? 0u : kOob;
+        const uint32_t off = (((uint32_t)row * (uint32_t)g.K + (uint32_t)k0) * ESZ) | out;
+#pragma unroll
+        for (int v = 0; v < AV; v++) st.x[j][v] = __builtin_amdgcn_raw_buffer_load_b128(rr.a, off + 16 * v, 0, 0);
+    }
+}
+
+// Converts requested pieces to the bf16 head (and tail) and writes them.
+template <bool BF16>
+__device__ __forceinline__ void stage_finish(const SmallArgs& g, int base, const StageRegs<BF16>& st, u32x4* hi,
+                                             u32x4* lo) {
+    constexpr int AV = BF16 ? 1 : 2;
+    const int n = (g.pass_spans * 16) << g.log2_mr;
+#pragma unroll
+    for (int j = 0; j < kStageU; j++) {
+        const int idx = base + j * (int)blockDim.x + (int)threadIdx.x;
+        float v[8];
+        if constexpr (BF16) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                v[2 * e] = __uint_as_float(st.x[j][0][e] << 16);
+                v[2 * e + 1] = __uint_as_float(st.x[j][0][e] & 0xFFFF0000u);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                v[e] = __uint_as_float(st.x[j][0][e]);
+                v[4 + e] = __uint_as_float(st.x[j][AV - 1][e]);
+            }
+        }
+        bf16x8 h, t;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            h[e] = (__bf16)v[e];
+            if constexpr (!BF16) t[e] = (__bf16)(v[e] - (float)h[e]);
+        }
+        if (idx < n) {
+            hi[idx] = __builtin_bit_cast(u32x4, h);
+            if constexpr (!BF16) lo[idx] = __builtin_bit_cast(u32x4, t);
+        }
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void stage_pass(const SmallArgs& g, const Res& rr, int pass, u32x4* hi, u32x4* lo) {
+    const int n = (g.pass_spans * 16) << g.log2_mr;
+    for (int base = 0; base < n; base += kStageU * (int)blockDim.x) {
+        StageRegs<BF16> st;
+        stage_issue<BF16>(g, rr, pass, base, st);
+        stage_finish<BF16>(g, base, st, hi, lo);
+    }
+}
+
+template <bool BF16, bool HAS_ZP, int NG, int NSB, bool SV>
+__global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
+    extern __shared__ __attribute__((aligned(16))) u32x4 lds[];
     const int WV = blockDim.x >> 6;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, grp = lane >> 4;
+    const int mr = 1 << g.log2_mr;
+    const int pieces = (g.pass_spans * 16) << g.log2_mr;    // staged 16-byte pieces per term
+    u32x4* hi = lds;
+    u32x4* lo = lds + pieces;
+    f32x4* red = reinterpret_cast<f32x4*>(lds + pieces * (BF16 ? 1 : 2));   // [WV][NG][64]
 
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(g.a), (short)0, (int)g.a_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(g.b), (short)0, (int)g.b_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(g.scales), (short)0, (int)g.s_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(HAS_ZP ? g.zp : g.b), (short)0, (int)(HAS_ZP ? g.z_bytes : 0), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rbias = __builtin_amdgcn_make_buffer_rsrc(
+    Res rr;
+    rr.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.a), (short)0, (int)g.a_bytes, 0x00020000);
+    rr.b = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.b), (short)0, (int)g.b_bytes, 0x00020000);
+    rr.s = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.scales), (short)0, (int)g.s_bytes, 0x00020000);
+    rr.z = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(HAS_ZP ? g.zp : g.b), (short)0,
+                                             (int)(HAS_ZP ? g.z_bytes : 0), 0x00020000);
+    rr.bias = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(g.bias ? g.bias : reinterpret_cast<const float*>(g.b)), (short)0,
         g.bias ? (int)(4 * g.N) : 0, 0x00020000);
 
-    // this wavefront's activations (requested first, so that waiting for them
-    // leaves the weights below in flight): row c, values 32 t + 8 g .. + 7 of
-    // each of its spans; rows past M and values past K read zeros
-    constexpr int ESZ = BF16 ? 2 : 4;
-    constexpr int AV = BF16 ? 1 : 2;              // 16-byte pieces per slice
-    u32x4 araw[P][4][AV];
-#pragma unroll
-    for (int j = 0; j < P; j++) {
-        const int sp = wave + j * WV;
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            const int k0 = sp * kSpan + 32 * t;
-            const uint32_t out = k0 < g.K ? 0u : kOob;
-            const uint32_t off = ((uint32_t)c * (uint32_t)g.K + (uint32_t)(k0 + 8 * grp)) * ESZ;
-#pragma unroll
-            for (int v = 0; v < AV; v++)
-                araw[j][t][v] = __builtin_amdgcn_raw_buffer_load_b128(ra, (off + 16 * v) | out, 0, 0);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);    // keep the activation requests first
+    // this workgroup's sets and items (workgroup-uniform)
+    const int my_sets = (int)blockIdx.x < g.n_sets ? (g.n_sets - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    const int total = my_sets * g.ipw;
 
-    // the first two iterations' weights; an iteration takes NG consecutive
-    // column groups.  Every stage is loaded, also past the last group (its
-    // loads read zeros): conditional loads would make the compiler wait for
-    // all loads in flight wherever the paths meet
-    const int64_t stride = (int64_t)gridDim.x * NG;
-    int64_t gi = (int64_t)blockIdx.x * NG;
-    Stage<NG, P> s0, s1;
-    load_stage<BF16, HAS_ZP, NG, P>(g, gi, wave, WV, lane, rb, rs, rz, rbias, s0);
-    load_stage<BF16, HAS_ZP, NG, P>(g, gi + stride, wave, WV, lane, rb, rs, rz, rbias, s1);
+    // one pass holds all of K: staged once.  The first pieces are requested
+    // before the first item's weights and converted after (loads complete in
+    // order: the weights stay in flight while A is written); the second
+    // item's weights follow (both at once could exceed the 63 loads the
+    // wait counter tracks)
+    Item<NG, NSB> s0, s1;
+    if (g.passes == 1) {
+        const int n = pieces;
+        StageRegs<BF16> st;
+        stage_issue<BF16>(g, rr, 0, 0, st);
+        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, 0, wave, WV, lane, s0);
+        stage_finish<BF16>(g, 0, st, hi, lo);
+        for (int base = kStageU * (int)blockDim.x; base < n; base += kStageU * (int)blockDim.x) {
+            stage_issue<BF16>(g, rr, 0, base, st);
+            stage_finish<BF16>(g, base, st, hi, lo);
+        }
+        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, 1, wave, WV, lane, s1);
+        __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the LDS writes
+        asm volatile("s_barrier" : : : "memory");
+    } else {
+        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, 0, wave, WV, lane, s0);
+        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, 1, wave, WV, lane, s1);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
-    // the activations as MFMA A operands (float32: bf16 head and tail)
-    bf16x8 ahi[P][4], alo[P][4];
+    f32x4 acc[NG];
 #pragma unroll
-    for (int j = 0; j < P; j++) {
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            float v[8];
-            if constexpr (BF16) {
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    v[2 * e] = __uint_as_float(araw[j][t][0][e] << 16);
-                    v[2 * e + 1] = __uint_as_float(araw[j][t][0][e] & 0xFFFF0000u);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    v[e] = __uint_as_float(araw[j][t][0][e]);
-                    v[4 + e] = __uint_as_float(araw[j][t][AV - 1][e]);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                ahi[j][t][e] = (__bf16)v[e];
-                if constexpr (!BF16) alo[j][t][e] = (__bf16)(v[e] - (float)ahi[j][t][e]);
-            }
-        }
-    }
+    for (int u = 0; u < NG; u++) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // NG column groups: this wavefront's partial sums over its spans, then
-    // the wavefronts' sums meet in LDS buffer `buf`
-    auto group = [&](const Stage<NG, P>& st, int64_t gcur, int buf) {
-#pragma unroll
-        for (int u = 0; u < NG; u++) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < P; j++) {
-            const int sp = wave + j * WV;
-            u32x4 w = st.w[u][j];
-            transpose_rows(w);
+    auto step = [&](const Item<NG, NSB>& it, int f) {
+        const int r = f / g.ipw;
+        const int i = f - r * g.ipw;
+        // a new pass: every wavefront is done with the previous one, then
+        // the next pass is staged (this waits for the weights in flight too)
+        if (g.passes > 1 && i % g.ipp == 0) {
+            asm volatile("s_barrier" : : : "memory");
+            stage_pass<BF16>(g, rr, i / g.ipp, hi, lo);
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            asm volatile("s_barrier" : : : "memory");
+        }
+        const int span = wave + i * WV;
+        if (span < g.spans) {
+            const int ls = (span - (i / g.ipp) * g.pass_spans) * 4;     // its first slice in LDS
+            // lanes of rows past mr read a stored row and take zeros instead
+            const int pos = grp * mr + (c & (mr - 1));
+            const bool live = c < mr;
+            bf16x8 ah[4], al[4];
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                const uint32_t blk = (uint32_t)(sp * kSpan + 32 * t) >> g.log2_bs;
-                float zf = 8.f;
-                if constexpr (HAS_ZP) zf = (float)__builtin_amdgcn_ubfe((uint32_t)st.z[u][j][t], 4u * (blk & 1u), 4);
-                const uint32_t lo = opaque_and(w[t], 0x0F0F0F0Fu);
-                const uint32_t hi = opaque_and(w[t] >> 4, 0x0F0F0F0Fu);
-                bf16x8 bq;
-                bq[0] = (__bf16)(ubyte_to_f32<0>(lo) - zf); bq[1] = (__bf16)(ubyte_to_f32<0>(hi) - zf);
-                bq[2] = (__bf16)(ubyte_to_f32<1>(lo) - zf); bq[3] = (__bf16)(ubyte_to_f32<1>(hi) - zf);
-                bq[4] = (__bf16)(ubyte_to_f32<2>(lo) - zf); bq[5] = (__bf16)(ubyte_to_f32<2>(hi) - zf);
-                bq[6] = (__bf16)(ubyte_to_f32<3>(lo) - zf); bq[7] = (__bf16)(ubyte_to_f32<3>(hi) - zf);
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[j][t], bq, zero, 0, 0, 0);
-                if constexpr (!BF16) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[j][t], bq, d, 0, 0, 0);
-                const float sc = BF16 ? __uint_as_float(st.s[u][j][t] << 16) : __uint_as_float(st.s[u][j][t]);
+                const u32x4 zero4 = {0u, 0u, 0u, 0u};
+                const u32x4 xh = hi[(ls + t) * 4 * mr + pos];
+                ah[t] = __builtin_bit_cast(bf16x8, live ? xh : zero4);
+                if constexpr (!BF16) {
+                    const u32x4 xl = lo[(ls + t) * 4 * mr + pos];
+                    al[t] = __builtin_bit_cast(bf16x8, live ? xl : zero4);
+                }
+            }
 #pragma unroll
-                for (int i = 0; i < 4; i++) acc[i] = fmaf(sc, d[i], acc[i]);
+            for (int u = 0; u < NG; u++) {
+                if (u >= g.ngw) break;
+                u32x4 w = it.w[u];
+                transpose_rows(w);
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    constexpr int SPB = 4 / NSB;
+                    const int b = t / SPB;
+                    float zf = 8.f;
+                    if constexpr (HAS_ZP) {
+                        const uint32_t blk = (uint32_t)(span * kSpan + 32 * t) >> g.log2_bs;
+                        constexpr int NZB = Item<NG, NSB>::NZB;
+                        zf = (float)__builtin_amdgcn_ubfe(it.z[u][b / 2 < NZB ? b / 2 : 0], 4u * (blk & 1u), 4);
+                    }
+                    const uint32_t lo4 = opaque_and(w[t], 0x0F0F0F0Fu);
+                    const uint32_t hi4 = opaque_and(w[t] >> 4, 0x0F0F0F0Fu);
+                    bf16x8 bq;
+                    bq[0] = (__bf16)(ubyte_to_f32<0>(lo4) - zf); bq[1] = (__bf16)(ubyte_to_f32<0>(hi4) - zf);
+                    bq[2] = (__bf16)(ubyte_to_f32<1>(lo4) - zf); bq[3] = (__bf16)(ubyte_to_f32<1>(hi4) - zf);
+                    bq[4] = (__bf16)(ubyte_to_f32<2>(lo4) - zf); bq[5] = (__bf16)(ubyte_to_f32<2>(hi4) - zf);
+                    bq[6] = (__bf16)(ubyte_to_f32<3>(lo4) - zf); bq[7] = (__bf16)(ubyte_to_f32<3>(hi4) - zf);
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                    f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], bq, zero, 0, 0, 0);
+                    if constexpr (!BF16) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[t], bq, d, 0, 0, 0);
+                    const float sc = BF16 ? __uint_as_float(it.s[u][b] << 16) : __uint_as_float(it.s[u][b]);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) acc[u][e] = fmaf(sc, d[e], acc[u][e]);
+                }
             }
         }
-        red[buf][u][wave * 64 + lane] = acc;
-        }
-        // LDS writes done, then meet (a fenced barrier would also wait for
-        // the weight loads in flight)
-        __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
-        asm volatile("s_barrier" : : : "memory");
-        // wavefront u < NG adds up group u in wavefront order and stores it:
-        // lane (c, g) holds rows 4 g .. 4 g + 3 of column c
-        if (wave < NG) {
-            // unrolled to the largest team with the missing slots added as
-            // +0 (x + 0 == x): a loop here would cost precise waits for the
-            // weights in flight
-            f32x4 v = red[buf][wave][lane];
+        // the end of a set: the wavefronts' sums meet in LDS (in wavefront
+        // order) and wavefront u stores group u; the first barrier keeps the
+        // buffer from being rewritten while the previous set is read
+        if (i == g.ipw - 1) {
+            asm volatile("s_barrier" : : : "memory");
 #pragma unroll
-            for (int w2 = 1; w2 < kMaxWaves; w2++) {
-                const f32x4 x = red[buf][wave][w2 * 64 + lane];
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                v += w2 < WV ? x : zero;
+            for (int u = 0; u < NG; u++) {
+                red[(wave * NG + u) * 64 + lane] = acc[u];
+                acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            const int col = (int)(gcur + wave) * 16 + c;
-            const float bv = __uint_as_float(st.bias);
-            if (col < g.N) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            asm volatile("s_barrier" : : : "memory");
+            if (wave < g.ngw) {
+                f32x4 v = red[wave * 64 + lane];
+                // unrolled to the largest workgroup, the missing wavefronts
+                // adding +0 (x + 0 == x): a loop would cost precise waits for
+                // the weights in flight
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int m = 4 * grp + i;
-                    if (m < g.M) {
-                        if constexpr (BF16)
-                            static_cast<uint16_t*>(g.y)[(int64_t)m * g.N + col] = f32_to_bf16_rtne(v[i] + bv);
-                        else
-                            static_cast<float*>(g.y)[(int64_t)m * g.N + col] = v[i] + bv;
+                for (int w2 = 1; w2 < kMaxWV; w2++) {
+                    const f32x4 x = red[((w2 < WV ? w2 : 0) * NG + wave) * 64 + lane];
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                    v += w2 < WV ? x : zero;
+                }
+                const int set = (int)blockIdx.x + r * (int)gridDim.x;
+                const int col = (set * g.ngw + wave) * 16 + c;
+                const float bv = __uint_as_float(it.bias);
+                if (col < g.N) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int m = 4 * grp + e;
+                        if (m < g.M) {
+                            if constexpr (BF16)
+                                static_cast<uint16_t*>(g.y)[(int64_t)m * g.N + col] = f32_to_bf16_rtne(v[e] + bv);
+                            else
+                                static_cast<float*>(g.y)[(int64_t)m * g.N + col] = v[e] + bv;
+                        }
                     }
                 }
             }
         }
     };
 
-    // gi is workgroup-uniform, so every wavefront reaches every barrier; the
-    // two LDS buffers alternate, so one barrier per group suffices (buffer b
-    // is rewritten only after the next group's barrier)
-    for (; gi < g.n_groups; gi += 2 * stride) {
-        group(s0, gi, 0);
-        load_stage<BF16, HAS_ZP, NG, P>(g, gi + 2 * stride, wave, WV, lane, rb, rs, rz, rbias, s0);
+    // f is workgroup-uniform, so every wavefront reaches every barrier
+    for (int f = 0; f < total; f += 2) {
+        step(s0, f);
+        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, f + 2, wave, WV, lane, s0);
         __builtin_amdgcn_sched_barrier(0);
-        if (gi + stride < g.n_groups) group(s1, gi + stride, 1);
-        load_stage<BF16, HAS_ZP, NG, P>(g, gi + 3 * stride, wave, WV, lane, rb, rs, rz, rbias, s1);
+        if (f + 1 < total) step(s1, f + 1);
+        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, f + 3, wave, WV, lane, s1);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 using SmallFn = void (*)(SmallArgs);
 
-// spans per wavefront: the activations of P spans stay in registers
-constexpr int kMaxP32 = 3, kMaxP16 = 4;
-
-int spans_per_wave(int64_t K) {
-    const int64_t spans = (K + kSpan - 1) / kSpan;
-    return (int)((spans + kMaxWaves - 1) / kMaxWaves);
+template <bool BF16, bool HAS_ZP, int NG, bool SV>
+SmallFn pick_ng(int nsb) {
+    switch (nsb) {
+        case 4: return smallm_kernel<BF16, HAS_ZP, NG, 4, SV>;
+        case 2: return smallm_kernel<BF16, HAS_ZP, NG, 2, SV>;
+        default: return smallm_kernel<BF16, HAS_ZP, NG, 1, SV>;
+    }
 }
 
 template <bool BF16, bool HAS_ZP>
-SmallFn pick(int P, int NG) {
-    (void)NG;
-    switch (P) {
-        case 1: return smallm_kernel<BF16, HAS_ZP, 1, 1>;
-        case 2: return smallm_kernel<BF16, HAS_ZP, 1, 2>;
-        case 3: return smallm_kernel<BF16, HAS_ZP, 1, 3>;
-        default:
-            if constexpr (BF16) return smallm_kernel<BF16, HAS_ZP, 1, 4>;
-            return nullptr;
-    }
+SmallFn pick(int ng, int nsb, bool sv) {
+    if (sv) return ng == 1 ? pick_ng<BF16, HAS_ZP, 1, true>(nsb) : pick_ng<BF16, HAS_ZP, kNG, true>(nsb);
+    return ng == 1 ? pick_ng<BF16, HAS_ZP, 1, false>(nsb) : pick_ng<BF16, HAS_ZP, kNG, false>(nsb);
 }
 
 int ilog2(int v) {
@@ -305,20 +456,31 @@ int ilog2(int v) {
     return r;
 }
 
-// Workgroups of f with `threads` threads resident per CU, cached per thread.
-int resident_per_cu(SmallFn f, int threads) {
-    struct Entry { SmallFn f; int threads; int n; };
+// Workgroups of f with `threads` threads and `lds` bytes resident per CU,
+// cached per thread; raises f's dynamic LDS limit first.
+int resident_per_cu(SmallFn f, int threads, size_t lds) {
+    struct Entry { SmallFn f; int threads; size_t lds; int n; };
     static thread_local Entry cache[32];
     static thread_local int used = 0;
     for (int i = 0; i < used; i++)
-        if (cache[i].f == f && cache[i].threads == threads) return cache[i].n;
+        if (cache[i].f == f && cache[i].threads == threads && cache[i].lds == lds) return cache[i].n;
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(f), threads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(f), threads, lds) !=
             hipSuccess || n < 1)
         n = 1;
-    cache[used % 32] = Entry{f, threads, n};
+    (void)hipGetLastError();
+    cache[used % 32] = Entry{f, threads, lds, n};
     if (used < 32) used++;
     return n;
+}
+
+// Wavefronts per workgroup: a function of K alone (it fixes the summation
+// order), one span per wavefront up to eight.
+int waves_for(int64_t K) {
+    const int64_t spans = (K + kSpan - 1) / kSpan;
+    return (int)(spans < kMaxWV ? spans : kMaxWV);
 }
 
 }  // namespace
@@ -326,9 +488,7 @@ int resident_per_cu(SmallFn f, int threads) {
 bool smallm_ok(const Problem& p) {
     const int esz = p.bf16 ? 2 : 4;
     const int64_t lim = int64_t(1) << 31;
-    return p.M >= 1 && p.M <= 16 && p.K % 32 == 0 && p.bs >= 32 &&
-           spans_per_wave(p.K) <= (p.bf16 ? kMaxP16 : kMaxP32) &&
-           p.M * p.K * esz < lim &&
+    return p.M >= 1 && p.M <= 16 && p.K % 32 == 0 && p.bs >= 32 && p.M * p.K * esz < lim &&
            p.N * p.col_bytes < lim && (int64_t)p.N * p.nb * esz < lim;
 }
 
@@ -340,27 +500,42 @@ int launch_smallm(const Problem& p, hipStream_t s) {
     a.col_bytes = (int)p.col_bytes; a.nb = p.nb; a.zp_row = p.zp_row;
     a.log2_bs = ilog2(p.bs);
     a.spans = (int)((p.K + kSpan - 1) / kSpan);
-    a.n_groups = (int)((p.N + 15) / 16);
     const int esz = p.bf16 ? 2 : 4;
     a.a_bytes = (uint32_t)(p.M * p.K * esz);
     a.b_bytes = (uint32_t)(p.N * p.col_bytes);
     a.s_bytes = (uint32_t)((int64_t)p.N * p.nb * esz);
     a.z_bytes = p.has_zp ? (uint32_t)((int64_t)p.N * p.zp_row) : 0u;
-    // P and WV from K alone (they fix the summation order); the grid only
-    // decides which workgroup takes a column group
-    const int P = spans_per_wave(p.K);
-    const int WV = (a.spans + P - 1) / P;
-    // one column group per iteration: more per iteration (more bytes in
-    // flight, fewer barriers) measured slower, the larger LDS and register
-    // footprint costing more occupancy than it saves
+    const int WV = waves_for(p.K);
+    a.log2_mr = p.M <= 8 ? 3 : 4;
+    // passes: as many spans as the staging LDS holds, a multiple of WV
+    const int span_bytes = (256 << a.log2_mr) * (p.bf16 ? 1 : 2);
+    int ps = (kStageMax / span_bytes) / WV * WV;
+    const int need = (a.spans + WV - 1) / WV * WV;
+    if (ps > need) ps = need;
+    a.pass_spans = ps;
+    a.passes = (a.spans + ps - 1) / ps;
+    a.ipw = (a.spans + WV - 1) / WV;
+    a.ipp = ps / WV;
+    // column groups per set: up to four once there are enough groups to give
+    // every CU two sets; the grid only decides which workgroup takes a set
     const int64_t cus = device_compute_units();
-    const int ng = 1;
-    SmallFn f = p.bf16 ? (p.has_zp ? pick<true, true>(P, ng) : pick<true, false>(P, ng))
-                       : (p.has_zp ? pick<false, true>(P, ng) : pick<false, false>(P, ng));
-    if (!f) return fail(MNB_E_UNSUPPORTED, "small-M: K=%lld beyond the register kernel", (long long)p.K);
-    int64_t blocks = cus * resident_per_cu(f, 64 * WV);
-    if (blocks > (a.n_groups + ng - 1) / ng) blocks = (a.n_groups + ng - 1) / ng;
-    hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(64 * WV), 0, s, a);
+    const int64_t groups = (p.N + 15) / 16;
+    int ngw = (int)(groups / (2 * cus));
+    if (ngw < 1) ngw = 1;
+    if (ngw > kNG) ngw = kNG;
+    a.ngw = ngw;
+    a.n_sets = (int)((groups + ngw - 1) / ngw);
+    const int nsb = p.bs >= 128 ? 1 : p.bs == 64 ? 2 : 4;
+    const int ng = ngw == 1 ? 1 : kNG;
+    // vector scale / zero-point loads when a span's blocks are aligned
+    // (scales [N][nb] and zero points [N][ceil(nb/2)] are element-aligned)
+    const bool sv = p.nb % nsb == 0 && (nsb < 4 || p.zp_row % 2 == 0);
+    SmallFn f = p.bf16 ? (p.has_zp ? pick<true, true>(ng, nsb, sv) : pick<true, false>(ng, nsb, sv))
+                       : (p.has_zp ? pick<false, true>(ng, nsb, sv) : pick<false, false>(ng, nsb, sv));
+    const size_t lds = (size_t)ps * span_bytes + (size_t)WV * ng * 64 * 16;
+    int64_t blocks = cus * resident_per_cu(f, 64 * WV, lds);
+    if (blocks > a.n_sets) blocks = a.n_sets;
+    hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(64 * WV), lds, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MNB_E_HIP, "small-M launch: %s", hipGetErrorString(e));
     return MNB_OK;
