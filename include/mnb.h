@@ -302,17 +302,16 @@ int mnb_argmax(int32_t dtype, int64_t M, int64_t N, const void* x,
 /* ---- gated MLP epilogue --------------------------------------------------------
  * mnb_gemv_silu_mul -- the fused gate||up decode projection (same page,
  * "Operator priority": the SiLU-gated MLP, Sigmoid(x) * x times the up
- * projection; "Phase Q2": gate projection, SiLU and gate/up multiplication).
+ * projection; "Phase Q5: scheduling and fusion": the gate projection, its
+ * SiLU and the gate/up product as one fusion).
  * B holds N = 2I columns, gate columns 0..I-1 then the matching up columns
  * I..2I-1 (one concatenated weight, as for the unfused fused-N launch);
  * bias, when given, has N entries.  With y = a x dequant(B) + bias:
  *   h[i] = silu(y[i]) * y[I + i],  silu(x) = x / (1 + exp(-x)),
  * evaluated in float32 on y before any rounding, then stored in act_dtype
- * (RTNE for bfloat16).  y[i] and y[I + i] are computed exactly as mnb_gemv
- * computes those columns when mnb_gemv holds at most four 32-value chunks
- * of K per lane; where it takes five (K = 2560, for one) their float32
- * summation orders differ, each within the same tolerance.  M must be 1,
- * N even and K within the decode kernel without split-K teams
+ * (RTNE for bfloat16).  y[i] and y[I + i] are summed exactly as mnb_gemv
+ * sums those columns (the same lane geometry, split-K wavefront teams
+ * included).  M must be 1, N even and K at most mnb_gemv_max_k
  * (MNB_E_UNSUPPORTED otherwise); h: [1][I]. */
 int mnb_gemv_silu_mul(const mnb_desc* d, int64_t M, const void* a,
                       const uint8_t* b_packed, const void* scales,

@@ -193,9 +193,13 @@ def _silu_tol(dt, g_ref, u_ref, Sg, Su, h_ref):
 
 @pytest.mark.parametrize("dt,K,I,bs,zp,bias", [("f32", 1024, 3072, 32, True, False),
                                                ("bf16", 2560, 9728, 128, False, False),
+                                               ("f32", 2560, 9728, 128, False, True),   # five chunks per lane
                                                ("f32", 1000, 333, 64, True, True),
                                                ("bf16", 96, 17, 16, True, True),
-                                               ("f32", 8192, 40, 32, False, True)])
+                                               ("f32", 8192, 40, 32, False, True),
+                                               ("f32", 9728, 200, 128, True, False),
+                                               ("f32", 12288, 64, 128, True, True),     # 2-wavefront teams
+                                               ("bf16", 16384, 33, 32, False, True)])   # 2-wavefront teams
 def test_gemv_silu_mul_matches_oracle(orc, dt, K, I, bs, zp, bias):
     log(f"silu gemv {dt} K={K} I={I} bs={bs} zp={zp} bias={bias}")
     inp = random_inputs(K, 2 * I, 1, bs, dt, zp, bias, seed=K + I)
@@ -216,11 +220,14 @@ def test_gemv_silu_mul_matches_oracle(orc, dt, K, I, bs, zp, bias):
                                             K=K, N=2 * I, block_size=bs))
 
 
-def test_gemv_silu_mul_rejects_split_k_geometry():
-    K, I, bs = 9728, 64, 128           # needs wavefront teams per column
+def test_gemv_silu_mul_beyond_register_kernel_is_refused():
+    """K past mnb_gemv_max_k (the decode kernel's limit) is refused; every
+    K up to it, split-K wavefront teams included, is served."""
+    K, I, bs = 20000, 16, 128
     inp = random_inputs(K, 2 * I, 1, bs, "f32", False, False, seed=3)
     g = inp.to(DEV)
     pw = mnb.PackedWeight.from_logical(g.q, g.scales, None, block_size=bs)
+    assert K > mnb.gemv_max_k(pw.desc)
     with pytest.raises(mnb.MnbError) as e:
         mnb.gemv_silu_mul(g.a, pw.b_packed, pw.scales, K=K, N=2 * I, block_size=bs)
     assert e.value.status == -2

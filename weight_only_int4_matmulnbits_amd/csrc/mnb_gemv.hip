@@ -37,10 +37,6 @@ namespace mnb {
 namespace {
 
 constexpr int kJMax = 5;          // chunks per lane held in registers
-// The gated kernel holds two column groups (gate and up) at once: five
-// chunks each would take all 256 VGPRs (one wavefront per SIMD) and, with
-// zero points and bias, more loads per iteration than the waits can count.
-constexpr int kJGated = 4;
 constexpr int kWMax = 4;          // wavefronts per column (split-K)
 constexpr int kWavesPerBlock = 4;
 constexpr size_t kMaxLds = 64 * 1024;    // staged activations per workgroup
@@ -197,13 +193,13 @@ __device__ __forceinline__ float reduce_lanes(float v, int log2_L) {
 
 // One iteration's loads, kept raw: decoding a scale or a zero-point nibble
 // here would make the wavefront wait for the load it just issued.
-template <bool BF16, bool HAS_ZP, int CB, int J, int U>
+template <bool BF16, bool HAS_ZP, int CB, int J>
 struct Group {
     using Chunk = typename ChunkT<CB>::type;
-    Chunk w[U][J];
-    uint32_t sc[U][J];   // float32 bits, or bfloat16 bits in the low half
-    uint32_t zb[U][J];   // packed zero-point byte (HAS_ZP)
-    uint32_t bias[U];    // float32 bits of the column's bias (0 without one)
+    Chunk w[J];
+    uint32_t sc[J];      // float32 bits, or bfloat16 bits in the low half
+    uint32_t zb[J];      // packed zero-point byte (HAS_ZP)
+    uint32_t bias;       // float32 bits of the column's bias (0 without one)
 };
 
 // One iteration's loads through buffer resources based at the group's
@@ -212,84 +208,77 @@ struct Group {
 // memory instructions on every path.
 constexpr uint32_t kOob = 0x80000000u;    // offset past any resource: reads zero
 
-// Gated epilogue (SILU): the U == 2 groups of an iteration are column group
-// `base` of the gate half and the same group of the up half.
-template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, int U, bool SILU>
-__device__ __forceinline__ void load_group(const GemvArgs& g, int64_t base, int p, int LT, int G,
-                                           int gsub, Group<BF16, HAS_ZP, CB, J, U>& r) {
+// Column group gi of the `width` columns starting at column col_off (the
+// whole of B, or the gate or the up half of a gated gate||up weight).
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J>
+__device__ __forceinline__ void load_group(const GemvArgs& g, int64_t gi, int64_t col_off, int64_t width, int p,
+                                           int LT, int G, int gsub, Group<BF16, HAS_ZP, CB, J>& r) {
     constexpr int CK = 2 * CB;
     constexpr int SSZ = BF16 ? 2 : 4;
+    const int64_t col0 = col_off + gi * G;
+    const int64_t ncol = gi < g.n_groups ? (width - gi * G < G ? width - gi * G : G) : 0;
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(g.b) + (ncol ? col0 * g.col_bytes : 0), (short)0,
+        (int)(ncol * g.col_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<uint8_t*>(const_cast<void*>(g.scales)) + (ncol ? col0 * g.nb * SSZ : 0), (short)0,
+        (int)(ncol * g.nb * SSZ), 0x00020000);
+    // the bias goes with the weights: a load issued late and consumed at
+    // once would wait for every load in flight (they complete in order)
+    const __amdgpu_buffer_rsrc_t rbias = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(g.bias ? g.bias : reinterpret_cast<const float*>(g.b)) + (ncol && g.bias ? col0 : 0),
+        (short)0, g.bias ? (int)(ncol * 4) : 0, 0x00020000);
+    r.bias = HAS_BIAS ? __builtin_amdgcn_raw_buffer_load_b32(rbias, (uint32_t)(4 * gsub), 0, 0) : 0u;
+    __amdgpu_buffer_rsrc_t rz;
+    if constexpr (HAS_ZP)
+        rz = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.zp) + (ncol ? col0 * g.zp_row : 0),
+                                               (short)0, (int)(ncol * g.zp_row), 0x00020000);
+    // scales and zero points first: loads complete in order, so they are in
+    // registers by the time the weights arrive
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t gi = SILU ? base : base + u;
-        const int64_t width = SILU ? g.half : g.N;           // columns of this group's half
-        const int64_t col0 = (SILU && u ? g.half : 0) + gi * G;
-        const int64_t ncol = gi < g.n_groups ? (width - gi * G < G ? width - gi * G : G) : 0;
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t*>(g.b) + (ncol ? col0 * g.col_bytes : 0), (short)0,
-            (int)(ncol * g.col_bytes), 0x00020000);
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            static_cast<uint8_t*>(const_cast<void*>(g.scales)) + (ncol ? col0 * g.nb * SSZ : 0), (short)0,
-            (int)(ncol * g.nb * SSZ), 0x00020000);
-        // the bias goes with the weights: a load issued late and consumed at
-        // once would wait for every load in flight (they complete in order)
-        const __amdgpu_buffer_rsrc_t rbias = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(g.bias ? g.bias : reinterpret_cast<const float*>(g.b)) + (ncol && g.bias ? col0 : 0),
-            (short)0, g.bias ? (int)(ncol * 4) : 0, 0x00020000);
-        r.bias[u] = HAS_BIAS ? __builtin_amdgcn_raw_buffer_load_b32(rbias, (uint32_t)(4 * gsub), 0, 0) : 0u;
-        __amdgpu_buffer_rsrc_t rz;
+    for (int j = 0; j < J; j++) {
+        const int c = p + j * LT;
+        // offsets of chunks past K forced past the resource (branch-free, so
+        // that every lane issues the same single load)
+        const uint32_t out = c < g.S ? 0u : kOob;
+        const int blk = (c * CK) >> g.log2_bs;
+        const uint32_t os = (uint32_t)((gsub * g.nb + blk) * SSZ) | out;
+        r.sc[j] = BF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0)
+                       : __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
         if constexpr (HAS_ZP)
-            rz = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.zp) + (ncol ? col0 * g.zp_row : 0),
-                                                   (short)0, (int)(ncol * g.zp_row), 0x00020000);
-        // scales and zero points first: loads complete in order, so they are
-        // in registers by the time the weights arrive
+            r.zb[j] = __builtin_amdgcn_raw_buffer_load_b8(rz, (uint32_t)(gsub * g.zp_row + (blk >> 1)) | out, 0, 0);
+    }
 #pragma unroll
-        for (int j = 0; j < J; j++) {
-            const int c = p + j * LT;
-            // offsets of chunks past K forced past the resource (branch-free,
-            // so that every lane issues the same single load)
-            const uint32_t out = c < g.S ? 0u : kOob;
-            const int blk = (c * CK) >> g.log2_bs;
-            const uint32_t os = (uint32_t)((gsub * g.nb + blk) * SSZ) | out;
-            r.sc[u][j] = BF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0)
-                              : __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
-            if constexpr (HAS_ZP)
-                r.zb[u][j] = __builtin_amdgcn_raw_buffer_load_b8(
-                    rz, (uint32_t)(gsub * g.zp_row + (blk >> 1)) | out, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < J; j++) {
-            const int c = p + j * LT;
-            const uint32_t out = c < g.S ? 0u : kOob;
-            const uint32_t ow = (uint32_t)(gsub * g.col_bytes + c * CB) | out;
-            if constexpr (CB == 16) {
-                r.w[u][j] = __builtin_amdgcn_raw_buffer_load_b128(rb, ow, 0, 0);
-            } else {
-                const uint64_t x = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rb, ow, 0, 0));
-                r.w[u][j] = u32x2{(uint32_t)x, (uint32_t)(x >> 32)};
-            }
+    for (int j = 0; j < J; j++) {
+        const int c = p + j * LT;
+        const uint32_t out = c < g.S ? 0u : kOob;
+        const uint32_t ow = (uint32_t)(gsub * g.col_bytes + c * CB) | out;
+        if constexpr (CB == 16) {
+            r.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, ow, 0, 0);
+        } else {
+            const uint64_t x = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rb, ow, 0, 0));
+            r.w[j] = u32x2{(uint32_t)x, (uint32_t)(x >> 32)};
         }
     }
 }
 
-// W wavefronts per column team, U column groups per team per iteration.
+// W wavefronts per column team, one column group per team per iteration.
 // SILU: the gate||up projection with the gated product fused into the
-// epilogue (page "Qwen3 CPU Inference Critical Path", "Phase Q2": gate
-// projection, SiLU and the gate/up multiplication): each iteration takes a
-// gate column group and the matching up group (U == 2), computed exactly as
-// unfused columns, and writes h = silu(gate) * up for the gate columns only.
+// epilogue (page "Qwen3 CPU Inference Critical Path", "Phase Q5: scheduling
+// and fusion": the gate projection, its SiLU and the gate/up product as one
+// fusion): the two register stages hold column group g of the gate half and
+// the same group of the up half; both go through exactly the geometry and
+// arithmetic of unfused columns (the sums are those mnb_gemv computes), and h
+// = silu(gate) * up is written for the gate columns only.
 // MR > 1: rows 0 .. M - 1 of A (M <= MR; the rows past M read zeros) with
 // one chunk of K per lane (J == 1, or 2 for two rows): every weight byte is
 // still read and unpacked once and serves all rows.
-template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, int U, int W, bool SILU = false, int MR = 1>
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, int W, bool SILU = false, int MR = 1>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     constexpr int CK = 2 * CB;        // values of K per chunk
     constexpr int NW = CB / 4;        // 32-bit words per chunk
     constexpr int TEAMS = kWavesPerBlock / W;
-    constexpr int UG = SILU ? 1 : U;  // column groups advanced per iteration
-    static_assert(W == 1 || U == 1, "split-K teams take one column at a time");
-    static_assert(!SILU || (U == 2 && W == 1), "the gated epilogue pairs two groups of one team");
-    static_assert(MR == 1 || (!SILU && U == 1 && J * MR <= 4 && CB == 16), "row kernel: one team column, <= 4 row chunks");
+    static_assert(MR == 1 || (!SILU && J * MR <= 4 && CB == 16), "row kernel: <= 4 row chunks");
     __shared__ float red[kWavesPerBlock * MR];
 
     const int lane = threadIdx.x & 63;
@@ -303,9 +292,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     const int gsub = lane >> g.log2_L;
 
     // iteration space: WG-uniform, so barriers (W > 1) are reached by all
-    const int64_t stride = (int64_t)gridDim.x * TEAMS * UG;
-    int64_t base = ((int64_t)blockIdx.x * TEAMS + team) * UG;
-    const int64_t team0 = (int64_t)blockIdx.x * TEAMS * UG;
+    const int64_t stride = (int64_t)gridDim.x * TEAMS;
+    int64_t base = (int64_t)blockIdx.x * TEAMS + team;
+    const int64_t team0 = (int64_t)blockIdx.x * TEAMS;
+    // the columns the groups index: all of B, or (gated) each half
+    const int64_t width = SILU ? g.half : g.N;
 
     // ---- activations: staged once per workgroup in LDS as they are (float32
     // or bfloat16), one RB-byte row per chunk; the 16-byte pieces of row c sit
@@ -362,17 +353,21 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
         }
     }
 
-    // the first two iterations' weights (the second only if this team has one)
-    Group<BF16, HAS_ZP, CB, J, U> g0, g1;
-    const bool two = base + stride < g.n_groups;     // wave-uniform
-    load_group<BF16, HAS_ZP, HAS_BIAS, CB, J, U, SILU>(g, base, p, LT, G, gsub, g0);
-    if (two) load_group<BF16, HAS_ZP, HAS_BIAS, CB, J, U, SILU>(g, base + stride, p, LT, G, gsub, g1);
+    // the first two stages' weights: the first two iterations (the second
+    // only if this team has one), or (gated) the gate and the up group of
+    // the first iteration
+    Group<BF16, HAS_ZP, CB, J> g0, g1;
+    const bool two = SILU || base + stride < g.n_groups;     // wave-uniform
+    load_group<BF16, HAS_ZP, HAS_BIAS, CB, J>(g, base, 0, width, p, LT, G, gsub, g0);
+    if (two)
+        load_group<BF16, HAS_ZP, HAS_BIAS, CB, J>(g, SILU ? base : base + stride, SILU ? g.half : 0, width, p,
+                                                  LT, G, gsub, g1);
 
     // wait for this wavefront's staging (all memory instructions but the
     // weight loads just issued, and the LDS writes), then meet the others.
     // A plain barrier: a fenced one would also wait for the weights.
     {
-        constexpr int NL = U * (J * (HAS_ZP ? 3 : 2) + (HAS_BIAS ? 1 : 0));     // loads per group
+        constexpr int NL = J * (HAS_ZP ? 3 : 2) + (HAS_BIAS ? 1 : 0);     // loads per group
         static_assert(2 * NL < 64, "vmcnt range");
         constexpr int W1 = (NL & 15) | (7 << 4) | (0 << 8) | ((NL >> 4) << 14);
         constexpr int W2 = ((2 * NL) & 15) | (7 << 4) | (0 << 8) | (((2 * NL) >> 4) << 14);
@@ -413,44 +408,41 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     // Two register stages used alternately (copying a stage would make the
     // wavefront wait for the loads just issued into it): while one
     // iteration is reduced, the next one's weights are in flight, and its
-    // own stage is refilled with the iteration after.
-    auto finish = [&](const Group<BF16, HAS_ZP, CB, J, U>& cur, int64_t gbase) {
-        float acc[U][MR];
+    // own stage is refilled with the iteration after.  reduce() leaves the
+    // column sums (before the bias) in the last lane of each column's lane
+    // group of the team's first wavefront.
+    auto reduce = [&](const Group<BF16, HAS_ZP, CB, J>& cur, float (&acc)[MR]) {
+        float s[MR];
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            float s[MR];
+        for (int r = 0; r < MR; r++) s[r] = 0.f;
 #pragma unroll
-            for (int r = 0; r < MR; r++) s[r] = 0.f;
+        for (int j = 0; j < J; j++) {
+            uint32_t words[NW];
 #pragma unroll
-            for (int j = 0; j < J; j++) {
-                uint32_t words[NW];
-#pragma unroll
-                for (int d = 0; d < NW; d++) words[d] = cur.w[u][j][d];
-                uint32_t zq = 8u;
-                if constexpr (HAS_ZP) {
-                    const int blk = ((p + j * LT) * CK) >> g.log2_bs;
-                    const uint32_t zb = cur.zb[u][j];
-                    zq = (blk & 1) ? ((zb >> 4) & 0xFu) : (zb & 0xFu);
-                }
-                uint32_t ze, zo;
-                zero_point_pairs(zq, ze, zo);
-                float dot[MR];
-                if constexpr (MR == 1)
-                    dot[0] = dot_words<NW>(words, av[j], ze, zo, nk);
-                else
-                    dot_words_rows<NW, MR>(words, &av[j * MR], ze, zo, nk, dot);
-                const float sc = BF16 ? __uint_as_float(cur.sc[u][j] << 16)
-                                      : __uint_as_float(cur.sc[u][j]);
-#pragma unroll
-                for (int r = 0; r < MR; r++) s[r] = fmaf(sc, dot[r], s[r]);
+            for (int d = 0; d < NW; d++) words[d] = cur.w[j][d];
+            uint32_t zq = 8u;
+            if constexpr (HAS_ZP) {
+                const int blk = ((p + j * LT) * CK) >> g.log2_bs;
+                const uint32_t zb = cur.zb[j];
+                zq = (blk & 1) ? ((zb >> 4) & 0xFu) : (zb & 0xFu);
             }
+            uint32_t ze, zo;
+            zero_point_pairs(zq, ze, zo);
+            float dot[MR];
+            if constexpr (MR == 1)
+                dot[0] = dot_words<NW>(words, av[j], ze, zo, nk);
+            else
+                dot_words_rows<NW, MR>(words, &av[j * MR], ze, zo, nk, dot);
+            const float sc = BF16 ? __uint_as_float(cur.sc[j] << 16) : __uint_as_float(cur.sc[j]);
 #pragma unroll
-            for (int r = 0; r < MR; r++) acc[u][r] = reduce_lanes(s[r], g.log2_L);
+            for (int r = 0; r < MR; r++) s[r] = fmaf(sc, dot[r], s[r]);
         }
+#pragma unroll
+        for (int r = 0; r < MR; r++) acc[r] = reduce_lanes(s[r], g.log2_L);
         if constexpr (W > 1) {
             if (lane == 63) {
 #pragma unroll
-                for (int r = 0; r < MR; r++) red[wave * MR + r] = acc[0][r];
+                for (int r = 0; r < MR; r++) red[wave * MR + r] = acc[r];
             }
             __syncthreads();
             if (wt == 0) {
@@ -459,59 +451,77 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
                     float v = red[team * W * MR + r];
 #pragma unroll
                     for (int w2 = 1; w2 < W; w2++) v += red[(team * W + w2) * MR + r];
-                    acc[0][r] = v;
+                    acc[r] = v;
                 }
             }
             __syncthreads();
         }
-        if constexpr (SILU) {
-            if ((lane & (L - 1)) == L - 1) {
-                const int64_t col = gbase * G + gsub;
-                if (gbase < g.n_groups && col < g.half) {
-                    float gate = acc[0][0], up = acc[1][0];
-                    if (HAS_BIAS) {
-                        gate += __uint_as_float(cur.bias[0]);
-                        up += __uint_as_float(cur.bias[1]);
-                    }
-                    const float h = gate / (1.0f + expf(-gate)) * up;
+    };
+    const bool writer = wt == 0 && (lane & (L - 1)) == L - 1;
+    if constexpr (SILU) {
+        // one column group per iteration: its gate half in g0, its up half
+        // in g1; the next group's halves are requested as each is reduced.
+        // base is workgroup-uniform in it0, so split-K barriers are reached
+        // by all
+        for (int64_t it0 = team0; it0 < g.n_groups; it0 += stride, base += stride) {
+            float gate[MR], up[MR];
+            reduce(g0, gate);
+            const float gbias = HAS_BIAS ? __uint_as_float(g0.bias) : 0.f;
+            if (base + stride < g.n_groups)
+                load_group<BF16, HAS_ZP, HAS_BIAS, CB, J>(g, base + stride, 0, width, p, LT, G, gsub, g0);
+            __builtin_amdgcn_sched_barrier(0);
+            reduce(g1, up);
+            if (writer) {
+                const int64_t col = base * G + gsub;
+                if (base < g.n_groups && col < g.half) {
+                    const float gv = gate[0] + gbias;
+                    const float uv = up[0] + (HAS_BIAS ? __uint_as_float(g1.bias) : 0.f);
+                    const float h = gv / (1.0f + expf(-gv)) * uv;
                     if constexpr (BF16)
                         static_cast<uint16_t*>(g.y)[col] = f32_to_bf16_rtne(h);
                     else
                         static_cast<float*>(g.y)[col] = h;
                 }
             }
-        } else if (wt == 0 && (lane & (L - 1)) == L - 1) {
+            if (base + stride < g.n_groups)
+                load_group<BF16, HAS_ZP, HAS_BIAS, CB, J>(g, base + stride, g.half, width, p, LT, G, gsub, g1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        auto store = [&](const Group<BF16, HAS_ZP, CB, J>& cur, const float (&acc)[MR], int64_t gi) {
+            if (!writer) return;
+            const int64_t col = gi * G + gsub;
+            if (gi < g.n_groups && col < g.N) {
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                const int64_t gi = gbase + u;
-                const int64_t col = gi * G + gsub;
-                if (gi < g.n_groups && col < g.N) {
-#pragma unroll
-                    for (int r = 0; r < MR; r++) {
-                        if (r >= g.M) break;
-                        float v = acc[u][r];
-                        if (HAS_BIAS) v += __uint_as_float(cur.bias[u]);
-                        if constexpr (BF16)
-                            static_cast<uint16_t*>(g.y)[r * g.N + col] = f32_to_bf16_rtne(v);
-                        else
-                            static_cast<float*>(g.y)[r * g.N + col] = v;
-                    }
+                for (int r = 0; r < MR; r++) {
+                    if (r >= g.M) break;
+                    float v = acc[r];
+                    if (HAS_BIAS) v += __uint_as_float(cur.bias);
+                    if constexpr (BF16)
+                        static_cast<uint16_t*>(g.y)[r * g.N + col] = f32_to_bf16_rtne(v);
+                    else
+                        static_cast<float*>(g.y)[r * g.N + col] = v;
                 }
             }
+        };
+        // it0 is WG-uniform, so the barriers of split-K teams are reached by
+        // all.  No exit between the halves (it would cost precise waits): the
+        // second half past the end loads zeros and skips its work.
+        for (int64_t it0 = team0; it0 < g.n_groups; it0 += 2 * stride, base += 2 * stride) {
+            float acc[MR];
+            reduce(g0, acc);
+            store(g0, acc, base);
+            if (base + 2 * stride < g.n_groups)
+                load_group<BF16, HAS_ZP, HAS_BIAS, CB, J>(g, base + 2 * stride, 0, width, p, LT, G, gsub, g0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (it0 + stride < g.n_groups) {
+                reduce(g1, acc);
+                store(g1, acc, base + stride);
+            }
+            if (base + 3 * stride < g.n_groups)
+                load_group<BF16, HAS_ZP, HAS_BIAS, CB, J>(g, base + 3 * stride, 0, width, p, LT, G, gsub, g1);
+            __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    // it0 is WG-uniform, so the barriers of split-K teams are reached by all.
-    // No exit between the halves (it would cost precise waits): the second
-    // half past the end loads zeros and skips its work.
-    for (int64_t it0 = team0; it0 < g.n_groups; it0 += 2 * stride, base += 2 * stride) {
-        finish(g0, base);
-        if (base + 2 * stride < g.n_groups)
-            load_group<BF16, HAS_ZP, HAS_BIAS, CB, J, U, SILU>(g, base + 2 * stride, p, LT, G, gsub, g0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (it0 + stride < g.n_groups) finish(g1, base + stride);
-        if (base + 3 * stride < g.n_groups)
-            load_group<BF16, HAS_ZP, HAS_BIAS, CB, J, U, SILU>(g, base + 3 * stride, p, LT, G, gsub, g1);
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -553,19 +563,19 @@ Geometry geometry(int64_t S, bool allow_split, int jmax = kJMax) {
 
 using GemvFn = void (*)(GemvArgs);
 
-template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J>
-GemvFn pick_j(int W, bool silu) {
-    if constexpr (J <= kJGated) {
-        if (silu) return W == 1 ? gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 2, 1, true> : nullptr;
-    } else {
-        if (silu) return nullptr;
-    }
-    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, 1>;
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, bool SILU>
+GemvFn pick_js(int W) {
+    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, SILU>;
     if constexpr (CB == 16) {
-        if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, 2>;
-        if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, 4>;
+        if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 2, SILU>;
+        if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 4, SILU>;
     }
     return nullptr;
+}
+
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J>
+GemvFn pick_j(int W, bool silu) {
+    return silu ? pick_js<BF16, HAS_ZP, HAS_BIAS, CB, J, true>(W) : pick_js<BF16, HAS_ZP, HAS_BIAS, CB, J, false>(W);
 }
 
 template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB>
@@ -588,9 +598,9 @@ GemvFn pick_b(int CB, int J, int W, bool silu) {
 // MR rows of A (block >= 32, so 16-byte chunks), J * MR <= 4
 template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int MR, int J>
 GemvFn pick_rows_j(int W) {
-    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 1, 1, false, MR>;
-    if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 1, 2, false, MR>;
-    if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 1, 4, false, MR>;
+    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 1, false, MR>;
+    if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 2, false, MR>;
+    if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 4, false, MR>;
     return nullptr;
 }
 
@@ -611,7 +621,7 @@ GemvFn pick_rows(bool bf16, bool has_zp, bool has_bias, int MR, int J, int W) {
     return has_bias ? pick_rows_b<false, false, true>(MR, J, W) : pick_rows_b<false, false, false>(MR, J, W);
 }
 
-// silu: the gated gate||up kernel (two column groups per iteration)
+// silu: the gated gate||up kernel
 GemvFn pick(bool bf16, bool has_zp, bool has_bias, int CB, int J, int W, bool silu) {
     if (bf16) {
         if (has_zp) return has_bias ? pick_b<true, true, true>(CB, J, W, silu) : pick_b<true, true, false>(CB, J, W, silu);
@@ -699,11 +709,10 @@ int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1) {
     a.log2_bs = ilog2(p.bs);
     a.half = silu ? p.N / 2 : 0;
     a.M = (int)p.M;
-    const Geometry geo = MR == 1 ? geometry(a.S, CB == 16, silu ? kJGated : kJMax) : geometry(a.S, true, 4 / MR);
+    // the gated kernel takes the plain geometry: its sums are mnb_gemv's
+    const Geometry geo = MR == 1 ? geometry(a.S, CB == 16, kJMax) : geometry(a.S, true, 4 / MR);
     if (geo.J == 0)
         return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld beyond the register kernel", (long long)p.K);
-    if (silu && geo.W != 1)
-        return fail(MNB_E_UNSUPPORTED, "gated gemv: K=%lld needs split-K wavefront teams", (long long)p.K);
     a.log2_L = geo.log2_L;
     const int G = geo.W == 1 ? (64 >> geo.log2_L) : 1;
     const int64_t cols = silu ? a.half : p.N;       // columns whose groups are walked
