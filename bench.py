@@ -444,6 +444,33 @@ def measure_next_rows(steps, warmup):
                        "fused_GBps": pw.weight_bytes / (t_f * 1e-6) / 1e9}
         del pw, y, h, g
     out["gate_up_silu"] = fused
+    # f4 at prefill: the Qwen3-4B gate||up at 2048 bf16 rows, the gated
+    # epilogue in the prefill kernel against the product then torch's SiLU and
+    # multiply (the unfused graph)
+    M, K, I, bs = 2048, 2560, 9728, 128
+    g = random_inputs(K, 2 * I, M, bs, "bf16", True, True, seed=5).to("cuda")
+    pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, g.bias, block_size=bs)
+    y = torch.empty(M, 2 * I, dtype=torch.bfloat16, device="cuda")
+    h = torch.empty(M, I, dtype=torch.bfloat16, device="cuda")
+    ws_u = mnb.workspace(mnb.workspace_bytes(pw.desc, M))
+    ws_f = mnb.workspace(mnb.gemm_silu_workspace_bytes(pw.desc, M))
+
+    def unfused_p():
+        pw.matmul(g.a, out=y, workspace=ws_u)
+        torch.mul(torch.nn.functional.silu(y[:, :I]), y[:, I:], out=h)
+
+    def fused_p():
+        mnb.gemm_silu_mul(g.a, pw.b_packed, pw.scales, pw.zp_packed, pw.bias, K=K, N=2 * I,
+                          block_size=bs, out=h, workspace=ws_f)
+
+    t_u = graph_time_us(unfused_p, max(5, steps // 2), warmup, reps=4)
+    t_f = graph_time_us(fused_p, max(5, steps // 2), warmup, reps=4)
+    fl = 2 * M * K * 2 * I
+    out["gate_up_silu_prefill"] = {
+        "workload": "Qwen3-4B gate||up 2560->2x9728 at 2048 bf16 rows, block 128, zero points, bias",
+        "unfused_us": t_u, "fused_us": t_f, "fused_TFLOPs": fl / (t_f * 1e-6) / 1e12,
+        "output_bytes_unfused": M * 2 * I * 2, "output_bytes_fused": M * I * 2}
+    del pw, y, h, g, ws_u, ws_f
     torch.cuda.empty_cache()
     return out
 

@@ -318,6 +318,27 @@ int mnb_gemv_silu_mul(const mnb_desc* d, int64_t M, const void* a,
                       const uint8_t* zp_packed, const float* bias, void* h,
                       void* stream);
 
+/* mnb_gemm_silu_mul -- the gated gate||up projection for any M (same page
+ * and passage as mnb_gemv_silu_mul; "INT4 MatMul is first", int4_gemm for
+ * prompt prefill).  B, bias and h as for mnb_gemv_silu_mul with A [M][K] and
+ * h [M][I], I = N / 2; plus a workspace of at least
+ * mnb_gemm_silu_workspace_bytes(d, M) bytes (256-byte aligned; NULL when
+ * that is 0).  Routes, by shape alone:
+ *   M == 1, K <= mnb_gemv_max_k: mnb_gemv_silu_mul (no workspace);
+ *   bfloat16, M > 128, K a multiple of 64 and of block_size: the prefill
+ *     kernel with the gated product in its epilogue -- each tile pairs 128
+ *     gate columns with the matching up columns, h is evaluated in float32 on
+ *     the unrounded sums and rounded once (only h [M][I] is written);
+ *   otherwise the unfused standard graph ("Phase Q5": each unfused graph
+ *     remains a correctness fallback): y = mnb_gemm into the workspace, then
+ *     h = silu(y_gate) * y_up in float32 on y rounded to act_dtype.
+ * N must be even (MNB_E_ARG otherwise). */
+size_t mnb_gemm_silu_workspace_bytes(const mnb_desc* d, int64_t M);
+int mnb_gemm_silu_mul(const mnb_desc* d, int64_t M, const void* a,
+                      const uint8_t* b_packed, const void* scales,
+                      const uint8_t* zp_packed, const float* bias, void* h,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- decode-step driver ------------------------------------------------------
  * One projection of a step: mnb_gemv when M == 1 and K <= mnb_gemv_max_k,
  * mnb_gemm otherwise.  A fused QKV or gate||up projection is one entry whose

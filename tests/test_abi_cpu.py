@@ -315,3 +315,24 @@ def test_sequence_workspace_is_the_largest_entry():
     g = ctypes.c_void_p()
     assert L.mnb_graph_create(arr, 3, None, 0, ctypes.byref(g)) == -1
     assert not g.value
+
+
+def test_gated_gemm_workspace_and_arguments():
+    import torch
+    # Qwen3-4B prefill gate||up: the wide kernel's split last round only
+    d = mnb.make_desc(2560, 19456, 128, torch.bfloat16, True)
+    assert mnb.gemm_silu_workspace_bytes(d, 2048) == 2 * 96 * 256 * 256 * 4
+    # one row: the gated decode GEMV, no workspace
+    assert mnb.gemm_silu_workspace_bytes(d, 1) == 0
+    # float32 activations: the unfused path keeps y [M][N] (after the
+    # product's own workspace, 256-byte aligned)
+    d32 = mnb.make_desc(1024, 6144, 32, has_zero_points=True)
+    assert mnb.gemm_silu_workspace_bytes(d32, 512) == 512 * 6144 * 4
+    # odd N is no gated weight
+    assert mnb.gemm_silu_workspace_bytes(mnb.make_desc(64, 7, 32), 4) == 0
+    L = mnb.lib()
+    odd = mnb.make_desc(64, 7, 32)
+    assert L.mnb_gemm_silu_mul(ctypes.byref(odd), 4, P16, P16, P16, None, None, P16, None, 0, None) == -1
+    assert "even" in L.mnb_last_error().decode()
+    assert L.mnb_gemm_silu_mul(ctypes.byref(d32), 512, P16, P16, P16, P16, None, P16, None, 0, None) == -1
+    assert "workspace" in L.mnb_last_error().decode()

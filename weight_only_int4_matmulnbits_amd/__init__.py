@@ -28,7 +28,8 @@ __all__ = [
     "scale_bytes", "zero_point_bytes", "gemv_max_k", "pack", "gemv", "gemm",
     "dequant", "PackedWeight", "Sequence", "version", "import_qdq", "qdq_is_native",
     "gather_rows", "argmax", "gemv_silu_mul", "workspace_bytes",
-    "argmax_workspace_bytes", "workspace", "gemm_noalloc",
+    "argmax_workspace_bytes", "workspace", "gemm_noalloc", "gemm_silu_mul",
+    "gemm_silu_workspace_bytes",
 ]
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
@@ -323,6 +324,39 @@ def gemv_silu_mul(a, b_packed, scales, zp_packed=None, bias=None, *, K, N, block
     check(lib().mnb_gemv_silu_mul(ctypes.byref(d), 1, _ptr(a), _ptr(b_packed), _ptr(scales),
                                   _ptr(zp_packed), _ptr(bias), _ptr(out), _stream(stream)),
           "mnb_gemv_silu_mul")
+    return out
+
+
+def gemm_silu_workspace_bytes(desc: Desc, M: int) -> int:
+    return int(lib().mnb_gemm_silu_workspace_bytes(ctypes.byref(desc), int(M)))
+
+
+def gemm_silu_mul(a, b_packed, scales, zp_packed=None, bias=None, *, K, N, block_size,
+                  out=None, stream=None, workspace=None) -> torch.Tensor:
+    """Gated gate||up projection for any M: B has N = 2I columns (gate, then
+    up); returns h [M][I] = silu(y[:, :I]) * y[:, I:] with y = a x dequant(B)
+    + bias.  workspace: at least gemm_silu_workspace_bytes(desc, M) bytes, or
+    None to have one allocated through torch."""
+    if a.dim() == 1:
+        a = a.view(1, -1)
+    M = a.shape[0]
+    d = make_desc(K, N, block_size, a.dtype, zp_packed is not None)
+    _need(a, "a", a.dtype, shape=(M, K))
+    _need(b_packed, "b_packed", torch.uint8, numel=packed_weight_bytes(d))
+    _need(scales, "scales", a.dtype, numel=N * _nb(K, block_size))
+    if zp_packed is not None:
+        _need(zp_packed, "zp_packed", torch.uint8, numel=zero_point_bytes(d))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, numel=N)
+    if out is None:
+        out = torch.empty((M, N // 2), dtype=a.dtype, device=a.device)
+    _need(out, "out", a.dtype, numel=M * (N // 2))
+    wp, wn, keep = _ws(workspace, gemm_silu_workspace_bytes(d, M), a.device)
+    check(lib().mnb_gemm_silu_mul(ctypes.byref(d), M, _ptr(a), _ptr(b_packed), _ptr(scales),
+                                  _ptr(zp_packed), _ptr(bias), _ptr(out), wp, wn, _stream(stream)),
+          "mnb_gemm_silu_mul")
+    if keep is not None and workspace is None and stream is not None:
+        keep.record_stream(stream)
     return out
 
 

@@ -382,6 +382,27 @@ int mnb_gemv_silu_mul(const mnb_desc* d, int64_t M, const void* a, const uint8_t
     return launch_gemv_silu(p, static_cast<hipStream_t>(stream));
 }
 
+size_t mnb_gemm_silu_workspace_bytes(const mnb_desc* d, int64_t M) {
+    if (mnb_validate(d, M) != MNB_OK || d->N % 2 != 0) return 0;
+    Problem p;
+    fill_problem(d, M, &p);
+    p.a = nullptr; p.b = nullptr; p.scales = nullptr; p.zp = nullptr; p.bias = nullptr; p.y = nullptr;
+    return gemm_silu_workspace_bytes(p);
+}
+
+int mnb_gemm_silu_mul(const mnb_desc* d, int64_t M, const void* a, const uint8_t* b_packed,
+                      const void* scales, const uint8_t* zp_packed, const float* bias, void* h,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    Problem p;
+    int st = check_matmul("mnb_gemm_silu_mul", d, M, a, b_packed, scales, zp_packed, bias, h, false, &p);
+    if (st != MNB_OK) return st;
+    if (d->N % 2 != 0)
+        return fail(MNB_E_ARG, "mnb_gemm_silu_mul: N=%lld must be even (gate half, then up half)", (long long)d->N);
+    st = check_workspace("mnb_gemm_silu_mul", gemm_silu_workspace_bytes(p), workspace, workspace_bytes);
+    if (st != MNB_OK) return st;
+    return launch_gemm_silu(p, static_cast<hipStream_t>(stream), workspace, workspace_bytes);
+}
+
 static int check_sequence(const mnb_matmul_args* ops, int64_t n_ops, std::vector<Problem>* out) {
     if (n_ops < 0 || (n_ops > 0 && !ops)) return fail(MNB_E_ARG, "sequence: ops NULL or n_ops < 0");
     out->resize((size_t)n_ops);

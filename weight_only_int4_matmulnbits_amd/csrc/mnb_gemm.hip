@@ -311,6 +311,10 @@ struct Bf16Args {
     // and store float32 partial tiles to tail_part[split][tail tile][256][256]
     int full_tiles, tail_tiles, tail_splits, tail_sps;
     float* tail_part;
+    // gated gate||up (wide kernel, SILU): I = N / 2; the 256 weight columns of
+    // a tile are 128 gate columns and the matching 128 up columns, and Y is
+    // h[M][I] = silu(gate) * up
+    int silu_half;
 };
 
 template <int BM, int BN, int WAVES>
@@ -534,6 +538,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(Bf16Args g) {
 //  * The bf16 tile leaves through LDS (free after the last barrier): each
 //    wavefront writes its 128 x 64 tile as 128-byte rows and stores 16-byte
 //    pieces of whole rows.
+//  * SILU (the gate||up projection with the gated product fused into the
+//    epilogue; page "Qwen3 CPU Inference Critical Path", "Phase Q5:
+//    scheduling and fusion"): a tile's 256 weight columns are 128 gate
+//    columns and the matching 128 up columns, placed so that each
+//    wavefront's two 32-column MFMA tiles are gate columns c .. c + 31 and
+//    up columns c .. c + 31: every lane then holds the gate and the up sums
+//    of the same column and rows, and writes h = silu(gate + bias) * (up +
+//    bias), evaluated in float32 and rounded once to bf16.  Y is h[M][N/2]:
+//    half the bytes of the unfused gate||up output.
 // Requires K % 64 == 0 and K % block_size == 0 (no partial K step or block).
 // ---------------------------------------------------------------------------
 constexpr int B4_M = 256, B4_N = 256, B4_K = 64;
@@ -547,7 +560,7 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
-template <bool HAS_ZP, bool BS16>
+template <bool HAS_ZP, bool BS16, bool SILU = false>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
     constexpr int TM = 4, TN = 2;
     constexpr int PANEL = 256 * B4_K * 2;               // one K step of one operand: 32 KiB
@@ -616,7 +629,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
 #pragma unroll
         for (int i = 0; i < AR; i++)
             st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rs, a_off + a_rows32 * i + 2u * (kbase + k0), 0, 0);
-        const int col = n0 + b_col;
+        int col = n0 + b_col;
+        if constexpr (SILU)   // wavefront block b_col / 64: gate columns, then the matching up columns
+            col = ((b_col >> 5) & 1 ? g.silu_half : 0) + (n0 >> 1) + 32 * (b_col >> 6) + (b_col & 31);
         const int kb = kbase + k0 + 32 * b_half;
         st.b = __builtin_amdgcn_raw_buffer_load_b128(
             rb_rs, (uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)kb / 2u, 0, 0);
@@ -758,6 +773,62 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(Bf16Args g) {
                     const int rr = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                     tp[rr * B4_N + c] = acc[i][jj][r];
                 }
+        }
+        return;
+    }
+    if constexpr (SILU) {
+        // lane c of this wavefront holds, for its 16 rows of each MFMA row
+        // tile i, the gate sums of h column hc (acc[i][0]) and the up sums
+        // of the same column (acc[i][1]).  Rows R and R + 1 are packed into a
+        // dword and lanes c and c ^ 1 swap halves (two adjacent columns of
+        // one row per lane); with I % 8 == 0 the dwords go through this
+        // wavefront's 8 KiB of LDS (64-byte rows) and leave as 16-byte
+        // pieces, otherwise they are stored directly.  Rows past M are
+        // dropped by the output's range check.
+        const int I = g.silu_half;
+        const int c = lane & 31;
+        const int hc = (n0 >> 1) + 32 * wn + c;
+        const bool ok = hc < I;
+        const float bg = g.bias && ok ? g.bias[hc] : 0.f;
+        const float bu = g.bias && ok ? g.bias[I + hc] : 0.f;
+        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+            g.y, (short)0, (int)((uint32_t)g.M * (uint32_t)I * 2u), 0x00020000);
+        const bool staged = (I & 7) == 0;
+        uint8_t* const wt = lds + wave * 8192;
+        const int odd = lane & 1;
+        const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+        const uint32_t rowb = 2u * (uint32_t)I;
+        const uint32_t vb = (uint32_t)(m0 + wm * 128 + 4 * (lane >> 5) + odd) * rowb + 2u * (uint32_t)(hc & ~1);
+        const bool pair_ok = (hc | 1) < I;
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float g0 = acc[i][0][r] + bg, g1 = acc[i][0][r + 1] + bg;
+                const float u0 = acc[i][1][r] + bu, u1 = acc[i][1][r + 1] + bu;
+                bf16x2 pr;
+                pr[0] = (__bf16)(g0 / (1.0f + expf(-g0)) * u0);
+                pr[1] = (__bf16)(g1 / (1.0f + expf(-g1)) * u1);
+                const uint32_t own = __builtin_bit_cast(uint32_t, pr);
+                const uint32_t oth = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
+                const uint32_t out = __builtin_amdgcn_perm(oth, own, sel);
+                const int row = i * 32 + 8 * (r >> 2) + (r & 3);   // + 4 (lane >> 5) + odd
+                if (staged)
+                    *reinterpret_cast<uint32_t*>(wt + (row + 4 * (lane >> 5) + odd) * 64 + 2 * (c & ~1)) = out;
+                else if (pair_ok)
+                    __builtin_amdgcn_raw_buffer_store_b32(out, ry, vb + (uint32_t)row * rowb, 0, 0);
+            }
+        if (staged) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): this wavefront's LDS writes
+            const int pc = lane & 3;                            // 16-byte piece of a 64-byte row
+            const int hcol = (n0 >> 1) + 32 * wn + 8 * pc;
+            const uint32_t vb2 = (uint32_t)(m0 + wm * 128 + (lane >> 2)) * rowb + 2u * (uint32_t)hcol;
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(wt + (16 * q + (lane >> 2)) * 64 + 16 * pc);
+                if (hcol < I)
+                    __builtin_amdgcn_raw_buffer_store_b128(v, ry, vb2 + (uint32_t)(16 * q) * rowb, 0, 0);
+            }
         }
         return;
     }
@@ -1231,6 +1302,73 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restric
     }
 }
 
+// The gated tail split: tail tile t's partials are in the wide kernel's
+// column order (wavefront block w: gate columns 32 w .. 32 w + 31 at tile
+// columns 64 w .., the matching up columns at 64 w + 32 ..); h column
+// 32 w + c of the tile is silu(gate + bias) * (up + bias) of the split sums
+// (in split order), rounded to bf16; four h columns per thread.
+__global__ __launch_bounds__(256) void tail_reduce_silu_kernel(const float* __restrict__ tp, int splits,
+                                                               int tail_tiles, int full_tiles, int mt, int M, int I,
+                                                               const float* __restrict__ bias,
+                                                               uint16_t* __restrict__ h) {
+    constexpr int TILE = B4_M * B4_N;
+    constexpr int HT = B4_N / 2;                        // h columns per tile
+    const int64_t total = (int64_t)tail_tiles * B4_M * HT / 4;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e0 = q * 4;
+        const int t = (int)(e0 / (B4_M * HT));
+        const int rc = (int)(e0 - (int64_t)t * (B4_M * HT));
+        const int r = rc / HT, hl = rc % HT;
+        const int tt = full_tiles + t;
+        const int m = (tt % mt) * B4_M + r, hc0 = (tt / mt) * HT + hl;
+        if (m >= M) continue;
+        const int gcol = (hl >> 5) * 64 + (hl & 31);     // gate column in the tile; up at + 32
+        const int64_t base = (int64_t)t * TILE + (int64_t)r * B4_N + gcol;
+        float4 gs = *reinterpret_cast<const float4*>(tp + base);
+        float4 us = *reinterpret_cast<const float4*>(tp + base + 32);
+        for (int sp = 1; sp < splits; sp++) {
+            const int64_t o = (int64_t)sp * tail_tiles * TILE + base;
+            const float4 zg = *reinterpret_cast<const float4*>(tp + o);
+            const float4 zu = *reinterpret_cast<const float4*>(tp + o + 32);
+            gs.x += zg.x; gs.y += zg.y; gs.z += zg.z; gs.w += zg.w;
+            us.x += zu.x; us.y += zu.y; us.z += zu.z; us.w += zu.w;
+        }
+        const float gv[4] = {gs.x, gs.y, gs.z, gs.w}, uv[4] = {us.x, us.y, us.z, us.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int hc = hc0 + e;
+            if (hc >= I) break;
+            const float gg = gv[e] + (bias ? bias[hc] : 0.f);
+            const float uu = uv[e] + (bias ? bias[I + hc] : 0.f);
+            h[(int64_t)m * I + hc] = f32_to_bf16_rtne(gg / (1.0f + expf(-gg)) * uu);
+        }
+    }
+}
+
+// The unfused path's second step: h[m][i] = silu(y[m][i]) * y[m][I + i] on
+// the product y (already rounded to the activation type), in float32.
+template <bool BF16>
+__global__ __launch_bounds__(256) void silu_mul_rows_kernel(const void* __restrict__ y, int64_t M, int64_t I,
+                                                            void* __restrict__ h) {
+    const int64_t total = M * I;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = q / I, i = q - m * I;
+        float gg, uu;
+        if constexpr (BF16) {
+            gg = bf16_to_f32(static_cast<const uint16_t*>(y)[m * 2 * I + i]);
+            uu = bf16_to_f32(static_cast<const uint16_t*>(y)[m * 2 * I + I + i]);
+        } else {
+            gg = static_cast<const float*>(y)[m * 2 * I + i];
+            uu = static_cast<const float*>(y)[m * 2 * I + I + i];
+        }
+        const float v = gg / (1.0f + expf(-gg)) * uu;
+        if constexpr (BF16)
+            static_cast<uint16_t*>(h)[q] = f32_to_bf16_rtne(v);
+        else
+            static_cast<float*>(h)[q] = v;
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -1334,7 +1472,114 @@ Plan plan_gemm(const Problem& p) {
 
 }  // namespace
 
+namespace {
+
+Bf16Args bf16_args(const Problem& p, const Plan& pl, void* ws) {
+    const int esz = p.bf16 ? 2 : 4;
+    Bf16Args b;
+    b.a = p.a; b.b = p.b; b.scales = p.scales; b.zp = p.has_zp ? p.zp : nullptr;
+    b.bias = p.bias; b.y = p.y;
+    b.M = (int)p.M; b.K = (int)p.K; b.N = (int)p.N; b.col_bytes = (int)p.col_bytes;
+    b.k_pad = (int)((int64_t)p.nb * p.bs); b.nb = p.nb; b.zp_row = p.zp_row;
+    int l2 = 0;
+    while ((1 << l2) < p.bs) l2++;
+    b.log2_bs = l2;
+    b.a_bytes = (uint32_t)(p.M * p.K * esz); b.b_bytes = (uint32_t)(p.N * p.col_bytes);
+    b.s_bytes = (uint32_t)(p.N * p.nb * esz); b.z_bytes = (uint32_t)(p.N * p.zp_row);
+    b.splits = pl.splits;
+    b.sps = pl.sps;
+    b.part = pl.splits > 1 ? static_cast<float*>(ws) : nullptr;
+    b.full_tiles = (int)(pl.tiles - pl.tail_tiles);
+    b.tail_tiles = pl.tail_tiles;
+    b.tail_splits = pl.tail_splits;
+    b.tail_sps = pl.tail_sps;
+    b.tail_part = pl.tail_tiles ? static_cast<float*>(ws) : nullptr;
+    b.silu_half = 0;
+    return b;
+}
+
+// The gated gate||up product on the wide kernel: no K split (the gated
+// epilogue needs whole sums); the last round of tiles may still be split
+// along K, its partials reduced by the gated tail kernel.
+Plan plan_gemm_silu(const Problem& p) {
+    Plan pl = plan_gemm(p);
+    if (pl.kind != Plan::WIDE) return pl;
+    Plan q;
+    q.kind = Plan::WIDE;
+    q.tiles = pl.tiles;
+    q.splits = 1;
+    q.sps = (int)(p.K / B4_K);
+    choose_tail_split(q, kPlanCUs, q.sps);
+    return q;
+}
+
+bool silu_decode(const Problem& p) { return p.M == 1 && p.K <= gemv_max_k(p.bs); }
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
 size_t gemm_workspace_bytes(const Problem& p) { return gemv_rows_ok(p) || smallm_ok(p) ? 0 : plan_gemm(p).ws; }
+
+size_t gemm_silu_workspace_bytes(const Problem& p) {
+    if (silu_decode(p)) return 0;
+    const Plan pl = plan_gemm_silu(p);
+    if (pl.kind == Plan::WIDE) return pl.ws;
+    // the unfused path: the product's own workspace, then y [M][N]
+    return align256(gemm_workspace_bytes(p)) + (size_t)(p.M * p.N) * (p.bf16 ? 2 : 4);
+}
+
+int launch_gemm_silu(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
+    if (silu_decode(p)) return launch_gemv_silu(p, s);
+    const Plan pl = plan_gemm_silu(p);
+    const size_t need = gemm_silu_workspace_bytes(p);
+    if (need && (!ws || ws_bytes < need))
+        return fail(MNB_E_ARG, "gemm_silu: workspace of %zu bytes, %zu needed", ws ? ws_bytes : (size_t)0, need);
+    const int64_t I = p.N / 2;
+    if (pl.kind == Plan::WIDE) {
+        Bf16Args b = bf16_args(p, pl, ws);
+        b.silu_half = (int)I;
+        const unsigned grid = (unsigned)(pl.tail_tiles ? b.full_tiles + (int64_t)pl.tail_tiles * pl.tail_splits
+                                                       : pl.tiles);
+        const bool bs16 = p.bs == 16;
+        auto kern = p.has_zp
+                        ? (bs16 ? gemm_bf16_wide_kernel<true, true, true> : gemm_bf16_wide_kernel<true, false, true>)
+                        : (bs16 ? gemm_bf16_wide_kernel<false, true, true> : gemm_bf16_wide_kernel<false, false, true>);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, s, b);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(MNB_E_HIP, "gated gemm launch: %s", hipGetErrorString(e));
+        if (pl.tail_tiles) {
+            const int64_t q = (int64_t)pl.tail_tiles * B4_M * (B4_N / 2) / 4;
+            int64_t blocks = (q + 255) / 256;
+            const int64_t cap = (int64_t)device_compute_units() * 8;
+            if (blocks > cap) blocks = cap;
+            hipLaunchKernelGGL(tail_reduce_silu_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                               static_cast<const float*>(ws), pl.tail_splits, pl.tail_tiles, b.full_tiles,
+                               (int)((p.M + B4_M - 1) / B4_M), (int)p.M, (int)I, p.bias,
+                               static_cast<uint16_t*>(p.y));
+            e = hipGetLastError();
+            if (e != hipSuccess) return fail(MNB_E_HIP, "gated tail reduction launch: %s", hipGetErrorString(e));
+        }
+        return MNB_OK;
+    }
+    // the unfused standard graph: the product into the workspace, then the
+    // gated rows
+    const size_t gws = align256(gemm_workspace_bytes(p));
+    Problem q = p;
+    q.y = static_cast<uint8_t*>(ws) + gws;
+    int st = launch_gemm(q, s, gws ? ws : nullptr, gws);
+    if (st != MNB_OK) return st;
+    int64_t blocks = (p.M * I + 255) / 256;
+    const int64_t cap = (int64_t)device_compute_units() * 8;
+    if (blocks > cap) blocks = cap;
+    if (p.bf16)
+        hipLaunchKernelGGL(silu_mul_rows_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, q.y, p.M, I, p.y);
+    else
+        hipLaunchKernelGGL(silu_mul_rows_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, q.y, p.M, I, p.y);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MNB_E_HIP, "gated rows launch: %s", hipGetErrorString(e));
+    return MNB_OK;
+}
 
 int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
     if (gemv_rows_ok(p)) return launch_gemv_rows(p, s);
@@ -1350,24 +1595,7 @@ int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes) {
     a.nb = p.nb; a.zp_row = p.zp_row; a.bs = p.bs;
     const int esz = p.bf16 ? 2 : 4;
     a.vec_a = ((p.K * esz) % 16 == 0) && ((reinterpret_cast<uintptr_t>(p.a) & 15) == 0);
-    Bf16Args b;
-    b.a = p.a; b.b = p.b; b.scales = p.scales; b.zp = p.has_zp ? p.zp : nullptr;
-    b.bias = p.bias; b.y = p.y;
-    b.M = (int)p.M; b.K = (int)p.K; b.N = (int)p.N; b.col_bytes = (int)p.col_bytes;
-    b.k_pad = (int)a.k_pad; b.nb = p.nb; b.zp_row = p.zp_row;
-    int l2 = 0;
-    while ((1 << l2) < p.bs) l2++;
-    b.log2_bs = l2;
-    b.a_bytes = (uint32_t)(p.M * p.K * esz); b.b_bytes = (uint32_t)(p.N * p.col_bytes);
-    b.s_bytes = (uint32_t)(p.N * p.nb * esz); b.z_bytes = (uint32_t)(p.N * p.zp_row);
-    b.splits = pl.splits;
-    b.sps = pl.sps;
-    b.part = pl.splits > 1 ? static_cast<float*>(ws) : nullptr;
-    b.full_tiles = (int)(pl.tiles - pl.tail_tiles);
-    b.tail_tiles = pl.tail_tiles;
-    b.tail_splits = pl.tail_splits;
-    b.tail_sps = pl.tail_sps;
-    b.tail_part = pl.tail_tiles ? static_cast<float*>(ws) : nullptr;
+    const Bf16Args b = bf16_args(p, pl, ws);
     const bool bs16 = p.bs == 16;
     const unsigned grid = (unsigned)(pl.tail_tiles ? b.full_tiles + (int64_t)pl.tail_tiles * pl.tail_splits
                                                    : pl.tiles * pl.splits);

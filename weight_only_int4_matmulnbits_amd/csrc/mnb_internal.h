@@ -57,6 +57,11 @@ size_t argmax_workspace_bytes(int64_t M, int64_t N);
 // it, and launch_gemm refuses a smaller one).
 int launch_gemm(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes);
 size_t gemm_workspace_bytes(const Problem& p);
+// The gated gate||up product (p.N = 2 * I, p.y = h [M][I]): the gated decode
+// GEMV at M == 1, the wide prefill kernel with its gated epilogue where it
+// applies, otherwise the product into the workspace and then the gated rows.
+int launch_gemm_silu(const Problem& p, hipStream_t s, void* ws, size_t ws_bytes);
+size_t gemm_silu_workspace_bytes(const Problem& p);
 // 1 <= M <= 16 on the matrix cores (K % 32 == 0, block_size >= 32, A 16-byte
 // aligned); launch_gemm takes it whenever smallm_ok holds.
 bool smallm_ok(const Problem& p);
