@@ -64,6 +64,8 @@ class Oracle:
         L.oracle_qdq_import.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp,
                                         i64, vp, vp, vp, vp]
         L.oracle_silu_mul.argtypes = [i64, vp, vp, vp]
+        L.oracle_rmsnorm.argtypes = [i64, i64, ctypes.c_int, vp, vp, ctypes.c_double, vp]
+        L.oracle_matmul_f64a.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_argmax.argtypes = [i64, i64, ctypes.c_int, vp, vp]
         for f in ("oracle_pack_weights", "oracle_unpack_weights",
                   "oracle_pack_zero_points", "oracle_unpack_zero_points",
@@ -195,6 +197,41 @@ class Oracle:
                                self._p(y), self._p(S), int(nthreads))
         return y, S
 
+
+    # -- RMSNorm into the projection input ------------------------------------
+    def rmsnorm(self, x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+        """binary64 a[m][k] = x / sqrt(mean_k x^2 + eps) * gamma[k]."""
+        x = np.ascontiguousarray(x)
+        gamma = np.ascontiguousarray(gamma)
+        M, K = x.shape
+        code = self._dtype_code(x)
+        assert self._dtype_code(gamma) == code and gamma.shape == (K,)
+        a = np.empty((M, K), np.float64)
+        self.lib.oracle_rmsnorm(M, K, code, self._p(x), self._p(gamma), float(eps), self._p(a))
+        return a
+
+    def matmul_f64a(self, a: np.ndarray, q: np.ndarray, zp: Optional[np.ndarray],
+                    scales: np.ndarray, bs: int, bias: Optional[np.ndarray] = None):
+        """(y, S) of binary64 activations a [M][K] against the quantized
+        weight (scales float32 or bfloat16 bit patterns)."""
+        a = np.ascontiguousarray(a, dtype=np.float64)
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales)
+        M, K = a.shape
+        N, K2 = q.shape
+        assert K == K2
+        nb = self.n_blocks(K, bs)
+        assert scales.shape == (N, nb)
+        if zp is not None:
+            zp = np.ascontiguousarray(zp, dtype=np.uint8)
+            assert zp.shape == (N, nb)
+        if bias is not None:
+            bias = np.ascontiguousarray(bias, dtype=np.float32)
+        y = np.empty((M, N), np.float64)
+        S = np.empty((M, N), np.float64)
+        self.lib.oracle_matmul_f64a(M, K, N, bs, self._dtype_code(scales), self._p(a), self._p(q),
+                                    self._p(zp), self._p(scales), self._p(bias), self._p(y), self._p(S))
+        return y, S
 
     # -- the QDQ encoding -----------------------------------------------------
     def qdq_unpack(self, packed: np.ndarray, count: int) -> np.ndarray:

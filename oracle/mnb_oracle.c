@@ -318,6 +318,53 @@ void oracle_silu_mul(int64_t n, const double *gate, const double *up, double *h)
     }
 }
 
+/* ---- RMS normalization of a projection's input (page "Qwen3 CPU Inference
+ * Critical Path", "Phase Q2": SimplifiedLayerNormalization lowered to the
+ * RMSNormalization engine; "Phase Q5": RMSNorm into the packed projection
+ * input).  The RMSNormalization definition over the last axis:
+ *   a[m][k] = x[m][k] / sqrt(mean_k x[m][k]^2 + eps) * gamma[k]
+ * in binary64 (x and gamma binary32 or bfloat16, gamma of length K). */
+void oracle_rmsnorm(int64_t M, int64_t K, int dtype, const void *x, const void *gamma, double eps,
+                    double *a) {
+    for (int64_t m = 0; m < M; m++) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double v = load_value(dtype, x, m * K + k);
+            ss += v * v;
+        }
+        double rms = sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; k++)
+            a[m * K + k] = load_value(dtype, x, m * K + k) / rms * load_value(dtype, gamma, k);
+    }
+}
+
+/* The matmul above on binary64 activations (the normalized input), scales
+ * in their own type: y and S as in oracle_matmul, k-sequential. */
+void oracle_matmul_f64a(int64_t M, int64_t K, int64_t N, int64_t bs, int scale_dtype, const double *a,
+                        const uint8_t *q, const uint8_t *zp, const void *scales, const float *bias,
+                        double *y, double *S) {
+    int64_t nb = oracle_n_blocks(K, bs);
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t m = 0; m < M; m++) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                int64_t b = k / bs;
+                int zero = zp ? zp[n * nb + b] : 8;
+                double w = (double)((int)q[n * K + k] - zero) * load_value(scale_dtype, scales, n * nb + b);
+                double p = a[m * K + k] * w;
+                acc += p;
+                mag += fabs(p);
+            }
+            if (bias) {
+                acc += (double)bias[n];
+                mag += fabs((double)bias[n]);
+            }
+            y[m * N + n] = acc;
+            S[m * N + n] = mag;
+        }
+    }
+}
+
 /* ---- greedy ArgMax ("final RMSNorm, LM-head GEMV, and greedy ArgMax"):
  * per row, the first index holding the largest value; a NaN counts as larger
  * than every number, so the first NaN wins. */

@@ -555,4 +555,64 @@ def pin_argmax_bruteforce(orc):
     assert orc.argmax(x).tolist() == want
 
 
+
+
+def pin_rmsnorm_exact(orc):
+    """Rows whose mean square is a perfect square (eps = 0): the normalized
+    input is rational and known by hand; eps enters under the root."""
+    x = np.array([[3, 4, 0, 0], [1, 1, 1, 1], [-2, 0, 0, 0], [0, 0, 0, 8]], np.float32)
+    g = np.array([1, 2, 3, 4], np.float32)
+    a = orc.rmsnorm(x, g, 0.0)
+    # rms: sqrt(25 / 4) = 5 / 2; 1; sqrt(4 / 4) = 1; sqrt(64 / 4) = 4
+    want = np.array([[1.2, 3.2, 0, 0], [1, 2, 3, 4], [-2, 0, 0, 0], [0, 0, 0, 8]])
+    assert np.allclose(a, want, rtol=1e-15, atol=0)
+    # eps = 1 on a unit row: rms = sqrt(1 + 1)
+    a1 = orc.rmsnorm(np.ones((1, 4), np.float32), np.ones(4, np.float32), 1.0)
+    assert np.allclose(a1, 1 / np.sqrt(2.0), rtol=1e-15)
+    # a zero row with eps > 0 is zero (no division by zero)
+    assert np.array_equal(orc.rmsnorm(np.zeros((1, 8), np.float32), np.ones(8, np.float32), 1e-6),
+                          np.zeros((1, 8)))
+    # bfloat16 bit patterns of the same exact values give the same result
+    assert np.allclose(orc.rmsnorm(_bf16_bits(x), _bf16_bits(g), 0.0), want, rtol=1e-15, atol=0)
+
+
+def pin_rmsnorm_invariants(orc):
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((3, 40)).astype(np.float32)
+    g = rng.standard_normal(40).astype(np.float32)
+    a = orc.rmsnorm(x, g, 0.0)
+    # scale invariance without eps; K = 1 gives sign(x) * gamma
+    assert np.allclose(orc.rmsnorm(x * np.float32(4.0), g, 0.0), a, rtol=1e-15, atol=0)
+    # (x * 3 rounds each input once in float32: relative 2^-24)
+    assert np.allclose(orc.rmsnorm(x * np.float32(3.0), g, 0.0), a, rtol=2.0 ** -22, atol=0)
+    assert np.array_equal(orc.rmsnorm(np.array([[-5.0]], np.float32), np.array([7.0], np.float32), 0.0),
+                          np.array([[-7.0]]))
+    # with gamma = 1 every row has mean square 1
+    a1 = orc.rmsnorm(x, np.ones(40, np.float32), 0.0)
+    assert np.allclose((a1 * a1).mean(axis=1), 1.0, rtol=1e-14)
+
+
+def pin_matmul_f64a_bruteforce(orc):
+    """Binary64 activations against the quantized weight: exact rational
+    evaluation on a tiny shape (the activations chosen dyadic, so every
+    product is exact), and agreement with the float32 matmul when the
+    activations are float32 values."""
+    from fractions import Fraction
+    rng = np.random.default_rng(5)
+    K, N, bs = 24, 5, 16
+    q = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    zp = rng.integers(0, 16, (N, 2), dtype=np.uint8)
+    sc = rng.uniform(0.005, 0.02, (N, 2)).astype(np.float32)
+    a = (rng.integers(-40, 41, (2, K)) / 8.0).astype(np.float64)
+    bias = rng.standard_normal(N).astype(np.float32)
+    y, S = orc.matmul_f64a(a, q, zp, sc, bs, bias)
+    for m in range(2):
+        for n in range(N):
+            acc = sum(Fraction(float(a[m, k])) * (int(q[n, k]) - int(zp[n, k // bs])) * Fraction(float(sc[n, k // bs]))
+                      for k in range(K)) + Fraction(float(bias[n]))
+            assert abs(float(acc) - y[m, n]) <= 1e-15 * S[m, n] + 1e-300
+    y32, S32 = orc.matmul(a.astype(np.float32), q, zp, sc, bs, bias=bias)
+    assert np.array_equal(y, y32) and np.array_equal(S, S32)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -66,6 +66,14 @@ MUTANTS = [
     ("silu_gate_factor_dropped", "h[i] = g * sig * up[i];", "h[i] = sig * up[i];"),
     ("argmax_last_of_ties", "if (isnan(v) || v > bv) {", "if (isnan(v) || v >= bv) {"),
     ("argmax_nan_ignored", "if (isnan(v) || v > bv) {", "if (v > bv) {"),
+    ("rmsnorm_sum_not_mean", "double rms = sqrt(ss / (double)K + eps);", "double rms = sqrt(ss + eps);"),
+    ("rmsnorm_eps_dropped", "double rms = sqrt(ss / (double)K + eps);", "double rms = sqrt(ss / (double)K);"),
+    ("rmsnorm_no_root", "double rms = sqrt(ss / (double)K + eps);", "double rms = ss / (double)K + eps;"),
+    ("rmsnorm_gamma_dropped", "/ rms * load_value(dtype, gamma, k);", "/ rms * 1.0;"),
+    ("rmsnorm_gamma_reversed", "/ rms * load_value(dtype, gamma, k);", "/ rms * load_value(dtype, gamma, K - 1 - k);"),
+    ("matmul_f64a_zero_point_dropped",
+     "double w = (double)((int)q[n * K + k] - zero) * load_value(scale_dtype, scales, n * nb + b);",
+     "double w = (double)((int)q[n * K + k]) * load_value(scale_dtype, scales, n * nb + b);"),
 ]
 
 
