@@ -444,6 +444,26 @@ def measure_next_rows(steps, warmup):
                        "fused_GBps": pw.weight_bytes / (t_f * 1e-6) / 1e9}
         del pw, y, h, g
     out["gate_up_silu"] = fused
+    # f4: RMSNorm fused into the decode projection input (Qwen3-4B qkv),
+    # against torch's normalization followed by the GEMV
+    K, N, bs = 2560, 6144, 128
+    g = random_inputs(K, N, 1, bs, "f32", False, False, seed=6).to("cuda")
+    pw = mnb.PackedWeight.from_logical(g.q, g.scales, block_size=bs)
+    gamma = torch.rand(K, device="cuda") + 0.5
+    xn = torch.empty_like(g.a)
+    y = torch.empty(1, N, device="cuda")
+
+    def unfused_n():
+        torch.mul(g.a * torch.rsqrt(g.a.pow(2).mean(-1, keepdim=True) + 1e-6), gamma, out=xn)
+        pw.matmul(xn, out=y)
+
+    t_u = graph_time_us(unfused_n, steps, warmup)
+    t_f = graph_time_us(lambda: mnb.gemv_rmsnorm(g.a, gamma, 1e-6, pw.b_packed, pw.scales, K=K, N=N,
+                                                 block_size=bs, out=y), steps, warmup)
+    t_p = graph_time_us(lambda: pw.matmul(g.a, out=y), steps, warmup)
+    out["rmsnorm_gemv"] = {"workload": "Qwen3-4B qkv 2560->6144 (fp32, block 128) on an RMS-normalized row",
+                           "unfused_us": t_u, "fused_us": t_f, "plain_gemv_us": t_p}
+    del pw, g, gamma, xn, y
     # f4 at prefill: the Qwen3-4B gate||up at 2048 bf16 rows, the gated
     # epilogue in the prefill kernel against the product then torch's SiLU and
     # multiply (the unfused graph)

@@ -339,6 +339,25 @@ int mnb_gemm_silu_mul(const mnb_desc* d, int64_t M, const void* a,
                       const uint8_t* zp_packed, const float* bias, void* h,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- RMSNorm into the projection input ------------------------------------------
+ * mnb_gemv_rmsnorm -- the decode projection of an RMS-normalized row (same
+ * page, "Phase Q5: scheduling and fusion": RMSNorm fused into the packed
+ * projection input; "Phase Q2": SimplifiedLayerNormalization lowered to the
+ * RMSNormalization engine):
+ *   a[k] = x[k] / sqrt(sum_k x[k]^2 / K + epsilon) * gamma[k],
+ *   y = a x dequant(B) (+ bias),
+ * the normalization computed by every workgroup from the staged row in
+ * float32 (fixed summation order) and applied as the row enters registers, so
+ * the normalized row never goes to memory.  x: [1][K] and gamma: [K] in
+ * act_dtype, both 16-byte aligned; epsilon finite and >= 0.  M must be 1 and
+ * K * element size a multiple of 16 with K * element size * 2 <= 64 KiB
+ * (MNB_E_UNSUPPORTED otherwise); the other arguments as for mnb_gemv. */
+int mnb_gemv_rmsnorm(const mnb_desc* d, int64_t M, const void* x,
+                     const void* gamma, float epsilon,
+                     const uint8_t* b_packed, const void* scales,
+                     const uint8_t* zp_packed, const float* bias, void* y,
+                     void* stream);
+
 /* ---- decode-step driver ------------------------------------------------------
  * One projection of a step: mnb_gemv when M == 1 and K <= mnb_gemv_max_k,
  * mnb_gemm otherwise.  A fused QKV or gate||up projection is one entry whose

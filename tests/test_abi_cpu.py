@@ -336,3 +336,19 @@ def test_gated_gemm_workspace_and_arguments():
     assert "even" in L.mnb_last_error().decode()
     assert L.mnb_gemm_silu_mul(ctypes.byref(d32), 512, P16, P16, P16, P16, None, P16, None, 0, None) == -1
     assert "workspace" in L.mnb_last_error().decode()
+
+
+def test_gemv_rmsnorm_argument_errors():
+    L = mnb.lib()
+    d = mnb.make_desc(64, 8, 32)
+
+    def call(desc, M=1, x=P16, gamma=0x20000, eps=1e-6, b=P16, s=P16, zp=None, y=P16):
+        return L.mnb_gemv_rmsnorm(ctypes.byref(desc), M, x, gamma, eps, b, s, zp, None, y, None)
+
+    assert call(d, gamma=None) == -1
+    assert call(d, gamma=0x20008) == -3              # gamma needs 16-byte alignment
+    assert call(d, eps=-1.0) == -1
+    assert call(d, eps=float("nan")) == -1
+    assert call(d, M=2) == -1
+    assert call(mnb.make_desc(66, 8, 32)) == -2      # K * 4 not a multiple of 16
+    assert call(mnb.make_desc(20000, 8, 32)) == -2   # past the decode kernel

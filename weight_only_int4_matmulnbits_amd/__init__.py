@@ -29,7 +29,7 @@ __all__ = [
     "dequant", "PackedWeight", "Sequence", "version", "import_qdq", "qdq_is_native",
     "gather_rows", "argmax", "gemv_silu_mul", "workspace_bytes",
     "argmax_workspace_bytes", "workspace", "gemm_noalloc", "gemm_silu_mul",
-    "gemm_silu_workspace_bytes",
+    "gemm_silu_workspace_bytes", "gemv_rmsnorm",
 ]
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
@@ -357,6 +357,32 @@ def gemm_silu_mul(a, b_packed, scales, zp_packed=None, bias=None, *, K, N, block
           "mnb_gemm_silu_mul")
     if keep is not None and workspace is None and stream is not None:
         keep.record_stream(stream)
+    return out
+
+
+def gemv_rmsnorm(x, gamma, eps, b_packed, scales, zp_packed=None, bias=None, *, K, N, block_size,
+                 out=None, stream=None) -> torch.Tensor:
+    """Decode projection of an RMS-normalized row: y = (x / sqrt(mean(x^2) +
+    eps) * gamma) x dequant(B) (+ bias), the normalization fused into the
+    GEMV's input staging.  x [1][K] (or [K]) and gamma [K] share the
+    activation dtype."""
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    d = make_desc(K, N, block_size, x.dtype, zp_packed is not None)
+    _need(x, "x", x.dtype, shape=(1, K))
+    _need(gamma, "gamma", x.dtype, numel=K)
+    _need(b_packed, "b_packed", torch.uint8, numel=packed_weight_bytes(d))
+    _need(scales, "scales", x.dtype, numel=N * _nb(K, block_size))
+    if zp_packed is not None:
+        _need(zp_packed, "zp_packed", torch.uint8, numel=zero_point_bytes(d))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, numel=N)
+    if out is None:
+        out = torch.empty((1, N), dtype=x.dtype, device=x.device)
+    _need(out, "out", x.dtype, numel=N)
+    check(lib().mnb_gemv_rmsnorm(ctypes.byref(d), 1, _ptr(x), _ptr(gamma), float(eps), _ptr(b_packed),
+                                 _ptr(scales), _ptr(zp_packed), _ptr(bias), _ptr(out), _stream(stream)),
+          "mnb_gemv_rmsnorm")
     return out
 
 

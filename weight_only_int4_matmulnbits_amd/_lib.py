@@ -31,7 +31,7 @@ EXPORTS = (
     "mnb_gather_rows", "mnb_argmax", "mnb_gemv_silu_mul",
     "mnb_workspace_bytes", "mnb_argmax_workspace_bytes",
     "mnb_sequence_workspace_bytes", "mnb_gemm_noalloc",
-    "mnb_gemm_silu_workspace_bytes", "mnb_gemm_silu_mul",
+    "mnb_gemm_silu_workspace_bytes", "mnb_gemm_silu_mul", "mnb_gemv_rmsnorm",
 )
 
 
@@ -126,6 +126,8 @@ def lib() -> ctypes.CDLL:
     L.mnb_gemm_silu_workspace_bytes.restype = sz
     L.mnb_gemm_silu_mul.argtypes = [pd, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.mnb_gemm_silu_mul.restype = ctypes.c_int
+    L.mnb_gemv_rmsnorm.argtypes = [pd, i64, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp]
+    L.mnb_gemv_rmsnorm.restype = ctypes.c_int
     pa = ctypes.POINTER(MatmulArgs)
     L.mnb_sequence_workspace_bytes.argtypes = [pa, i64]
     L.mnb_sequence_workspace_bytes.restype = sz

@@ -382,6 +382,25 @@ int mnb_gemv_silu_mul(const mnb_desc* d, int64_t M, const void* a, const uint8_t
     return launch_gemv_silu(p, static_cast<hipStream_t>(stream));
 }
 
+int mnb_gemv_rmsnorm(const mnb_desc* d, int64_t M, const void* x, const void* gamma, float epsilon,
+                     const uint8_t* b_packed, const void* scales, const uint8_t* zp_packed, const float* bias,
+                     void* y, void* stream) {
+    Problem p;
+    int st = check_matmul("mnb_gemv_rmsnorm", d, M, x, b_packed, scales, zp_packed, bias, y, true, &p);
+    if (st != MNB_OK) return st;
+    if (!gamma) return fail(MNB_E_ARG, "mnb_gemv_rmsnorm: gamma must be non-NULL");
+    if (!aligned(gamma, 16)) return fail(MNB_E_ALIGN, "mnb_gemv_rmsnorm: gamma must be 16-byte aligned");
+    if (!(epsilon >= 0.f) || epsilon > 3.0e38f)
+        return fail(MNB_E_ARG, "mnb_gemv_rmsnorm: epsilon must be finite and >= 0");
+    const int esz = d->act_dtype == MNB_BF16 ? 2 : 4;
+    if ((d->K * esz) % 16 != 0)
+        return fail(MNB_E_UNSUPPORTED, "mnb_gemv_rmsnorm: K * element size must be a multiple of 16");
+    if (!takes_gemv(p))
+        return fail(MNB_E_UNSUPPORTED, "mnb_gemv_rmsnorm: K=%lld exceeds mnb_gemv_max_k=%lld", (long long)p.K,
+                    (long long)gemv_max_k(p.bs));
+    return launch_gemv_rmsnorm(p, gamma, epsilon, static_cast<hipStream_t>(stream));
+}
+
 size_t mnb_gemm_silu_workspace_bytes(const mnb_desc* d, int64_t M) {
     if (mnb_validate(d, M) != MNB_OK || d->N % 2 != 0) return 0;
     Problem p;

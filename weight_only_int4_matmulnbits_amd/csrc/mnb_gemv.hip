@@ -53,6 +53,8 @@ struct GemvArgs {
     int a16;                  // K * element size is a multiple of 16 and A is 16-byte aligned
     int64_t half;             // gated epilogue: columns per half (gate | up); 0 otherwise
     int M;                    // rows of A and Y (1 for the decode GEMV; up to MR)
+    const void* gamma;        // RMSNorm fused into the input (one row): gamma [K], or NULL
+    float eps;
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -330,6 +332,19 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
                     (uint32_t)(row * RB + 16 * piece), 0, 0, 0);
             }
         }
+        if (g.gamma) {
+            // the RMSNorm weights, staged like A after it
+            const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<void*>(g.gamma), (short)0, (int)(g.K * ESZ), 0x00020000);
+            for (int r = wave; r < nreq; r += kWavesPerBlock) {
+                const int row = r * (64 / NV) + lane / NV;
+                const int pos = lane % NV;
+                const int piece = pos ^ ((row / RPS) % NV);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rg, (void __attribute__((address_space(3)))*)(a_lds + 1024 * (MR * nreq + r)), 16,
+                    (uint32_t)(row * RB + 16 * piece), 0, 0, 0);
+            }
+        }
     } else {
         // K * element size not a multiple of 16: element-wise loads
         for (int i = threadIdx.x; i < g.S * NV; i += nthr) {
@@ -378,6 +393,51 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
         asm volatile("s_barrier" : : : "memory");
     }
     const NibbleMasks nk = nibble_masks();
+    // RMSNorm fused into the input (page "Qwen3 CPU Inference Critical
+    // Path", "Phase Q5": RMSNorm into the packed projection input; one row):
+    // the sum of squares over this lane's chunks -- the team's lanes of a
+    // column cover K once -- reduced by the lane tree (and the team's
+    // wavefronts in order), then a = (x * r) * gamma with r = 1 / sqrt(mean +
+    // eps), all in float32
+    const uint8_t* const g_lds = a_lds + 1024 * (MR * nreq);
+    float inv_rms = 1.f;
+    if (g.gamma) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; j++) {
+            const int c = p + j * LT;
+            if (c < g.S) {
+#pragma unroll
+                for (int v = 0; v < NV; v++) {
+                    const u32x4 x = *reinterpret_cast<const u32x4*>(a_lds + c * RB + 16 * (v ^ ((c / RPS) % NV)));
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        if constexpr (BF16) {
+                            const float x0 = __uint_as_float(x[e] << 16), x1 = __uint_as_float(x[e] & 0xFFFF0000u);
+                            ss = fmaf(x0, x0, ss);
+                            ss = fmaf(x1, x1, ss);
+                        } else {
+                            const float x0 = __uint_as_float(x[e]);
+                            ss = fmaf(x0, x0, ss);
+                        }
+                    }
+                }
+            }
+        }
+        ss = reduce_lanes(ss, g.log2_L);
+        // every lane takes its lane group's sum (held by the group's last lane)
+        ss = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane | (L - 1)) << 2, __builtin_bit_cast(int, ss)));
+        if constexpr (W > 1) {
+            if (lane == 63) red[wave] = ss;
+            __syncthreads();
+            float v = red[team * W];
+#pragma unroll
+            for (int w2 = 1; w2 < W; w2++) v += red[team * W + w2];
+            ss = v;
+            __syncthreads();
+        }
+        inv_rms = 1.0f / sqrtf(ss / (float)g.K + g.eps);
+    }
     // this lane's chunks of A in registers, for each row
     float av[MR * J][CK];
 #pragma unroll
@@ -396,6 +456,19 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
                         av[mj][8 * v + 2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
                     } else {
                         av[mj][4 * v + e] = __uint_as_float(x[e]);
+                    }
+                }
+                if (g.gamma) {
+                    const u32x4 gw = *reinterpret_cast<const u32x4*>(g_lds + c * RB + 16 * (v ^ ((c / RPS) % NV)));
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        if constexpr (BF16) {
+                            av[mj][8 * v + 2 * e] = (av[mj][8 * v + 2 * e] * inv_rms) * __uint_as_float(gw[e] << 16);
+                            av[mj][8 * v + 2 * e + 1] =
+                                (av[mj][8 * v + 2 * e + 1] * inv_rms) * __uint_as_float(gw[e] & 0xFFFF0000u);
+                        } else {
+                            av[mj][4 * v + e] = (av[mj][4 * v + e] * inv_rms) * __uint_as_float(gw[e]);
+                        }
                     }
                 }
             }
@@ -697,7 +770,7 @@ size_t rows_lds(const Problem& p, int MR) {
 
 // silu: p.N = 2 * half columns (gate half, then up half), y receives half
 // values of silu(gate) * up.  MR > 1: the row kernel (p.M rows, p.M <= MR).
-int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1) {
+int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1, const void* gamma = nullptr, float eps = 0.f) {
     const int CB = p.bs >= 32 ? 16 : 8;
     const int CK = 2 * CB;
     GemvArgs a;
@@ -709,6 +782,8 @@ int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1) {
     a.log2_bs = ilog2(p.bs);
     a.half = silu ? p.N / 2 : 0;
     a.M = (int)p.M;
+    a.gamma = gamma;
+    a.eps = eps;
     // the gated kernel takes the plain geometry: its sums are mnb_gemv's
     const Geometry geo = MR == 1 ? geometry(a.S, CB == 16, kJMax) : geometry(a.S, true, 4 / MR);
     if (geo.J == 0)
@@ -724,7 +799,11 @@ int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1) {
     // The staging writes whole 1 KiB requests (nreq per row in the kernel),
     // so every row is rounded up to a whole KiB of LDS; the row kernel stages
     // row m at m * ceil(S * CK * esz / 1 KiB) KiB.
-    const size_t lds = MR == 1 ? (size_t)(((int64_t)a.S * CK * esz + 1023) / 1024) * 1024 : rows_lds(p, MR);
+    size_t lds = MR == 1 ? (size_t)(((int64_t)a.S * CK * esz + 1023) / 1024) * 1024 : rows_lds(p, MR);
+    if (gamma) {
+        if (!a.a16) return fail(MNB_E_UNSUPPORTED, "gemv rmsnorm: K * element size must be a multiple of 16");
+        lds *= 2;                                   // gamma staged after A
+    }
     if (lds > kMaxLds)
         return fail(MNB_E_UNSUPPORTED, "gemv: K=%lld needs %zu bytes of LDS", (long long)p.K, lds);
     // Fill the chip with resident teams of W wavefronts (the kernel's real
@@ -766,5 +845,9 @@ bool gemv_rows_ok(const Problem& p) {
 int launch_gemv_rows(const Problem& p, hipStream_t s) { return launch(p, s, false, rows_mr(p.M)); }
 
 int launch_gemv_silu(const Problem& p, hipStream_t s) { return launch(p, s, true); }
+
+int launch_gemv_rmsnorm(const Problem& p, const void* gamma, float eps, hipStream_t s) {
+    return launch(p, s, false, 1, gamma, eps);
+}
 
 }  // namespace mnb

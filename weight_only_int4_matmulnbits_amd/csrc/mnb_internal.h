@@ -42,6 +42,9 @@ bool gemv_rows_ok(const Problem& p);
 int launch_gemv_rows(const Problem& p, hipStream_t s);
 // p.N = 2 * half: the gate half then the up half; y [half] = silu(gate) * up.
 int launch_gemv_silu(const Problem& p, hipStream_t s);
+// One row whose input is RMS-normalized on the fly: a = x / sqrt(mean x^2 +
+// eps) * gamma (gamma [K] in the activation type, 16-byte aligned).
+int launch_gemv_rmsnorm(const Problem& p, const void* gamma, float eps, hipStream_t s);
 // QDQ normalization (axis 0: W[K][N], scales/zp [nb][N]; axis 1: W[N][K],
 // scales/zp [N][nb]) into the MatMulNBits storage of p (p.has_zp is true).
 int launch_import_qdq(const Problem& p, int axis, const uint8_t* w_q, const void* scales_q, const uint8_t* zp_q,
