@@ -355,142 +355,153 @@ def graph_time_us(fn, steps, warmup, reps=20):
     return e0.elapsed_time(e1) * 1e3 / (steps * reps)
 
 
-def measure_next_rows(steps, warmup):
+def measure_next_rows(steps, warmup, only=None):
     """One measurement per row beyond the decode / prefill step: the small-M
     steps (speculative blocks of 4, 8 and 16 rows), the LM head with greedy
     ArgMax and the tied-embedding gather, the QDQ import, and the fused
-    gate||up SiLU GEMV against its unfused pair."""
+    gate||up SiLU GEMV against its unfused pair.  `only`: the names of the
+    rows to run (all when None)."""
     import torch
     import weight_only_int4_matmulnbits_amd as mnb
     from workloads import workload
     from workloads.generate import random_inputs
 
     out = {}
+
+    def want(name):
+        return only is None or name in only
+
     # f1: the 0.6B decode step with 4, 8 and 16 rows per projection
-    sm = {}
-    for M in (4, 8, 16):
-        wm = workload(2, M=M)
-        r = measure_step(wm, steps, warmup, 20)
-        gbs = r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
-        sm[f"M{M}"] = {"workload": f"Qwen3-0.6B-shaped INT4 step, {M} rows (speculative block)",
-                       "ms_per_step": r["ms_per_step"], "p50_ms": r["samples"]["p50_ms"],
-                       "launches": r["launches"], "weight_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-                       "rows_per_s": M / (r["ms_per_step"] * 1e-3)}
-    out["small_m"] = sm
+    if want("small_m"):
+        sm = {}
+        for M in (4, 8, 16):
+            wm = workload(2, M=M)
+            r = measure_step(wm, steps, warmup, 20)
+            gbs = r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+            sm[f"M{M}"] = {"workload": f"Qwen3-0.6B-shaped INT4 step, {M} rows (speculative block)",
+                           "ms_per_step": r["ms_per_step"], "p50_ms": r["samples"]["p50_ms"],
+                           "launches": r["launches"], "weight_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                           "rows_per_s": M / (r["ms_per_step"] * 1e-3)}
+        out["small_m"] = sm
     # f2: LM head (tied weight, N = vocabulary) + greedy token, and the gather
-    K, N, bs = 1024, 151936, 32
-    g = random_inputs(K, N, 1, bs, "f32", True, False, seed=1).to("cuda")
-    pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, block_size=bs)
-    logits = torch.empty(1, N, device="cuda")
-    tok = torch.empty(1, dtype=torch.int64, device="cuda")
-    aws = mnb.workspace(mnb.argmax_workspace_bytes(1, N))
-    ids1 = torch.tensor([151935], device="cuda")
-    ids512 = torch.randint(0, N, (512,), device="cuda", generator=torch.Generator("cuda").manual_seed(2))
-    rows1 = torch.empty(1, K, device="cuda")
-    rows512 = torch.empty(512, K, device="cuda")
-    t_lm = graph_time_us(lambda: pw.matmul(g.a, out=logits), steps, warmup)
-    t_lm_arg = graph_time_us(lambda: (pw.matmul(g.a, out=logits), mnb.argmax(logits, out=tok, workspace=aws)),
-                             steps, warmup)
-    t_g1 = graph_time_us(lambda: mnb.gather_rows(ids1, pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N,
-                                                 block_size=bs, out=rows1), steps, warmup)
-    t_g512 = graph_time_us(lambda: mnb.gather_rows(ids512, pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N,
-                                                   block_size=bs, out=rows512), steps, warmup)
-    row_read = K // 2 + (K // bs) * 4 + (K // bs + 1) // 2
-    out["lm_head_argmax"] = {
-        "workload": "Qwen3-0.6B tied LM head 1024->151936 (fp32, block 32, zero points) + greedy ArgMax",
-        "lm_head_us": t_lm, "lm_head_GBps": pw.weight_bytes / (t_lm * 1e-6) / 1e9,
-        "lm_head_plus_argmax_us": t_lm_arg, "argmax_added_us": t_lm_arg - t_lm}
-    out["embedding_gather"] = {
-        "workload": "rows of the same packed tied weight, fp32 out",
-        "rows_1_us": t_g1, "rows_512_us": t_g512,
-        "rows_512_GBps": 512 * (row_read + 4 * K) / (t_g512 * 1e-6) / 1e9}
-    del pw, logits, rows512, aws
-    # f3: QDQ import of the 4B gate||up weight (axis 0 -> N-major)
-    K, N, bs = 2560, 19456, 128
-    gen = torch.Generator("cuda").manual_seed(3)
-    w_q = torch.randint(0, 256, (K * N // 2,), dtype=torch.uint8, device="cuda", generator=gen)
-    z_q = torch.randint(0, 256, ((K // bs) * N // 2,), dtype=torch.uint8, device="cuda", generator=gen)
-    s_q = torch.rand((K // bs) * N, device="cuda", generator=gen).to(torch.bfloat16)
-    mnb.import_qdq(w_q, s_q, z_q, K=K, N=N, block_size=bs, axis=0)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        mnb.import_qdq(w_q, s_q, z_q, K=K, N=N, block_size=bs, axis=0)
-    e1.record()
-    torch.cuda.synchronize()
-    t_imp = e0.elapsed_time(e1) * 1e3 / 5
-    moved = 2 * (w_q.numel() + z_q.numel() + 2 * s_q.numel())
-    out["qdq_import"] = {"workload": "Qwen3-4B gate||up 2560x19456 QDQ (axis 0, block 128) -> MatMulNBits",
-                         "us": t_imp, "GBps_read_plus_written": moved / (t_imp * 1e-6) / 1e9,
-                         "tied_lm_head_copy_avoided": mnb.qdq_is_native(1024, 151936, 32, axis=1)}
-    del w_q, z_q, s_q
-    # f4: gate||up with silu(gate) * up fused, against the unfused pair
-    fused = {}
-    for name, K, I, bs, dt in (("0.6B", 1024, 3072, 32, "f32"), ("4B", 2560, 9728, 128, "f32")):
-        g = random_inputs(K, 2 * I, 1, bs, dt, name == "0.6B", False, seed=4).to("cuda")
+    if want("lm_head_argmax"):
+        K, N, bs = 1024, 151936, 32
+        g = random_inputs(K, N, 1, bs, "f32", True, False, seed=1).to("cuda")
         pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, block_size=bs)
-        y = torch.empty(1, 2 * I, dtype=g.a.dtype, device="cuda")
-        h = torch.empty(1, I, dtype=g.a.dtype, device="cuda")
+        logits = torch.empty(1, N, device="cuda")
+        tok = torch.empty(1, dtype=torch.int64, device="cuda")
+        aws = mnb.workspace(mnb.argmax_workspace_bytes(1, N))
+        ids1 = torch.tensor([151935], device="cuda")
+        ids512 = torch.randint(0, N, (512,), device="cuda", generator=torch.Generator("cuda").manual_seed(2))
+        rows1 = torch.empty(1, K, device="cuda")
+        rows512 = torch.empty(512, K, device="cuda")
+        t_lm = graph_time_us(lambda: pw.matmul(g.a, out=logits), steps, warmup)
+        t_lm_arg = graph_time_us(lambda: (pw.matmul(g.a, out=logits), mnb.argmax(logits, out=tok, workspace=aws)),
+                                 steps, warmup)
+        t_g1 = graph_time_us(lambda: mnb.gather_rows(ids1, pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N,
+                                                     block_size=bs, out=rows1), steps, warmup)
+        t_g512 = graph_time_us(lambda: mnb.gather_rows(ids512, pw.b_packed, pw.scales, pw.zp_packed, K=K, N=N,
+                                                       block_size=bs, out=rows512), steps, warmup)
+        row_read = K // 2 + (K // bs) * 4 + (K // bs + 1) // 2
+        out["lm_head_argmax"] = {
+            "workload": "Qwen3-0.6B tied LM head 1024->151936 (fp32, block 32, zero points) + greedy ArgMax",
+            "lm_head_us": t_lm, "lm_head_GBps": pw.weight_bytes / (t_lm * 1e-6) / 1e9,
+            "lm_head_plus_argmax_us": t_lm_arg, "argmax_added_us": t_lm_arg - t_lm}
+        out["embedding_gather"] = {
+            "workload": "rows of the same packed tied weight, fp32 out",
+            "rows_1_us": t_g1, "rows_512_us": t_g512,
+            "rows_512_GBps": 512 * (row_read + 4 * K) / (t_g512 * 1e-6) / 1e9}
+        del pw, logits, rows512, aws
+    # f3: QDQ import of the 4B gate||up weight (axis 0 -> N-major)
+    if want("qdq_import"):
+        K, N, bs = 2560, 19456, 128
+        gen = torch.Generator("cuda").manual_seed(3)
+        w_q = torch.randint(0, 256, (K * N // 2,), dtype=torch.uint8, device="cuda", generator=gen)
+        z_q = torch.randint(0, 256, ((K // bs) * N // 2,), dtype=torch.uint8, device="cuda", generator=gen)
+        s_q = torch.rand((K // bs) * N, device="cuda", generator=gen).to(torch.bfloat16)
+        mnb.import_qdq(w_q, s_q, z_q, K=K, N=N, block_size=bs, axis=0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            mnb.import_qdq(w_q, s_q, z_q, K=K, N=N, block_size=bs, axis=0)
+        e1.record()
+        torch.cuda.synchronize()
+        t_imp = e0.elapsed_time(e1) * 1e3 / 5
+        moved = 2 * (w_q.numel() + z_q.numel() + 2 * s_q.numel())
+        out["qdq_import"] = {"workload": "Qwen3-4B gate||up 2560x19456 QDQ (axis 0, block 128) -> MatMulNBits",
+                             "us": t_imp, "GBps_read_plus_written": moved / (t_imp * 1e-6) / 1e9,
+                             "tied_lm_head_copy_avoided": mnb.qdq_is_native(1024, 151936, 32, axis=1)}
+        del w_q, z_q, s_q
+    # f4: gate||up with silu(gate) * up fused, against the unfused pair
+    if want("gate_up_silu"):
+        fused = {}
+        for name, K, I, bs, dt in (("0.6B", 1024, 3072, 32, "f32"), ("4B", 2560, 9728, 128, "f32")):
+            g = random_inputs(K, 2 * I, 1, bs, dt, name == "0.6B", False, seed=4).to("cuda")
+            pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, block_size=bs)
+            y = torch.empty(1, 2 * I, dtype=g.a.dtype, device="cuda")
+            h = torch.empty(1, I, dtype=g.a.dtype, device="cuda")
 
-        def unfused():
-            pw.matmul(g.a, out=y)
-            torch.mul(torch.nn.functional.silu(y[:, :I]), y[:, I:], out=h)
+            def unfused():
+                pw.matmul(g.a, out=y)
+                torch.mul(torch.nn.functional.silu(y[:, :I]), y[:, I:], out=h)
 
-        t_u = graph_time_us(unfused, steps, warmup)
-        t_f = graph_time_us(lambda: mnb.gemv_silu_mul(g.a, pw.b_packed, pw.scales, pw.zp_packed, K=K,
-                                                      N=2 * I, block_size=bs, out=h), steps, warmup)
-        fused[name] = {"K": K, "I": I, "dtype": dt, "unfused_us": t_u, "fused_us": t_f,
-                       "fused_GBps": pw.weight_bytes / (t_f * 1e-6) / 1e9}
-        del pw, y, h, g
-    out["gate_up_silu"] = fused
+            t_u = graph_time_us(unfused, steps, warmup)
+            t_f = graph_time_us(lambda: mnb.gemv_silu_mul(g.a, pw.b_packed, pw.scales, pw.zp_packed, K=K,
+                                                          N=2 * I, block_size=bs, out=h), steps, warmup)
+            fused[name] = {"K": K, "I": I, "dtype": dt, "unfused_us": t_u, "fused_us": t_f,
+                           "fused_GBps": pw.weight_bytes / (t_f * 1e-6) / 1e9}
+            del pw, y, h, g
+        out["gate_up_silu"] = fused
     # f4: RMSNorm fused into the decode projection input (Qwen3-4B qkv),
     # against torch's normalization followed by the GEMV
-    K, N, bs = 2560, 6144, 128
-    g = random_inputs(K, N, 1, bs, "f32", False, False, seed=6).to("cuda")
-    pw = mnb.PackedWeight.from_logical(g.q, g.scales, block_size=bs)
-    gamma = torch.rand(K, device="cuda") + 0.5
-    xn = torch.empty_like(g.a)
-    y = torch.empty(1, N, device="cuda")
+    if want("rmsnorm_gemv"):
+        K, N, bs = 2560, 6144, 128
+        g = random_inputs(K, N, 1, bs, "f32", False, False, seed=6).to("cuda")
+        pw = mnb.PackedWeight.from_logical(g.q, g.scales, block_size=bs)
+        gamma = torch.rand(K, device="cuda") + 0.5
+        xn = torch.empty_like(g.a)
+        y = torch.empty(1, N, device="cuda")
 
-    def unfused_n():
-        torch.mul(g.a * torch.rsqrt(g.a.pow(2).mean(-1, keepdim=True) + 1e-6), gamma, out=xn)
-        pw.matmul(xn, out=y)
+        def unfused_n():
+            torch.mul(g.a * torch.rsqrt(g.a.pow(2).mean(-1, keepdim=True) + 1e-6), gamma, out=xn)
+            pw.matmul(xn, out=y)
 
-    t_u = graph_time_us(unfused_n, steps, warmup)
-    t_f = graph_time_us(lambda: mnb.gemv_rmsnorm(g.a, gamma, 1e-6, pw.b_packed, pw.scales, K=K, N=N,
-                                                 block_size=bs, out=y), steps, warmup)
-    t_p = graph_time_us(lambda: pw.matmul(g.a, out=y), steps, warmup)
-    out["rmsnorm_gemv"] = {"workload": "Qwen3-4B qkv 2560->6144 (fp32, block 128) on an RMS-normalized row",
-                           "unfused_us": t_u, "fused_us": t_f, "plain_gemv_us": t_p}
-    del pw, g, gamma, xn, y
+        t_u = graph_time_us(unfused_n, steps, warmup)
+        t_f = graph_time_us(lambda: mnb.gemv_rmsnorm(g.a, gamma, 1e-6, pw.b_packed, pw.scales, K=K, N=N,
+                                                     block_size=bs, out=y), steps, warmup)
+        t_p = graph_time_us(lambda: pw.matmul(g.a, out=y), steps, warmup)
+        out["rmsnorm_gemv"] = {"workload": "Qwen3-4B qkv 2560->6144 (fp32, block 128) on an RMS-normalized row",
+                               "unfused_us": t_u, "fused_us": t_f, "plain_gemv_us": t_p}
+        del pw, g, gamma, xn, y
     # f4 at prefill: the Qwen3-4B gate||up at 2048 bf16 rows, the gated
     # epilogue in the prefill kernel against the product then torch's SiLU and
     # multiply (the unfused graph)
-    M, K, I, bs = 2048, 2560, 9728, 128
-    g = random_inputs(K, 2 * I, M, bs, "bf16", True, True, seed=5).to("cuda")
-    pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, g.bias, block_size=bs)
-    y = torch.empty(M, 2 * I, dtype=torch.bfloat16, device="cuda")
-    h = torch.empty(M, I, dtype=torch.bfloat16, device="cuda")
-    ws_u = mnb.workspace(mnb.workspace_bytes(pw.desc, M))
-    ws_f = mnb.workspace(mnb.gemm_silu_workspace_bytes(pw.desc, M))
+    if want("gate_up_silu_prefill"):
+        M, K, I, bs = 2048, 2560, 9728, 128
+        g = random_inputs(K, 2 * I, M, bs, "bf16", True, True, seed=5).to("cuda")
+        pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, g.bias, block_size=bs)
+        y = torch.empty(M, 2 * I, dtype=torch.bfloat16, device="cuda")
+        h = torch.empty(M, I, dtype=torch.bfloat16, device="cuda")
+        ws_u = mnb.workspace(mnb.workspace_bytes(pw.desc, M))
+        ws_f = mnb.workspace(mnb.gemm_silu_workspace_bytes(pw.desc, M))
 
-    def unfused_p():
-        pw.matmul(g.a, out=y, workspace=ws_u)
-        torch.mul(torch.nn.functional.silu(y[:, :I]), y[:, I:], out=h)
+        def unfused_p():
+            pw.matmul(g.a, out=y, workspace=ws_u)
+            torch.mul(torch.nn.functional.silu(y[:, :I]), y[:, I:], out=h)
 
-    def fused_p():
-        mnb.gemm_silu_mul(g.a, pw.b_packed, pw.scales, pw.zp_packed, pw.bias, K=K, N=2 * I,
-                          block_size=bs, out=h, workspace=ws_f)
+        def fused_p():
+            mnb.gemm_silu_mul(g.a, pw.b_packed, pw.scales, pw.zp_packed, pw.bias, K=K, N=2 * I,
+                              block_size=bs, out=h, workspace=ws_f)
 
-    t_u = graph_time_us(unfused_p, max(5, steps // 2), warmup, reps=4)
-    t_f = graph_time_us(fused_p, max(5, steps // 2), warmup, reps=4)
-    fl = 2 * M * K * 2 * I
-    out["gate_up_silu_prefill"] = {
-        "workload": "Qwen3-4B gate||up 2560->2x9728 at 2048 bf16 rows, block 128, zero points, bias",
-        "unfused_us": t_u, "fused_us": t_f, "fused_TFLOPs": fl / (t_f * 1e-6) / 1e12,
-        "output_bytes_unfused": M * 2 * I * 2, "output_bytes_fused": M * I * 2}
-    del pw, y, h, g, ws_u, ws_f
+        t_u = graph_time_us(unfused_p, max(5, steps // 2), warmup, reps=4)
+        t_f = graph_time_us(fused_p, max(5, steps // 2), warmup, reps=4)
+        fl = 2 * M * K * 2 * I
+        out["gate_up_silu_prefill"] = {
+            "workload": "Qwen3-4B gate||up 2560->2x9728 at 2048 bf16 rows, block 128, zero points, bias",
+            "unfused_us": t_u, "fused_us": t_f, "fused_TFLOPs": fl / (t_f * 1e-6) / 1e12,
+            "output_bytes_unfused": M * 2 * I * 2, "output_bytes_fused": M * I * 2}
+        del pw, y, h, g, ws_u, ws_f
     torch.cuda.empty_cache()
     return out
 
@@ -593,10 +604,10 @@ def summarize_trace(trace_dir, cfg, steps, warmup, samples=MIN_SAMPLES, bench_js
         with open(bench_json) as f:
             rec = json.loads([l for l in f if l.startswith("{")][-1])
         un = rec["ms_per_step"] * 1e3
-        out.append(f"same run, untraced event timing (bench JSON): {un:.1f} us per graph-replayed step; "
-                   f"traced median sum of kernel durations {s_sum / 1e3:.1f} us "
-                   f"({'within' if s_sum / 1e3 <= un else 'above'} it: tracer overhead "
-                   f"{max(0.0, s_sum / 1e3 - un):.1f} us per step, {100 * (s_sum / 1e3 / un - 1):+.1f} %)")
+        out.append(f"event timing printed by the same run (bench JSON; HIP events, taken while the tracer "
+                   f"ran): {un:.1f} us per graph-replayed step; the median sum of traced kernel durations, "
+                   f"{s_sum / 1e3:.1f} us, is {'within' if s_sum / 1e3 <= un else 'above'} it "
+                   f"({100 * (s_sum / 1e3 / un - 1):+.1f} %)")
     return "\n".join(out)
 
 
@@ -665,17 +676,25 @@ def traffic_from(fetch_dir, write_dir, cfg, copy_mib, kind="gemv"):
 
 def counters_from(dirs, cus=256):
     """Per-kernel averages of the counters of one or more rocprofv3 `--pmc`
-    runs (run_counter_collection.csv), library kernels only, plus the derived
-    fractions that need them: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
-    (GRBM_GUI_ACTIVE x CUs x 4 SIMDs), wait = SQ_WAIT_INST_ANY /
-    SQ_WAVE_CYCLES, LDS bank conflicts per LDS instruction."""
+    runs (run_counter_collection.csv), library kernels and the plain copy of
+    --copy-calibration, plus the derived
+    fractions that need them.  GRBM_GUI_ACTIVE is summed over the chip's 8
+    XCDs, so the kernel's own active cycles are GRBM_GUI_ACTIVE / 8; MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES (summed over every SIMD) / (those cycles x CUs x 4
+    SIMDs), wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, LDS bank conflicts per
+    LDS instruction."""
     import collections
     per = collections.defaultdict(lambda: collections.defaultdict(list))
     for d in dirs:
         for r in _read_csv(os.path.join(d, "run_counter_collection.csv")):
-            if "mnb::" not in r["Kernel_Name"] or "pack_" in r["Kernel_Name"]:
+            name = r["Kernel_Name"]
+            if "copyBuffer" in name:
+                name = "copy (reference for scaling byte counters)"
+            elif "mnb::" not in name or "pack_" in name:
                 continue
-            per[_short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            else:
+                name = _short(name)
+            per[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
     out = []
     for k, cs in sorted(per.items(), key=lambda kv: -len(next(iter(kv[1].values())))):
         n = max(len(v) for v in cs.values())
@@ -684,8 +703,10 @@ def counters_from(dirs, cus=256):
         for c in sorted(avg):
             out.append(f"    {c:<28} {avg[c]:16.1f}")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg and avg["GRBM_GUI_ACTIVE"] > 0:
-            out.append(f"    -> MFMA busy {100 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (avg['GRBM_GUI_ACTIVE'] * cus * 4):.1f} % "
-                       f"of {cus} CUs x 4 SIMDs over the kernel's GPU-active cycles")
+            active = avg["GRBM_GUI_ACTIVE"] / 8
+            out.append(f"    -> {active:.0f} active cycles per XCD; MFMA busy "
+                       f"{100 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (active * cus * 4):.1f} % "
+                       f"of {cus} CUs x 4 SIMDs over them")
         if "SQ_WAIT_INST_ANY" in avg and avg.get("SQ_WAVE_CYCLES", 0) > 0:
             out.append(f"    -> waiting on any instruction {100 * avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.1f} % "
                        f"of wave cycles")
@@ -716,6 +737,10 @@ def main():
     ap.add_argument("--bench-json", metavar="FILE",
                     help="with --summarize-trace: the JSON line the traced run printed, to state "
                          "the tracer's overhead against the same run's untraced timing")
+    ap.add_argument("--next-rows", nargs="+", metavar="ROW",
+                    help="run only these rows of extra.next_rows (small_m, lm_head_argmax, "
+                         "qdq_import, gate_up_silu, rmsnorm_gemv, gate_up_silu_prefill), print "
+                         "them as one JSON line and exit (for profiling one row)")
     ap.add_argument("--counters-from", nargs="+", metavar="DIR",
                     help="per-kernel averages of rocprofv3 --pmc runs of this bench and exit; no GPU")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -758,6 +783,11 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {n} bytes read, {n} bytes written")
         del src, dst
+
+    if args.next_rows:
+        rows = measure_next_rows(max(10, args.steps // 3), max(2, args.warmup // 2), only=set(args.next_rows))
+        print(json.dumps(rows), flush=True)
+        return
 
     w = workload(args.config)
     r = measure_step(w, args.steps, args.warmup, args.samples)
