@@ -400,6 +400,54 @@ int mnb_graph_create(const mnb_matmul_args* ops, int64_t n_ops,
 int mnb_graph_launch(mnb_graph* g, void* stream);
 int mnb_graph_destroy(mnb_graph* g);
 
+/* ---- persistent decode step ---------------------------------------------------
+ * A decode step (every entry M == 1) as ONE cooperative launch that stays
+ * resident for the whole step: one workgroup per compute unit, each of whose
+ * compute wavefronts requests the next entry's packed weights before it waits
+ * for the previous entry to finish.  (Page "Qwen3 CPU Inference Critical
+ * Path", "Phase Q5: scheduling and fusion": the step is a chain of
+ * projections whose only dependence is the activation row; "INT4 MatMul is
+ * first": batch-1 projections are bound by the weight stream.)
+ *
+ * Ordering.  Entry i + 1 reads its activation row only after EVERY
+ * workgroup has written its part of entry i's y (write-through stores,
+ * acknowledged before a device-wide arrival counter is raised), so an entry
+ * whose input `a` is an earlier entry's `y` sees that output.  The outputs
+ * are those of mnb_gemv: every column has the same float32 bits (same
+ * geometry, loads and summation order).
+ *
+ * Supported entries: M == 1, one activation type for all entries, block_size
+ * >= 32, K * element size a multiple of 16, a K whose decode-GEMV geometry
+ * keeps each column in one wavefront (at most 10,240; the few K below that
+ * for which split-K teams sum more efficiently are refused), and at most
+ * 4,096 outputs per workgroup and entry (N up to about a million columns on
+ * 256 compute units).  Others
+ * return MNB_E_UNSUPPORTED naming the entry; use mnb_matmul_sequence or
+ * mnb_graph_* for them.
+ *
+ * Workspace.  mnb_step_workspace_bytes(ops, n) bytes (a function of n alone;
+ * 0 if an entry is invalid or unsupported), 256-byte aligned, owned by the
+ * caller, not overlapping any y: it holds the arrival counters and the entry
+ * table.  mnb_step_create validates everything, then (synchronously, with
+ * hipMemset / hipMemcpy on the current device) writes the table for the
+ * current device's compute-unit count; the workspace must stay untouched and
+ * alive until mnb_step_destroy.  The handle records the entries' pointers.
+ * Launches that may overlap on the device must not share a step.
+ *
+ * mnb_step_launch enqueues one cooperative launch on `stream` (the device
+ * current at creation must be current).  mnb_step_check synchronizes the
+ * stream and reports whether any launch since the last check stopped waiting
+ * for the other workgroups (a bounded wait ran out: the grid was not
+ * co-resident); that launch's outputs are then undefined and the call
+ * returns MNB_E_HIP.  Every wait is bounded, so a launch always completes. */
+typedef struct mnb_step mnb_step;
+size_t mnb_step_workspace_bytes(const mnb_matmul_args* ops, int64_t n_ops);
+int mnb_step_create(const mnb_matmul_args* ops, int64_t n_ops,
+                    void* workspace, size_t workspace_bytes, mnb_step** out);
+int mnb_step_launch(mnb_step* step, void* stream);
+int mnb_step_check(mnb_step* step, void* stream);
+int mnb_step_destroy(mnb_step* step);
+
 /* Text for a status code (static storage). */
 const char* mnb_status_string(int status);
 /* Detail of the most recent error on the calling thread ("" if none). */

@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import weight_only_int4_matmulnbits_amd as mnb
 from weight_only_int4_matmulnbits_amd import _lib
@@ -352,3 +353,48 @@ def test_gemv_rmsnorm_argument_errors():
     assert call(d, M=2) == -1
     assert call(mnb.make_desc(66, 8, 32)) == -2      # K * 4 not a multiple of 16
     assert call(mnb.make_desc(20000, 8, 32)) == -2   # past the decode kernel
+
+
+def test_persistent_step_workspace_and_refusals():
+    """mnb_step_*: the workspace is the counter header (2304 bytes) plus the
+    entry table (112 bytes an entry, rounded up to 256), and entries the step
+    kernel does not take are refused before any HIP call."""
+    L = mnb.lib()
+
+    def mk(K, N, M=1, bs=128, dt=torch.float32, zp=False):
+        return _lib.MatmulArgs(desc=mnb.make_desc(K, N, bs, act_dtype=dt, has_zero_points=zp), M=M, a=P16,
+                               b_packed=P16, scales=P16, zp_packed=P16 if zp else None, bias=None, y=P16)
+
+    # the Qwen3-4B decode step's 145 entries
+    layer = [mk(2560, 6144), mk(4096, 2560), mk(2560, 19456), mk(9728, 2560)]
+    ents = layer * 36 + [mk(2560, 151936)]
+    arr = (_lib.MatmulArgs * len(ents))(*ents)
+    assert L.mnb_step_workspace_bytes(arr, len(ents)) == 2304 + ((145 * 112 + 255) // 256) * 256
+    one = (_lib.MatmulArgs * 1)(mk(1024, 3072, bs=32, zp=True))
+    assert L.mnb_step_workspace_bytes(one, 1) == 2304 + 256
+    h = ctypes.c_void_p()
+    # refusals: status, and nothing launched (no GPU here)
+    cases = [
+        ((mk(1024, 64, M=2),), -2),                  # M != 1
+        ((mk(1024, 64, bs=16),), -2),                # 16-value blocks
+        ((mk(1022, 64),), -2),                       # K * 4 not a multiple of 16
+        ((mk(12288, 64),), -2),                      # needs split-K wavefront teams
+        ((mk(1024, 64), mk(1024, 64, dt=torch.bfloat16)), -2),    # mixed activation types
+    ]
+    for ents, st in cases:
+        arr = (_lib.MatmulArgs * len(ents))(*ents)
+        assert L.mnb_step_workspace_bytes(arr, len(ents)) == 0, ents
+        assert L.mnb_step_create(arr, len(ents), 0x100000, 1 << 20, ctypes.byref(h)) == st
+        assert not h.value
+    assert L.mnb_step_create(one, 0, 0x100000, 1 << 20, ctypes.byref(h)) == -1          # n_ops 0
+    assert L.mnb_step_create(one, 1, None, 0, ctypes.byref(h)) == -1                     # no workspace
+    assert L.mnb_step_create(one, 1, 0x100000, 2304 + 255, ctypes.byref(h)) == -1       # too small
+    assert L.mnb_step_create(one, 1, 0x100010, 1 << 20, ctypes.byref(h)) == -3          # misaligned
+    assert L.mnb_step_create(one, 1, 0x100000, 1 << 20, None) == -1
+    # y inside the workspace
+    bad = (_lib.MatmulArgs * 1)(_lib.MatmulArgs(desc=mnb.make_desc(1024, 64, 32), M=1, a=P16, b_packed=P16,
+                                                scales=P16, zp_packed=None, bias=None, y=0x100100))
+    assert L.mnb_step_create(bad, 1, 0x100000, 1 << 20, ctypes.byref(h)) == -1
+    assert L.mnb_step_launch(None, None) == -1
+    assert L.mnb_step_check(None, None) == -1
+    assert L.mnb_step_destroy(None) == 0

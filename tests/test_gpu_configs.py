@@ -6,7 +6,8 @@ first, last and 30 random columns of every launch; for the prefill steps the
 first, last and 6 random rows times the first, last and 14 random columns of
 every launch; for the 0.6B step with 4 rows per projection (the bench's
 small-M row) all rows times the first, last and 30 random columns.  A
-captured-graph replay must reproduce the eager step bit for bit.
+captured-graph replay must reproduce the eager step bit for bit, and so must
+the decode steps' persistent launch.
 """
 
 import numpy as np
@@ -65,6 +66,20 @@ def test_config_step_parity(orc, cfg):
                 assert torch.equal(e, y), f"graph replay {rep} differs"
             step.run()            # eager work between replays
             torch.cuda.synchronize()
+        if w.M == 1:
+            # the persistent step kernel: the same bits in one launch, over
+            # several launches with eager work between them
+            log(f"config {cfg}: persistent step")
+            step.make_persistent()
+            for rep in range(3):
+                for _, _, y in step.items:
+                    y.fill_(float("nan"))
+                step.launch_persistent()
+                step.persistent.check()
+                for i, (e, (_, _, y)) in enumerate(zip(eager, step.items)):
+                    assert torch.equal(e, y), f"persistent launch {rep} differs at {w.launches[i].name}"
+                step.run()
+                torch.cuda.synchronize()
     step.close()
 
 

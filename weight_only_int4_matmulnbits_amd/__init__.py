@@ -29,7 +29,7 @@ __all__ = [
     "dequant", "PackedWeight", "Sequence", "version", "import_qdq", "qdq_is_native",
     "gather_rows", "argmax", "gemv_silu_mul", "workspace_bytes",
     "argmax_workspace_bytes", "workspace", "gemm_noalloc", "gemm_silu_mul",
-    "gemm_silu_workspace_bytes", "gemv_rmsnorm",
+    "gemm_silu_workspace_bytes", "gemv_rmsnorm", "PersistentStep",
 ]
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
@@ -487,6 +487,52 @@ class Sequence:
         if self._graph is not None:
             check(lib().mnb_graph_destroy(self._graph), "mnb_graph_destroy")
             self._graph = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class PersistentStep:
+    """A decode step (every projection M == 1) as one cooperative launch of
+    the library's persistent step kernel: each projection reads its input
+    only after every workgroup has written the previous projection's output.
+    The caller keeps every tensor alive while the step exists; the step owns
+    the workspace that holds its arrival counters and projection table."""
+
+    def __init__(self, items: TSeq[Tuple[PackedWeight, torch.Tensor, torch.Tensor]]):
+        self._keep: List = list(items)
+        n = len(self._keep)
+        self._args = (MatmulArgs * max(n, 1))()
+        for i, (w, a, y) in enumerate(self._keep):
+            self._args[i] = w.args(a, y)
+        self.n = n
+        self._h = None
+        self.workspace_bytes = int(lib().mnb_step_workspace_bytes(self._args, n))
+        if self.workspace_bytes == 0:
+            # the same checks again, for the library's reason
+            check(lib().mnb_step_create(self._args, n, None, 0, ctypes.byref(ctypes.c_void_p())),
+                  "mnb_step_create")
+        dev = self._keep[0][1].device
+        self._ws = workspace(self.workspace_bytes, dev)
+        h = ctypes.c_void_p()
+        check(lib().mnb_step_create(self._args, n, ctypes.c_void_p(self._ws.data_ptr()), self._ws.numel(),
+                                    ctypes.byref(h)), "mnb_step_create")
+        self._h = h
+
+    def launch(self, stream=None) -> None:
+        check(lib().mnb_step_launch(self._h, _stream(stream)), "mnb_step_launch")
+
+    def check(self, stream=None) -> None:
+        """Synchronizes the stream; raises if a launch gave up waiting."""
+        check(lib().mnb_step_check(self._h, _stream(stream)), "mnb_step_check")
+
+    def close(self) -> None:
+        if self._h is not None:
+            check(lib().mnb_step_destroy(self._h), "mnb_step_destroy")
+            self._h = None
 
     def __del__(self):
         try:

@@ -32,6 +32,8 @@ EXPORTS = (
     "mnb_workspace_bytes", "mnb_argmax_workspace_bytes",
     "mnb_sequence_workspace_bytes", "mnb_gemm_noalloc",
     "mnb_gemm_silu_workspace_bytes", "mnb_gemm_silu_mul", "mnb_gemv_rmsnorm",
+    "mnb_step_workspace_bytes", "mnb_step_create", "mnb_step_launch", "mnb_step_check",
+    "mnb_step_destroy",
 )
 
 
@@ -139,6 +141,15 @@ def lib() -> ctypes.CDLL:
     L.mnb_graph_launch.restype = ctypes.c_int
     L.mnb_graph_destroy.argtypes = [vp]
     L.mnb_graph_destroy.restype = ctypes.c_int
+    L.mnb_step_workspace_bytes.argtypes = [pa, i64]
+    L.mnb_step_workspace_bytes.restype = sz
+    L.mnb_step_create.argtypes = [pa, i64, vp, sz, ctypes.POINTER(vp)]
+    L.mnb_step_create.restype = ctypes.c_int
+    for f in ("mnb_step_launch", "mnb_step_check"):
+        getattr(L, f).argtypes = [vp, vp]
+        getattr(L, f).restype = ctypes.c_int
+    L.mnb_step_destroy.argtypes = [vp]
+    L.mnb_step_destroy.restype = ctypes.c_int
     for f in ("mnb_status_string",):
         getattr(L, f).argtypes = [ctypes.c_int]
         getattr(L, f).restype = ctypes.c_char_p

@@ -25,7 +25,8 @@ PROBE_SOURCE = "mnb_probe.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["mnb_api.hip", "mnb_pack.hip", "mnb_gemv.hip", "mnb_gemm.hip", "mnb_smallm.hip", "mnb_aux.hip"]
+SOURCES = ["mnb_api.hip", "mnb_pack.hip", "mnb_gemv.hip", "mnb_gemm.hip", "mnb_smallm.hip", "mnb_aux.hip",
+           "mnb_step.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

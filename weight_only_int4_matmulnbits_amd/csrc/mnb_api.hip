@@ -158,6 +158,14 @@ struct mnb_graph {
     hipGraphExec_t exec;
 };
 
+struct mnb_step {
+    int device;         // the device the table was written for
+    int grid;           // workgroups (one per CU of that device)
+    bool bf16;
+    int64_t n_ops;
+    void* workspace;    // the caller's: counters and the entry table
+};
+
 extern "C" {
 
 int mnb_validate(const mnb_desc* d, int64_t M) {
@@ -542,6 +550,92 @@ int mnb_graph_destroy(mnb_graph* g) {
     if (e1 != hipSuccess || e2 != hipSuccess)
         return fail(MNB_E_HIP, "mnb_graph_destroy: %s",
                     hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+    return MNB_OK;
+}
+
+// Entries of a persistent step: each a valid product with M == 1 that the
+// step kernel takes, all of one activation type.
+static int check_step(const mnb_matmul_args* ops, int64_t n_ops, std::vector<Problem>* probs) {
+    if (n_ops < 1) return fail(MNB_E_ARG, "step: n_ops=%lld, must be >= 1", (long long)n_ops);
+    if (n_ops > (int64_t(1) << 20)) return fail(MNB_E_OVERFLOW, "step: n_ops=%lld too large", (long long)n_ops);
+    int st = check_sequence(ops, n_ops, probs);
+    if (st != MNB_OK) return st;
+    for (int64_t i = 0; i < n_ops; i++) {
+        const Problem& p = (*probs)[(size_t)i];
+        if (p.bf16 != (*probs)[0].bf16)
+            return fail(MNB_E_UNSUPPORTED, "step entry %lld: every entry must have the activation type of entry 0",
+                        (long long)i);
+        st = step_supports(p, i);
+        if (st != MNB_OK) return st;
+    }
+    return MNB_OK;
+}
+
+size_t mnb_step_workspace_bytes(const mnb_matmul_args* ops, int64_t n_ops) {
+    std::vector<Problem> probs;
+    try {
+        if (check_step(ops, n_ops, &probs) != MNB_OK) return 0;
+    } catch (const std::bad_alloc&) {
+        return 0;
+    }
+    return step_workspace_bytes(n_ops);
+}
+
+int mnb_step_create(const mnb_matmul_args* ops, int64_t n_ops, void* workspace, size_t workspace_bytes,
+                    mnb_step** out) {
+    if (!out) return fail(MNB_E_ARG, "mnb_step_create: out is NULL");
+    *out = nullptr;
+    std::vector<Problem> probs;
+    int st;
+    try {
+        st = check_step(ops, n_ops, &probs);
+    } catch (const std::bad_alloc&) {
+        return fail(MNB_E_ARG, "mnb_step_create: out of host memory");
+    }
+    if (st != MNB_OK) return st;
+    st = check_workspace("mnb_step_create", step_workspace_bytes(n_ops), workspace, workspace_bytes);
+    if (st != MNB_OK) return st;
+    const size_t ws_need = step_workspace_bytes(n_ops);
+    for (int64_t i = 0; i < n_ops; i++) {
+        const Problem& p = probs[(size_t)i];
+        if (overlap(workspace, ws_need, p.y, (size_t)p.N * (p.bf16 ? 2 : 4)))
+            return fail(MNB_E_ARG, "mnb_step_create: entry %lld: y overlaps the workspace", (long long)i);
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MNB_E_HIP, "mnb_step_create: hipGetDevice: %s", hipGetErrorString(e));
+    int grid = 0;
+    st = step_grid(probs[0].bf16, &grid);
+    if (st != MNB_OK) return st;
+    try {
+        st = step_prepare(probs.data(), n_ops, grid, workspace);
+    } catch (const std::bad_alloc&) {
+        return fail(MNB_E_ARG, "mnb_step_create: out of host memory");
+    }
+    if (st != MNB_OK) return st;
+    mnb_step* h = new (std::nothrow) mnb_step{dev, grid, probs[0].bf16, n_ops, workspace};
+    if (!h) return fail(MNB_E_ARG, "mnb_step_create: out of host memory");
+    *out = h;
+    return MNB_OK;
+}
+
+int mnb_step_launch(mnb_step* h, void* stream) {
+    if (!h) return fail(MNB_E_ARG, "mnb_step_launch: step is NULL");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MNB_E_HIP, "mnb_step_launch: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev != h->device)
+        return fail(MNB_E_ARG, "mnb_step_launch: created on device %d, current device %d", h->device, dev);
+    return step_launch(h->bf16, h->grid, h->workspace, h->n_ops, static_cast<hipStream_t>(stream));
+}
+
+int mnb_step_check(mnb_step* h, void* stream) {
+    if (!h) return fail(MNB_E_ARG, "mnb_step_check: step is NULL");
+    return step_check(h->workspace, static_cast<hipStream_t>(stream));
+}
+
+int mnb_step_destroy(mnb_step* h) {
+    delete h;
     return MNB_OK;
 }
 

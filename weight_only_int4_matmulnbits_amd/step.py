@@ -7,7 +7,8 @@ plan keeps packed weights for every token ("Phase Q1": plan-owned packed
 weights reused by every token).  A step here is the model's projections in
 layer order -- fused QKV, o, gate||up (one launch over the concatenated N),
 down -- followed by the LM head, all enqueued on one stream by the library's
-sequence driver (or replayed as one captured graph).
+sequence driver (or replayed as one captured graph), or, for a decode step,
+run as one launch of the persistent step kernel.
 
 Inputs are the seeded synthetic tensors of ``workloads``; weights are packed
 once on the GPU (the preparation step) and the logical values are dropped.
@@ -23,7 +24,7 @@ import torch
 from workloads.generate import projection_inputs
 from workloads.qwen3 import Workload
 
-from . import PackedWeight, Sequence
+from . import PackedWeight, PersistentStep, Sequence
 
 
 class Step:
@@ -48,6 +49,7 @@ class Step:
             del inp
         self.pack_seconds = pack_s
         self.sequence = Sequence(self.items)
+        self.persistent: Optional[PersistentStep] = None
 
     @property
     def weight_bytes(self) -> int:
@@ -66,6 +68,16 @@ class Step:
     def replay(self, stream=None) -> None:
         self.sequence.replay(stream)
 
+    def make_persistent(self) -> PersistentStep:
+        """The same projections as one persistent launch (decode steps only):
+        launch_persistent() then computes what run() computes, bit for bit."""
+        if self.persistent is None:
+            self.persistent = PersistentStep(self.items)
+        return self.persistent
+
+    def launch_persistent(self, stream=None) -> None:
+        self.make_persistent().launch(stream)
+
     def logical_inputs(self, launch_idx: int, device="cuda"):
         """Regenerate the logical (unpacked) inputs of one launch; identical to
         what was packed because the generator is seeded per tensor."""
@@ -74,3 +86,5 @@ class Step:
 
     def close(self) -> None:
         self.sequence.close()
+        if self.persistent is not None:
+            self.persistent.close()
