@@ -170,12 +170,13 @@ def cpu_baselines(cfg, budget_s, rows=None):
 
 # ---- GPU measurements -------------------------------------------------------
 
-def measure_step(w, steps, warmup, samples=MIN_SAMPLES):
+def measure_step(w, steps, warmup, samples=MIN_SAMPLES, persistent=True):
     """Build one step of workload w (weights packed on the GPU), capture it
     as one graph and time its replays; for a decode step also the eager
-    (sequence driver) step.  The launch order of a traced run is: one eager
-    step, warmup + steps + samples graph replays, then (decode) warmup +
-    steps eager steps."""
+    (sequence driver) step and the step as one persistent launch.  The
+    launch order of a traced run is: one eager step, warmup + steps + samples
+    graph replays, then (decode) warmup + steps eager steps and warmup +
+    steps persistent launches."""
     import torch
     from weight_only_int4_matmulnbits_amd.step import Step
 
@@ -192,10 +193,63 @@ def measure_step(w, steps, warmup, samples=MIN_SAMPLES):
     if w.M == 1:
         ms_e, _, _ = time_runs(step.run, steps, warmup, 0)
         out["eager_ms_per_step"] = ms_e
+    if w.M == 1 and persistent:
+        # the same step as one persistent launch (mnb_step_*), for comparison
+        step.make_persistent()
+        ms_p, _, _ = time_runs(step.launch_persistent, steps, warmup, 0)
+        step.persistent.check()
+        out["persistent_ms_per_step"] = ms_p
+        log(f"[bench] {w.title}: {ms_p:.4f} ms/step as one persistent launch")
     step.close()
     del step
     torch.cuda.empty_cache()
     return out
+
+
+def trace_persistent(cfg, launches=5):
+    """Where the time of the persistent decode step goes: one traced launch
+    (after `launches` untraced ones) of the step as a single mnb_step launch,
+    from the phase timestamps every workgroup's control wavefront records
+    (mnb_step_set_trace).  Per projection kind, means over its projections of
+    the median over workgroups of: the wait (from the last workgroup's
+    arrival after the previous projection to the poll that sees it), the row
+    staging, the compute phase (row staged to the workgroup's sums complete),
+    the output store and its acknowledgement, and the projection's span
+    (last arrival to last arrival)."""
+    import numpy as np
+    import torch
+    from weight_only_int4_matmulnbits_amd.step import Step
+    from workloads import workload
+
+    w = workload(cfg)
+    st = Step(w, "cuda", seed=0)
+    p = st.make_persistent()
+    for _ in range(launches):
+        st.launch_persistent()
+    tr = p.trace_buffer()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    st.launch_persistent()
+    e1.record()
+    p.check()
+    t = tr.cpu().numpy().astype(np.float64) / 100.0          # microseconds (100 MHz)
+    t -= t[:, 0, 0].min()
+    arrive = t[:, :, 4].max(axis=0)
+    names = [L.name.split(".")[-1] for L in w.launches]
+    rows = {}
+    for i in range(len(names)):
+        wait = t[:, i, 1] - arrive[i - 1] if i else np.zeros(t.shape[0])
+        rows.setdefault(names[i], []).append(
+            (np.median(wait), np.median(t[:, i, 2] - t[:, i, 1]), np.median(t[:, i, 3] - t[:, i, 2]),
+             np.median(t[:, i, 4] - t[:, i, 3]), arrive[i] - (arrive[i - 1] if i else 0.0)))
+    out = [f"{w.title}: one persistent launch {e0.elapsed_time(e1) * 1e3:.1f} us (event-timed, traced), "
+           f"{t.shape[0]} workgroups, {len(names)} projections; last arrival at {arrive[-1]:.1f} us",
+           f"{'projection':10} {'count':>5} {'wait':>7} {'stage':>7} {'compute':>8} {'store':>7} {'span':>7}  (us)"]
+    for k, v in rows.items():
+        a = np.array(v).mean(axis=0)
+        out.append(f"{k:10} {len(v):5d} " + " ".join(f"{x:7.2f}" for x in a))
+    st.close()
+    return "\n".join(out)
 
 
 def measured_traffic(cfg, kind):
@@ -250,6 +304,9 @@ def summary(w, r, with_samples=True):
         s["weight_GBps"] = r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
         s["hbm_frac"] = s["weight_GBps"] / HBM_PEAK_GBS
         s["eager_ms_per_step"] = round(r["eager_ms_per_step"], 5)
+        if "persistent_ms_per_step" in r:
+            s["persistent_ms_per_step"] = round(r["persistent_ms_per_step"], 5)
+            s["persistent_weight_GBps"] = r["weight_bytes"] / (r["persistent_ms_per_step"] * 1e-3) / 1e9
     else:
         s["TFLOPs"] = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
         s["mfma_frac"] = s["TFLOPs"] / BF16_PEAK_TFLOPS
@@ -516,8 +573,10 @@ def _read_csv(path):
 
 
 def _library_rows(rows):
-    # dispatches of this library's matmul kernels (packing excluded)
-    return [r for r in rows if "mnb::" in r["Kernel_Name"] and "pack_" not in r["Kernel_Name"]]
+    # dispatches of this library's per-projection kernels (packing and the
+    # persistent step kernel, timed after the steps, excluded)
+    return [r for r in rows if "mnb::" in r["Kernel_Name"] and "pack_" not in r["Kernel_Name"]
+            and "step_kernel" not in r["Kernel_Name"]]
 
 
 def _short(name):
@@ -649,6 +708,7 @@ def traffic_from(fetch_dir, write_dir, cfg, copy_mib, kind="gemv"):
     except (OSError, ValueError):
         rec = {}
     srcs = {"gemv": ["weight_only_int4_matmulnbits_amd/csrc/mnb_gemv.hip",
+                     "weight_only_int4_matmulnbits_amd/csrc/mnb_gemv_core.h",
                      "weight_only_int4_matmulnbits_amd/csrc/mnb_internal.h"],
             "gemm": ["weight_only_int4_matmulnbits_amd/csrc/mnb_gemm.hip",
                      "weight_only_int4_matmulnbits_amd/csrc/mnb_internal.h"]}[kind]
@@ -741,6 +801,12 @@ def main():
                     help="run only these rows of extra.next_rows (small_m, lm_head_argmax, "
                          "qdq_import, gate_up_silu, rmsnorm_gemv, gate_up_silu_prefill), print "
                          "them as one JSON line and exit (for profiling one row)")
+    ap.add_argument("--no-persistent", action="store_true",
+                    help="decode configs: do not time the step as one persistent launch (profiling "
+                         "runs: rocprofv3 can end with a segmentation fault after cooperative launches)")
+    ap.add_argument("--trace-step", action="store_true",
+                    help="decode configs: print where the time of the persistent step launch goes "
+                         "(phase timestamps of every workgroup) and exit")
     ap.add_argument("--counters-from", nargs="+", metavar="DIR",
                     help="per-kernel averages of rocprofv3 --pmc runs of this bench and exit; no GPU")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -784,13 +850,17 @@ def main():
         log(f"[bench] copy calibration: {n} bytes read, {n} bytes written")
         del src, dst
 
+    if args.trace_step:
+        print(trace_persistent(args.config), flush=True)
+        return
+
     if args.next_rows:
         rows = measure_next_rows(max(10, args.steps // 3), max(2, args.warmup // 2), only=set(args.next_rows))
         print(json.dumps(rows), flush=True)
         return
 
     w = workload(args.config)
-    r = measure_step(w, args.steps, args.warmup, args.samples)
+    r = measure_step(w, args.steps, args.warmup, args.samples, persistent=not args.no_persistent)
     dec = w.M == 1
     value = (r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 if dec
              else r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12)
@@ -818,6 +888,8 @@ def main():
     }
     if dec:
         line["eager_ms_per_step"] = r["eager_ms_per_step"]
+        if "persistent_ms_per_step" in r:
+            line["persistent_ms_per_step"] = r["persistent_ms_per_step"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baselines(args.config, args.cpu_budget, rows=None if dec else 2)
     if not args.no_extra:
@@ -826,7 +898,7 @@ def main():
             if c == args.config:
                 continue
             wc = workload(c)
-            rc = measure_step(wc, args.steps, args.warmup, args.samples)
+            rc = measure_step(wc, args.steps, args.warmup, args.samples, persistent=not args.no_persistent)
             extra[f"config{c}"] = summary(wc, rc)
             if c in (5, 3) and not args.no_cpu_baseline:
                 extra[f"config{c}"]["cpu_baseline"] = cpu_baselines(c, 3.0, rows=2)

@@ -448,6 +448,20 @@ int mnb_step_launch(mnb_step* step, void* stream);
 int mnb_step_check(mnb_step* step, void* stream);
 int mnb_step_destroy(mnb_step* step);
 
+/* Phase timestamps of later launches, for profiling (page "Qwen3 CPU
+ * Inference Critical Path", "INT4 MatMul is first": the kernel corpus reports
+ * where the time of a matmul goes).  `trace` is device memory of at least
+ * mnb_step_trace_bytes(step) bytes (8-byte aligned; NULL turns tracing off),
+ * owned by the caller and overwritten by every launch: uint64 values
+ * [workgroup][entry][5] of the 100 MHz s_memrealtime counter, taken by each
+ * workgroup's control wavefront before it waits for entry i - 1, after that
+ * wait, with entry i's activation row staged, with the workgroup's sums of
+ * entry i complete, and with its outputs of entry i acknowledged.
+ * mnb_step_trace_bytes returns 0 for NULL; mnb_step_set_trace returns
+ * MNB_E_ARG for a short buffer, MNB_E_ALIGN for a misaligned one. */
+size_t mnb_step_trace_bytes(const mnb_step* step);
+int mnb_step_set_trace(mnb_step* step, void* trace, size_t trace_bytes);
+
 /* Text for a status code (static storage). */
 const char* mnb_status_string(int status);
 /* Detail of the most recent error on the calling thread ("" if none). */

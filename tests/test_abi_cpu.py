@@ -398,3 +398,5 @@ def test_persistent_step_workspace_and_refusals():
     assert L.mnb_step_launch(None, None) == -1
     assert L.mnb_step_check(None, None) == -1
     assert L.mnb_step_destroy(None) == 0
+    assert L.mnb_step_trace_bytes(None) == 0
+    assert L.mnb_step_set_trace(None, None, 0) == -1

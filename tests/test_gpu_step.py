@@ -156,3 +156,26 @@ def test_unsupported_entries_are_refused():
         mnb.PersistentStep([(pw3, g3.a, torch.empty(1, 64, device="cuda")),
                             (pw2, g2.a, torch.empty(1, 64, dtype=torch.bfloat16, device="cuda"))])
     assert e.value.status == -2
+
+
+def test_trace_timestamps_are_ordered_and_change_nothing():
+    shapes = [(1024, 3072), (3072, 1024), (1024, 2048)]
+    ins, pws, a0, ys = _chain(shapes, 32, "f32", True, False, seed=9)
+    ref = _reference(pws, a0)
+    step = mnb.PersistentStep(_items(pws, a0, ys))
+    tr = step.trace_buffer()
+    step.launch()
+    step.check()
+    for i, (r, y) in enumerate(zip(ref, ys)):
+        assert torch.equal(r, y), f"projection {i} with tracing on"
+    t = tr.cpu()
+    assert t.shape[1:] == (len(shapes), 5) and t.shape[0] >= 1
+    assert (t > 0).all()
+    # per workgroup and projection the five phases are in order, and each
+    # projection starts after the previous one's outputs are acknowledged
+    assert (t[:, :, 1:] >= t[:, :, :-1]).all()
+    assert (t[:, 1:, 0] >= t[:, :-1, 4]).all()
+    # every workgroup saw every arrival of projection i - 1 before staging row
+    # i (up to 1 us of skew between the clocks of different CUs)
+    assert (t[:, 1:, 1].min(dim=0).values >= t[:, :-1, 4].max(dim=0).values - 100).all()
+    step.close()

@@ -525,6 +525,17 @@ class PersistentStep:
     def launch(self, stream=None) -> None:
         check(lib().mnb_step_launch(self._h, _stream(stream)), "mnb_step_launch")
 
+    def trace_buffer(self) -> torch.Tensor:
+        """Turns on the phase timestamps of later launches and returns their
+        buffer: int64 [workgroups][entries][5] of the 100 MHz device clock
+        (before the wait for the previous entry, after it, row staged, sums
+        complete, outputs acknowledged)."""
+        n = int(lib().mnb_step_trace_bytes(self._h)) // 8
+        t = torch.zeros(n, dtype=torch.int64, device=self._keep[0][1].device)
+        check(lib().mnb_step_set_trace(self._h, ctypes.c_void_p(t.data_ptr()), 8 * n), "mnb_step_set_trace")
+        self._trace = t
+        return t.view(-1, self.n, 5)
+
     def check(self, stream=None) -> None:
         """Synchronizes the stream; raises if a launch gave up waiting."""
         check(lib().mnb_step_check(self._h, _stream(stream)), "mnb_step_check")

@@ -33,7 +33,7 @@ EXPORTS = (
     "mnb_sequence_workspace_bytes", "mnb_gemm_noalloc",
     "mnb_gemm_silu_workspace_bytes", "mnb_gemm_silu_mul", "mnb_gemv_rmsnorm",
     "mnb_step_workspace_bytes", "mnb_step_create", "mnb_step_launch", "mnb_step_check",
-    "mnb_step_destroy",
+    "mnb_step_destroy", "mnb_step_trace_bytes", "mnb_step_set_trace",
 )
 
 
@@ -150,6 +150,10 @@ def lib() -> ctypes.CDLL:
         getattr(L, f).restype = ctypes.c_int
     L.mnb_step_destroy.argtypes = [vp]
     L.mnb_step_destroy.restype = ctypes.c_int
+    L.mnb_step_trace_bytes.argtypes = [vp]
+    L.mnb_step_trace_bytes.restype = sz
+    L.mnb_step_set_trace.argtypes = [vp, vp, sz]
+    L.mnb_step_set_trace.restype = ctypes.c_int
     for f in ("mnb_status_string",):
         getattr(L, f).argtypes = [ctypes.c_int]
         getattr(L, f).restype = ctypes.c_char_p

@@ -164,6 +164,7 @@ struct mnb_step {
     bool bf16;
     int64_t n_ops;
     void* workspace;    // the caller's: counters and the entry table
+    void* trace;        // the caller's phase-timestamp buffer, or NULL
 };
 
 extern "C" {
@@ -613,7 +614,7 @@ int mnb_step_create(const mnb_matmul_args* ops, int64_t n_ops, void* workspace, 
         return fail(MNB_E_ARG, "mnb_step_create: out of host memory");
     }
     if (st != MNB_OK) return st;
-    mnb_step* h = new (std::nothrow) mnb_step{dev, grid, probs[0].bf16, n_ops, workspace};
+    mnb_step* h = new (std::nothrow) mnb_step{dev, grid, probs[0].bf16, n_ops, workspace, nullptr};
     if (!h) return fail(MNB_E_ARG, "mnb_step_create: out of host memory");
     *out = h;
     return MNB_OK;
@@ -626,7 +627,23 @@ int mnb_step_launch(mnb_step* h, void* stream) {
     if (e != hipSuccess) return fail(MNB_E_HIP, "mnb_step_launch: hipGetDevice: %s", hipGetErrorString(e));
     if (dev != h->device)
         return fail(MNB_E_ARG, "mnb_step_launch: created on device %d, current device %d", h->device, dev);
-    return step_launch(h->bf16, h->grid, h->workspace, h->n_ops, static_cast<hipStream_t>(stream));
+    return step_launch(h->bf16, h->grid, h->workspace, h->n_ops, h->trace, static_cast<hipStream_t>(stream));
+}
+
+size_t mnb_step_trace_bytes(const mnb_step* h) {
+    return h ? (size_t)h->grid * (size_t)h->n_ops * 5 * sizeof(uint64_t) : 0;
+}
+
+int mnb_step_set_trace(mnb_step* h, void* trace, size_t trace_bytes) {
+    if (!h) return fail(MNB_E_ARG, "mnb_step_set_trace: step is NULL");
+    if (trace) {
+        if (trace_bytes < mnb_step_trace_bytes(h))
+            return fail(MNB_E_ARG, "mnb_step_set_trace: %zu bytes given, %zu needed", trace_bytes,
+                        mnb_step_trace_bytes(h));
+        if (!aligned(trace, 8)) return fail(MNB_E_ALIGN, "mnb_step_set_trace: trace must be 8-byte aligned");
+    }
+    h->trace = trace;
+    return MNB_OK;
 }
 
 int mnb_step_check(mnb_step* h, void* stream) {

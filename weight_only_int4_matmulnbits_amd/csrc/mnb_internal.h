@@ -74,13 +74,14 @@ int64_t gemv_max_k(int bs);
 // bytes for n entries (arrival counters and the entry table); whether the
 // step kernel takes problem p (MNB_E_UNSUPPORTED with the reason if not);
 // the grid (one workgroup per CU; HIP calls); writing the table for that grid
-// into ws (synchronous); one cooperative launch; and, after the stream, the
+// into ws (synchronous); one cooperative launch (trace: the optional phase
+// timestamps, grid * n * 5 uint64, or NULL); and, after the stream, the
 // error word (a wait that ran out).
 size_t step_workspace_bytes(int64_t n_ops);
 int step_supports(const Problem& p, int64_t idx);
 int step_grid(bool bf16, int* grid);
 int step_prepare(const Problem* probs, int64_t n, int grid, void* ws);
-int step_launch(bool bf16, int grid, void* ws, int64_t n, hipStream_t s);
+int step_launch(bool bf16, int grid, void* ws, int64_t n, void* trace, hipStream_t s);
 int step_check(void* ws, hipStream_t s);
 int device_compute_units();   // CUs of the current device (cached); sizes grids only
 

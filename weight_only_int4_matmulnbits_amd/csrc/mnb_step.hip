@@ -96,6 +96,11 @@ struct StepArgs {
     uint32_t* done;
     uint32_t* error;
     int n_ops;
+    // optional phase timestamps (s_memrealtime, 100 MHz): for workgroup w and
+    // entry i, trace[(w * n_ops + i) * 5 + k] at k = 0 before the wait for
+    // entry i - 1, 1 after it, 2 with row i staged, 3 with the workgroup's
+    // sums of entry i complete, 4 with its outputs acknowledged; or NULL
+    uint64_t* trace;
 };
 
 // One item's loads, kept raw (decoding them here would wait for them).
@@ -337,8 +342,10 @@ __device__ void control_wave(const StepArgs& s, uint8_t* act, const float* out, 
     bool waiting = true;
     for (int i = 0; i < n; i++) {
         const StepOp o = op_at(s.ops, i);
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         // every workgroup's outputs of projection i - 1 are in memory
         if (i > 0 && waiting) waiting = wait_arrivals(s, (uint32_t)i * (uint32_t)G, lane);
+        const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
         // stage row i: 1 KiB requests, the swizzle of the decode GEMV
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<void*>(o.a), (short)0, o.K * ESZ, 0x00020000);
@@ -351,8 +358,10 @@ __device__ void control_wave(const StepArgs& s, uint8_t* act, const float* out, 
                 0, 0, kCoherent);
         }
         __builtin_amdgcn_s_waitcnt(0);
+        const uint64_t t2 = __builtin_amdgcn_s_memrealtime();
         wg_barrier<40>();              // S(i)
         wg_barrier<41>();              // D(i)
+        const uint64_t t3 = __builtin_amdgcn_s_memrealtime();
         // the workgroup's sums of projection i, written through to memory
         const int Gc = 64 >> o.log2_L;
         const int per_wave = o.n_items * Gc;
@@ -371,6 +380,10 @@ __device__ void control_wave(const StepArgs& s, uint8_t* act, const float* out, 
             }
         }
         __builtin_amdgcn_s_waitcnt(0);     // acknowledged
+        const uint64_t t4 = __builtin_amdgcn_s_memrealtime();
+        if (s.trace && lane < 5)
+            s.trace[((size_t)blockIdx.x * n + i) * 5 + lane] =
+                lane == 0 ? t0 : lane == 1 ? t1 : lane == 2 ? t2 : lane == 3 ? t3 : t4;
         if (i + 1 < n && lane == 0)
             __hip_atomic_fetch_add(s.counters + (blockIdx.x % kCounters) * kCounterStride, 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
@@ -488,7 +501,7 @@ int step_grid(bool bf16, int* grid) {
     return MNB_OK;
 }
 
-int step_launch(bool bf16, int grid, void* ws, int64_t n, hipStream_t s) {
+int step_launch(bool bf16, int grid, void* ws, int64_t n, void* trace, hipStream_t s) {
     StepArgs a;
     uint8_t* base = static_cast<uint8_t*>(ws);
     a.ops = (OpTable)(base + kHeaderBytes);
@@ -496,6 +509,7 @@ int step_launch(bool bf16, int grid, void* ws, int64_t n, hipStream_t s) {
     a.done = reinterpret_cast<uint32_t*>(base + kDoneOffset);
     a.error = reinterpret_cast<uint32_t*>(base + kErrorOffset);
     a.n_ops = (int)n;
+    a.trace = static_cast<uint64_t*>(trace);
     void* args[] = {&a};
     const hipError_t e = hipLaunchCooperativeKernel(step_fn(bf16), dim3((unsigned)grid), dim3(kThreads), args,
                                                     (unsigned)kLdsBytes, s);
