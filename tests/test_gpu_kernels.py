@@ -553,6 +553,26 @@ def test_small_m_parity_sweep(orc, dt, bs):
     log(f"small-M {dt} bs={bs}: worst err/tol {worst:.3g}")
 
 
+@pytest.mark.parametrize("dt,M,K,N,bs,zp,bias", [("f32", 10, 3072, 12000, 64, True, True),
+                                                  ("bf16", 16, 5120, 12000, 128, False, True)])
+def test_small_m_passes_with_several_sets_per_workgroup(orc, dt, M, K, N, bs, zp, bias):
+    """K longer than one staged pass and more column sets than resident
+    workgroups: a workgroup stages every pass again for each further set.
+    Sampled columns against the oracle, and a slice of the columns launched
+    alone (where each is in a workgroup's first set) bit-identical."""
+    log(f"small-M passes {dt} M={M} K={K} N={N} bs={bs}")
+    inp, g = _inputs(K, N, M, bs, dt, zp, bias, seed=K + N + M)
+    y = _packed(g, bs).matmul(g.a)
+    rng = np.random.default_rng(K)
+    cols = sorted({0, 16 * 300 + 5, N - 1, *map(int, rng.choice(N, size=40, replace=False))})
+    y_ref, S = oracle_ref(orc, inp, cols=cols)
+    assert_close(out_f64(y[:, torch.as_tensor(cols, device=DEV)]), y_ref, S, dt, f"M={M} K={K} N={N}")
+    lo, hi = 16 * 700, 16 * 700 + 48
+    part = mnb.PackedWeight.from_logical(g.q[lo:hi], g.scales[lo:hi], None if g.zp is None else g.zp[lo:hi],
+                                         None if g.bias is None else g.bias[lo:hi], block_size=bs)
+    assert torch.equal(part.matmul(g.a), y[:, lo:hi])
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("M", [2, 16])
 def test_small_m_exact_arithmetic_bit_exact(orc, dt, M):

@@ -9,12 +9,14 @@
 // Mapping on CDNA4.  One v_mfma_f32_16x16x32_bf16 multiplies 16 rows of A (rows
 // past M are zeros) by 32 K values of 16 columns (a "column group").  K is cut
 // into spans of 128 values (four MFMA slices of 32).  A workgroup of WV
-// wavefronts stages A once in LDS, already in the MFMA operand layout
-// (float32 activations as a bf16 head and tail, a = hi + lo), for as many
-// spans as fit (a "pass"; longer K is staged pass by pass).  It then walks
-// over "group sets" of up to four column groups; wavefront w takes spans w,
-// w + WV, ... of every column group of the set, so each weight byte is read by
-// exactly one wavefront and one staged activation slice serves the whole set.
+// wavefronts walks over "group sets" of up to four column groups; wavefront w
+// takes spans w, w + WV, ... of every column group of the set, so each weight
+// byte is read by exactly one wavefront.  Each wavefront stages the rows of A
+// for its own spans in LDS, already in the MFMA operand layout (float32
+// activations as a bf16 head and tail, a = hi + lo), once for as many spans
+// as fit (a "pass"; longer K is staged pass by pass, again for each set), so
+// one staged slice serves every column group it meets and no wavefront waits
+// for another's staging.
 // Weights stream through two register stages (the next item's loads are in
 // flight while one is multiplied).  For a span, lane l = c + 16 g reads the 16
 // packed bytes (32 values, K offset 32 g of the span) of column c; a 4 x 4
@@ -34,6 +36,8 @@
 // concatenated launches (fused QKV, gate||up) are bit-identical to separate
 // ones.  With one nonzero activation the result is float32((q - zp) * s)
 // exactly.  No atomics, no workspace.
+#include <type_traits>
+
 #include "mnb_internal.h"
 
 namespace mnb {
@@ -86,20 +90,42 @@ struct Res {
     __amdgpu_buffer_rsrc_t a, b, s, z, bias;
 };
 
-// The loads of item f of this wavefront: set r = f / ipw of this workgroup,
-// span wave + (f % ipw) * WV, every column group of the set.  Items past the
-// last set or span, values past K and columns past N read zeros (offsets
+// Where item f of a wavefront lies: set r of the workgroup (f / ipw), item i
+// of the set (f % ipw), and for staged passes the pass and the item within it
+// (i / ipp, i % ipp).  Items are visited in order, so the position advances
+// by counting (wavefront-uniform scalar operations, no divisions).
+struct Pos {
+    int r, i, pass, ip;
+};
+
+__device__ __forceinline__ void advance(const SmallArgs& g, Pos& p) {
+    p.i++;
+    p.ip++;
+    if (p.ip == g.ipp) {
+        p.ip = 0;
+        p.pass++;
+    }
+    if (p.i == g.ipw) {
+        p.i = 0;
+        p.ip = 0;
+        p.pass = 0;
+        p.r++;
+    }
+}
+
+// The loads of the item at position p of this wavefront: set p.r of this
+// workgroup, span wave + p.i * WV, every column group of the set.  Items past
+// the last set or span, values past K and columns past N read zeros (offsets
 // forced past the resources), so every lane issues the same loads whatever
 // the shape.
 template <bool BF16, bool HAS_ZP, int NG, int NSB, bool SV>
-__device__ __forceinline__ void load_item(const SmallArgs& g, const Res& rr, int f, int wave, int WV, int lane,
+__device__ __forceinline__ void load_item(const SmallArgs& g, const Res& rr, const Pos& p, int wave, int WV, int lane,
                                           Item<NG, NSB>& it) {
     constexpr int ESZ = BF16 ? 2 : 4;
     constexpr int SPB = 4 / NSB;                 // slices per scale block
     const int c = lane & 15, grp = lane >> 4;
-    const int r = f / g.ipw;
-    const int span = wave + (f - r * g.ipw) * WV;
-    const int set = (int)blockIdx.x + r * (int)gridDim.x;
+    const int span = wave + p.i * WV;
+    const int set = (int)blockIdx.x + p.r * (int)gridDim.x;
     const uint32_t set_out = set < g.n_sets ? 0u : kOob;
     const uint32_t span_out = span < g.spans ? 0u : kOob;
     {
@@ -186,86 +212,129 @@ __device__ __forceinline__ void transpose_rows(u32x4& w) {
     w = u32x4{q01[0], q01[1], q23[0], q23[1]};
 }
 
-// Stages the activations of the pass's spans into LDS: for the first mr
-// rows (8 when M <= 8, else 16), slice j (32 values) of the pass at
-// hi[(j * 4 + g) * mr + row] (and lo): values 8 g .. 8 g + 7 of the slice for
-// that row, the A operand of MFMA lane row + 16 g; rows past M and values
-// past K are zeros (rows past mr are never stored: their lanes read zeros).  Each thread requests kStageU pieces before it
-// converts any (a load consumed at once would serialize the round trips).
-constexpr int kStageU = 8;
+// Activations in LDS: for the first mr rows of A (8 when M <= 8, else 16),
+// slice j (32 values) of a pass at hi[(j * 4 + g) * mr + row] (and lo): values
+// 8 g .. 8 g + 7 of the slice for that row, the A operand of MFMA lane
+// row + 16 g; rows past M and values past K are zeros (rows past mr are never
+// stored: their lanes read zeros).
 
+// One piece (8 values of a row) as the bf16 head h and, for float32
+// activations, the bf16 tail t = bf16(a - h).
 template <bool BF16>
-struct StageRegs {
-    u32x4 x[kStageU][BF16 ? 1 : 2];
+__device__ __forceinline__ void convert_piece(const u32x4 (&x)[BF16 ? 1 : 2], u32x4& hv, u32x4& tv) {
+    float v[8];
+    if constexpr (BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            v[2 * e] = __uint_as_float(x[0][e] << 16);
+            v[2 * e + 1] = __uint_as_float(x[0][e] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            v[e] = __uint_as_float(x[0][e]);
+            v[4 + e] = __uint_as_float(x[1][e]);
+        }
+    }
+    bf16x8 h, t;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        h[e] = (__bf16)v[e];
+        if constexpr (!BF16) t[e] = (__bf16)(v[e] - (float)h[e]);
+    }
+    hv = __builtin_bit_cast(u32x4, h);
+    if constexpr (!BF16) tv = __builtin_bit_cast(u32x4, t);
+}
+
+// Each wavefront stages only the spans it multiplies (w, w + WV, ...) of a
+// pass, into their places of the layout above, so no other wavefront waits
+// for it and none overwrites it.  Of its items i0, i0 + 1, ... (spans
+// w + i WV), lane l takes pieces q = 0 .. nq - 1 of the list: item
+// i0 + q / P, piece j = (q % P) * 64 + l of that span's 16 mr in row order
+// (row j / 16, values 8 (j % 16) .. 8 (j % 16) + 7 of the span), so that 16
+// lanes read one row's span contiguously; P = mr / 4 pieces per lane and
+// span.  Only the pieces of the list are requested, up to U at a time (12
+// for the first pass; 4 for later passes, which are staged while both
+// register stages of weights are live).
+template <bool BF16, int U>
+struct OwnRegs {
+    u32x4 x[U][BF16 ? 1 : 2];
 };
 
-// Requests pieces base .. of the pass into registers.
-template <bool BF16>
-__device__ __forceinline__ void stage_issue(const SmallArgs& g, const Res& rr, int pass, int base, StageRegs<BF16>& st) {
+struct OwnList {
+    int i0;         // first item of the list
+    int base;       // first span of the pass (its LDS position 0)
+    int nq;         // pieces per lane
+};
+
+// Staged index (LDS position) and source of piece q of the list.
+__device__ __forceinline__ void own_piece(const SmallArgs& g, int wave, int WV, int lane, const OwnList& o, int q,
+                                          int& idx, int& row, int& k0) {
+    const int l2p = g.log2_mr - 2;
+    const int span = wave + (o.i0 + (q >> l2p)) * WV;
+    const int j = ((q & ((1 << l2p) - 1)) << 6) + lane;
+    row = j >> 4;
+    k0 = span * kSpan + 8 * (j & 15);
+    idx = ((span - o.base) << (g.log2_mr + 4)) + ((j & 15) << g.log2_mr) + row;
+}
+
+template <bool BF16, int U>
+__device__ __forceinline__ void own_issue(const SmallArgs& g, const Res& rr, int wave, int WV, int lane,
+                                          const OwnList& o, int q0, OwnRegs<BF16, U>& st) {
     constexpr int ESZ = BF16 ? 2 : 4;
-    constexpr int AV = BF16 ? 1 : 2;             // 16-byte loads per piece
-    const int n = (g.pass_spans * 16) << g.log2_mr;
-    const int mr = 1 << g.log2_mr;
 #pragma unroll
-    for (int j = 0; j < kStageU; j++) {
-        const int idx = base + j * (int)blockDim.x + (int)threadIdx.x;
-        const int sl = idx >> (g.log2_mr + 2), rem = idx & (4 * mr - 1);
-        const int row = rem & (mr - 1);
-        const int k0 = (pass * g.pass_spans * 4 + sl) * 32 + 8 * (rem >> g.log2_mr);
-        const uint32_t out = (idx < n && row < g.M && k0 < g.K) ? 0u : kOob;
-        const uint32_t off = (((uint32_t)row * (uint32_t)g.K + (uint32_t)k0) * ESZ) | out;
+    for (int j = 0; j < U; j++) {
+        if (q0 + j < o.nq) {
+            int idx, row, k0;
+            own_piece(g, wave, WV, lane, o, q0 + j, idx, row, k0);
+            const uint32_t out = (row < g.M && k0 < g.K) ? 0u : kOob;
+            const uint32_t off = (((uint32_t)row * (uint32_t)g.K + (uint32_t)k0) * ESZ) | out;
 #pragma unroll
-        for (int v = 0; v < AV; v++) st.x[j][v] = __builtin_amdgcn_raw_buffer_load_b128(rr.a, off + 16 * v, 0, 0);
-    }
-}
-
-// Converts requested pieces to the bf16 head (and tail) and writes them.
-template <bool BF16>
-__device__ __forceinline__ void stage_finish(const SmallArgs& g, int base, const StageRegs<BF16>& st, u32x4* hi,
-                                             u32x4* lo) {
-    constexpr int AV = BF16 ? 1 : 2;
-    const int n = (g.pass_spans * 16) << g.log2_mr;
-#pragma unroll
-    for (int j = 0; j < kStageU; j++) {
-        const int idx = base + j * (int)blockDim.x + (int)threadIdx.x;
-        float v[8];
-        if constexpr (BF16) {
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                v[2 * e] = __uint_as_float(st.x[j][0][e] << 16);
-                v[2 * e + 1] = __uint_as_float(st.x[j][0][e] & 0xFFFF0000u);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                v[e] = __uint_as_float(st.x[j][0][e]);
-                v[4 + e] = __uint_as_float(st.x[j][AV - 1][e]);
-            }
-        }
-        bf16x8 h, t;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            h[e] = (__bf16)v[e];
-            if constexpr (!BF16) t[e] = (__bf16)(v[e] - (float)h[e]);
-        }
-        if (idx < n) {
-            hi[idx] = __builtin_bit_cast(u32x4, h);
-            if constexpr (!BF16) lo[idx] = __builtin_bit_cast(u32x4, t);
+            for (int v = 0; v < (BF16 ? 1 : 2); v++)
+                st.x[j][v] = __builtin_amdgcn_raw_buffer_load_b128(rr.a, off + 16 * v, 0, 0);
         }
     }
 }
 
-template <bool BF16>
-__device__ __forceinline__ void stage_pass(const SmallArgs& g, const Res& rr, int pass, u32x4* hi, u32x4* lo) {
-    const int n = (g.pass_spans * 16) << g.log2_mr;
-    for (int base = 0; base < n; base += kStageU * (int)blockDim.x) {
-        StageRegs<BF16> st;
-        stage_issue<BF16>(g, rr, pass, base, st);
-        stage_finish<BF16>(g, base, st, hi, lo);
+template <bool BF16, int U>
+__device__ __forceinline__ void own_finish(const SmallArgs& g, int wave, int WV, int lane, const OwnList& o, int q0,
+                                           const OwnRegs<BF16, U>& st, u32x4* hi, u32x4* lo) {
+#pragma unroll
+    for (int j = 0; j < U; j++) {
+        if (q0 + j < o.nq) {
+            int idx, row, k0;
+            own_piece(g, wave, WV, lane, o, q0 + j, idx, row, k0);
+            u32x4 h, t;
+            convert_piece<BF16>(st.x[j], h, t);
+            hi[idx] = h;
+            if constexpr (!BF16) lo[idx] = t;
+        }
     }
 }
 
-template <bool BF16, bool HAS_ZP, int NG, int NSB, bool SV>
+// The list of pass `pass` of this wavefront: its items pass * ipp .. below
+// (pass + 1) * ipp whose spans lie below K.
+__device__ __forceinline__ OwnList own_list(const SmallArgs& g, int wave, int WV, int pass) {
+    const int own = (g.spans - wave + WV - 1) / WV;      // items with a span below K
+    const int i0 = pass * g.ipp;
+    const int i1 = i0 + g.ipp < own ? i0 + g.ipp : own;
+    return OwnList{i0, pass * g.pass_spans, (i1 > i0 ? i1 - i0 : 0) << (g.log2_mr - 2)};
+}
+
+// Stages pieces q0 .. of the list, U at a time.
+template <bool BF16, int U>
+__device__ __forceinline__ void own_stage(const SmallArgs& g, const Res& rr, int wave, int WV, int lane,
+                                          const OwnList& o, int q0, u32x4* hi, u32x4* lo) {
+    for (; q0 < o.nq; q0 += U) {
+        OwnRegs<BF16, U> st;
+        own_issue<BF16, U>(g, rr, wave, WV, lane, o, q0, st);
+        own_finish<BF16, U>(g, wave, WV, lane, o, q0, st, hi, lo);
+    }
+}
+
+// MP: K takes several passes (a separate instance, so that the single-pass
+// loop carries no staging code: its register use and waits stay lean).
+template <bool BF16, bool HAS_ZP, int NG, int NSB, bool SV, bool MP>
 __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
     extern __shared__ __attribute__((aligned(16))) u32x4 lds[];
     const int WV = blockDim.x >> 6;
@@ -292,28 +361,29 @@ __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
     const int my_sets = (int)blockIdx.x < g.n_sets ? (g.n_sets - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
     const int total = my_sets * g.ipw;
 
-    // one pass holds all of K: staged once.  The first pieces are requested
-    // before the first item's weights and converted after (loads complete in
-    // order: the weights stay in flight while A is written); the second
-    // item's weights follow (both at once could exceed the 63 loads the
-    // wait counter tracks)
+    // the positions of the next item to multiply and of the next to request
+    Pos ps{0, 0, 0, 0};
+    Pos pl = ps;
+
+    // The first pass of this wavefront's own spans: its first pieces are
+    // requested before the first item's weights and converted after (loads
+    // complete in order: the weights stay in flight while A is written); the
+    // second item's weights follow (both at once could exceed the 63 loads
+    // the wait counter tracks).  A wavefront reads only what it wrote, so
+    // waiting for its own LDS writes is enough.
     Item<NG, NSB> s0, s1;
-    if (g.passes == 1) {
-        const int n = pieces;
-        StageRegs<BF16> st;
-        stage_issue<BF16>(g, rr, 0, 0, st);
-        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, 0, wave, WV, lane, s0);
-        stage_finish<BF16>(g, 0, st, hi, lo);
-        for (int base = kStageU * (int)blockDim.x; base < n; base += kStageU * (int)blockDim.x) {
-            stage_issue<BF16>(g, rr, 0, base, st);
-            stage_finish<BF16>(g, base, st, hi, lo);
-        }
-        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, 1, wave, WV, lane, s1);
-        __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the LDS writes
-        asm volatile("s_barrier" : : : "memory");
-    } else {
-        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, 0, wave, WV, lane, s0);
-        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, 1, wave, WV, lane, s1);
+    {
+        constexpr int U = 12;
+        const OwnList o = own_list(g, wave, WV, 0);
+        OwnRegs<BF16, U> st;
+        own_issue<BF16, U>(g, rr, wave, WV, lane, o, 0, st);
+        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, pl, wave, WV, lane, s0);
+        advance(g, pl);
+        own_finish<BF16, U>(g, wave, WV, lane, o, 0, st, hi, lo);
+        own_stage<BF16, U>(g, rr, wave, WV, lane, o, U, hi, lo);
+        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, pl, wave, WV, lane, s1);
+        advance(g, pl);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -321,20 +391,22 @@ __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
 #pragma unroll
     for (int u = 0; u < NG; u++) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](const Item<NG, NSB>& it, int f) {
-        const int r = f / g.ipw;
-        const int i = f - r * g.ipw;
-        // a new pass: every wavefront is done with the previous one, then
-        // the next pass is staged (this waits for the weights in flight too)
-        if (g.passes > 1 && i % g.ipp == 0) {
-            asm volatile("s_barrier" : : : "memory");
-            stage_pass<BF16>(g, rr, i / g.ipp, hi, lo);
-            __builtin_amdgcn_s_waitcnt(0xC07F);
-            asm volatile("s_barrier" : : : "memory");
+    auto step = [&](const Item<NG, NSB>& it, const Pos& p, int) {
+        const int r = p.r;
+        const int i = p.i;
+        // the first item of a later pass (or the first pass of a later set):
+        // this wavefront restages its own spans of that pass (this waits for
+        // the weights in flight too); no other wavefront reads them
+        if constexpr (MP) {
+            if (p.ip == 0 && (p.pass > 0 || r > 0)) {
+                own_stage<BF16, 4>(g, rr, wave, WV, lane, own_list(g, wave, WV, p.pass), 0, hi, lo);
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         const int span = wave + i * WV;
         if (span < g.spans) {
-            const int ls = (span - (i / g.ipp) * g.pass_spans) * 4;     // its first slice in LDS
+            const int ls = (span - p.pass * g.pass_spans) * 4;     // its first slice in LDS
             // lanes of rows past mr read a stored row and take zeros instead
             const int pos = grp * mr + (c & (mr - 1));
             const bool live = c < mr;
@@ -424,30 +496,37 @@ __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
 
     // f is workgroup-uniform, so every wavefront reaches every barrier
     for (int f = 0; f < total; f += 2) {
-        step(s0, f);
-        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, f + 2, wave, WV, lane, s0);
+        step(s0, ps, 0);
+        advance(g, ps);
+        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, pl, wave, WV, lane, s0);
+        advance(g, pl);
         __builtin_amdgcn_sched_barrier(0);
-        if (f + 1 < total) step(s1, f + 1);
-        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, f + 3, wave, WV, lane, s1);
+        if (f + 1 < total) step(s1, ps, 0);
+        advance(g, ps);
+        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, pl, wave, WV, lane, s1);
+        advance(g, pl);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 using SmallFn = void (*)(SmallArgs);
 
-template <bool BF16, bool HAS_ZP, int NG, bool SV>
+template <bool BF16, bool HAS_ZP, int NG, bool SV, bool MP>
 SmallFn pick_ng(int nsb) {
     switch (nsb) {
-        case 4: return smallm_kernel<BF16, HAS_ZP, NG, 4, SV>;
-        case 2: return smallm_kernel<BF16, HAS_ZP, NG, 2, SV>;
-        default: return smallm_kernel<BF16, HAS_ZP, NG, 1, SV>;
+        case 4: return smallm_kernel<BF16, HAS_ZP, NG, 4, SV, MP>;
+        case 2: return smallm_kernel<BF16, HAS_ZP, NG, 2, SV, MP>;
+        default: return smallm_kernel<BF16, HAS_ZP, NG, 1, SV, MP>;
     }
 }
 
+// Several passes take one column group per set (ng == 1).
 template <bool BF16, bool HAS_ZP>
-SmallFn pick(int ng, int nsb, bool sv) {
-    if (sv) return ng == 1 ? pick_ng<BF16, HAS_ZP, 1, true>(nsb) : pick_ng<BF16, HAS_ZP, kNG, true>(nsb);
-    return ng == 1 ? pick_ng<BF16, HAS_ZP, 1, false>(nsb) : pick_ng<BF16, HAS_ZP, kNG, false>(nsb);
+SmallFn pick(int ng, int nsb, bool sv, bool mp) {
+    if (mp) return sv ? pick_ng<BF16, HAS_ZP, 1, true, true>(nsb) : pick_ng<BF16, HAS_ZP, 1, false, true>(nsb);
+    if (sv)
+        return ng == 1 ? pick_ng<BF16, HAS_ZP, 1, true, false>(nsb) : pick_ng<BF16, HAS_ZP, kNG, true, false>(nsb);
+    return ng == 1 ? pick_ng<BF16, HAS_ZP, 1, false, false>(nsb) : pick_ng<BF16, HAS_ZP, kNG, false, false>(nsb);
 }
 
 int ilog2(int v) {
@@ -517,11 +596,12 @@ int launch_smallm(const Problem& p, hipStream_t s) {
     a.ipw = (a.spans + WV - 1) / WV;
     a.ipp = ps / WV;
     // column groups per set: up to four once there are enough groups to give
-    // every CU two sets; the grid only decides which workgroup takes a set
+    // every CU two sets (one with several passes); the grid only decides
+    // which workgroup takes a set
     const int64_t cus = device_compute_units();
     const int64_t groups = (p.N + 15) / 16;
     int ngw = (int)(groups / (2 * cus));
-    if (ngw < 1) ngw = 1;
+    if (ngw < 1 || a.passes > 1) ngw = 1;
     if (ngw > kNG) ngw = kNG;
     a.ngw = ngw;
     a.n_sets = (int)((groups + ngw - 1) / ngw);
@@ -530,8 +610,9 @@ int launch_smallm(const Problem& p, hipStream_t s) {
     // vector scale / zero-point loads when a span's blocks are aligned
     // (scales [N][nb] and zero points [N][ceil(nb/2)] are element-aligned)
     const bool sv = p.nb % nsb == 0 && (nsb < 4 || p.zp_row % 2 == 0);
-    SmallFn f = p.bf16 ? (p.has_zp ? pick<true, true>(ng, nsb, sv) : pick<true, false>(ng, nsb, sv))
-                       : (p.has_zp ? pick<false, true>(ng, nsb, sv) : pick<false, false>(ng, nsb, sv));
+    const bool mp = a.passes > 1;
+    SmallFn f = p.bf16 ? (p.has_zp ? pick<true, true>(ng, nsb, sv, mp) : pick<true, false>(ng, nsb, sv, mp))
+                       : (p.has_zp ? pick<false, true>(ng, nsb, sv, mp) : pick<false, false>(ng, nsb, sv, mp));
     const size_t lds = (size_t)ps * span_bytes + (size_t)WV * ng * 64 * 16;
     int64_t blocks = cus * resident_per_cu(f, 64 * WV, lds);
     if (blocks > a.n_sets) blocks = a.n_sets;
