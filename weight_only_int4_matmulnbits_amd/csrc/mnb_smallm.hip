@@ -51,6 +51,7 @@ constexpr int kSpan = 128;                  // K values per span
 constexpr int kNG = 4;                      // column groups per set (at most)
 constexpr int kMaxWV = 8;                   // wavefronts per workgroup
 constexpr int kStageMax = 128 * 1024;       // LDS for staged activations
+static_assert(kStageMax / (256 * 16 * 2) >= kMaxWV, "a pass holds at least one span per wavefront");
 constexpr uint32_t kOob = 0x80000000u;      // offset past any resource: reads zero
 
 struct SmallArgs {
@@ -202,6 +203,14 @@ __device__ __forceinline__ void load_item(const SmallArgs& g, const Res& rr, con
     }
 }
 
+// bf16(a) in the low half and bf16(b) in the high half (round to nearest
+// even; exact here: the values are small integers).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 // 4 x 4 transpose of 32-bit words across the four 16-lane rows: afterwards
 // row r word t is what row t word r was.
 __device__ __forceinline__ void transpose_rows(u32x4& w) {
@@ -215,8 +224,9 @@ __device__ __forceinline__ void transpose_rows(u32x4& w) {
 // Activations in LDS: for the first mr rows of A (8 when M <= 8, else 16),
 // slice j (32 values) of a pass at hi[(j * 4 + g) * mr + row] (and lo): values
 // 8 g .. 8 g + 7 of the slice for that row, the A operand of MFMA lane
-// row + 16 g; rows past M and values past K are zeros (rows past mr are never
-// stored: their lanes read zeros).
+// row + 16 g; rows past M and values past K are zeros (rows past mr are not
+// staged: their lanes read row c mod mr, and their products land in output
+// rows that are never stored).
 
 // One piece (8 values of a row) as the bf16 head h and, for float32
 // activations, the bf16 tail t = bf16(a - h).
@@ -253,9 +263,10 @@ __device__ __forceinline__ void convert_piece(const u32x4 (&x)[BF16 ? 1 : 2], u3
 // i0 + q / P, piece j = (q % P) * 64 + l of that span's 16 mr in row order
 // (row j / 16, values 8 (j % 16) .. 8 (j % 16) + 7 of the span), so that 16
 // lanes read one row's span contiguously; P = mr / 4 pieces per lane and
-// span.  Only the pieces of the list are requested, up to U at a time (12
-// for the first pass; 4 for later passes, which are staged while both
-// register stages of weights are live).
+// span.  Only the pieces of the list are requested, up to U at a time (8 for
+// the first pass, which covers a pass of up to four spans per wavefront at 8
+// rows; 4 for later passes, staged while both register stages of weights are
+// live).
 template <bool BF16, int U>
 struct OwnRegs {
     u32x4 x[U][BF16 ? 1 : 2];
@@ -373,7 +384,7 @@ __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
     // waiting for its own LDS writes is enough.
     Item<NG, NSB> s0, s1;
     {
-        constexpr int U = 12;
+        constexpr int U = 8;
         const OwnList o = own_list(g, wave, WV, 0);
         OwnRegs<BF16, U> st;
         own_issue<BF16, U>(g, rr, wave, WV, lane, o, 0, st);
@@ -407,19 +418,15 @@ __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
         const int span = wave + i * WV;
         if (span < g.spans) {
             const int ls = (span - p.pass * g.pass_spans) * 4;     // its first slice in LDS
-            // lanes of rows past mr read a stored row and take zeros instead
+            // lanes of rows past mr read staged row c mod mr: MFMA output
+            // rows depend only on their own A rows, so those products land
+            // in rows >= mr, which are never stored
             const int pos = grp * mr + (c & (mr - 1));
-            const bool live = c < mr;
             bf16x8 ah[4], al[4];
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                const u32x4 zero4 = {0u, 0u, 0u, 0u};
-                const u32x4 xh = hi[(ls + t) * 4 * mr + pos];
-                ah[t] = __builtin_bit_cast(bf16x8, live ? xh : zero4);
-                if constexpr (!BF16) {
-                    const u32x4 xl = lo[(ls + t) * 4 * mr + pos];
-                    al[t] = __builtin_bit_cast(bf16x8, live ? xl : zero4);
-                }
+                ah[t] = __builtin_bit_cast(bf16x8, hi[(ls + t) * 4 * mr + pos]);
+                if constexpr (!BF16) al[t] = __builtin_bit_cast(bf16x8, lo[(ls + t) * 4 * mr + pos]);
             }
 #pragma unroll
             for (int u = 0; u < NG; u++) {
@@ -438,11 +445,13 @@ __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
                     }
                     const uint32_t lo4 = opaque_and(w[t], 0x0F0F0F0Fu);
                     const uint32_t hi4 = opaque_and(w[t] >> 4, 0x0F0F0F0Fu);
-                    bf16x8 bq;
-                    bq[0] = (__bf16)(ubyte_to_f32<0>(lo4) - zf); bq[1] = (__bf16)(ubyte_to_f32<0>(hi4) - zf);
-                    bq[2] = (__bf16)(ubyte_to_f32<1>(lo4) - zf); bq[3] = (__bf16)(ubyte_to_f32<1>(hi4) - zf);
-                    bq[4] = (__bf16)(ubyte_to_f32<2>(lo4) - zf); bq[5] = (__bf16)(ubyte_to_f32<2>(hi4) - zf);
-                    bq[6] = (__bf16)(ubyte_to_f32<3>(lo4) - zf); bq[7] = (__bf16)(ubyte_to_f32<3>(hi4) - zf);
+                    // values 2e and 2e + 1 (byte e, low then high nibble) as
+                    // one packed conversion each
+                    const bf16x8 bq = __builtin_bit_cast(
+                        bf16x8, u32x4{bf16_pair(ubyte_to_f32<0>(lo4) - zf, ubyte_to_f32<0>(hi4) - zf),
+                                      bf16_pair(ubyte_to_f32<1>(lo4) - zf, ubyte_to_f32<1>(hi4) - zf),
+                                      bf16_pair(ubyte_to_f32<2>(lo4) - zf, ubyte_to_f32<2>(hi4) - zf),
+                                      bf16_pair(ubyte_to_f32<3>(lo4) - zf, ubyte_to_f32<3>(hi4) - zf)});
                     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                     f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], bq, zero, 0, 0, 0);
                     if constexpr (!BF16) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[t], bq, d, 0, 0, 0);
