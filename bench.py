@@ -428,10 +428,11 @@ def measure_next_rows(steps, warmup, only=None):
     def want(name):
         return only is None or name in only
 
-    # f1: the 0.6B decode step with 4, 8 and 16 rows per projection
+    # f1: the 0.6B decode step with 4, 8 and 16 rows per projection, each
+    # also as a multiple of the same step at one row (measured here too)
     if want("small_m"):
         sm = {}
-        for M in (4, 8, 16):
+        for M in (1, 4, 8, 16):
             wm = workload(2, M=M)
             r = measure_step(wm, steps, warmup, 20)
             gbs = r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
@@ -439,6 +440,8 @@ def measure_next_rows(steps, warmup, only=None):
                            "ms_per_step": r["ms_per_step"], "p50_ms": r["samples"]["p50_ms"],
                            "launches": r["launches"], "weight_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                            "rows_per_s": M / (r["ms_per_step"] * 1e-3)}
+            if M > 1:
+                sm[f"M{M}"]["x_one_row"] = r["ms_per_step"] / sm["M1"]["ms_per_step"]
         out["small_m"] = sm
     # f2: LM head (tied weight, N = vocabulary) + greedy token, and the gather
     if want("lm_head_argmax"):
