@@ -9,14 +9,15 @@
 // Mapping on CDNA4.  One v_mfma_f32_16x16x32_bf16 multiplies 16 rows of A (rows
 // past M are zeros) by 32 K values of 16 columns (a "column group").  K is cut
 // into spans of 128 values (four MFMA slices of 32).  A workgroup of WV
-// wavefronts walks over "group sets" of up to four column groups; wavefront w
-// takes spans w, w + WV, ... of every column group of the set, so each weight
-// byte is read by exactly one wavefront.  Each wavefront stages the rows of A
-// for its own spans in LDS, already in the MFMA operand layout (float32
-// activations as a bf16 head and tail, a = hi + lo), once for as many spans
-// as fit (a "pass"; longer K is staged pass by pass, again for each set), so
-// one staged slice serves every column group it meets and no wavefront waits
-// for another's staging.
+// wavefronts walks over column groups (a "set" each); wavefront w takes spans
+// w, w + WV, ... of the group, so each weight byte is read by exactly one
+// wavefront.  Each wavefront stages the rows of A for its own spans in LDS,
+// already in the MFMA operand layout (float32 activations as a bf16 head and
+// tail, a = hi + lo), once for as many spans as fit (a "pass"; longer K is
+// staged pass by pass, again for each set), so one staged slice serves every
+// column group the workgroup takes and no wavefront waits for another's
+// staging.  (Sets of several column groups, sharing each staged slice within
+// an item, needed twice the registers, one workgroup per CU, and were slower.)
 // Weights stream through two register stages (the next item's loads are in
 // flight while one is multiplied).  For a span, lane l = c + 16 g reads the 16
 // packed bytes (32 values, K offset 32 g of the span) of column c; a 4 x 4
@@ -36,7 +37,6 @@
 // concatenated launches (fused QKV, gate||up) are bit-identical to separate
 // ones.  With one nonzero activation the result is float32((q - zp) * s)
 // exactly.  No atomics, no workspace.
-#include <type_traits>
 
 #include "mnb_internal.h"
 
@@ -48,7 +48,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSpan = 128;                  // K values per span
-constexpr int kNG = 4;                      // column groups per set (at most)
 constexpr int kMaxWV = 8;                   // wavefronts per workgroup
 constexpr int kStageMax = 128 * 1024;       // LDS for staged activations
 static_assert(kStageMax / (256 * 16 * 2) >= kMaxWV, "a pass holds at least one span per wavefront");
@@ -64,8 +63,7 @@ struct SmallArgs {
     int M, K, N;
     int col_bytes, nb, zp_row, log2_bs;
     int spans;              // ceil(K / 128)
-    int ngw;                // column groups per set (1 .. kNG)
-    int n_sets;             // ceil(ceil(N / 16) / ngw)
+    int n_sets;             // column groups: ceil(N / 16)
     int pass_spans;         // spans staged per pass, a multiple of WV
     int passes;             // ceil(spans / pass_spans)
     int ipw;                // items per wavefront per set: ceil(spans / WV)
@@ -78,13 +76,13 @@ struct SmallArgs {
 // larger), NZB zero-point bytes per span (two blocks per byte).  With SV the
 // NSB scales of a span are one aligned vector load and its zero-point bytes
 // one load (nb a multiple of NSB); otherwise one load each.
-template <int NG, int NSB>
+template <int NSB>
 struct Item {
     static constexpr int NZB = (NSB + 1) / 2;
-    u32x4 w[NG];             // 32 packed values per lane and group
-    uint32_t s[NG][NSB];     // scale bits
-    uint32_t z[NG][NZB];     // zero-point bytes
-    uint32_t bias;           // float32 bits of the bias of column c of group `wave`
+    u32x4 w;                 // 32 packed values per lane
+    uint32_t s[NSB];         // scale bits
+    uint32_t z[NZB];         // zero-point bytes
+    uint32_t bias;           // float32 bits of the bias of column c
 };
 
 struct Res {
@@ -115,13 +113,13 @@ __device__ __forceinline__ void advance(const SmallArgs& g, Pos& p) {
 }
 
 // The loads of the item at position p of this wavefront: set p.r of this
-// workgroup, span wave + p.i * WV, every column group of the set.  Items past
-// the last set or span, values past K and columns past N read zeros (offsets
-// forced past the resources), so every lane issues the same loads whatever
-// the shape.
-template <bool BF16, bool HAS_ZP, int NG, int NSB, bool SV>
+// workgroup (a column group), span wave + p.i * WV.  Items past the last
+// set or span, values past K and columns past N read zeros (offsets forced
+// past the resources), so every lane issues the same loads whatever the
+// shape.
+template <bool BF16, bool HAS_ZP, int NSB, bool SV>
 __device__ __forceinline__ void load_item(const SmallArgs& g, const Res& rr, const Pos& p, int wave, int WV, int lane,
-                                          Item<NG, NSB>& it) {
+                                          Item<NSB>& it) {
     constexpr int ESZ = BF16 ? 2 : 4;
     constexpr int SPB = 4 / NSB;                 // slices per scale block
     const int c = lane & 15, grp = lane >> 4;
@@ -129,17 +127,12 @@ __device__ __forceinline__ void load_item(const SmallArgs& g, const Res& rr, con
     const int set = (int)blockIdx.x + p.r * (int)gridDim.x;
     const uint32_t set_out = set < g.n_sets ? 0u : kOob;
     const uint32_t span_out = span < g.spans ? 0u : kOob;
+    const int col = set * 16 + c;
+    it.bias = __builtin_amdgcn_raw_buffer_load_b32(rr.bias, (uint32_t)col * 4u | set_out | (col < g.N ? 0u : kOob), 0, 0);
     {
-        const int col = (set * g.ngw + (wave < g.ngw ? wave : 0)) * 16 + c;
-        it.bias = __builtin_amdgcn_raw_buffer_load_b32(rr.bias, (uint32_t)col * 4u | set_out | (col < g.N ? 0u : kOob),
-                                                       0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < NG; u++) {
-        const int col = (set * g.ngw + u) * 16 + c;
-        const uint32_t o = ((u < g.ngw && col < g.N) ? set_out : kOob) | span_out;
+        const uint32_t o = (col < g.N ? set_out : kOob) | span_out;
         const uint32_t kw = (span * kSpan + 32 * grp < g.K) ? 0u : kOob;
-        it.w[u] = __builtin_amdgcn_raw_buffer_load_b128(
+        it.w = __builtin_amdgcn_raw_buffer_load_b128(
             rr.b, ((uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)(span * 64 + 16 * grp)) | o | kw, 0, 0);
         if constexpr (SV) {
             // the span's NSB consecutive scales and NZB consecutive zero-point
@@ -150,35 +143,35 @@ __device__ __forceinline__ void load_item(const SmallArgs& g, const Res& rr, con
             if constexpr (NSB * ESZ == 16) {
                 const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rr.s, os, 0, 0);
 #pragma unroll
-                for (int b = 0; b < 4; b++) it.s[u][b] = v[b];
+                for (int b = 0; b < 4; b++) it.s[b] = v[b];
             } else if constexpr (NSB * ESZ == 8) {
                 const uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rr.s, os, 0, 0));
                 if constexpr (BF16) {
 #pragma unroll
-                    for (int b = 0; b < 4; b++) it.s[u][b] = (uint32_t)(v >> (16 * b)) & 0xFFFFu;
+                    for (int b = 0; b < 4; b++) it.s[b] = (uint32_t)(v >> (16 * b)) & 0xFFFFu;
                 } else {
-                    it.s[u][0] = (uint32_t)v;
-                    it.s[u][1] = (uint32_t)(v >> 32);
+                    it.s[0] = (uint32_t)v;
+                    it.s[1] = (uint32_t)(v >> 32);
                 }
             } else if constexpr (NSB * ESZ == 4) {
                 const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rr.s, os, 0, 0);
                 if constexpr (BF16 && NSB == 2) {
-                    it.s[u][0] = v & 0xFFFFu;
-                    it.s[u][1] = v >> 16;
+                    it.s[0] = v & 0xFFFFu;
+                    it.s[1] = v >> 16;
                 } else {
-                    it.s[u][0] = v;
+                    it.s[0] = v;
                 }
             } else {
-                it.s[u][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rr.s, os, 0, 0);
+                it.s[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rr.s, os, 0, 0);
             }
             if constexpr (HAS_ZP) {
                 const uint32_t oz = ((uint32_t)col * (uint32_t)g.zp_row + (blk >> 1)) | o | (k0 < g.K ? 0u : kOob);
-                if constexpr (Item<NG, NSB>::NZB == 2) {
+                if constexpr (Item<NSB>::NZB == 2) {
                     const uint32_t v = __builtin_amdgcn_raw_buffer_load_b16(rr.z, oz, 0, 0);
-                    it.z[u][0] = v & 0xFFu;
-                    it.z[u][1] = v >> 8;
+                    it.z[0] = v & 0xFFu;
+                    it.z[1] = v >> 8;
                 } else {
-                    it.z[u][0] = __builtin_amdgcn_raw_buffer_load_b8(rr.z, oz, 0, 0);
+                    it.z[0] = __builtin_amdgcn_raw_buffer_load_b8(rr.z, oz, 0, 0);
                 }
             }
         } else {
@@ -187,15 +180,15 @@ __device__ __forceinline__ void load_item(const SmallArgs& g, const Res& rr, con
                 const int k0 = span * kSpan + 32 * SPB * b;
                 const uint32_t blk = (uint32_t)k0 >> g.log2_bs;
                 const uint32_t os = (((uint32_t)col * (uint32_t)g.nb + blk) * ESZ) | o | (k0 < g.K ? 0u : kOob);
-                it.s[u][b] = BF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rr.s, os, 0, 0)
+                it.s[b] = BF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rr.s, os, 0, 0)
                                   : __builtin_amdgcn_raw_buffer_load_b32(rr.s, os, 0, 0);
             }
             if constexpr (HAS_ZP) {
 #pragma unroll
-                for (int b = 0; b < Item<NG, NSB>::NZB; b++) {
+                for (int b = 0; b < Item<NSB>::NZB; b++) {
                     const int k0 = span * kSpan + 64 * SPB * b;
                     const uint32_t blk = (uint32_t)k0 >> g.log2_bs;
-                    it.z[u][b] = __builtin_amdgcn_raw_buffer_load_b8(
+                    it.z[b] = __builtin_amdgcn_raw_buffer_load_b8(
                         rr.z, ((uint32_t)col * (uint32_t)g.zp_row + (blk >> 1)) | o | (k0 < g.K ? 0u : kOob), 0, 0);
                 }
             }
@@ -345,7 +338,7 @@ __device__ __forceinline__ void own_stage(const SmallArgs& g, const Res& rr, int
 
 // MP: K takes several passes (a separate instance, so that the single-pass
 // loop carries no staging code: its register use and waits stay lean).
-template <bool BF16, bool HAS_ZP, int NG, int NSB, bool SV, bool MP>
+template <bool BF16, bool HAS_ZP, int NSB, bool SV, bool MP>
 __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
     extern __shared__ __attribute__((aligned(16))) u32x4 lds[];
     const int WV = blockDim.x >> 6;
@@ -356,7 +349,7 @@ __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
     const int pieces = (g.pass_spans * 16) << g.log2_mr;    // staged 16-byte pieces per term
     u32x4* hi = lds;
     u32x4* lo = lds + pieces;
-    f32x4* red = reinterpret_cast<f32x4*>(lds + pieces * (BF16 ? 1 : 2));   // [WV][NG][64]
+    f32x4* red = reinterpret_cast<f32x4*>(lds + pieces * (BF16 ? 1 : 2));   // [WV][64]
 
     Res rr;
     rr.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.a), (short)0, (int)g.a_bytes, 0x00020000);
@@ -382,27 +375,25 @@ __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
     // second item's weights follow (both at once could exceed the 63 loads
     // the wait counter tracks).  A wavefront reads only what it wrote, so
     // waiting for its own LDS writes is enough.
-    Item<NG, NSB> s0, s1;
+    Item<NSB> s0, s1;
     {
         constexpr int U = 8;
         const OwnList o = own_list(g, wave, WV, 0);
         OwnRegs<BF16, U> st;
         own_issue<BF16, U>(g, rr, wave, WV, lane, o, 0, st);
-        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, pl, wave, WV, lane, s0);
+        load_item<BF16, HAS_ZP, NSB, SV>(g, rr, pl, wave, WV, lane, s0);
         advance(g, pl);
         own_finish<BF16, U>(g, wave, WV, lane, o, 0, st, hi, lo);
         own_stage<BF16, U>(g, rr, wave, WV, lane, o, U, hi, lo);
-        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, pl, wave, WV, lane, s1);
+        load_item<BF16, HAS_ZP, NSB, SV>(g, rr, pl, wave, WV, lane, s1);
         advance(g, pl);
         __builtin_amdgcn_s_waitcnt(0xC07F);
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    f32x4 acc[NG];
-#pragma unroll
-    for (int u = 0; u < NG; u++) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](const Item<NG, NSB>& it, const Pos& p, int) {
+    auto step = [&](const Item<NSB>& it, const Pos& p) {
         const int r = p.r;
         const int i = p.i;
         // the first item of a later pass (or the first pass of a later set):
@@ -428,64 +419,57 @@ __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
                 ah[t] = __builtin_bit_cast(bf16x8, hi[(ls + t) * 4 * mr + pos]);
                 if constexpr (!BF16) al[t] = __builtin_bit_cast(bf16x8, lo[(ls + t) * 4 * mr + pos]);
             }
+            u32x4 w = it.w;
+            transpose_rows(w);
 #pragma unroll
-            for (int u = 0; u < NG; u++) {
-                if (u >= g.ngw) break;
-                u32x4 w = it.w[u];
-                transpose_rows(w);
-#pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    constexpr int SPB = 4 / NSB;
-                    const int b = t / SPB;
-                    float zf = 8.f;
-                    if constexpr (HAS_ZP) {
-                        const uint32_t blk = (uint32_t)(span * kSpan + 32 * t) >> g.log2_bs;
-                        constexpr int NZB = Item<NG, NSB>::NZB;
-                        zf = (float)__builtin_amdgcn_ubfe(it.z[u][b / 2 < NZB ? b / 2 : 0], 4u * (blk & 1u), 4);
-                    }
-                    const uint32_t lo4 = opaque_and(w[t], 0x0F0F0F0Fu);
-                    const uint32_t hi4 = opaque_and(w[t] >> 4, 0x0F0F0F0Fu);
-                    // values 2e and 2e + 1 (byte e, low then high nibble) as
-                    // one packed conversion each
-                    const bf16x8 bq = __builtin_bit_cast(
-                        bf16x8, u32x4{bf16_pair(ubyte_to_f32<0>(lo4) - zf, ubyte_to_f32<0>(hi4) - zf),
-                                      bf16_pair(ubyte_to_f32<1>(lo4) - zf, ubyte_to_f32<1>(hi4) - zf),
-                                      bf16_pair(ubyte_to_f32<2>(lo4) - zf, ubyte_to_f32<2>(hi4) - zf),
-                                      bf16_pair(ubyte_to_f32<3>(lo4) - zf, ubyte_to_f32<3>(hi4) - zf)});
-                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                    f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], bq, zero, 0, 0, 0);
-                    if constexpr (!BF16) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[t], bq, d, 0, 0, 0);
-                    const float sc = BF16 ? __uint_as_float(it.s[u][b] << 16) : __uint_as_float(it.s[u][b]);
-#pragma unroll
-                    for (int e = 0; e < 4; e++) acc[u][e] = fmaf(sc, d[e], acc[u][e]);
+            for (int t = 0; t < 4; t++) {
+                constexpr int SPB = 4 / NSB;
+                const int b = t / SPB;
+                float zf = 8.f;
+                if constexpr (HAS_ZP) {
+                    const uint32_t blk = (uint32_t)(span * kSpan + 32 * t) >> g.log2_bs;
+                    constexpr int NZB = Item<NSB>::NZB;
+                    zf = (float)__builtin_amdgcn_ubfe(it.z[b / 2 < NZB ? b / 2 : 0], 4u * (blk & 1u), 4);
                 }
+                const uint32_t lo4 = opaque_and(w[t], 0x0F0F0F0Fu);
+                const uint32_t hi4 = opaque_and(w[t] >> 4, 0x0F0F0F0Fu);
+                // values 2e and 2e + 1 (byte e, low then high nibble) as one
+                // packed conversion each
+                const bf16x8 bq = __builtin_bit_cast(
+                    bf16x8, u32x4{bf16_pair(ubyte_to_f32<0>(lo4) - zf, ubyte_to_f32<0>(hi4) - zf),
+                                  bf16_pair(ubyte_to_f32<1>(lo4) - zf, ubyte_to_f32<1>(hi4) - zf),
+                                  bf16_pair(ubyte_to_f32<2>(lo4) - zf, ubyte_to_f32<2>(hi4) - zf),
+                                  bf16_pair(ubyte_to_f32<3>(lo4) - zf, ubyte_to_f32<3>(hi4) - zf)});
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], bq, zero, 0, 0, 0);
+                if constexpr (!BF16) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[t], bq, d, 0, 0, 0);
+                const float sc = BF16 ? __uint_as_float(it.s[b] << 16) : __uint_as_float(it.s[b]);
+#pragma unroll
+                for (int e = 0; e < 4; e++) acc[e] = fmaf(sc, d[e], acc[e]);
             }
         }
         // the end of a set: the wavefronts' sums meet in LDS (in wavefront
-        // order) and wavefront u stores group u; the first barrier keeps the
+        // order) and wavefront 0 stores them; the first barrier keeps the
         // buffer from being rewritten while the previous set is read
         if (i == g.ipw - 1) {
             asm volatile("s_barrier" : : : "memory");
-#pragma unroll
-            for (int u = 0; u < NG; u++) {
-                red[(wave * NG + u) * 64 + lane] = acc[u];
-                acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            red[wave * 64 + lane] = acc;
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
             __builtin_amdgcn_s_waitcnt(0xC07F);
             asm volatile("s_barrier" : : : "memory");
-            if (wave < g.ngw) {
-                f32x4 v = red[wave * 64 + lane];
+            if (wave == 0) {
+                f32x4 v = red[lane];
                 // unrolled to the largest workgroup, the missing wavefronts
                 // adding +0 (x + 0 == x): a loop would cost precise waits for
                 // the weights in flight
 #pragma unroll
                 for (int w2 = 1; w2 < kMaxWV; w2++) {
-                    const f32x4 x = red[((w2 < WV ? w2 : 0) * NG + wave) * 64 + lane];
+                    const f32x4 x = red[(w2 < WV ? w2 : 0) * 64 + lane];
                     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                     v += w2 < WV ? x : zero;
                 }
                 const int set = (int)blockIdx.x + r * (int)gridDim.x;
-                const int col = (set * g.ngw + wave) * 16 + c;
+                const int col = set * 16 + c;
                 const float bv = __uint_as_float(it.bias);
                 if (col < g.N) {
 #pragma unroll
@@ -505,14 +489,14 @@ __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
 
     // f is workgroup-uniform, so every wavefront reaches every barrier
     for (int f = 0; f < total; f += 2) {
-        step(s0, ps, 0);
+        step(s0, ps);
         advance(g, ps);
-        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, pl, wave, WV, lane, s0);
+        load_item<BF16, HAS_ZP, NSB, SV>(g, rr, pl, wave, WV, lane, s0);
         advance(g, pl);
         __builtin_amdgcn_sched_barrier(0);
-        if (f + 1 < total) step(s1, ps, 0);
+        if (f + 1 < total) step(s1, ps);
         advance(g, ps);
-        load_item<BF16, HAS_ZP, NG, NSB, SV>(g, rr, pl, wave, WV, lane, s1);
+        load_item<BF16, HAS_ZP, NSB, SV>(g, rr, pl, wave, WV, lane, s1);
         advance(g, pl);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -520,22 +504,19 @@ __global__ __launch_bounds__(64 * kMaxWV) void smallm_kernel(SmallArgs g) {
 
 using SmallFn = void (*)(SmallArgs);
 
-template <bool BF16, bool HAS_ZP, int NG, bool SV, bool MP>
-SmallFn pick_ng(int nsb) {
+template <bool BF16, bool HAS_ZP, bool SV, bool MP>
+SmallFn pick_nsb(int nsb) {
     switch (nsb) {
-        case 4: return smallm_kernel<BF16, HAS_ZP, NG, 4, SV, MP>;
-        case 2: return smallm_kernel<BF16, HAS_ZP, NG, 2, SV, MP>;
-        default: return smallm_kernel<BF16, HAS_ZP, NG, 1, SV, MP>;
+        case 4: return smallm_kernel<BF16, HAS_ZP, 4, SV, MP>;
+        case 2: return smallm_kernel<BF16, HAS_ZP, 2, SV, MP>;
+        default: return smallm_kernel<BF16, HAS_ZP, 1, SV, MP>;
     }
 }
 
-// Several passes take one column group per set (ng == 1).
 template <bool BF16, bool HAS_ZP>
-SmallFn pick(int ng, int nsb, bool sv, bool mp) {
-    if (mp) return sv ? pick_ng<BF16, HAS_ZP, 1, true, true>(nsb) : pick_ng<BF16, HAS_ZP, 1, false, true>(nsb);
-    if (sv)
-        return ng == 1 ? pick_ng<BF16, HAS_ZP, 1, true, false>(nsb) : pick_ng<BF16, HAS_ZP, kNG, true, false>(nsb);
-    return ng == 1 ? pick_ng<BF16, HAS_ZP, 1, false, false>(nsb) : pick_ng<BF16, HAS_ZP, kNG, false, false>(nsb);
+SmallFn pick(int nsb, bool sv, bool mp) {
+    if (mp) return sv ? pick_nsb<BF16, HAS_ZP, true, true>(nsb) : pick_nsb<BF16, HAS_ZP, false, true>(nsb);
+    return sv ? pick_nsb<BF16, HAS_ZP, true, false>(nsb) : pick_nsb<BF16, HAS_ZP, false, false>(nsb);
 }
 
 int ilog2(int v) {
@@ -604,25 +585,18 @@ int launch_smallm(const Problem& p, hipStream_t s) {
     a.passes = (a.spans + ps - 1) / ps;
     a.ipw = (a.spans + WV - 1) / WV;
     a.ipp = ps / WV;
-    // column groups per set: up to four once there are enough groups to give
-    // every CU two sets (one with several passes); the grid only decides
-    // which workgroup takes a set
+    // one set per column group; the grid only decides which workgroup takes a
+    // set
     const int64_t cus = device_compute_units();
-    const int64_t groups = (p.N + 15) / 16;
-    int ngw = (int)(groups / (2 * cus));
-    if (ngw < 1 || a.passes > 1) ngw = 1;
-    if (ngw > kNG) ngw = kNG;
-    a.ngw = ngw;
-    a.n_sets = (int)((groups + ngw - 1) / ngw);
+    a.n_sets = (int)((p.N + 15) / 16);
     const int nsb = p.bs >= 128 ? 1 : p.bs == 64 ? 2 : 4;
-    const int ng = ngw == 1 ? 1 : kNG;
     // vector scale / zero-point loads when a span's blocks are aligned
     // (scales [N][nb] and zero points [N][ceil(nb/2)] are element-aligned)
     const bool sv = p.nb % nsb == 0 && (nsb < 4 || p.zp_row % 2 == 0);
     const bool mp = a.passes > 1;
-    SmallFn f = p.bf16 ? (p.has_zp ? pick<true, true>(ng, nsb, sv, mp) : pick<true, false>(ng, nsb, sv, mp))
-                       : (p.has_zp ? pick<false, true>(ng, nsb, sv, mp) : pick<false, false>(ng, nsb, sv, mp));
-    const size_t lds = (size_t)ps * span_bytes + (size_t)WV * ng * 64 * 16;
+    SmallFn f = p.bf16 ? (p.has_zp ? pick<true, true>(nsb, sv, mp) : pick<true, false>(nsb, sv, mp))
+                       : (p.has_zp ? pick<false, true>(nsb, sv, mp) : pick<false, false>(nsb, sv, mp));
+    const size_t lds = (size_t)ps * span_bytes + (size_t)WV * 64 * 16;
     int64_t blocks = cus * resident_per_cu(f, 64 * WV, lds);
     if (blocks > a.n_sets) blocks = a.n_sets;
     hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(64 * WV), lds, s, a);
