@@ -587,15 +587,15 @@ def _short(name):
     return name.replace("void ", "")
 
 
-def summarize_trace(trace_dir, cfg, steps, warmup, samples=MIN_SAMPLES, bench_json=None):
+def summarize_trace(trace_dir, cfg, steps, warmup, samples=MIN_SAMPLES, bench_json=None, rows=None):
     """Per-kernel statistics and the timed graph-replayed steps of one
     `bench.py --config cfg --steps steps --warmup warmup --samples samples
-    --no-extra` run under `rocprofv3 --kernel-trace --stats`; with the JSON
-    line that run printed, the tracer's overhead against its untraced
-    event-timed step."""
+    --no-extra` run under `rocprofv3 --kernel-trace --stats` (with `--rows
+    rows` when given); with the JSON line that run printed, the tracer's
+    overhead against its untraced event-timed step."""
     from workloads import workload
     import statistics
-    w = workload(cfg)
+    w = workload(cfg, M=rows) if rows else workload(cfg)
     n = len(w.launches)
     rows = _library_rows(_read_csv(os.path.join(trace_dir, "run_kernel_trace.csv")))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
@@ -654,13 +654,14 @@ def summarize_trace(trace_dir, cfg, steps, warmup, samples=MIN_SAMPLES, bench_js
                 while i < len(st) and "reduce" in st[i]["Kernel_Name"]:
                     red += int(st[i]["End_Timestamp"]) - int(st[i]["Start_Timestamp"])
                     i += 1
-                per.setdefault(nm, []).append((g, red, 2 * w.M * L.K * L.N))
+                per.setdefault(nm, []).append((g, red, 2 * w.M * L.K * L.N, w.weight_bytes(L)))
         for nm in kinds:
             v = per[nm]
             g = statistics.median(x[0] for x in v) / 1e3
             r = statistics.median(x[1] for x in v) / 1e3
-            fl = v[0][2]
-            out.append(f"  {nm:<8} GEMM {g:9.1f} us ({fl / (g * 1e-6) / 1e12:7.1f} TFLOP/s)  reduction {r:6.1f} us")
+            fl, wb = v[0][2], v[0][3]
+            out.append(f"  {nm:<8} GEMM {g:9.2f} us ({fl / (g * 1e-6) / 1e12:7.1f} TFLOP/s, weights "
+                       f"{wb / (g * 1e-6) / 1e9:7.1f} GB/s)  reduction {r:6.1f} us")
         out.append(f"average launch (GEMM + reduction) {s_sum / 1e3 / n:.3f} us over {n} launches per step")
     if bench_json:
         with open(bench_json) as f:
@@ -804,6 +805,9 @@ def main():
                     help="run only these rows of extra.next_rows (small_m, lm_head_argmax, "
                          "qdq_import, gate_up_silu, rmsnorm_gemv, gate_up_silu_prefill), print "
                          "them as one JSON line and exit (for profiling one row)")
+    ap.add_argument("--rows", type=int, metavar="M",
+                    help="profiling: the config's step with M rows per projection (implies --no-extra "
+                         "and --no-cpu-baseline; also for --summarize-trace)")
     ap.add_argument("--no-persistent", action="store_true",
                     help="decode configs: do not time the step as one persistent launch (profiling "
                          "runs: rocprofv3 can end with a segmentation fault after cooperative launches)")
@@ -817,9 +821,11 @@ def main():
                          "runs of this bench (same --config, --copy-calibration), update "
                          "profiles/traffic.json and exit; no GPU is used")
     args = ap.parse_args()
+    if args.rows:
+        args.no_extra = args.no_cpu_baseline = True
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.config, args.steps, args.warmup, args.samples,
-                              args.bench_json))
+                              args.bench_json, args.rows))
         return
     if args.counters_from:
         print(counters_from(args.counters_from))
@@ -862,7 +868,7 @@ def main():
         print(json.dumps(rows), flush=True)
         return
 
-    w = workload(args.config)
+    w = workload(args.config, M=args.rows) if args.rows else workload(args.config)
     r = measure_step(w, args.steps, args.warmup, args.samples, persistent=not args.no_persistent)
     dec = w.M == 1
     value = (r["weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 if dec
