@@ -4,8 +4,9 @@ library's sequence driver on one stream), checked against the oracle on
 sampled outputs: all columns of the single GEMV; for the decode steps the
 first, last and 30 random columns of every launch; for the prefill steps the
 first, last and 6 random rows times the first, last and 14 random columns of
-every launch; for the 0.6B step with 4 rows per projection (the bench's
-small-M row) all rows times the first, last and 30 random columns.  A
+every launch; for the 0.6B step with 4, 8 and 16 rows per projection (the
+bench's small-M rows: the 2-4-row GEMV, then the matrix-core small-M
+kernel) all rows times the first, last and 30 random columns.  A
 captured-graph replay must reproduce the eager step bit for bit, and so must
 the decode steps' persistent launch.
 """
@@ -26,21 +27,24 @@ def _sample(n, k, rng):
     return sorted({0, n - 1, *map(int, extra)})
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, "2m4"])
+SMALL_M_STEPS = {"2m4": 4, "2m8": 8, "2m16": 16}     # the 0.6B step at M rows
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, *SMALL_M_STEPS])
 def test_config_step_parity(orc, cfg):
-    w = workload(2, M=4) if cfg == "2m4" else workload(cfg)
+    w = workload(2, M=SMALL_M_STEPS[cfg]) if cfg in SMALL_M_STEPS else workload(cfg)
     log(f"config {cfg}: building {w.title} ({len(w.launches)} launches)")
     step = Step(w, "cuda", seed=0)
     step.run()
     torch.cuda.synchronize()
-    rng = np.random.default_rng(24 if cfg == "2m4" else cfg)
+    rng = np.random.default_rng(20 + SMALL_M_STEPS[cfg] if cfg in SMALL_M_STEPS else cfg)
     worst = 0.0
     for i, (pw, a, y) in enumerate(step.items):
         inp = step.logical_inputs(i)
         N = inp.N
         if cfg == 1:
             rows, cols = None, None
-        elif w.M <= 4:
+        elif w.M <= 16:
             rows, cols = None, _sample(N, 30, rng)
         else:
             rows, cols = _sample(w.M, 6, rng), _sample(N, 14, rng)
@@ -54,7 +58,7 @@ def test_config_step_parity(orc, cfg):
                                         f"config {cfg} launch {w.launches[i].name}"))
         del inp
     log(f"config {cfg}: worst err/tol {worst:.3g}")
-    if cfg in (2, 4, "2m4"):
+    if cfg in (2, 4, *SMALL_M_STEPS):
         eager = [y.clone() for _, _, y in step.items]
         for _, _, y in step.items:
             y.fill_(float("nan"))
