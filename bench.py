@@ -16,7 +16,10 @@ max and the raw samples.  The same protocol times the other workloads in
 ``extra``: the Qwen3-4B prefill step (2048 bf16 rows, the MFMA bar) with its
 own roofline block, the Qwen3-0.6B decode and prefill steps, the single
 1024->3072 GEMV cold (rotating over 512 copies, 1 GB) and hot, the plain
-streaming read of 1 GB (achievable HBM, the control arm), and ``next_rows``:
+streaming read of 1 GB (achievable HBM, the control arm), each distinct
+projection of the headline step alone, cold, beside a plain read of its bytes
+(``decode_projections``: the per-launch floor of moving those bytes), and
+``next_rows``:
 small M (4, 8, 16 rows), the tied LM head with greedy ArgMax and the
 embedding gather, the QDQ import, and the fused gate||up SiLU GEMV against the
 unfused pair.
@@ -382,6 +385,75 @@ def measure_config1(steps, warmup, copies=512):
     out["hbm_frac_cold"] = out["cold"]["GBps"] / HBM_PEAK_GBS
     del cold, pw
     torch.cuda.empty_cache()
+    return out
+
+
+def measure_decode_projections(steps, warmup, cfg=4, min_bytes=600 << 20):
+    """Each distinct projection of a decode step alone, cold: a graph of
+    back-to-back decode GEMV launches, each on its own copy of the weights
+    (together more than the last-level cache), and beside it a graph of plain
+    16-byte streaming reads of the same number of bytes from the same number
+    of distinct buffers (libmnb_probe).  The read is the floor of a launch
+    that only moves the projection's bytes; the GEMV's excess over it is what
+    the unpacking, the dot products, the reductions and the stores add."""
+    import ctypes
+    import math
+    import torch
+    import weight_only_int4_matmulnbits_amd as mnb
+    from workloads import workload
+    from workloads.generate import projection_inputs
+
+    L = probe_lib()
+    w = workload(cfg)
+    first = {}
+    for i, launch in enumerate(w.launches):
+        first.setdefault(launch.name.split(".")[-1], i)
+    out = {"workload": f"{w.title}: each distinct projection alone, cold (one graph of launches on "
+                       f"distinct copies, at least {min_bytes >> 20} MiB in all)"}
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    for kind, i in first.items():
+        inp = projection_inputs(w, i, 0, "cuda")
+        pw = mnb.PackedWeight.from_logical(inp.q, inp.scales, inp.zp, inp.bias, block_size=w.block_size)
+        nbytes = pw.weight_bytes
+        copies = max(3, math.ceil(min_bytes / nbytes))
+        ws = [pw] + [mnb.PackedWeight(pw.K, pw.N, pw.block_size, pw.act_dtype, pw.b_packed.clone(),
+                                      pw.scales.clone(), None if pw.zp_packed is None else pw.zp_packed.clone(),
+                                      pw.bias) for _ in range(copies - 1)]
+        y = torch.empty(1, pw.N, dtype=inp.a.dtype, device="cuda")
+        seq = mnb.Sequence([(x, inp.a, y) for x in ws])
+        seq.capture()
+        ms_g, _, raw_g = time_runs(seq.replay, max(3, steps // 10), max(2, warmup // 2), 10)
+        seq.close()
+        del seq, ws, y
+        torch.cuda.empty_cache()
+        # the same bytes read by the probe, each launch from its own buffer
+        rb = (nbytes + 255) // 256 * 256
+        buf = torch.ones(copies * rb // 4, dtype=torch.float32, device="cuda")
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cs):
+            h = ctypes.c_void_p(cs.cuda_stream)
+            for c in range(copies):
+                rc = L.mnb_probe_stream_read(ctypes.c_void_p(buf.data_ptr() + c * rb), nbytes // 16 * 16,
+                                             ctypes.c_void_p(sink.data_ptr()), h)
+                if rc != 0:
+                    raise RuntimeError(f"probe read failed: {rc}")
+        ms_r, _, raw_r = time_runs(g.replay, max(3, steps // 10), max(2, warmup // 2), 10)
+        del g, buf
+        torch.cuda.empty_cache()
+        gemv_us, read_us = ms_g * 1e3 / copies, ms_r * 1e3 / copies
+        out[kind] = {"K": pw.K, "N": pw.N, "weight_bytes": nbytes, "copies": copies,
+                     "gemv_us": gemv_us, "gemv_GBps": nbytes / (gemv_us * 1e-6) / 1e9,
+                     "gemv_p50_us": statistics.median(raw_g) * 1e3 / copies,
+                     "read_us": read_us, "read_GBps": (nbytes // 16 * 16) / (read_us * 1e-6) / 1e9,
+                     "read_p50_us": statistics.median(raw_r) * 1e3 / copies,
+                     "gemv_over_read": gemv_us / read_us}
+        log(f"[bench] {kind}: gemv {gemv_us:.2f} us vs read {read_us:.2f} us ({nbytes / 1e6:.2f} MB)")
+        del pw, inp
+        torch.cuda.empty_cache()
+    del sink
     return out
 
 
@@ -805,6 +877,9 @@ def main():
                     help="run only these rows of extra.next_rows (small_m, lm_head_argmax, "
                          "qdq_import, gate_up_silu, rmsnorm_gemv, gate_up_silu_prefill), print "
                          "them as one JSON line and exit (for profiling one row)")
+    ap.add_argument("--decode-projections", action="store_true",
+                    help="decode configs: each distinct projection alone, cold, beside a plain read "
+                         "of its bytes (extra.decode_projections); print it as one JSON line and exit")
     ap.add_argument("--rows", type=int, metavar="M",
                     help="profiling: the config's step with M rows per projection (implies --no-extra "
                          "and --no-cpu-baseline; also for --summarize-trace)")
@@ -863,6 +938,10 @@ def main():
         print(trace_persistent(args.config), flush=True)
         return
 
+    if args.decode_projections:
+        print(json.dumps(measure_decode_projections(args.steps, args.warmup, args.config)), flush=True)
+        return
+
     if args.next_rows:
         rows = measure_next_rows(max(10, args.steps // 3), max(2, args.warmup // 2), only=set(args.next_rows))
         print(json.dumps(rows), flush=True)
@@ -914,6 +993,9 @@ def main():
         log("[bench] config 1 (cold and hot), the 1 GiB streaming-read control arm")
         extra["config1"] = measure_config1(args.steps, args.warmup)
         extra["control_read"] = measure_control_read(args.steps, args.warmup)
+        if dec:
+            log("[bench] decode projections alone, cold, beside plain reads of their bytes")
+            extra["decode_projections"] = measure_decode_projections(args.steps, args.warmup, args.config)
         ach = extra["control_read"]["GBps"]
         line["roofline"]["achievable_GBps_control"] = ach if dec else None
         if dec:
