@@ -14,6 +14,7 @@ namespace {
 constexpr int kJMax = 5;          // chunks per lane held in registers
 constexpr int kWMax = 4;          // wavefronts per column (split-K)
 constexpr uint32_t kOob = 0x80000000u;    // buffer offset past any resource: the load reads zero
+constexpr int kNonTemporal = 2;           // cache policy of a load whose bytes are read once (nt)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

@@ -19,7 +19,8 @@
 // staging.  (Sets of several column groups, sharing each staged slice within
 // an item, needed twice the registers, one workgroup per CU, and were slower.)
 // Weights stream through two register stages (the next item's loads are in
-// flight while one is multiplied).  For a span, lane l = c + 16 g reads the 16
+// flight while one is multiplied), read non-temporally: each byte is read
+// once, and streamed past the caches it leaves A resident.  For a span, lane l = c + 16 g reads the 16
 // packed bytes (32 values, K offset 32 g of the span) of column c; a 4 x 4
 // word transpose across the four 16-lane rows (v_permlane32_swap,
 // v_permlane16_swap) gives lane (c, g) word t = values 32 t + 8 g ..
@@ -52,6 +53,7 @@ constexpr int kMaxWV = 8;                   // wavefronts per workgroup
 constexpr int kStageMax = 128 * 1024;       // LDS for staged activations
 static_assert(kStageMax / (256 * 16 * 2) >= kMaxWV, "a pass holds at least one span per wavefront");
 constexpr uint32_t kOob = 0x80000000u;      // offset past any resource: reads zero
+constexpr int kNonTemporal = 2;             // cache policy of the weight loads: each byte is read once
 
 struct SmallArgs {
     const void* a;
@@ -133,7 +135,7 @@ __device__ __forceinline__ void load_item(const SmallArgs& g, const Res& rr, con
         const uint32_t o = (col < g.N ? set_out : kOob) | span_out;
         const uint32_t kw = (span * kSpan + 32 * grp < g.K) ? 0u : kOob;
         it.w = __builtin_amdgcn_raw_buffer_load_b128(
-            rr.b, ((uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)(span * 64 + 16 * grp)) | o | kw, 0, 0);
+            rr.b, ((uint32_t)col * (uint32_t)g.col_bytes + (uint32_t)(span * 64 + 16 * grp)) | o | kw, 0, kNonTemporal);
         if constexpr (SV) {
             // the span's NSB consecutive scales and NZB consecutive zero-point
             // bytes, each as one load (aligned: nb is a multiple of NSB)

@@ -185,7 +185,8 @@ __device__ __forceinline__ void request(const StepArgs& s, const Cursor& c, int 
     for (int j = 0; j < kJMax; j++) {
         const int ch = p + j * L;
         const uint32_t out = (j < o.J && ch < o.S) ? 0u : kOob;
-        r.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)(gsub * o.col_bytes + ch * 16) | out, 0, 0);
+        r.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)(gsub * o.col_bytes + ch * 16) | out, 0,
+                                                       kNonTemporal);
     }
 }
 
