@@ -784,6 +784,9 @@ def traffic_from(fetch_dir, write_dir, cfg, copy_mib, kind="gemv"):
     except (OSError, ValueError):
         rec = {}
     srcs = {"gemv": ["weight_only_int4_matmulnbits_amd/csrc/mnb_gemv.hip",
+                     "weight_only_int4_matmulnbits_amd/csrc/mnb_gemv_kernel.h",
+                     "weight_only_int4_matmulnbits_amd/csrc/mnb_gemv_f32.hip",
+                     "weight_only_int4_matmulnbits_amd/csrc/mnb_gemv_bf16.hip",
                      "weight_only_int4_matmulnbits_amd/csrc/mnb_gemv_core.h",
                      "weight_only_int4_matmulnbits_amd/csrc/mnb_internal.h"],
             "gemm": ["weight_only_int4_matmulnbits_amd/csrc/mnb_gemm.hip",

@@ -25,8 +25,10 @@ PROBE_SOURCE = "mnb_probe.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["mnb_api.hip", "mnb_pack.hip", "mnb_gemv.hip", "mnb_gemm.hip", "mnb_smallm.hip", "mnb_aux.hip",
-           "mnb_step.hip"]
+# the longest compiles first (the GEMV instances of each activation type and
+# the prefill GEMM), so that they start at once
+SOURCES = ["mnb_gemv_f32.hip", "mnb_gemv_bf16.hip", "mnb_gemm.hip", "mnb_gemv.hip", "mnb_api.hip", "mnb_pack.hip",
+           "mnb_smallm.hip", "mnb_aux.hip", "mnb_step.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -58,7 +60,7 @@ def build(verbose: bool = False) -> str:
         if src != PROBE_SOURCE:
             objs.append(obj)
         cmds.append([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-    with cf.ThreadPoolExecutor(max_workers=min(len(cmds), 4)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4, 8)) as ex:
         for log in ex.map(_run, cmds):
             if verbose and log.strip():
                 print(log, file=sys.stderr)

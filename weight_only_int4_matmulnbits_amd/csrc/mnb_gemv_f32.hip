@@ -1,0 +1,14 @@
+// The decode GEMV's float32 instances (the kernel is in mnb_gemv_kernel.h).
+#include "mnb_gemv_kernel.h"
+
+namespace mnb {
+
+GemvFn gemv_pick_f32(bool has_zp, bool has_bias, int CB, int J, int W, bool silu, bool rms, bool nts) {
+    return pick_type<false>(has_zp, has_bias, CB, J, W, silu, rms, nts);
+}
+
+GemvFn gemv_pick_rows_f32(bool has_zp, bool has_bias, int MR, int J, int W, bool nts) {
+    return pick_rows_type<false>(has_zp, has_bias, MR, J, W, nts);
+}
+
+}  // namespace mnb
