@@ -753,19 +753,31 @@ def traffic_from(fetch_dir, write_dir, cfg, copy_mib, kind="gemv"):
     kernel of the same run.  Updates profiles/traffic.json (with the hash of
     the kernel sources the counters were taken with) and returns the text."""
     import hashlib
+    from workloads import workload
+    w = workload(cfg)
     known = copy_mib << 20
     res, lines = {}, []
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _read_csv(os.path.join(d, "run_counter_collection.csv")) if r["Counter_Name"] == name]
         cal = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        lib = [float(r["Counter_Value"]) for r in _library_rows(rows)]
+        lib_rows = _library_rows(rows)
+        lib = [float(r["Counter_Value"]) for r in lib_rows]
         factor = known / (max(cal) * 1024.0)
-        per = sum(lib) / len(lib) * 1024.0 * factor
+        if w.M == 1:
+            # decode: one dispatch per launch of the step
+            n_units, unit = len(lib), "dispatch"
+        else:
+            # prefill: a projection is its product kernel plus any split-K or
+            # tail reduction (and gated-row) dispatches; count the products
+            n_units = sum(1 for r in lib_rows if "reduce" not in r["Kernel_Name"]
+                          and "silu_mul_rows" not in r["Kernel_Name"])
+            unit = "projection"
+        per = sum(lib) / n_units * 1024.0 * factor
         res[name] = (per, factor)
+        over = "" if w.M == 1 else f" over {n_units} {unit}s"
         lines.append(f"{name}: copy of {copy_mib} MiB: counter {max(cal):.1f} KiB -> factor {factor:.3f}; "
-                     f"{len(lib)} dispatches, {sum(lib) / len(lib):.1f} KiB raw -> {per / 1e6:.4f} MB per dispatch")
-    from workloads import workload
-    w = workload(cfg)
+                     f"{len(lib)} dispatches{over}, {sum(lib) / n_units:.1f} KiB raw -> "
+                     f"{per / 1e6:.4f} MB per {unit}")
     tot = res["FETCH_SIZE"][0] + res["WRITE_SIZE"][0]
     if w.M == 1:
         alg = w.step_weight_bytes() / len(w.launches)
@@ -775,8 +787,8 @@ def traffic_from(fetch_dir, write_dir, cfg, copy_mib, kind="gemv"):
         # a prefill projection must read A and the packed weight once and write Y once
         esz = 4 if w.act_dtype == "f32" else 2
         alg = sum(w.weight_bytes(L) + esz * w.M * (L.K + L.N) for L in w.launches) / len(w.launches)
-        lines.append(f"HBM traffic per dispatch {tot / 1e6:.4f} MB; per projection the minimum "
-                     f"(A + packed weight read once, Y written once) averages {alg / 1e6:.4f} MB")
+        lines.append(f"HBM traffic per projection {tot / 1e6:.4f} MB (reductions included) vs the minimum "
+                     f"(A + packed weight read once, Y written once) {alg / 1e6:.4f} MB ({tot / alg:.3f}x)")
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -803,11 +815,12 @@ def traffic_from(fetch_dir, write_dir, cfg, copy_mib, kind="gemv"):
                            "write_bytes_per_launch": res["WRITE_SIZE"][0], "fetch_factor": res["FETCH_SIZE"][1],
                            "write_factor": res["WRITE_SIZE"][1]}
     rec[kind] = ent
-    rec["note"] = ("HBM bytes per library dispatch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs "
-                   "(KiB per dispatch, averaged over the run's dispatches), each scaled by known bytes / the "
-                   "counter's reading for one plain device-to-device copy (__amd_rocclr_copyBuffer) in the same "
-                   "run.  Valid only while the kernel sources hash to kernel_sha256; written by "
-                   "bench.py --traffic-from.")
+    rec["note"] = ("HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs (KiB per "
+                   "dispatch summed over the run and divided by its decode dispatches, or by its prefill "
+                   "projections, whose split-K and tail reductions count with them), each scaled by known "
+                   "bytes / the counter's reading for one plain device-to-device copy "
+                   "(__amd_rocclr_copyBuffer) in the same run.  Valid only while the kernel sources hash to "
+                   "kernel_sha256; written by bench.py --traffic-from.")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     return "\n".join(lines)
