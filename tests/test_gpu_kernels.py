@@ -258,6 +258,23 @@ def test_fused_launch_bit_identical_to_separate(M):
         assert torch.equal(pp.matmul(a), yf[:, perm])
 
 
+@pytest.mark.parametrize("K,bs,dt,zp,bias,N", [(2560, 128, "f32", True, True, 131072 + 37),
+                                                (2560, 128, "bf16", False, False, 131072 + 37),
+                                                (4096, 64, "f32", True, False, 40000)])
+def test_wide_gemv_bit_identical_to_narrow_launches(K, bs, dt, zp, bias, N):
+    """A one-row launch over so many columns that its teams each walk many
+    column groups (an LM head) holds the activations in registers; narrow
+    launches read them from LDS chunk by chunk.  Both add the same values in
+    the same order, so every column has the same bits."""
+    log(f"wide vs narrow gemv K={K} bs={bs} {dt} N={N}")
+    inp, g = _inputs(K, N, 1, bs, dt, zp, bias, seed=K + N)
+    y = _packed(g, bs).matmul(g.a)
+    for lo, hi in [(0, 1000), (N - 517, N), (N // 2, N // 2 + 64)]:
+        part = mnb.PackedWeight.from_logical(g.q[lo:hi], g.scales[lo:hi], g.zp[lo:hi] if zp else None,
+                                             g.bias[lo:hi] if bias else None, block_size=bs)
+        assert torch.equal(part.matmul(g.a), y[:, lo:hi]), (lo, hi)
+
+
 @pytest.mark.parametrize("M", [1, 20])
 def test_pad_nibbles_do_not_matter(M):
     K, N, bs = 100, 33, 64          # partial last block (36 of 64 values)

@@ -8,9 +8,9 @@ namespace {
 
 constexpr size_t kMaxLds = kGemvMaxLds;
 
-GemvFn pick(bool bf16, bool has_zp, bool has_bias, int CB, int J, int W, bool silu, bool rms, bool nts) {
-    return bf16 ? gemv_pick_bf16(has_zp, has_bias, CB, J, W, silu, rms, nts)
-                : gemv_pick_f32(has_zp, has_bias, CB, J, W, silu, rms, nts);
+GemvFn pick(bool bf16, bool has_zp, bool has_bias, int CB, int J, int W, bool silu, int input, bool nts) {
+    return bf16 ? gemv_pick_bf16(has_zp, has_bias, CB, J, W, silu, input, nts)
+                : gemv_pick_f32(has_zp, has_bias, CB, J, W, silu, input, nts);
 }
 
 GemvFn pick_rows(bool bf16, bool has_zp, bool has_bias, int MR, int J, int W, bool nts) {
@@ -141,10 +141,25 @@ int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1, const void* g
     // lines, which stay cached (non-temporal scales slowed the 4B step 3 %).
     // (RMSNorm: exactly with 8-byte chunks, the instances there are)
     const bool nts = gamma ? CB != 16 : p.bs <= 32;
-    const bool actl = MR == 1 && !gamma && geo.J > 1;
-    GemvFn f = MR == 1 ? pick(p.bf16, p.has_zp, p.bias != nullptr, CB, geo.J, geo.W, silu, gamma != nullptr, nts)
+    bool actl = MR == 1 && !gamma && geo.J > 1;
+    GemvFn f = MR == 1 ? pick(p.bf16, p.has_zp, p.bias != nullptr, CB, geo.J, geo.W, silu,
+                              gamma ? kInputRms : kInputLds, nts)
                        : pick_rows(p.bf16, p.has_zp, p.bias != nullptr, MR, geo.J, geo.W, nts);
     if (!f) return fail(MNB_E_UNSUPPORTED, "gemv: no kernel for J=%d W=%d", geo.J, geo.W);
+    // A launch whose resident teams would each walk more than four column
+    // groups (the LM heads) reads its activations once into registers: read
+    // from LDS per chunk they would be read again for every group (the 4B LM
+    // head 49.0 us that way, 43.2 us with registers).
+    if (actl && !silu && nts == (CB != 16)) {
+        const int64_t resident_teams = cus * resident_per_cu(f, lds) * teams_per_block;
+        if (a.n_groups > 4 * resident_teams) {
+            const GemvFn fr = pick(p.bf16, p.has_zp, p.bias != nullptr, CB, geo.J, geo.W, false, kInputRegs, nts);
+            if (fr) {
+                f = fr;
+                actl = false;
+            }
+        }
+    }
     const int64_t teams = a.n_groups;
     int64_t blocks = (teams + teams_per_block - 1) / teams_per_block;
     int64_t max_blocks = cus * resident_per_cu(f, lds);

@@ -3,8 +3,8 @@
 
 namespace mnb {
 
-GemvFn gemv_pick_f32(bool has_zp, bool has_bias, int CB, int J, int W, bool silu, bool rms, bool nts) {
-    return pick_type<false>(has_zp, has_bias, CB, J, W, silu, rms, nts);
+GemvFn gemv_pick_f32(bool has_zp, bool has_bias, int CB, int J, int W, bool silu, int input, bool nts) {
+    return pick_type<false>(has_zp, has_bias, CB, J, W, silu, input, nts);
 }
 
 GemvFn gemv_pick_rows_f32(bool has_zp, bool has_bias, int MR, int J, int W, bool nts) {

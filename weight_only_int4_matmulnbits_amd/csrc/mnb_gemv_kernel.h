@@ -64,12 +64,17 @@ struct GemvArgs {
 
 using GemvFn = void (*)(GemvArgs);
 
+// How the one-row kernel takes its activations: read from the staged row in
+// LDS chunk by chunk where a lane holds several chunks (else registers), held
+// in registers for all columns, or held in registers RMS-normalized.
+enum GemvInput { kInputLds = 0, kInputRegs = 1, kInputRms = 2 };
+
 // The kernel for one activation type (defined once per type, in
 // mnb_gemv_f32.hip and mnb_gemv_bf16.hip): one row (silu: gated gate||up;
-// rms: RMSNorm fused into the input) or MR rows; nullptr where no kernel
-// has that shape.  nts: scales, zero points and bias read non-temporally.
-GemvFn gemv_pick_f32(bool has_zp, bool has_bias, int CB, int J, int W, bool silu, bool rms, bool nts);
-GemvFn gemv_pick_bf16(bool has_zp, bool has_bias, int CB, int J, int W, bool silu, bool rms, bool nts);
+// input: a GemvInput) or MR rows; nullptr where no kernel has that shape.
+// nts: scales, zero points and bias read non-temporally.
+GemvFn gemv_pick_f32(bool has_zp, bool has_bias, int CB, int J, int W, bool silu, int input, bool nts);
+GemvFn gemv_pick_bf16(bool has_zp, bool has_bias, int CB, int J, int W, bool silu, int input, bool nts);
 GemvFn gemv_pick_rows_f32(bool has_zp, bool has_bias, int MR, int J, int W, bool nts);
 GemvFn gemv_pick_rows_bf16(bool has_zp, bool has_bias, int MR, int J, int W, bool nts);
 
@@ -196,17 +201,20 @@ __device__ __forceinline__ void load_group(const GemvArgs& g, int64_t gi, int64_
 // (ACTL) reads each chunk's values from the staged copy in LDS as the chunk
 // is reduced, one chunk ahead of its use, which leaves room for more
 // resident wavefronts (144 instead of 236 VGPRs at five float32 chunks per
-// lane).  The row kernel, RMS (normalized once) and one chunk per lane (no
-// next chunk to read ahead, and few registers anyway) hold the lane's chunks
-// in registers for all columns.
-template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, int W, bool SILU, int MR, bool NTS, bool RMS>
+// lane).  The row kernel, RMS (normalized once), one chunk per lane (no next
+// chunk to read ahead, and few registers anyway) and REGS (launches with
+// many column groups per team, where the LDS reads would repeat for every
+// group) hold the lane's chunks in registers for all columns.
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, int W, bool SILU, int MR, bool NTS, bool RMS,
+          bool REGS>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     constexpr int CK = 2 * CB;        // values of K per chunk
     constexpr int NW = CB / 4;        // 32-bit words per chunk
     constexpr int TEAMS = kWavesPerBlock / W;
     static_assert(MR == 1 || (!SILU && J * MR <= 4 && CB == 16), "row kernel: <= 4 row chunks");
     static_assert(!RMS || (MR == 1 && !SILU), "RMSNorm: one row, plain epilogue");
-    constexpr bool ACTL = MR == 1 && !RMS && J > 1;
+    static_assert(!REGS || (MR == 1 && !SILU && !RMS && J > 1), "register input: the plain one-row kernel");
+    constexpr bool ACTL = MR == 1 && !RMS && !REGS && J > 1;
     __shared__ float red[kWavesPerBlock * MR];
 
     const int lane = threadIdx.x & 63;
@@ -558,37 +566,43 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
 
 
 // ---- kernel choice for one activation type ----
-// (the plain and the gated kernel at every geometry; RMSNorm with the
-// scale policy the launcher gives it: non-temporal exactly for 8-byte chunks)
+// (the plain and the gated kernel at every geometry; RMSNorm and the
+// register-held input with the scale policy the launcher gives them:
+// non-temporal exactly for 8-byte chunks)
 
-template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, bool SILU, bool NTS, bool RMS>
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, bool SILU, bool NTS, bool RMS, bool REGS>
 GemvFn pick_js(int W) {
-    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, SILU, 1, NTS, RMS>;
+    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, SILU, 1, NTS, RMS, REGS>;
     if constexpr (CB == 16) {
-        if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 2, SILU, 1, NTS, RMS>;
-        if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 4, SILU, 1, NTS, RMS>;
+        if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 2, SILU, 1, NTS, RMS, REGS>;
+        if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 4, SILU, 1, NTS, RMS, REGS>;
     }
     return nullptr;
 }
 
 template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, bool NTS>
-GemvFn pick_j(int W, bool silu, bool rms) {
-    if (silu) return pick_js<BF16, HAS_ZP, HAS_BIAS, CB, J, true, NTS, false>(W);
-    if (rms) {
-        if constexpr (NTS == (CB != 16)) return pick_js<BF16, HAS_ZP, HAS_BIAS, CB, J, false, NTS, true>(W);
+GemvFn pick_j(int W, bool silu, int input) {
+    if (silu) return pick_js<BF16, HAS_ZP, HAS_BIAS, CB, J, true, NTS, false, false>(W);
+    if (input == kInputRms) {
+        if constexpr (NTS == (CB != 16)) return pick_js<BF16, HAS_ZP, HAS_BIAS, CB, J, false, NTS, true, false>(W);
         return nullptr;
     }
-    return pick_js<BF16, HAS_ZP, HAS_BIAS, CB, J, false, NTS, false>(W);
+    if (input == kInputRegs) {
+        if constexpr (J > 1 && NTS == (CB != 16))
+            return pick_js<BF16, HAS_ZP, HAS_BIAS, CB, J, false, NTS, false, true>(W);
+        return nullptr;
+    }
+    return pick_js<BF16, HAS_ZP, HAS_BIAS, CB, J, false, NTS, false, false>(W);
 }
 
 template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, bool NTS>
-GemvFn pick_cb(int J, int W, bool silu, bool rms) {
+GemvFn pick_cb(int J, int W, bool silu, int input) {
     switch (J) {
-        case 1: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 1, NTS>(W, silu, rms);
-        case 2: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 2, NTS>(W, silu, rms);
-        case 3: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 3, NTS>(W, silu, rms);
-        case 4: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 4, NTS>(W, silu, rms);
-        case 5: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 5, NTS>(W, silu, rms);
+        case 1: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 1, NTS>(W, silu, input);
+        case 2: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 2, NTS>(W, silu, input);
+        case 3: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 3, NTS>(W, silu, input);
+        case 4: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 4, NTS>(W, silu, input);
+        case 5: return pick_j<BF16, HAS_ZP, HAS_BIAS, CB, 5, NTS>(W, silu, input);
         default: return nullptr;
     }
 }
@@ -596,26 +610,26 @@ GemvFn pick_cb(int J, int W, bool silu, bool rms) {
 // 8-byte chunks come with 16-value blocks only, where the small loads are
 // always non-temporal
 template <bool BF16, bool HAS_ZP, bool HAS_BIAS>
-GemvFn pick_b(int CB, int J, int W, bool silu, bool rms, bool nts) {
-    if (CB != 16) return pick_cb<BF16, HAS_ZP, HAS_BIAS, 8, true>(J, W, silu, rms);
-    return nts ? pick_cb<BF16, HAS_ZP, HAS_BIAS, 16, true>(J, W, silu, rms)
-               : pick_cb<BF16, HAS_ZP, HAS_BIAS, 16, false>(J, W, silu, rms);
+GemvFn pick_b(int CB, int J, int W, bool silu, int input, bool nts) {
+    if (CB != 16) return pick_cb<BF16, HAS_ZP, HAS_BIAS, 8, true>(J, W, silu, input);
+    return nts ? pick_cb<BF16, HAS_ZP, HAS_BIAS, 16, true>(J, W, silu, input)
+               : pick_cb<BF16, HAS_ZP, HAS_BIAS, 16, false>(J, W, silu, input);
 }
 
 template <bool BF16>
-GemvFn pick_type(bool has_zp, bool has_bias, int CB, int J, int W, bool silu, bool rms, bool nts) {
-    if (has_zp) return has_bias ? pick_b<BF16, true, true>(CB, J, W, silu, rms, nts)
-                                : pick_b<BF16, true, false>(CB, J, W, silu, rms, nts);
-    return has_bias ? pick_b<BF16, false, true>(CB, J, W, silu, rms, nts)
-                    : pick_b<BF16, false, false>(CB, J, W, silu, rms, nts);
+GemvFn pick_type(bool has_zp, bool has_bias, int CB, int J, int W, bool silu, int input, bool nts) {
+    if (has_zp) return has_bias ? pick_b<BF16, true, true>(CB, J, W, silu, input, nts)
+                                : pick_b<BF16, true, false>(CB, J, W, silu, input, nts);
+    return has_bias ? pick_b<BF16, false, true>(CB, J, W, silu, input, nts)
+                    : pick_b<BF16, false, false>(CB, J, W, silu, input, nts);
 }
 
 // MR rows of A (block >= 32, so 16-byte chunks), J * MR <= 4
 template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int MR, int J, bool NTS>
 GemvFn pick_rows_j(int W) {
-    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 1, false, MR, NTS, false>;
-    if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 2, false, MR, NTS, false>;
-    if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 4, false, MR, NTS, false>;
+    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 1, false, MR, NTS, false, false>;
+    if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 2, false, MR, NTS, false, false>;
+    if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 4, false, MR, NTS, false, false>;
     return nullptr;
 }
 
