@@ -164,7 +164,13 @@ int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1, const void* g
     int64_t blocks = (teams + teams_per_block - 1) / teams_per_block;
     int64_t max_blocks = cus * resident_per_cu(f, lds);
     if (!actl && max_blocks > 2 * cus && 2 * teams <= 5 * (2 * cus * teams_per_block)) max_blocks = 2 * cus;
-    if (blocks > max_blocks) blocks = max_blocks;
+    // The LDS-reading kernel gives every team one column group where that
+    // takes at most twice the resident workgroups (the rest start as the
+    // first ones finish): the 4B gate||up, 1.6 groups per resident team,
+    // made the step 0.4 % faster so; the same grid with two groups for every
+    // team (fewer workgroups, each walking the same number of groups) made
+    // it 4 % slower.
+    if (blocks > max_blocks && !(actl && blocks <= 2 * max_blocks)) blocks = max_blocks;
     hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(64 * kGemvWavesPerBlock), lds, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MNB_E_HIP, "gemv launch: %s", hipGetErrorString(e));
