@@ -60,3 +60,22 @@ def test_gemv_rmsnorm_exact_invariants():
     assert torch.equal(y1, y4)
     z = mnb.gemv_rmsnorm(torch.zeros_like(g.a), gamma, 1e-6, pw.b_packed, pw.scales, pw.zp_packed, pw.bias, **kw)
     assert torch.equal(z[0], pw.bias)
+
+
+@pytest.mark.parametrize("K,N,bs,dt", [(2560, 131072 + 37, 128, "f32"), (4096, 40000, 64, "bf16")])
+def test_wide_rmsnorm_gemv_bit_identical_to_narrow_launches(K, N, bs, dt):
+    """The columns of a wide launch (teams walking many column groups, grids
+    past the resident workgroups) have the bits of the same columns in
+    narrow launches: the normalization and the summation order depend on
+    (K, block_size) only."""
+    log(f"wide vs narrow rmsnorm gemv {dt} K={K} N={N} bs={bs}")
+    inp = random_inputs(K, N, 1, bs, dt, True, False, seed=K + 3)
+    g = inp.to(DEV)
+    gamma = _gamma(K, dt, K + 1).to(DEV)
+    pw = mnb.PackedWeight.from_logical(g.q, g.scales, g.zp, None, block_size=bs)
+    y = mnb.gemv_rmsnorm(g.a, gamma, 1e-6, pw.b_packed, pw.scales, pw.zp_packed, None, K=K, N=N, block_size=bs)
+    for lo, hi in [(0, 1000), (N - 517, N)]:
+        part = mnb.PackedWeight.from_logical(g.q[lo:hi], g.scales[lo:hi], g.zp[lo:hi], None, block_size=bs)
+        yp = mnb.gemv_rmsnorm(g.a, gamma, 1e-6, part.b_packed, part.scales, part.zp_packed, None,
+                              K=K, N=hi - lo, block_size=bs)
+        assert torch.equal(yp, y[:, lo:hi]), (lo, hi)
