@@ -260,12 +260,14 @@ def test_fused_launch_bit_identical_to_separate(M):
 
 @pytest.mark.parametrize("K,bs,dt,zp,bias,N", [(2560, 128, "f32", True, True, 131072 + 37),
                                                 (2560, 128, "bf16", False, False, 131072 + 37),
-                                                (4096, 64, "f32", True, False, 40000)])
+                                                (4096, 64, "f32", True, False, 40000),
+                                                (12288, 128, "f32", True, True, 3001)])
 def test_wide_gemv_bit_identical_to_narrow_launches(K, bs, dt, zp, bias, N):
     """A one-row launch over so many columns that its teams each walk many
     column groups (an LM head) holds the activations in registers; narrow
     launches read them from LDS chunk by chunk.  Both add the same values in
-    the same order, so every column has the same bits."""
+    the same order, so every column has the same bits.  K = 12288: split-K
+    teams of two wavefronts on a grid past the resident workgroups."""
     log(f"wide vs narrow gemv K={K} bs={bs} {dt} N={N}")
     inp, g = _inputs(K, N, 1, bs, dt, zp, bias, seed=K + N)
     y = _packed(g, bs).matmul(g.a)
