@@ -189,13 +189,14 @@ size_t mnb_workspace_bytes(const mnb_desc* d, int64_t M);
  * (block_size >= 32, K * element size a multiple of 16; K up to 8192 for
  * two rows and 4096 for three or four with float32 activations, twice that
  * with bfloat16) go through the decode GEMV: each unpacked weight feeds one
- * float32 FMA per row.  Otherwise 1 <= M <= 16 (K % 32 == 0,
- * block_size >= 32, K up to 3072 for float32 and 4096 for bfloat16
- * activations) take a matrix-core kernel: the exact integers (q - zp) meet
- * the activations (float32 as bf16 head + tail) and each 32-value partial
- * sum is scaled in float32.  In both, as in mnb_gemv, a column's float32
- * summation order depends only on K (and the row count class), so
- * concatenated launches are bit-identical to separate ones. */
+ * float32 FMA per row; but N > 32768 (an LM head), where the matrix-core
+ * kernel takes the shape, goes there.  Otherwise 1 <= M <= 16 (K % 32 == 0,
+ * block_size >= 32) take a matrix-core kernel: the exact integers (q - zp)
+ * meet the activations (float32 as bf16 head + tail) and each 32-value
+ * partial sum is scaled in float32.  In both, as in mnb_gemv, a column's
+ * float32 summation order depends only on K (and the row count class), so
+ * concatenated launches are bit-identical to separate ones (at 2 <= M <= 4,
+ * launches on the same side of N = 32768). */
 int mnb_gemm(const mnb_desc* d, int64_t M, const void* a,
              const uint8_t* b_packed, const void* scales,
              const uint8_t* zp_packed, const float* bias, void* y,

@@ -183,6 +183,12 @@ int launch_gemv(const Problem& p, hipStream_t s) { return launch(p, s, false); }
 
 bool gemv_rows_ok(const Problem& p) {
     if (p.M < 2 || p.M > 4 || p.bs < 32) return false;
+    // The LM heads (more than 32768 columns; every per-layer projection of
+    // these models has at most 19456) go to the matrix-core kernel where it
+    // takes them: there the row kernel's teams walk dozens of column groups
+    // each, and the 0.6B step at 4 rows took 0.588 instead of 0.610 ms so
+    // (its LM head 62 us in the row kernel, about 39 us on the matrix cores).
+    if (p.N > 32768 && smallm_ok(p)) return false;
     const int esz = p.bf16 ? 2 : 4;
     if ((p.K * esz) % 16 != 0 || p.M * p.K * esz >= (int64_t(1) << 31))
         return false;

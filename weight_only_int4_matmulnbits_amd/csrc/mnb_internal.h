@@ -37,7 +37,8 @@ int launch_pack(int64_t K, int64_t N, int bs, const uint8_t* q,
 int launch_dequant(const Problem& p, int out_kind, void* w, hipStream_t s);
 int launch_gemv(const Problem& p, hipStream_t s);
 // 2 <= M <= 4 rows through the decode GEMV (each weight unpacked once for all
-// rows) when the shape allows it (gemv_rows_ok); launch_gemm takes it then.
+// rows) when the shape allows it and is no LM head (gemv_rows_ok);
+// launch_gemm takes it then.
 bool gemv_rows_ok(const Problem& p);
 int launch_gemv_rows(const Problem& p, hipStream_t s);
 // p.N = 2 * half: the gate half then the up half; y [half] = silu(gate) * up.
