@@ -123,8 +123,9 @@ int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1, const void* g
     // Fill the chip with resident teams of W wavefronts (the kernel's real
     // occupancy), one column group per team per iteration: unrolling several
     // groups per iteration costs more in occupancy than it saves.  For the
-    // kernels that hold activations in registers (rows, RMSNorm): when two
-    // workgroups per CU already leave each team at most 2.5 groups, use only
+    // kernels that hold activations in registers (rows, RMSNorm, one chunk
+    // per lane, the LM heads): when two workgroups per CU already leave each
+    // team at most 2.5 groups, use only
     // those (a team with two groups has the second in flight while it
     // reduces the first, 2-7 % faster on the few-MB decode projections).  The
     // one-row kernel that reads them from LDS (several chunks per lane) fills
@@ -149,7 +150,7 @@ int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1, const void* g
     // A launch whose resident teams would each walk more than four column
     // groups (the LM heads) reads its activations once into registers: read
     // from LDS per chunk they would be read again for every group (the 4B LM
-    // head 49.0 us that way, 43.2 us with registers).
+    // head, cold, 49.5 us that way and 43.9 us with registers on one box).
     if (actl && !silu && nts == (CB != 16)) {
         const int64_t resident_teams = cus * resident_per_cu(f, lds) * teams_per_block;
         if (a.n_groups > 4 * resident_teams) {
