@@ -163,6 +163,20 @@ int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1, const void* g
     }
     const int64_t teams = a.n_groups;
     int64_t blocks = (teams + teams_per_block - 1) / teams_per_block;
+    // Where one column group per team takes at most twice the workgroups
+    // that the single-stage kernel keeps resident (every per-layer decode
+    // projection), that kernel on that grid: with the registers of the second
+    // stage free, more workgroups are resident and each team's loads go out
+    // at once (the 4B decode step 0.908 -> 0.828 ms, the 0.6B step 0.379 ->
+    // 0.365 ms on one box; the 4B gate||up's 1216 workgroups all resident).
+    bool one = false;
+    if (actl && !silu) {
+        const GemvFn f1 = pick(p.bf16, p.has_zp, p.bias != nullptr, CB, geo.J, geo.W, false, kInputLdsOne, nts);
+        if (f1 && blocks <= 2 * cus * resident_per_cu(f1, lds)) {
+            f = f1;
+            one = true;
+        }
+    }
     int64_t max_blocks = cus * resident_per_cu(f, lds);
     if (!actl && max_blocks > 2 * cus && 2 * teams <= 5 * (2 * cus * teams_per_block)) max_blocks = 2 * cus;
     // The LDS-reading kernel gives every team one column group where that
@@ -171,7 +185,7 @@ int launch(const Problem& p, hipStream_t s, bool silu, int MR = 1, const void* g
     // made the step 0.4 % faster so; the same grid with two groups for every
     // team (fewer workgroups, each walking the same number of groups) made
     // it 4 % slower.
-    if (blocks > max_blocks && !(actl && blocks <= 2 * max_blocks)) blocks = max_blocks;
+    if (!one && blocks > max_blocks && !(actl && blocks <= 2 * max_blocks)) blocks = max_blocks;
     hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(64 * kGemvWavesPerBlock), lds, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MNB_E_HIP, "gemv launch: %s", hipGetErrorString(e));

@@ -65,9 +65,11 @@ struct GemvArgs {
 using GemvFn = void (*)(GemvArgs);
 
 // How the one-row kernel takes its activations: read from the staged row in
-// LDS chunk by chunk where a lane holds several chunks (else registers), held
-// in registers for all columns, or held in registers RMS-normalized.
-enum GemvInput { kInputLds = 0, kInputRegs = 1, kInputRms = 2 };
+// LDS chunk by chunk where a lane holds several chunks (else registers; a
+// form with a single register stage, for grids that give every team at
+// most one column group), held in registers for all columns, or held in
+// registers RMS-normalized.
+enum GemvInput { kInputLds = 0, kInputRegs = 1, kInputRms = 2, kInputLdsOne = 3 };
 
 // The kernel for one activation type (defined once per type, in
 // mnb_gemv_f32.hip and mnb_gemv_bf16.hip): one row (silu: gated gate||up;
@@ -205,8 +207,11 @@ __device__ __forceinline__ void load_group(const GemvArgs& g, int64_t gi, int64_
 // chunk to read ahead, and few registers anyway) and REGS (launches with
 // many column groups per team, where the LDS reads would repeat for every
 // group) hold the lane's chunks in registers for all columns.
+// ONE: the LDS-reading kernel on a grid that gives every team at most one
+// column group: no second register stage (90 instead of 144 VGPRs at five
+// float32 chunks per lane, five workgroups per CU instead of three).
 template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, int W, bool SILU, int MR, bool NTS, bool RMS,
-          bool REGS>
+          bool REGS, bool ONE>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     constexpr int CK = 2 * CB;        // values of K per chunk
     constexpr int NW = CB / 4;        // 32-bit words per chunk
@@ -215,6 +220,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     static_assert(!RMS || (MR == 1 && !SILU), "RMSNorm: one row, plain epilogue");
     static_assert(!REGS || (MR == 1 && !SILU && !RMS && J > 1), "register input: the plain one-row kernel");
     constexpr bool ACTL = MR == 1 && !RMS && !REGS && J > 1;
+    static_assert(!ONE || (ACTL && !SILU), "one group per team: the plain LDS-reading kernel");
     __shared__ float red[kWavesPerBlock * MR];
 
     const int lane = threadIdx.x & 63;
@@ -306,11 +312,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
     // only if this team has one), or (gated) the gate and the up group of
     // the first iteration
     Group<BF16, HAS_ZP, CB, J> g0, g1;
-    const bool two = SILU || base + stride < g.n_groups;     // wave-uniform
+    const bool two = !ONE && (SILU || base + stride < g.n_groups);     // wave-uniform
     load_group<BF16, HAS_ZP, HAS_BIAS, CB, J, NTS>(g, base, 0, width, p, LT, G, gsub, g0);
-    if (two)
-        load_group<BF16, HAS_ZP, HAS_BIAS, CB, J, NTS>(g, SILU ? base : base + stride, SILU ? g.half : 0, width, p,
-                                                  LT, G, gsub, g1);
+    if constexpr (!ONE) {
+        if (two)
+            load_group<BF16, HAS_ZP, HAS_BIAS, CB, J, NTS>(g, SILU ? base : base + stride, SILU ? g.half : 0, width,
+                                                      p, LT, G, gsub, g1);
+    }
 
     // wait for this wavefront's staging (all memory instructions but the
     // weight loads just issued, and the LDS writes), then meet the others.
@@ -546,6 +554,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
         // it0 is WG-uniform, so the barriers of split-K teams are reached by
         // all.  No exit between the halves (it would cost precise waits): the
         // second half past the end loads zeros and skips its work.
+        if constexpr (ONE) {
+            // every team has at most one column group (the grid covers them all)
+            float acc[MR];
+            reduce(g0, acc);
+            store(g0, acc, base);
+            return;
+        }
         for (int64_t it0 = team0; it0 < g.n_groups; it0 += 2 * stride, base += 2 * stride) {
             float acc[MR];
             reduce(g0, acc);
@@ -570,12 +585,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void gemv_kernel(GemvArgs g) {
 // register-held input with the scale policy the launcher gives them:
 // non-temporal exactly for 8-byte chunks)
 
-template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, bool SILU, bool NTS, bool RMS, bool REGS>
+template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int CB, int J, bool SILU, bool NTS, bool RMS, bool REGS,
+          bool ONE = false>
 GemvFn pick_js(int W) {
-    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, SILU, 1, NTS, RMS, REGS>;
+    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 1, SILU, 1, NTS, RMS, REGS, ONE>;
     if constexpr (CB == 16) {
-        if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 2, SILU, 1, NTS, RMS, REGS>;
-        if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 4, SILU, 1, NTS, RMS, REGS>;
+        if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 2, SILU, 1, NTS, RMS, REGS, ONE>;
+        if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, CB, J, 4, SILU, 1, NTS, RMS, REGS, ONE>;
     }
     return nullptr;
 }
@@ -585,6 +601,10 @@ GemvFn pick_j(int W, bool silu, int input) {
     if (silu) return pick_js<BF16, HAS_ZP, HAS_BIAS, CB, J, true, NTS, false, false>(W);
     if (input == kInputRms) {
         if constexpr (NTS == (CB != 16)) return pick_js<BF16, HAS_ZP, HAS_BIAS, CB, J, false, NTS, true, false>(W);
+        return nullptr;
+    }
+    if (input == kInputLdsOne) {
+        if constexpr (J > 1) return pick_js<BF16, HAS_ZP, HAS_BIAS, CB, J, false, NTS, false, false, true>(W);
         return nullptr;
     }
     if (input == kInputRegs) {
@@ -627,9 +647,9 @@ GemvFn pick_type(bool has_zp, bool has_bias, int CB, int J, int W, bool silu, in
 // MR rows of A (block >= 32, so 16-byte chunks), J * MR <= 4
 template <bool BF16, bool HAS_ZP, bool HAS_BIAS, int MR, int J, bool NTS>
 GemvFn pick_rows_j(int W) {
-    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 1, false, MR, NTS, false, false>;
-    if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 2, false, MR, NTS, false, false>;
-    if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 4, false, MR, NTS, false, false>;
+    if (W == 1) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 1, false, MR, NTS, false, false, false>;
+    if (W == 2) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 2, false, MR, NTS, false, false, false>;
+    if (W == 4) return gemv_kernel<BF16, HAS_ZP, HAS_BIAS, 16, J, 4, false, MR, NTS, false, false, false>;
     return nullptr;
 }
 
